@@ -1,0 +1,22 @@
+"""CPU oracle for the integer motion and PSNR sums (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import this package. The GPU
+library never does, and this package never imports the GPU library: the two share no code.
+
+`iir_oracle.c` holds the arithmetic; `oracle.py` builds it with gcc and marshals numpy arrays.
+"""
+from .oracle import (  # noqa: F401
+    SOURCE,
+    OracleError,
+    OracleLib,
+    blur,
+    build,
+    clip,
+    compile_source,
+    default,
+    library_path,
+    sad,
+    scores,
+    sse,
+    taps,
+)

@@ -1,0 +1,348 @@
+"""Pins that tie the CPU oracle to facts fixed outside its own code.
+
+Each ``pin_*`` function takes a loaded oracle (``oracle.OracleLib``) and raises AssertionError when
+the oracle disagrees with a brute-force evaluation, a library routine, a closed form or an
+invariant. ``test_oracle_pins.py`` runs them on the real oracle; ``test_oracle_mutants.py`` runs
+them on deliberately broken copies and requires every copy to fail at least one pin.
+
+Readings of the pages used here (the pages fix none of the three numerically):
+  * taps (3571, 16004, 26386, 16004, 3571), sum 2^16 (sigma = 1 sampled Gaussian);
+  * round half up at both shifts (>> bpc after the vertical pass, >> 16 after the horizontal);
+  * whole-sample mirror at the edges (numpy 'reflect' == scipy.ndimage 'mirror').
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import scipy.ndimage as ndi
+
+TAPS = (3571, 16004, 26386, 16004, 3571)
+SIZES = [(3, 3), (4, 7), (9, 5), (17, 23), (32, 32), (5, 64), (70, 3)]
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _planes(bpc, seed, sizes=SIZES):
+    r = _rng(seed)
+    peak = (1 << bpc) - 1
+    dt = np.uint8 if bpc == 8 else np.uint16
+    out = []
+    for h, w in sizes:
+        out.append(r.integers(0, peak + 1, size=(h, w)).astype(dt))
+        yy, xx = np.mgrid[0:h, 0:w]
+        out.append((((yy + xx) % 2) * peak).astype(dt))
+        out.append((r.integers(0, 2, size=(h, w)) * peak).astype(dt))
+    return out
+
+
+def brute_force_blur(x: np.ndarray, bpc: int) -> np.ndarray:
+    """25 multiply-adds per output: for each of the 5 columns of the output's 5x5 window, its own
+    vertical 5-tap sum rounded by the bit depth, then the 5 horizontal taps rounded by 16. The edge
+    mirror comes from numpy's whole-sample 'reflect' padding, not from the oracle's index rule."""
+    h, w = x.shape
+    xp = np.pad(x.astype(np.int64), 2, mode="reflect")
+    g = np.array(TAPS, dtype=np.int64)
+    out = np.zeros((h, w), dtype=np.int64)
+    for l in range(5):
+        v = np.zeros((h, w), dtype=np.int64)
+        for k in range(5):
+            v += g[k] * xp[k:k + h, l:l + w]
+        v = (v + (1 << (bpc - 1))) >> bpc
+        out += g[l] * v
+    return ((out + 32768) >> 16).astype(np.uint16)
+
+
+def scipy_blur(x: np.ndarray, bpc: int) -> np.ndarray:
+    """The same separable filter through scipy.ndimage.correlate1d (mode 'mirror')."""
+    g = np.array(TAPS, dtype=np.float64)
+    v = ndi.correlate1d(x.astype(np.int64), g, axis=0, mode="mirror")
+    v = (v + (1 << (bpc - 1))) >> bpc
+    b = ndi.correlate1d(v, g, axis=1, mode="mirror")
+    return ((b + 32768) >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------------------------
+# taps
+
+
+def pin_taps(o):
+    g = [int(v) for v in o.taps()]
+    assert g == list(TAPS), g
+    assert sum(g) == 1 << 16
+
+
+# ---------------------------------------------------------------------------------------------
+# blur
+
+
+def pin_blur_brute_force(o):
+    for bpc in (8, 10):
+        for i, x in enumerate(_planes(bpc, 11 + bpc)):
+            got, want = o.blur(x, bpc), brute_force_blur(x, bpc)
+            assert np.array_equal(got, want), (bpc, i, x.shape)
+
+
+def pin_blur_brute_force_large(o):
+    r = _rng(5)
+    for (h, w), bpc in (((723, 1283), 8), ((131, 257), 10)):
+        x = r.integers(0, 1 << bpc, size=(h, w)).astype(np.uint8 if bpc == 8 else np.uint16)
+        assert np.array_equal(o.blur(x, bpc), brute_force_blur(x, bpc)), (h, w, bpc)
+
+
+def pin_blur_scipy(o):
+    for bpc in (8, 10):
+        for i, x in enumerate(_planes(bpc, 23 + bpc)):
+            assert np.array_equal(o.blur(x, bpc), scipy_blur(x, bpc)), (bpc, i, x.shape)
+
+
+def pin_blur_constant(o):
+    """A flat plane stays flat, scaled to 16 bits: c * 2^(16 - bpc)."""
+    for bpc in (8, 10):
+        for c in (0, 1, 77, (1 << bpc) - 1):
+            for h, w in ((3, 3), (6, 16), (11, 4)):
+                x = np.full((h, w), c, dtype=np.uint8 if bpc == 8 else np.uint16)
+                assert np.all(o.blur(x, bpc) == c << (16 - bpc)), (bpc, c, h, w)
+
+
+# 5x5 response to one full-scale sample in the middle of a zero plane, hand-derived from the taps:
+# vertical 8-bit values (g*255 + 128) >> 8 = 3557, 15941, 26283; each row then (g*V + 32768) >> 16.
+# At 10 bits the vertical values are (g*1023 + 512) >> 10 = 3568, 15988, 26360; the vertical pass
+# rounds first, so the response is not symmetric under transposition (1437 above, 1436 left).
+IMPULSE_8 = [[194, 869, 1432, 869, 194],
+             [869, 3893, 6418, 3893, 869],
+             [1432, 6418, 10582, 6418, 1432],
+             [869, 3893, 6418, 3893, 869],
+             [194, 869, 1432, 869, 194]]
+IMPULSE_10 = [[194, 871, 1437, 871, 194],
+              [871, 3904, 6437, 3904, 871],
+              [1436, 6437, 10613, 6437, 1436],
+              [871, 3904, 6437, 3904, 871],
+              [194, 871, 1437, 871, 194]]
+
+
+def pin_blur_impulse(o):
+    for bpc, resp in ((8, IMPULSE_8), (10, IMPULSE_10)):
+        x = np.zeros((9, 11), dtype=np.uint8 if bpc == 8 else np.uint16)
+        x[4, 5] = (1 << bpc) - 1
+        b = o.blur(x, bpc).astype(np.int64)
+        want = np.zeros((9, 11), dtype=np.int64)
+        want[2:7, 3:8] = resp
+        assert np.array_equal(b, want), (bpc, b)
+
+
+# A vertical 0 -> full-scale step at column k: every column's vertical value is 0 or 65280 (8-bit,
+# (65536*255 + 128) >> 8) or 65472 (10-bit); across the step the blurred row rises through the
+# cumulative tap sums 3571, 19575, 45961, 61965 scaled by that value and rounded.
+STEP_8 = [0, 3557, 19499, 45781, 61723, 65280]
+STEP_10 = [0, 3568, 19556, 45916, 61904, 65472]
+
+
+def pin_blur_step(o):
+    for bpc, prof in ((8, STEP_8), (10, STEP_10)):
+        x = np.zeros((7, 16), dtype=np.uint8 if bpc == 8 else np.uint16)
+        x[:, 8:] = (1 << bpc) - 1
+        b = o.blur(x, bpc)
+        for i in range(7):
+            assert list(b[i, 5:11]) == prof, (bpc, i, list(b[i]))
+
+
+def pin_blur_mirror_edges(o):
+    """A step placed one column from the left edge: the mirror makes column -1 equal column 1, so
+    output column 0 sees (x1, x1... ) = the mirrored neighbours, which differs from clamping."""
+    for bpc in (8, 10):
+        peak = (1 << bpc) - 1
+        x = np.zeros((5, 8), dtype=np.uint8 if bpc == 8 else np.uint16)
+        x[:, 1] = peak  # column 1 bright: mirrored into column -1
+        b = o.blur(x, bpc).astype(np.int64)
+        vmax = ((65536 * peak) + (1 << (bpc - 1))) >> bpc
+        # column 0 sees taps g1 (col -1 -> 1) and g1 (col 1): 2*16004 of vmax
+        assert b[2, 0] == (2 * 16004 * vmax + 32768) >> 16, b[2]
+        # column 2 sees g1 from column 1 only
+        assert b[2, 2] == (16004 * vmax + 32768) >> 16, b[2]
+        # the right edge mirrors the same way: flip the plane
+        bf = o.blur(np.ascontiguousarray(x[:, ::-1]), bpc).astype(np.int64)
+        assert np.array_equal(bf, b[:, ::-1])
+
+
+def pin_blur_flip(o):
+    for bpc in (8, 10):
+        for x in _planes(bpc, 41 + bpc):
+            b = o.blur(x, bpc)
+            assert np.array_equal(o.blur(np.ascontiguousarray(x[::-1]), bpc), b[::-1])
+            assert np.array_equal(o.blur(np.ascontiguousarray(x[:, ::-1]), bpc), b[:, ::-1])
+
+
+def pin_blur_range_and_linearity(o):
+    r = _rng(3)
+    for bpc in (8, 10):
+        peak = (1 << bpc) - 1
+        dt = np.uint8 if bpc == 8 else np.uint16
+        for h, w in ((3, 3), (12, 19), (40, 7)):
+            x = r.integers(0, peak // 2, size=(h, w)).astype(dt)
+            b = o.blur(x, bpc).astype(np.int64)
+            assert b.min() >= 0 and b.max() <= peak << (16 - bpc)
+            for c in (1, 5, peak // 2):
+                bc = o.blur((x.astype(np.int64) + c).astype(dt), bpc).astype(np.int64)
+                assert np.array_equal(bc, b + (c << (16 - bpc))), (bpc, c)
+
+
+def pin_blur_bit_depth(o):
+    """10-bit blur of 4x equals the 8-bit blur of x: floor((4a + 512)/1024) = floor((a + 128)/256)."""
+    for x in _planes(8, 59):
+        assert np.array_equal(o.blur((x.astype(np.uint16) * 4), 10), o.blur(x, 8))
+
+
+def pin_blur_error_bound(o):
+    """The integer result is within 1 of the exact real-valued 2-D filter scaled to 16 bits."""
+    g = np.array(TAPS, dtype=np.float64) / 65536.0
+    for bpc in (8, 10):
+        for x in _planes(bpc, 61 + bpc):
+            h, w = x.shape
+            xp = np.pad(x.astype(np.float64), 2, mode="reflect")
+            exact = np.zeros((h, w))
+            for k in range(5):
+                for l in range(5):
+                    exact += g[k] * g[l] * xp[k:k + h, l:l + w]
+            err = np.abs(o.blur(x, bpc) - exact * (1 << (16 - bpc)))
+            assert err.max() <= 1.0, (bpc, x.shape, err.max())
+
+
+def pin_blur_translation(o):
+    """Away from the edges a shifted input gives a shifted output."""
+    r = _rng(8)
+    x = r.integers(0, 256, size=(40, 40)).astype(np.uint8)
+    b = o.blur(x, 8)
+    bs = o.blur(np.ascontiguousarray(x[3:, 5:]), 8)
+    assert np.array_equal(bs[2:-2, 2:-2], b[5:-2, 7:-2])
+
+
+# ---------------------------------------------------------------------------------------------
+# SSE and SAD
+
+
+def pin_sse_brute_force(o):
+    r = _rng(13)
+    for bpc in (8, 10):
+        peak = (1 << bpc) - 1
+        dt = np.uint8 if bpc == 8 else np.uint16
+        for h, w in SIZES + [(1, 1), (1, 9), (8, 1)]:
+            a = r.integers(0, peak + 1, size=(h, w)).astype(dt)
+            b = r.integers(0, peak + 1, size=(h, w)).astype(dt)
+            want = sum((int(p) - int(q)) ** 2 for p, q in zip(a.ravel(), b.ravel()))
+            assert o.sse(a, b, bpc) == want
+            assert o.sse(b, a, bpc) == want
+            assert o.sse(a, a, bpc) == 0
+
+
+def pin_sse_constant(o):
+    for bpc in (8, 10):
+        dt = np.uint8 if bpc == 8 else np.uint16
+        a = np.full((6, 16), 100, dtype=dt)
+        b = np.full((6, 16), 103, dtype=dt)
+        assert o.sse(a, b, bpc) == 96 * 9
+        full = np.full((3, 5), (1 << bpc) - 1, dtype=dt)
+        assert o.sse(full, np.zeros_like(full), bpc) == 15 * ((1 << bpc) - 1) ** 2
+
+
+def pin_sad_brute_force(o):
+    r = _rng(17)
+    for h, w in SIZES:
+        a = r.integers(0, 65536, size=(h, w)).astype(np.uint16)
+        b = r.integers(0, 65536, size=(h, w)).astype(np.uint16)
+        want = sum(abs(int(p) - int(q)) for p, q in zip(a.ravel(), b.ravel()))
+        assert o.sad(a, b) == want
+        assert o.sad(b, a) == want
+        assert o.sad(a, a) == 0
+
+
+# ---------------------------------------------------------------------------------------------
+# whole clip
+
+
+def _tiny_clip(bpc, f, h, w, seed):
+    r = _rng(seed)
+    dt = np.uint8 if bpc == 8 else np.uint16
+    hc, wc = (h + 1) // 2, (w + 1) // 2
+    mk = lambda *s: r.integers(0, 1 << bpc, size=s).astype(dt)  # noqa: E731
+    return ((mk(f, h, w), mk(f, hc, wc), mk(f, hc, wc)), (mk(f, h, w), mk(f, hc, wc), mk(f, hc, wc)))
+
+
+def pin_clip_composition(o):
+    """Per frame: SSE of each plane by brute force, SAD of brute-force blurs of consecutive frames."""
+    for bpc, (f, h, w) in ((8, (4, 7, 9)), (10, (3, 5, 6)), (8, (3, 3, 3)), (8, (2, 11, 4))):
+        ref, dist = _tiny_clip(bpc, f, h, w, 100 + h)
+        sums, hm = o.clip(ref, dist, bpc)
+        assert list(hm) == [0] + [1] * (f - 1)
+        prev = None
+        for t in range(f):
+            for p in range(3):
+                d = ref[p][t].astype(np.int64) - dist[p][t].astype(np.int64)
+                assert int(sums[t, 1 + p]) == int((d * d).sum()), (t, p)
+            cur = brute_force_blur(ref[0][t], bpc).astype(np.int64)
+            want = 0 if prev is None else int(np.abs(cur - prev).sum())
+            assert int(sums[t, 0]) == want, (bpc, t)
+            prev = cur
+
+
+def pin_clip_split(o):
+    """A clip run in two parts, the second given the first's last blurred plane, matches one run."""
+    ref, dist = _tiny_clip(8, 6, 9, 12, 7)
+    whole, hm = o.clip(ref, dist, 8)
+    a, hma, last = o.clip(tuple(p[:2] for p in ref), tuple(p[:2] for p in dist), 8,
+                          want_last_blur=True)
+    b, hmb = o.clip(tuple(p[2:] for p in ref), tuple(p[2:] for p in dist), 8, prev_blur=last)
+    assert np.array_equal(np.concatenate([a, b]), whole)
+    assert list(hma) + list(hmb) == list(hm) == [0, 1, 1, 1, 1, 1]
+
+
+def pin_clip_constant_motion(o):
+    """Constant frames c then c + d: SAD = N |d| 2^(16 - bpc), so motion = |d| (8-bit units)."""
+    for bpc in (8, 10):
+        dt = np.uint8 if bpc == 8 else np.uint16
+        h, w = 6, 16
+        hc, wc = 3, 8
+        y = np.stack([np.full((h, w), 100, dt), np.full((h, w), 103, dt), np.full((h, w), 97, dt)])
+        c = np.full((3, hc, wc), 50, dt)
+        sums, hm = o.clip((y, c, c), (y, c, c), bpc)
+        n = h * w
+        assert list(sums[:, 0]) == [0, n * 3 << (16 - bpc), n * 6 << (16 - bpc)]
+        assert int(sums[:, 1:].sum()) == 0
+        s = o.scores(w, h, bpc, sums[2], hm[2])
+        assert s["motion"] == 6.0 * (1 << (16 - bpc)) / 256.0
+
+
+def pin_scores(o):
+    """PSNR of a constant difference d is 10 log10(peak^2 / d^2); zero error gives +inf."""
+    for bpc in (8, 10):
+        peak = (1 << bpc) - 1
+        w, h = 8, 6
+        n, nc = 48, 12
+        for d in (1, 3, 17):
+            s = o.scores(w, h, bpc, [0, n * d * d, nc * d * d, 0], 0)
+            want = 10 * math.log10(peak * peak / (d * d))
+            assert abs(s["psnr"][0] - want) <= 1e-12 * want
+            assert abs(s["psnr"][1] - want) <= 1e-12 * want
+            assert s["psnr"][2] == math.inf
+            assert s["mse"][0] == d * d and s["mse"][2] == 0.0
+            assert s["motion"] == 0.0
+        s = o.scores(w, h, bpc, [256 * 48 * 5, 0, 0, 0], 1)
+        assert s["motion"] == 5.0
+    # odd sizes: chroma planes are ceil(W/2) x ceil(H/2)
+    s = o.scores(5, 3, 8, [0, 0, 6 * 4, 0], 0)
+    assert s["mse"][1] == 4.0
+
+
+def pin_rejects_out_of_range(o):
+    x = np.full((4, 4), 1024, dtype=np.uint16)
+    try:
+        o.blur(x, 10)
+    except Exception:
+        pass
+    else:
+        raise AssertionError("a 10-bit sample of 1024 was accepted")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

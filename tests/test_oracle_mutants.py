@@ -1,0 +1,63 @@
+"""Every plausible single mistake planted in a copy of the oracle must fail at least one pin.
+
+Each mutant is a textual edit of iir_oracle.c compiled into a temporary library on the CPU; the real
+oracle is never modified. This shows the pins would notice a dropped term, a wrong sign or index,
+a transposed operand or a wrong constant in the oracle.
+"""
+import os
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+MUTANTS = [
+    ("half_sample_mirror_low", "i = -i;", "i = -i - 1;"),
+    ("half_sample_mirror_high", "i = 2 * n - 2 - i;", "i = 2 * n - 1 - i;"),
+    ("no_vertical_round", "v[i * w + j] = (acc + vround) >> bpc;", "v[i * w + j] = acc >> bpc;"),
+    ("no_horizontal_round", "(uint16_t)((acc + 32768) >> 16)", "(uint16_t)(acc >> 16)"),
+    ("vertical_shift_fixed_8", "(acc + vround) >> bpc;", "(acc + vround) >> 8;"),
+    ("dropped_vertical_tap", "for (int k = 0; k < 5; ++k)\n                acc",
+     "for (int k = 0; k < 4; ++k)\n                acc"),
+    ("dropped_horizontal_tap", "for (int l = 0; l < 5; ++l)", "for (int l = 1; l < 5; ++l)"),
+    ("vertical_pass_on_columns", "sample(plane, pitch, mirror(i + k - 2, h), j, bpc)",
+     "sample(plane, pitch, i, mirror(j + k - 2, w), bpc)"),
+    ("horizontal_pass_on_rows", "v[i * w + mirror(j + l - 2, w)]", "v[mirror(i + l - 2, h) * w + j]"),
+    ("off_by_one_window", "mirror(j + l - 2, w)", "mirror(j + l - 1, w)"),
+    ("truncated_taps", "floor(65536.0 * w[k] / s + 0.5)", "floor(65536.0 * w[k] / s)"),
+    ("sigma_two", "exp(-0.5 * (double)(k * k))", "exp(-0.125 * (double)(k * k))"),
+    ("sse_abs_not_square", "s += (uint64_t)(d * d);", "s += (uint64_t)(d < 0 ? -d : d);"),
+    ("sse_signed_square", "s += (uint64_t)(d * d);", "s += (uint64_t)(d * (d < 0 ? 1 : d));"),
+    ("sad_signed", "(uint64_t)(a[n] > b[n] ? a[n] - b[n] : b[n] - a[n])", "(uint64_t)(a[n] - b[n])"),
+    ("sad_against_first_frame", "        prev = cur;\n        cur = tmp;",
+     "        if (!have_prev) { prev = cur; cur = tmp; }"),
+    ("first_frame_has_motion", "has_motion[t] = have_prev;", "has_motion[t] = 1;"),
+    ("chroma_floor_size", "wc = (w + 1) / 2, hc = (h + 1) / 2;", "wc = w / 2, hc = h / 2;"),
+    ("ignores_prev_blur", "int have_prev = prev_blur != NULL;", "int have_prev = 0;"),
+    ("motion_over_255", "(256.0 * npx[0])", "(255.0 * npx[0])"),
+    ("psnr_peak_not_squared", "log10(peak * peak / mse)", "log10(peak / mse)"),
+    ("psnr_uses_sse", "10.0 * log10(peak * peak / mse)", "10.0 * log10(peak * peak / (double)sums[1 + c])"),
+    ("range_check_off", "if (sample(plane, pitch, i, j, bpc) > maxv)",
+     "if (sample(plane, pitch, i, j, bpc) > maxv + 1)"),
+]
+
+
+def _run_pins(lib):
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except Exception as e:  # an AssertionError, or an error the mutant's bad output raised
+            failed.append((pin.__name__, type(e).__name__))
+    return failed
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique in the oracle source"
+    mpath = tmp_path / f"{name}.c"
+    mpath.write_text(src.replace(old, new))
+    lib = oracle.OracleLib(oracle.compile_source(str(mpath), str(tmp_path / f"lib{name}.so")))
+    failed = _run_pins(lib)
+    assert failed, f"mutant {name} passed every pin"

@@ -1,0 +1,189 @@
+"""Benchmark: frames/s of the integer motion + PSNR sums on 3840x2160 8-bit 4:2:0, one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu]
+
+A step is one pass of the whole path over one batch: one iir_submit_clip of the 50-frame clip
+(resident in HBM before timing starts) and one iir_collect of its 50 results. W untimed steps, then
+K timed steps between two device synchronisations. Prints one JSON line.
+
+roofline: the main kernel's algorithmic bytes per launch (every ref and dist sample read once,
+plus the blurred-luma state read and written once per launch) divided by its mean duration,
+measured with HIP events on the context's stream, against the 8 TB/s HBM peak. traffic: HBM bytes
+per launch from the committed rocprofv3 counter summary for this workload, reported only while
+the kernel source still matches the one the counters were taken on.
+cpu_baseline: the plain C oracle (single thread) over the same frames, on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "integer_image_reductions_amd", "csrc", "iir_kernels.hip")
+
+WORKLOADS = {
+    "c3": "3840x2160 8-bit 4:2:0, 50 frame pairs, motion SAD + Y/U/V SSE",
+    "c4": "3840x2160 10-bit 4:2:0 (uint16), 50 frame pairs, motion SAD + Y/U/V SSE",
+    "c2": "1920x1080 8-bit 4:2:0, 48 frame pairs, motion SAD + Y/U/V SSE",
+    "c1": "576x324 8-bit 4:2:0, 10 frame pairs, motion SAD + Y/U/V SSE",
+    "c5": "960x544 8-bit 4:2:0, 301-frame resident clip, motion SAD + Y/U/V SSE",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def algorithmic_bytes(w: int, h: int, bpc: int, frames: int) -> int:
+    """Bytes one launch must move: each sample of the 6 planes of every frame pair read once, and
+    the blurred luma state (uint16 per luma pixel) read once and written once per launch."""
+    b = 1 if bpc == 8 else 2
+    n, nc = w * h, ((w + 1) // 2) * ((h + 1) // 2)
+    return frames * 2 * b * (n + 2 * nc) + 4 * n
+
+
+def load_traffic(workload: str):
+    path = os.path.join(ROOT, "profiles", f"frames_kernel_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_sha256") != kernel_sha():
+        log("traffic counters were taken on a different kernel source; reporting null")
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(clip, max_seconds: float = 20.0):
+    import oracle
+    t0 = time.perf_counter()
+    frames = 0
+    # whole clip when it fits the budget; else the leading frames that do (estimated from one)
+    est = None
+    one = clip.slice(0, 1)
+    ts = time.perf_counter()
+    oracle.clip(one.ref, one.dist, clip.bpc)
+    est = time.perf_counter() - ts
+    n = max(1, min(clip.frames, int(max_seconds / max(est, 1e-6))))
+    sub = clip.slice(0, n)
+    t0 = time.perf_counter()
+    oracle.clip(sub.ref, sub.dist, clip.bpc)
+    dt = time.perf_counter() - t0
+    frames = n
+    return {"value": frames / dt, "unit": "frames/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {frames} of {clip.frames} frame pairs of the same workload, one pass, "
+                      f"single-threaded C oracle ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--probe", action="store_true", help="also measure the memory ceilings")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by frames with no collective; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import integer_image_reductions_amd as iir
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    log("generating", args.workload)
+    clip = synth.make_clip(args.workload)
+    ref, dist = iir.upload_planes(clip.ref, dev), iir.upload_planes(clip.dist, dev)
+    torch.cuda.synchronize()
+    F, W, H, bpc = clip.frames, clip.width, clip.height, clip.bpc
+    log("uploaded", F, "frame pairs")
+
+    ctx = iir.Context(W, H, bpc, max_batch=F, timing=True)
+    geo = ctx.geometry()
+    chunks = ctx.plan_chunks(F)
+    for _ in range(args.warmup):
+        ctx.submit_clip(ref, dist)
+        ctx.collect()
+    torch.cuda.synchronize()
+    kms = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ctx.submit_clip(ref, dist)
+        ctx.collect()
+        kms.append(ctx.kernel_time_ms())
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1000.0 * elapsed / args.steps
+    frames_per_s = F * args.steps / elapsed
+    kernel_ms = float(np.mean(kms))
+    alg = algorithmic_bytes(W, H, bpc, F)
+    achieved = alg / (kernel_ms * 1e-3) / 1e9
+    log(f"kernel {kernel_ms * 1e3:.1f} us/launch (median {np.median(kms) * 1e3:.1f}), "
+        f"step {ms_step * 1e3:.1f} us, {achieved:.0f} GB/s")
+
+    out = {
+        "metric": "frames/s at 3840x2160 4:2:0 motion+PSNR; achieved HBM GB/s vs peak",
+        "value": frames_per_s,
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8" if bpc == 8 else "u16",
+        "data": "synthetic (seeded value-noise clip of the workload's shape; see synth.py)",
+        "config": {"workload": WORKLOADS[args.workload], "width": W, "height": H, "bpc": bpc,
+                   "frames_per_step": F, "chroma": "4:2:0", "tiles": geo["tiles"],
+                   "time_chunks": chunks, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(args.workload),
+                     "kernel": "frames_kernel", "kernel_us": kernel_ms * 1e3,
+                     "algorithmic_bytes_per_launch": alg},
+    }
+    if args.probe:
+        nbytes = 1 << 30
+        a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        ceil = {}
+        for mode, name, mult in ((0, "read", 1), (1, "write", 1), (2, "copy", 2)):
+            ms = iir.probe_bandwidth(mode, a, b, iters=20)
+            ceil[name] = mult * nbytes / (ms * 1e-3) / 1e9
+        out["ceilings_GBps"] = ceil
+        out["roofline"]["frac_of_read_ceiling"] = achieved / ceil["read"]
+        del a, b
+    ctx.close()
+    if not args.no_cpu:
+        log("cpu baseline")
+        out["cpu_baseline"] = cpu_baseline(clip)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

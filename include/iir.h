@@ -1,0 +1,215 @@
+/*
+ * iir.h -- C ABI of the integer motion + PSNR library for AMD MI355X (gfx950).
+ *
+ * Per frame pair of an 8- or 10-bit planar 4:2:0 video, the library returns four exact 64-bit sums:
+ *
+ *   SAD     sum over the luma plane of |Bl_t - Bl_(t-1)|, where Bl is the reference luma after a
+ *           5-tap separable fixed-point Gaussian blur with mirrored edges: the vertical pass is
+ *           rounded by a shift of the bit depth and the horizontal pass by a shift of 16
+ *           ("ADR-1392: CUDA motion, PSNR and moment kernels add one atomic per block ...",
+ *           Context and Decision 4; "Research-0735: CUDA motion kernel ncu hotpath analysis
+ *           (576x324)", Key observations 2). Taps (3571, 16004, 26386, 16004, 3571), whole-sample
+ *           mirror and round-half-up are this library's readings where the pages give no numbers.
+ *   SSE[c]  sum over plane c in {Y, U, V} of (ref - dist)^2 ("ADR-1392", Context and Decision 2).
+ *
+ * Every sum is computed exactly in integers, so the order of the reduction does not matter
+ * ("ADR-1392", Context: the sums are order-independent). Derived doubles (iir_scores_of) are
+ * computed on the host.
+ *
+ * Frames stay on the device: the caller owns all frame memory (device pointers, e.g. torch
+ * tensors); nothing returns to the host inside a frame, and each submission ends with one small
+ * readback of its sums behind an event ("ADR-1380: The CUDA SpEED twins are device-resident ...",
+ * Decision, second item: submit on the picture's stream, read a small result back behind an event,
+ * collect waits once).
+ *
+ * Conventions for every call:
+ *   - the return value is IIR_OK (0) or a negative IIR_E* code; no call throws or aborts;
+ *   - on IIR_EDEVICE the HIP error text is available from iir_last_error() (thread-local);
+ *   - a context is used by one host thread at a time and is bound to one HIP stream;
+ *   - argument checks happen on the host before any device work is enqueued.
+ */
+#ifndef IIR_H
+#define IIR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IIR_API __attribute__((visibility("default")))
+
+enum {
+    IIR_OK = 0,
+    IIR_EINVAL = -1,  /* bad argument: null pointer, size, bit depth, pitch or alignment */
+    IIR_ENODEV = -2,  /* no usable gfx950 device with that index */
+    IIR_ENOMEM = -3,  /* device or pinned host allocation failed (iir_create only) */
+    IIR_EDEVICE = -4, /* a HIP call failed; see iir_last_error() */
+    IIR_EBUSY = -5,   /* the submission would exceed max_batch uncollected frames */
+    IIR_ESTATE = -6   /* call not valid in the context's current state */
+};
+
+#define IIR_CHROMA_420 420
+
+/* iir_config.flags */
+#define IIR_FLAG_TIMING 1u /* record HIP events around each main kernel launch (iir_kernel_time) */
+
+/*
+ * One plane of one frame. data is a DEVICE pointer, pitch is the distance between rows in bytes.
+ * Samples are uint8 (bpc 8) or little-endian uint16 holding 0..1023 (bpc 10). data and pitch must
+ * both be multiples of 16 bytes, and pitch >= width * bytes-per-sample. Samples >= 2^bpc are a
+ * precondition violation: the sums are then unspecified (the kernels still stay in bounds).
+ */
+typedef struct iir_plane {
+    const void *data;
+    int64_t pitch;
+    int32_t width;
+    int32_t height;
+} iir_plane;
+
+/* A 4:2:0 frame: plane[0] = Y (W x H), plane[1] = U, plane[2] = V (ceil(W/2) x ceil(H/2)). */
+typedef struct iir_frame {
+    iir_plane plane[3];
+} iir_frame;
+
+typedef struct iir_config {
+    int32_t width;     /* luma width, >= 3 and <= 32768 */
+    int32_t height;    /* luma height, >= 3 and <= 32768 */
+    int32_t bpc;       /* 8 or 10 */
+    int32_t chroma;    /* IIR_CHROMA_420 */
+    int32_t max_batch; /* max frames uncollected at once (and per submission), 1..65536 */
+    uint32_t flags;    /* IIR_FLAG_* */
+} iir_config;
+
+/*
+ * Exact sums of one frame pair. has_motion is 0 for the first frame after iir_create or iir_reset
+ * (there is no previous blurred frame; sad is then 0) and 1 otherwise.
+ */
+typedef struct iir_result {
+    uint64_t sad;
+    uint64_t sse[3];
+    int32_t has_motion;
+    int32_t reserved;
+} iir_result;
+
+/*
+ * Scores derived from one iir_result on the host in IEEE double ("ADR-1392", Consequences names
+ * the psnr_*, mse_* and motion outputs; the formulas are this library's readings):
+ *   motion  = sad / (256 * W * H)   (mean absolute blurred difference in 8-bit units; 0 when
+ *                                    has_motion is 0)
+ *   mse[c]  = sse[c] / (W_c * H_c)
+ *   psnr[c] = 10 * log10(peak^2 / mse[c]), peak = 2^bpc - 1; +infinity when sse[c] == 0.
+ */
+typedef struct iir_scores {
+    double motion;
+    double mse[3];
+    double psnr[3];
+} iir_scores;
+
+typedef struct iir_ctx iir_ctx;
+
+/*
+ * Create a context for one frame geometry on HIP device `device`, enqueuing all of its work on
+ * `hip_stream` (a hipStream_t; NULL means the device's null stream). Allocates everything the
+ * context will ever use: the blurred-luma state (two planes of uint16 in a tiled layout), the
+ * device sum slots, pinned readback and descriptor staging, and events. Nothing is allocated
+ * afterwards. Errors: IIR_EINVAL (config), IIR_ENODEV (no such device or not gfx950),
+ * IIR_ENOMEM, IIR_EDEVICE. *out is set only on success.
+ */
+IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, iir_ctx **out);
+
+/*
+ * Enqueue one frame pair (asynchronous: returns before the GPU runs it). ref and dist are host
+ * structs describing device planes; the planes must stay valid and unmodified until the result
+ * has been collected. One kernel launch and one 32-byte-per-slot readback; no host wait.
+ * Errors: IIR_EINVAL, IIR_EBUSY (max_batch frames already pending), IIR_EDEVICE.
+ */
+IIR_API int iir_submit(iir_ctx *ctx, const iir_frame *ref, const iir_frame *dist);
+
+/*
+ * Enqueue nframes consecutive frame pairs in one launch (asynchronous). ref[t] and dist[t]
+ * describe frame t; every frame of a clip must use frame 0's pitches. When every plane advances
+ * by a constant byte stride from frame to frame (e.g. one (F, H, W) tensor per plane), the
+ * pointers travel in the kernel arguments; otherwise a descriptor table is copied to the device
+ * first. Results are appended to the pending queue in frame order. Motion continues from the
+ * previous submission's last frame. Errors: IIR_EINVAL (nframes < 1 or > max_batch, bad frame),
+ * IIR_EBUSY, IIR_EDEVICE.
+ */
+IIR_API int iir_submit_clip(iir_ctx *ctx, const iir_frame *ref, const iir_frame *dist,
+                            int32_t nframes);
+
+/*
+ * Wait once for all pending submissions and copy up to `max` results, oldest first, into the
+ * HOST array `out`; *n_out receives the number copied. Results beyond `max` stay queued for the
+ * next call. With nothing pending it returns IIR_OK with *n_out = 0.
+ * Errors: IIR_EINVAL (null out or n_out, max < 0), IIR_EDEVICE.
+ */
+IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_out);
+
+/*
+ * iir_submit_clip followed by iir_collect of exactly those nframes results into the host array
+ * `out` (which must hold nframes entries). Requires nothing else pending (IIR_ESTATE otherwise).
+ */
+IIR_API int iir_run_clip(iir_ctx *ctx, const iir_frame *ref, const iir_frame *dist,
+                         int32_t nframes, iir_result *out);
+
+/* Derive the scores of one result for a configuration (pure host code). Errors: IIR_EINVAL. */
+IIR_API int iir_scores_of(const iir_config *cfg, const iir_result *r, iir_scores *s);
+
+/* Forget the previous frame: the next submitted frame gets has_motion = 0. Enqueues nothing. */
+IIR_API int iir_reset(iir_ctx *ctx);
+
+/*
+ * Write the blurred reference luma of the most recently submitted frame as a W x H uint16 plane
+ * into the DEVICE buffer dst (row pitch `pitch` bytes, >= 2 W, multiple of 4), enqueued on the
+ * context's stream. IIR_ESTATE if no frame has been submitted since create/reset.
+ */
+IIR_API int iir_export_blur(iir_ctx *ctx, void *dst, int64_t pitch);
+
+/*
+ * Duration in milliseconds of the main kernel of the most recent submission, from HIP events on
+ * the context's stream. Needs IIR_FLAG_TIMING and a completed submission (collect first);
+ * IIR_ESTATE otherwise.
+ */
+IIR_API int iir_kernel_time(iir_ctx *ctx, float *ms);
+
+/* Launch geometry chosen at create, for reports and tests. */
+typedef struct iir_geometry {
+    int32_t rows_per_tile;     /* output luma rows per wavefront tile */
+    int32_t lanes_out;         /* output lanes per wavefront (4 luma columns each) */
+    int32_t strips;            /* tiles across */
+    int32_t row_tiles;         /* tiles down */
+    int32_t tiles;             /* strips * row_tiles */
+    int32_t sum_slots;         /* partial accumulators per sum, folded on the host */
+    int32_t max_chunks;        /* most time chunks one launch may split a clip into */
+    int32_t reserved;
+} iir_geometry;
+IIR_API int iir_get_geometry(const iir_ctx *ctx, iir_geometry *out);
+
+/* Time chunks the next iir_submit_clip of nframes frames will use (1 = no split). */
+IIR_API int iir_plan_chunks(const iir_ctx *ctx, int32_t nframes, int32_t *chunks);
+
+/*
+ * Memory-ceiling probe in the manner of "Making it fast: three rounds on one pipeline", section
+ * "First, find the ceiling": a kernel that only moves memory. mode 0 reads `bytes` from src,
+ * mode 1 writes `bytes` to dst, mode 2 copies src to dst. src/dst are DEVICE buffers of at least
+ * `bytes` (multiple of 4096, 16-byte aligned). Runs `iters` launches on hip_stream between two
+ * events and returns the mean milliseconds per launch in *ms. Errors: IIR_EINVAL, IIR_EDEVICE.
+ */
+IIR_API int iir_probe_bandwidth(int32_t device, void *hip_stream, int32_t mode, const void *src,
+                                void *dst, int64_t bytes, int32_t iters, float *ms);
+
+/* Release everything the context owns. Waits for its pending work first. NULL is a no-op. */
+IIR_API void iir_destroy(iir_ctx *ctx);
+
+/* Static text for an IIR_* code. */
+IIR_API const char *iir_strerror(int code);
+
+/* Detail of the last failure on this thread (HIP error text or the failed check). */
+IIR_API const char *iir_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IIR_H */

@@ -1,0 +1,20 @@
+"""Integer motion (blurred-luma SAD) and PSNR (per-plane SSE) sums on AMD MI355X.
+
+The computation lives in libiir.so (HIP kernels for gfx950 behind the C ABI in include/iir.h);
+this package is its Python binding. Import is cheap: the library loads on first use.
+"""
+from .binding import (  # noqa: F401
+    IIR_CHROMA_420,
+    IIR_FLAG_TIMING,
+    LIB_PATH,
+    PLANE_ALIGN,
+    SIGNATURES,
+    Context,
+    IIRError,
+    frame_of,
+    load_library,
+    probe_bandwidth,
+    sample_dtype,
+    scores,
+    upload_planes,
+)

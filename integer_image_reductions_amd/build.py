@@ -1,0 +1,72 @@
+"""Build libiir.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+    python -m integer_image_reductions_amd.build          # build
+    python -m integer_image_reductions_amd.build --asm    # also write the gfx950 assembly
+
+The library lands next to this file so that tests, the smoke check and the benchmark load exactly
+this build.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libiir.so")
+SOURCES = [os.path.join(CSRC, "iir_kernels.hip"), os.path.join(CSRC, "iir_host.cpp")]
+ARCH = "gfx950"
+
+# -packed-fp32-ops: never emit packed fp32 VALU ops (the kernels are integer-only anyway).
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-fvisibility=hidden", "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libiir.so)")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libiir.so; always recompiles."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *COMMON, "-shared", *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building libiir.so")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def assembly(out_dir: str) -> str:
+    """Write the gfx950 assembly of the kernels (for resource and instruction checks)."""
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "iir_kernels-gfx950.s")
+    cmd = [hipcc(), *COMMON, "--cuda-device-only", "-S", SOURCES[0], "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--asm", metavar="DIR", help="also write the kernel assembly into DIR")
+    ap.add_argument("-v", action="store_true")
+    args = ap.parse_args()
+    print(build(args.v))
+    if args.asm:
+        print(assembly(args.asm))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,54 @@
+// iir_internal.h -- the contract between the host library (iir_host.cpp) and the gfx950 kernels
+// (iir_kernels.hip): tile geometry constants and the one argument struct every launch takes by
+// value. One header for both sides, so the host sizes grids and buffers with the numbers the
+// kernels assume ("ADR-1392: CUDA motion, PSNR and moment kernels add one atomic per block ...",
+// Decision 2 keeps the PSNR block geometry in one header shared by the kernel and its dispatch).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace iir {
+
+constexpr int kWave = 64;          // CDNA wavefront; one wavefront is one workgroup
+constexpr int kRowsPerTile = 16;   // output luma rows per tile (even, multiple of 4)
+constexpr int kMaxLanesOut = 62;   // output lanes per wavefront: lane 0 and lane lanes_out + 1
+                                   // are the left and right halo lanes
+constexpr int kSumSlots = 8;       // partial slots per sum (one per XCD), added up on the host
+constexpr int kSums = 4;           // SAD, SSE_Y, SSE_U, SSE_V
+constexpr int kLumaCols = 4;       // luma columns per lane
+
+// Device pointers of one frame pair: ref Y, U, V, then dist Y, U, V.
+struct FramePtrs {
+    const uint8_t *p[6];
+};
+
+struct KernelArgs {
+    // frames: plane k of frame t is base[k] + t * fstride[k], unless table is set, in which
+    // case it is table[t].p[k]; every frame uses pitch[k]
+    const uint8_t *base[6];
+    int64_t fstride[6];
+    int32_t pitch[6];
+    const FramePtrs *table;
+    // blurred reference luma of the frame before this launch (read when has_prev), and of the
+    // launch's last frame (written); tiled: uint2 at [(tile * kRowsPerTile + row) * kWave + lane]
+    const uint32_t *ring_in;
+    uint32_t *ring_out;
+    // per-frame sums [nframes][kSums][kSumSlots], zeroed before the launch
+    unsigned long long *sums;
+    // the other sum buffer, cleared here for the next submission
+    unsigned long long *zero;
+    int32_t zero_n;
+    int32_t W, H, Wc, Hc;
+    int32_t lanes_out, strips, row_tiles, tiles;
+    int32_t nframes, chunks, chunk_len;
+    int32_t has_prev;
+};
+
+// Host-side launchers (iir_kernels.hip). Each returns the launch's hipError_t.
+hipError_t launch_frames(int bpc, const KernelArgs &a, hipStream_t stream);
+hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
+                         int lanes_out, int row_tiles, hipStream_t stream);
+hipError_t launch_probe(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream);
+
+}  // namespace iir

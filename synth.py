@@ -83,15 +83,16 @@ def chroma_from_luma(y: np.ndarray, bpc: int):
 def block_mean(p: np.ndarray, b: int = 8) -> np.ndarray:
     """b x b block means rounded half up; partial blocks at the edges average what they hold."""
     h, w = p.shape
-    hp, wp = -(-h // b) * b, -(-w // b) * b
-    acc = np.zeros((hp, wp), dtype=np.int64)
+    hb, wb = -(-h // b), -(-w // b)
+    acc = np.zeros((hb * b, wb * b), dtype=np.int32)
     acc[:h, :w] = p
-    cnt = np.zeros((hp, wp), dtype=np.int64)
-    cnt[:h, :w] = 1
-    s = acc.reshape(hp // b, b, wp // b, b).sum(axis=(1, 3))
-    n = cnt.reshape(hp // b, b, wp // b, b).sum(axis=(1, 3))
-    m = (2 * s + n) // (2 * n)
-    return np.repeat(np.repeat(m, b, axis=0), b, axis=1)[:h, :w]
+    s = acc.reshape(hb, b, wb, b).sum(axis=(1, 3), dtype=np.int32)
+    rows = np.minimum(b, h - b * np.arange(hb))
+    cols = np.minimum(b, w - b * np.arange(wb))
+    n = rows[:, None] * cols[None, :]
+    m = ((2 * s + n) // (2 * n)).astype(p.dtype)
+    out = np.broadcast_to(m[:, None, :, None], (hb, b, wb, b)).reshape(hb * b, wb * b)
+    return out[:h, :w]
 
 
 def value_noise(rng: np.random.Generator, h: int, w: int, cells=(64, 32, 16),

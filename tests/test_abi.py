@@ -1,0 +1,121 @@
+"""The C-ABI library without a GPU: exports, argument checks, host-side score derivation."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import integer_image_reductions_amd as iir
+from integer_image_reductions_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    hdr = open(os.path.join(ROOT, "include", "iir.h")).read()
+    return re.findall(r"IIR_API\s+[\w\s\*]*?\b(iir_\w+)\s*\(", hdr)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return iir.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(n for n, _, _ in B.SIGNATURES) == sorted(names)
+
+
+def test_strerror_all_codes(lib):
+    for code in range(0, -7, -1):
+        assert lib.iir_strerror(code).decode() not in ("", "unknown error")
+    assert lib.iir_strerror(-99).decode() == "unknown error"
+
+
+def _create(lib, **kw):
+    cfg = B.Config(kw.get("w", 64), kw.get("h", 32), kw.get("bpc", 8), kw.get("chroma", 420),
+                   kw.get("max_batch", 4), kw.get("flags", 0))
+    h = ctypes.c_void_p()
+    return lib.iir_create(ctypes.byref(cfg), kw.get("device", 0), None, ctypes.byref(h))
+
+
+@pytest.mark.parametrize("kw", [dict(bpc=9), dict(bpc=16), dict(chroma=444), dict(w=2),
+                                dict(h=2), dict(w=40000), dict(max_batch=0),
+                                dict(max_batch=70000), dict(flags=8)])
+def test_create_rejects_bad_config(lib, kw):
+    assert _create(lib, **kw) == B.IIR_EINVAL
+    assert lib.iir_last_error().decode()
+
+
+def test_create_null_out(lib):
+    cfg = B.Config(64, 32, 8, 420, 4, 0)
+    assert lib.iir_create(ctypes.byref(cfg), 0, None, None) == B.IIR_EINVAL
+    assert lib.iir_create(None, 0, None, ctypes.byref(ctypes.c_void_p())) == B.IIR_EINVAL
+
+
+def test_create_without_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert _create(lib) == B.IIR_ENODEV
+
+
+def test_null_context_calls(lib):
+    out = (B.Result * 1)()
+    n = ctypes.c_int32()
+    f = B.Frame()
+    assert lib.iir_submit(None, ctypes.byref(f), ctypes.byref(f)) == B.IIR_EINVAL
+    assert lib.iir_submit_clip(None, ctypes.byref(f), ctypes.byref(f), 1) == B.IIR_EINVAL
+    assert lib.iir_collect(None, out, 1, ctypes.byref(n)) == B.IIR_EINVAL
+    assert lib.iir_run_clip(None, ctypes.byref(f), ctypes.byref(f), 1, out) == B.IIR_EINVAL
+    assert lib.iir_reset(None) == B.IIR_EINVAL
+    assert lib.iir_export_blur(None, None, 0) == B.IIR_EINVAL
+    assert lib.iir_kernel_time(None, ctypes.byref(ctypes.c_float())) == B.IIR_EINVAL
+    assert lib.iir_get_geometry(None, ctypes.byref(B.Geometry())) == B.IIR_EINVAL
+    assert lib.iir_plan_chunks(None, 1, ctypes.byref(n)) == B.IIR_EINVAL
+    lib.iir_destroy(None)
+
+
+def test_probe_rejects_bad_arguments(lib):
+    ms = ctypes.c_float()
+    assert lib.iir_probe_bandwidth(0, None, 3, None, None, 4096, 1, ctypes.byref(ms)) == B.IIR_EINVAL
+    assert lib.iir_probe_bandwidth(0, None, 0, None, None, 4096, 1, ctypes.byref(ms)) == B.IIR_EINVAL
+    assert lib.iir_probe_bandwidth(0, None, 1, None, ctypes.c_void_p(4096), 100, 1,
+                                   ctypes.byref(ms)) == B.IIR_EINVAL
+
+
+def test_scores_of_rejects(lib):
+    r, s = B.Result(), B.Scores()
+    assert lib.iir_scores_of(None, ctypes.byref(r), ctypes.byref(s)) == B.IIR_EINVAL
+    cfg = B.Config(8, 8, 12, 420, 1, 0)
+    assert lib.iir_scores_of(ctypes.byref(cfg), ctypes.byref(r), ctypes.byref(s)) == B.IIR_EINVAL
+
+
+def _close(a, b):
+    if math.isinf(a) or math.isinf(b):
+        return a == b
+    return abs(a - b) <= 1e-12 * max(abs(a), abs(b), 1e-300)
+
+
+@pytest.mark.parametrize("bpc", [8, 10])
+def test_scores_match_oracle(bpc):
+    """Host score derivation in the library equals the oracle's within 1e-12 relative."""
+    r = np.random.default_rng(bpc)
+    for w, h in ((3840, 2160), (576, 324), (5, 3), (1283, 723)):
+        for _ in range(20):
+            sums = [int(v) for v in r.integers(0, 2 ** 40, size=4)]
+            if r.random() < 0.2:
+                sums[1 + int(r.integers(0, 3))] = 0
+            hm = int(r.integers(0, 2))
+            a = iir.scores(w, h, bpc, sums, hm)
+            b = oracle.scores(w, h, bpc, sums, hm)
+            assert _close(a["motion"], b["motion"])
+            for c in range(3):
+                assert _close(a["mse"][c], b["mse"][c])
+                assert _close(a["psnr"][c], b["psnr"][c])

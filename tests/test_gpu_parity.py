@@ -1,0 +1,205 @@
+"""GPU parity: every sum of the HIP path equals the oracle's exactly, through the C ABI.
+
+Small clips span several tiles with ragged tails in both directions; the five named workloads run
+at full size in the launch configuration the benchmark uses (one submit_clip per clip), and every
+frame of every workload is compared with the oracle.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import integer_image_reductions_amd as iir
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(clip):
+    return iir.upload_planes(clip.ref), iir.upload_planes(clip.dist)
+
+
+def _oracle(clip, prev_blur=None, last=False):
+    return oracle.clip(clip.ref, clip.dist, clip.bpc, prev_blur=prev_blur, want_last_blur=last)
+
+
+def _blur_np(ctx):
+    b = ctx.export_blur()
+    import torch
+    torch.cuda.synchronize()
+    return b.cpu().numpy().view(np.uint16)
+
+
+def _check(clip, sums, hm, want, want_hm, what):
+    assert list(hm) == list(want_hm), what
+    bad = np.argwhere(sums != want)
+    assert bad.size == 0, f"{what}: first mismatch frame {bad[0][0]} sum {bad[0][1]}: " \
+                          f"{sums[bad[0][0]]} vs {want[bad[0][0]]}"
+
+
+TINY = [(3, 3), (4, 7), (9, 5), (17, 23), (5, 64), (64, 5), (70, 3), (33, 18), (131, 17),
+        (250, 40), (255, 33), (258, 35), (500, 17), (1283, 723)]
+
+
+@pytest.mark.parametrize("bpc", [8, 10])
+@pytest.mark.parametrize("w,h", TINY, ids=[f"{w}x{h}" for w, h in TINY])
+def test_tiny_sweep(w, h, bpc):
+    kinds = ["uniform", "extreme", "checker", "impulse"]
+    for i, kind in enumerate(kinds):
+        frames = 3 if w * h < 200_000 else 2
+        clip = synth.random_clip(w, h, bpc, frames, seed=1000 + 7 * w + h + i, kind=kind)
+        _say("tiny", w, h, bpc, kind)
+        ref, dist = _dev(clip)
+        with iir.Context(w, h, bpc, max_batch=8) as ctx:
+            sums, hm = ctx.run_clip(ref, dist)
+            want, want_hm, last = _oracle(clip, last=True)
+            _check(clip, sums, hm, want, want_hm, f"{kind} {w}x{h} {bpc}")
+            assert np.array_equal(_blur_np(ctx), last), f"blurred plane {kind} {w}x{h} {bpc}"
+
+
+@pytest.mark.parametrize("bpc", [8, 10])
+def test_streaming_equals_batch_equals_split(bpc):
+    w, h = 300, 70
+    clip = synth.random_clip(w, h, bpc, 9, seed=77, kind="uniform")
+    ref, dist = _dev(clip)
+    want, want_hm = _oracle(clip)
+    _say("streaming/batch/split", bpc)
+    with iir.Context(w, h, bpc, max_batch=16) as ctx:
+        for t in range(9):
+            ctx.submit([p[t] for p in ref], [p[t] for p in dist])
+        sums, hm = ctx.collect()
+        _check(clip, sums, hm, want, want_hm, "streaming")
+    with iir.Context(w, h, bpc, max_batch=16) as ctx:
+        ctx.submit_clip(tuple(p[:4] for p in ref), tuple(p[:4] for p in dist))
+        ctx.submit_clip(tuple(p[4:] for p in ref), tuple(p[4:] for p in dist))
+        sums, hm = ctx.collect()
+        _check(clip, sums, hm, want, want_hm, "split")
+        # partial collects keep the rest queued
+        ctx.reset()
+        ctx.submit_clip(ref, dist)
+        s1, h1 = ctx.collect(4)
+        s2, h2 = ctx.collect()
+        assert len(s1) == 4 and len(s2) == 5
+        _check(clip, np.concatenate([s1, s2]), np.concatenate([h1, h2]), want, want_hm, "partial")
+
+
+def test_reset_restarts_motion():
+    w, h = 64, 40
+    clip = synth.random_clip(w, h, 8, 4, seed=5)
+    ref, dist = _dev(clip)
+    _say("reset")
+    with iir.Context(w, h, 8, max_batch=8) as ctx:
+        ctx.run_clip(tuple(p[:2] for p in ref), tuple(p[:2] for p in dist))
+        ctx.reset()
+        sums, hm = ctx.run_clip(tuple(p[2:] for p in ref), tuple(p[2:] for p in dist))
+    want, want_hm = _oracle(clip.slice(2, 4))
+    _check(clip, sums, hm, want, want_hm, "after reset")
+
+
+def test_frame_table_path():
+    """Frames at unrelated addresses (descriptor table copied to the device)."""
+    w, h, f = 260, 50, 6
+    clip = synth.random_clip(w, h, 10, f, seed=9, kind="extreme")
+    order = [3, 0, 5, 1, 4, 2]
+    ref, dist = _dev(clip)
+    rf = [tuple(p[t] for p in ref) for t in order]
+    df = [tuple(p[t] for p in dist) for t in order]
+    perm = clip.__class__(clip.name, w, h, 10, tuple(p[order] for p in clip.ref),
+                          tuple(p[order] for p in clip.dist))
+    want, want_hm = _oracle(perm)
+    _say("table path")
+    with iir.Context(w, h, 10, max_batch=8) as ctx:
+        ctx.submit_frames(rf, df)
+        sums, hm = ctx.collect()
+    _check(perm, sums, hm, want, want_hm, "table")
+
+
+@pytest.mark.parametrize("target", ["1", "100000"])
+def test_time_chunks_match(target, monkeypatch):
+    """Splitting a clip into time chunks (each re-blurring the frame before it) changes nothing."""
+    monkeypatch.setenv("IIR_TARGET_WAVES", target)
+    monkeypatch.setenv("IIR_MIN_CHUNK", "2")
+    w, h, f = 200, 48, 11
+    clip = synth.random_clip(w, h, 8, f, seed=31)
+    ref, dist = _dev(clip)
+    want, want_hm = _oracle(clip)
+    _say("chunks", target)
+    with iir.Context(w, h, 8, max_batch=16) as ctx:
+        chunks = ctx.plan_chunks(f)
+        assert (chunks == 1) == (target == "1")
+        ctx.run_clip(tuple(p[:1] for p in ref), tuple(p[:1] for p in dist))
+        sums, hm = ctx.run_clip(tuple(p[1:] for p in ref), tuple(p[1:] for p in dist))
+    _check(clip, sums, hm, want[1:], want_hm[1:], f"chunks={chunks}")
+
+
+def test_errors_on_device():
+    import torch
+    w, h = 64, 32
+    clip = synth.random_clip(w, h, 8, 3, seed=2)
+    ref, dist = _dev(clip)
+    _say("errors")
+    with iir.Context(w, h, 8, max_batch=2) as ctx:
+        with pytest.raises(iir.IIRError) as e:
+            ctx.export_blur()
+        assert e.value.code == -6
+        with pytest.raises(iir.IIRError) as e:
+            ctx.submit_clip(ref, dist)  # 3 > max_batch
+        assert e.value.code == -1
+        ctx.submit_clip(tuple(p[:2] for p in ref), tuple(p[:2] for p in dist))
+        with pytest.raises(iir.IIRError) as e:
+            ctx.submit([p[2] for p in ref], [p[2] for p in dist])
+        assert e.value.code == -5
+        with pytest.raises(iir.IIRError) as e:
+            ctx.run_clip(tuple(p[:1] for p in ref), tuple(p[:1] for p in dist))
+        assert e.value.code == -6
+        ctx.collect()
+        # misaligned plane: a view starting one byte in
+        bad = torch.zeros((h, w + 16), dtype=torch.uint8, device="cuda")[:, 1:w + 1]
+        with pytest.raises(iir.IIRError) as e:
+            ctx.submit([bad, ref[1][0], ref[2][0]], [p[0] for p in dist])
+        assert e.value.code == -1
+
+
+def _score_check(clip, sums, hm):
+    for t in range(len(sums)):
+        a = iir.scores(clip.width, clip.height, clip.bpc, sums[t], hm[t])
+        b = oracle.scores(clip.width, clip.height, clip.bpc, sums[t], hm[t])
+        for x, y in [(a["motion"], b["motion"])] + list(zip(a["psnr"] + a["mse"],
+                                                             b["psnr"] + b["mse"])):
+            assert (x == y) or abs(x - y) <= 1e-12 * abs(y)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c5", "c3", "c4"])
+def test_workload_full(name):
+    """Every frame of a named workload, at full size, in the benchmark's launch configuration."""
+    _say("workload", name, "generate")
+    clip = synth.make_clip(name)
+    ref, dist = _dev(clip)
+    _say("workload", name, "gpu")
+    with iir.Context(clip.width, clip.height, clip.bpc, max_batch=clip.frames) as ctx:
+        sums, hm = ctx.run_clip(ref, dist)
+        blur = _blur_np(ctx)
+    _say("workload", name, "oracle")
+    want, want_hm, last = _oracle(clip, last=True)
+    _check(clip, sums, hm, want, want_hm, name)
+    assert np.array_equal(blur, last)
+    _score_check(clip, sums, hm)
+    if name in ("c3", "c4"):
+        np.save(os.path.join(os.environ.get("TMPDIR", "/tmp"), f"iir_{name}_sad.npy"), sums[:, 0])
+
+
+def test_bit_depth_invariance_4k():
+    """The 10-bit 4K reference is 4x the 8-bit one, so the per-frame SADs are identical."""
+    p8 = os.path.join(os.environ.get("TMPDIR", "/tmp"), "iir_c3_sad.npy")
+    p10 = os.path.join(os.environ.get("TMPDIR", "/tmp"), "iir_c4_sad.npy")
+    if not (os.path.exists(p8) and os.path.exists(p10)):
+        pytest.skip("needs test_workload_full[c3] and [c4] in the same run")
+    assert np.array_equal(np.load(p8), np.load(p10))

@@ -57,8 +57,11 @@ enum {
 /*
  * One plane of one frame. data is a DEVICE pointer, pitch is the distance between rows in bytes.
  * Samples are uint8 (bpc 8) or little-endian uint16 holding 0..1023 (bpc 10). data and pitch must
- * both be multiples of 16 bytes, and pitch >= width * bytes-per-sample. Samples >= 2^bpc are a
- * precondition violation: the sums are then unspecified (the kernels still stay in bounds).
+ * both be multiples of 16 bytes, pitch >= width * bytes-per-sample, and height * pitch < 2^32.
+ * The whole height * pitch bytes must be readable device memory (the kernels load whole 16-byte
+ * aligned groups, which may reach past the last column of a row up to its pitch; those bytes never
+ * affect a result). Samples >= 2^bpc are a precondition violation: the sums are then unspecified
+ * (the kernels still stay in bounds).
  */
 typedef struct iir_plane {
     const void *data;

@@ -140,6 +140,9 @@ int check_plane(const iir_ctx *c, const iir_plane &p, int idx, const char *which
     if (p.pitch < (int64_t)w * c->bps || p.pitch > INT32_MAX)
         return fail(IIR_EINVAL, "%s plane %d: pitch %lld outside [%lld, 2^31)", which, idx,
                     (long long)p.pitch, (long long)w * c->bps);
+    if ((int64_t)h * p.pitch > (int64_t)UINT32_MAX)
+        return fail(IIR_EINVAL, "%s plane %d: %d rows of pitch %lld exceed 4 GiB", which, idx, h,
+                    (long long)p.pitch);
     if ((p.pitch % kAlign) || ((uintptr_t)p.data % kAlign))
         return fail(IIR_EINVAL, "%s plane %d: data and pitch must be multiples of %d bytes", which,
                     idx, kAlign);
@@ -263,8 +266,11 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
         a.table = c->table_dev + c->queued;
     }
     for (int k = 0; k < 3; ++k) {
+        const int64_t rows = k == 0 ? c->cfg.height : c->Hc;
         a.pitch[k] = (int32_t)ref[0].plane[k].pitch;
         a.pitch[k + 3] = (int32_t)dist[0].plane[k].pitch;
+        a.span[k] = (uint32_t)(rows * ref[0].plane[k].pitch);
+        a.span[k + 3] = (uint32_t)(rows * dist[0].plane[k].pitch);
     }
     a.ring_in = c->ring[c->ring_cur];
     a.ring_out = c->ring[c->ring_cur ^ 1];

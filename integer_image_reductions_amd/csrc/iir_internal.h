@@ -29,6 +29,7 @@ struct KernelArgs {
     const uint8_t *base[6];
     int64_t fstride[6];
     int32_t pitch[6];
+    uint32_t span[6];  // readable bytes of each plane (rows * pitch), below 2^32
     const FramePtrs *table;
     // blurred reference luma of the frame before this launch (read when has_prev), and of the
     // launch's last frame (written); tiled: uint2 at [(tile * kRowsPerTile + row) * kWave + lane]

@@ -51,6 +51,7 @@ constexpr uint32_t T10 = G1 | (G0 << 16);
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t dot2u(uint32_t a, uint32_t b, uint32_t c)
 {
@@ -139,89 +140,66 @@ struct Px<8> {
 };
 template <>
 struct Px<10> {
-    typedef uint2 Luma;  // 4 luma samples, 2 per dword
+    typedef u32x2 Luma;  // 4 luma samples, 2 per dword
     static constexpr int kBytes = 2;
 };
 
-// 4 samples at columns c..c+3 of a luma row, mirrored at the left and right edges.
-template <int BPC>
-__device__ __forceinline__ typename Px<BPC>::Luma load_luma(const uint8_t *row, int c, int W,
-                                                            bool on, bool fast)
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// A buffer resource over one plane: base in SGPRs, `bytes` as its range. Loads then take the
+// row offset in an SGPR (soffset) and the lane's column offset in one VGPR (voffset), so no
+// per-row VALU address arithmetic and no 64-bit address registers are needed.
+__device__ __forceinline__ Rsrc plane_rsrc(const uint8_t *p, uint32_t bytes)
 {
-    typedef typename Px<BPC>::Luma L;
-    L v = {};
-    if (on) {
-        if (fast) {
-            v = *reinterpret_cast<const L *>(row + c * Px<BPC>::kBytes);
-        } else if constexpr (BPC == 8) {
-            uint32_t u = 0;
-            for (int b = 0; b < 4; ++b)
-                u |= (uint32_t)row[mirror_clamp(c + b, W)] << (8 * b);
-            v = u;
-        } else {
-            const uint16_t *r16 = reinterpret_cast<const uint16_t *>(row);
-            uint32_t e[4];
-            for (int b = 0; b < 4; ++b)
-                e[b] = r16[mirror_clamp(c + b, W)];
-            v.x = e[0] | (e[1] << 16);
-            v.y = e[2] | (e[3] << 16);
-        }
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint32_t ld32(Rsrc r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+
+template <int BPC>
+__device__ __forceinline__ typename Px<BPC>::Luma ld_luma(Rsrc r, uint32_t voff, uint32_t soff)
+{
+    if constexpr (BPC == 8) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+    } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+        return u32x2{v[0], v[1]};
     }
+}
+
+__device__ __forceinline__ int uni(int v)
+{
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+// A value the compiler must treat as changed on every frame, so per-row products of it are not
+// hoisted out of the frame loop into dozens of live scalar registers.
+__device__ __forceinline__ uint32_t opaque(uint32_t v)
+{
+    asm volatile("" : "+s"(v));
     return v;
 }
 
-// Distorted luma of an output lane. Columns at or past W take the reference sample instead, so
-// their squared difference is 0.
-template <int BPC>
-__device__ __forceinline__ typename Px<BPC>::Luma load_dist(const uint8_t *row, int c, int W,
-                                                            bool on, bool full,
-                                                            typename Px<BPC>::Luma ref)
+// Plane k of frame t (wave-uniform; scalar loads when it comes from the frame table).
+__device__ __forceinline__ const uint8_t *frame_plane(const KernelArgs &a, int t, int k)
 {
-    typedef typename Px<BPC>::Luma L;
-    L v = ref;
-    if (on) {
-        if (full) {
-            v = *reinterpret_cast<const L *>(row + c * Px<BPC>::kBytes);
-        } else if constexpr (BPC == 8) {
-            uint32_t u = ref;
-            for (int b = 0; b < 4; ++b)
-                if (c + b < W)
-                    u = (u & ~(0xffu << (8 * b))) | ((uint32_t)row[c + b] << (8 * b));
-            v = u;
-        } else {
-            const uint16_t *r16 = reinterpret_cast<const uint16_t *>(row);
-            uint32_t e[4] = {ref.x & 0xffffu, ref.x >> 16, ref.y & 0xffffu, ref.y >> 16};
-            for (int b = 0; b < 4; ++b)
-                if (c + b < W)
-                    e[b] = r16[c + b];
-            v.x = e[0] | (e[1] << 16);
-            v.y = e[2] | (e[3] << 16);
-        }
+    if (a.table) {
+        typedef __attribute__((address_space(4))) const FramePtrs cFramePtrs;
+        const cFramePtrs *tb = (const cFramePtrs *)(uintptr_t)a.table;
+        return tb[t].p[k];
     }
-    return v;
+    return a.base[k] + (int64_t)t * a.fstride[k];
 }
 
-// One chroma dword (4 samples at 8 bits, 2 at 10 bits) starting at sample cb; samples at or past
-// wc read as 0 in both ref and dist.
-template <int BPC>
-__device__ __forceinline__ uint32_t load_chroma(const uint8_t *row, int cb, int wc, bool on)
+// Both 16-bit halves of v shifted left by 6. Takes the dword by value: __builtin_bit_cast must
+// not be applied to a vector element expression such as a.y (clang reads element 0 there).
+__device__ __forceinline__ uint32_t scale64(uint32_t v)
 {
-    constexpr int per = 4 / Px<BPC>::kBytes;
-    uint32_t v = 0;
-    if (on) {
-        if (cb + per <= wc) {
-            v = *reinterpret_cast<const uint32_t *>(row + cb * Px<BPC>::kBytes);
-        } else if constexpr (BPC == 8) {
-            for (int b = 0; b < 4; ++b)
-                if (cb + b < wc)
-                    v |= (uint32_t)row[cb + b] << (8 * b);
-        } else {
-            const uint16_t *r16 = reinterpret_cast<const uint16_t *>(row);
-            if (cb < wc)
-                v = r16[cb];
-        }
-    }
-    return v;
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, v) << 6);
 }
 
 // (row a, row b) 16-bit pairs of the lane's 4 columns, the vertical filter's operands.
@@ -236,10 +214,8 @@ __device__ __forceinline__ void column_pairs(typename Px<BPC>::Luma a, typename 
         p[3] = perm(b, a, 0x0c070c03u);
     } else {
         // 10-bit samples scaled by 64 (still < 2^16): the vertical shift by 10 becomes >> 16
-        const uint32_t ax = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a.x) << 6);
-        const uint32_t ay = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a.y) << 6);
-        const uint32_t bx = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, b.x) << 6);
-        const uint32_t by = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, b.y) << 6);
+        const uint32_t ax = scale64(a.x), ay = scale64(a.y);
+        const uint32_t bx = scale64(b.x), by = scale64(b.y);
         p[0] = perm(bx, ax, 0x05040100u);
         p[1] = perm(bx, ax, 0x07060302u);
         p[2] = perm(by, ay, 0x05040100u);
@@ -247,80 +223,325 @@ __device__ __forceinline__ void column_pairs(typename Px<BPC>::Luma a, typename 
     }
 }
 
+// Squared-error accumulation of one luma group (4 samples) or one chroma dword. 8-bit keeps
+// sum(r^2 + d^2) in s and sum(r d) in s2; 10-bit keeps the sum of squared differences in s.
 template <int BPC>
-__global__ __launch_bounds__(kWave) void frames_kernel(const KernelArgs a)
+__device__ __forceinline__ void sse_luma(typename Px<BPC>::Luma r, typename Px<BPC>::Luma d,
+                                         uint32_t &s, uint32_t &s2)
+{
+    if constexpr (BPC == 8) {
+        s = dot4u(d, d, dot4u(r, r, s));
+        s2 = dot4u(r, d, s2);
+    } else {
+        s = sqdiff2(r.y, d.y, sqdiff2(r.x, d.x, s));
+    }
+}
+
+template <int BPC>
+__device__ __forceinline__ void sse_chroma(uint32_t r, uint32_t d, uint32_t &s, uint32_t &s2)
+{
+    if constexpr (BPC == 8) {
+        s = dot4u(d, d, dot4u(r, r, s));
+        s2 = dot4u(r, d, s2);
+    } else {
+        s = sqdiff2(r, d, s);
+    }
+}
+
+// r with the samples outside a per-lane validity mask cleared
+template <int BPC>
+__device__ __forceinline__ typename Px<BPC>::Luma masked(typename Px<BPC>::Luma r, uint32_t m0,
+                                                         uint32_t m1)
+{
+    if constexpr (BPC == 8) {
+        return r & m0;
+    } else {
+        return u32x2{r.x & m0, r.y & m1};
+    }
+}
+
+// Everything one wavefront knows about its tile, fixed for the whole launch. Scalars are
+// wave-uniform (kept in SGPRs); the rest are per lane.
+struct Tile {
+    int tile, chunk, strip, r0;  // scalar
+    int rows_valid;              // scalar: output rows of the tile inside the frame
+    int lane;
+    uint32_t luma_off;           // byte offset of the lane's 4 luma samples in a row
+    uint32_t w0, w1;             // 16-bit weights of the lane's blurred pairs (1 = valid column)
+    bool out_lane;               // lane owns output columns
+    uint32_t coff[4];            // byte offsets of the lane's chroma dword in ref U, dist U,
+                                 // ref V, dist V (column, plus one row for the upper half-wave
+                                 // at 8 bits)
+    int crow0;                   // scalar: first chroma row of the tile
+    bool c_on;                   // lane reads chroma
+    // edges (careful path only)
+    bool left_fix;               // lane 1 of the leftmost strip: mirror the columns left of 0
+    bool right_fix;              // lane holding column W-1: mirror the columns right of it
+    int right_rem;               // scalar: W % 4
+    uint32_t ym0, ym1;           // luma sample masks for SSE (valid columns)
+    uint32_t cm;                 // chroma sample mask for SSE (valid columns)
+    bool c_upper;                // 8-bit: lane reads the second chroma row of each step
+};
+
+// One frame of one tile: blur the reference luma (vertical pass once per column and row,
+// horizontal taps through DPP neighbours), SAD against the previous blurred tile held in
+// registers, SSE of the luma and chroma tiles, one wavefront reduction and one atomic per sum.
+// CAREFUL adds the frame-edge mirror fix-ups, ragged rows and masked tails; interior tiles (the
+// vast majority) run without any of it.
+template <int BPC, bool CAREFUL>
+__device__ __forceinline__ void frame_pass(const KernelArgs &a, const Tile &T, int t,
+                                           bool accumulate, uint32_t (&prev0)[kRowsPerTile],
+                                           uint32_t (&prev1)[kRowsPerTile], uint32_t &sum_prev,
+                                           bool &have_prev)
 {
     typedef typename Px<BPC>::Luma Luma;
     constexpr int TH = kRowsPerTile;
-    // vertical rounding constant, and the selector taking the 16-bit vertical value out of the
-    // 32-bit sums of columns (0, 1): bytes 1-2 (>> 8) at 8 bits, bytes 2-3 (>> 16) for scaled 10
     constexpr uint32_t kVRound = BPC == 8 ? 128u : 32768u;
     constexpr uint32_t kVSel = BPC == 8 ? 0x06050201u : 0x07060302u;
+    const int H = a.H;
 
+    Rsrc rs[6];
+    uint32_t pitch[6];
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+        rs[k] = plane_rsrc(frame_plane(a, t, k), a.span[k]);
+        pitch[k] = opaque((uint32_t)a.pitch[k]);
+    }
+
+    // reference luma rows r0-2 .. r0+TH+1, mirrored at the top and bottom
+    Luma R[TH + 5];
+#pragma unroll
+    for (int k = 0; k < TH + 4; ++k) {
+        const int row = CAREFUL ? mirror_clamp(T.r0 - 2 + k, H) : T.r0 - 2 + k;
+        R[k] = ld_luma<BPC>(rs[0], T.luma_off, (uint32_t)row * pitch[0]);
+    }
+    R[TH + 4] = Luma{};
+
+    // distorted luma rows of the tile (rows past the frame re-read the last row; not counted)
+    Luma D[TH];
+    if (accumulate) {
+#pragma unroll
+        for (int i = 0; i < TH; ++i) {
+            const int row = CAREFUL ? min(T.r0 + i, H - 1) : T.r0 + i;
+            D[i] = ld_luma<BPC>(rs[3], T.luma_off, (uint32_t)row * pitch[3]);
+        }
+    }
+
+    // chroma dwords of the tile: ref U, dist U, ref V, dist V; 8-bit steps cover two rows
+    constexpr int CS = BPC == 8 ? TH / 4 : TH / 2;
+    constexpr int CSTEP = BPC == 8 ? 2 : 1;
+    uint32_t cu[CS], du[CS], cv[CS], dv[CS];
+    if (accumulate) {
+#pragma unroll
+        for (int k = 0; k < CS; ++k) {
+            // the upper half-wave's row is one further down (its coff adds a pitch); at a ragged
+            // bottom every lane whose row is past the plane re-reads the last row instead
+            const int row = T.crow0 + CSTEP * k;
+            if constexpr (CAREFUL) {
+                const int rl = min(row, a.Hc - 1);
+                const bool up = T.c_upper && row + 1 < a.Hc;
+                cu[k] = ld32(rs[1], T.coff[0] - (T.c_upper && !up ? pitch[1] : 0u), (uint32_t)rl * pitch[1]);
+                du[k] = ld32(rs[4], T.coff[1] - (T.c_upper && !up ? pitch[4] : 0u), (uint32_t)rl * pitch[4]);
+                cv[k] = ld32(rs[2], T.coff[2] - (T.c_upper && !up ? pitch[2] : 0u), (uint32_t)rl * pitch[2]);
+                dv[k] = ld32(rs[5], T.coff[3] - (T.c_upper && !up ? pitch[5] : 0u), (uint32_t)rl * pitch[5]);
+            } else {
+                cu[k] = ld32(rs[1], T.coff[0], (uint32_t)row * pitch[1]);
+                du[k] = ld32(rs[4], T.coff[1], (uint32_t)row * pitch[4]);
+                cv[k] = ld32(rs[2], T.coff[2], (uint32_t)row * pitch[2]);
+                dv[k] = ld32(rs[5], T.coff[3], (uint32_t)row * pitch[5]);
+            }
+        }
+    }
+
+    // SSE of the chroma tiles first, which frees their registers before the blur
+    uint32_t su = 0, su2 = 0, sv = 0, sv2 = 0;
+    if (accumulate) {
+#pragma unroll
+        for (int k = 0; k < CS; ++k) {
+            uint32_t ru = cu[k], rdu = du[k], rv = cv[k], rdv = dv[k];
+            if constexpr (CAREFUL) {
+                const int row = T.crow0 + CSTEP * k + (T.c_upper ? 1 : 0);
+                const uint32_t m = row < a.Hc ? T.cm : 0u;
+                ru &= m;
+                rdu &= m;
+                rv &= m;
+                rdv &= m;
+            }
+            sse_chroma<BPC>(ru, rdu, su, su2);
+            sse_chroma<BPC>(rv, rdv, sv, sv2);
+        }
+    }
+
+    // blur, SAD against the previous blurred tile, and SSE of the luma rows as they go by
+    uint32_t acc_c = 0, acc_min = 0, sy = 0, sy2 = 0;
+#pragma unroll
+    for (int i = 0; i < TH; ++i) {
+        uint32_t pa[4], pb[4], pc[4];
+        column_pairs<BPC>(R[i], R[i + 1], pa);      // rows i-2, i-1
+        column_pairs<BPC>(R[i + 2], R[i + 3], pb);  // rows i,   i+1
+        column_pairs<BPC>(R[i + 4], R[i + 5], pc);  // rows i+2 (i+3 has tap 0)
+        uint32_t v[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            v[b] = dot2u(pc[b], T0z, dot2u(pb[b], T21, dot2u(pa[b], T01, kVRound)));
+        uint32_t q0 = perm(v[1], v[0], kVSel);  // V of columns c, c+1
+        uint32_t q1 = perm(v[3], v[2], kVSel);  // V of columns c+2, c+3
+        uint32_t ql = from_left(q1);            // V of columns c-2, c-1
+        if constexpr (CAREFUL) {
+            // (V(2), V(1)) stands for columns -2, -1
+            ql = T.left_fix ? perm(q0, q1, 0x07060100u) : ql;
+            if (T.right_rem == 1) {  // columns W, W+1 -> W-2, W-3
+                q0 = T.right_fix ? perm(ql, q0, 0x07060100u) : q0;
+                q1 = T.right_fix ? ql : q1;
+            } else if (T.right_rem == 2) {
+                q1 = T.right_fix ? perm(ql, q0, 0x07060100u) : q1;
+            } else if (T.right_rem == 3) {
+                q1 = T.right_fix ? perm(q0, q1, 0x07060100u) : q1;
+            }
+        }
+        uint32_t qr = from_right(q0);  // V of columns c+4, c+5
+        if constexpr (CAREFUL) {
+            if (T.right_rem == 0)
+                qr = T.right_fix ? perm(q0, q1, 0x07060100u) : qr;
+            else if (T.right_rem == 3)
+                qr = T.right_fix ? q0 : qr;
+        }
+        const uint32_t h0 = dot2u(q1, T0z, dot2u(q0, T21, dot2u(ql, T01, 32768u)));
+        const uint32_t h1 = dot2u(q1, T10, dot2u(q0, T12, dot2u(ql, Tz0, 32768u)));
+        const uint32_t h2 = dot2u(qr, T0z, dot2u(q1, T21, dot2u(q0, T01, 32768u)));
+        const uint32_t h3 = dot2u(qr, T10, dot2u(q1, T12, dot2u(q0, Tz0, 32768u)));
+        const uint32_t c0 = perm(h1, h0, 0x07060302u);  // Bl of columns c, c+1
+        const uint32_t c1 = perm(h3, h2, 0x07060302u);  // Bl of columns c+2, c+3
+        if (!CAREFUL || i < T.rows_valid) {
+            acc_c = dot2u(c1, T.w1, dot2u(c0, T.w0, acc_c));
+            acc_min = dot2u(pkmin(c1, prev1[i]), T.w1, dot2u(pkmin(c0, prev0[i]), T.w0, acc_min));
+            if (accumulate) {
+                Luma r = R[i + 2], d = D[i];
+                if constexpr (CAREFUL) {
+                    r = masked<BPC>(r, T.ym0, T.ym1);
+                    d = masked<BPC>(d, T.ym0, T.ym1);
+                }
+                sse_luma<BPC>(r, d, sy, sy2);
+            }
+        }
+        prev0[i] = c0;
+        prev1[i] = c1;
+    }
+
+    if (accumulate) {
+        const uint32_t sad = have_prev ? acc_c + sum_prev - 2u * acc_min : 0u;
+        const unsigned long long t_sad = wave_sum(sad);
+        const unsigned long long t_y = wave_sum(T.out_lane ? sy - 2u * sy2 : 0u);
+        const unsigned long long t_u = wave_sum(T.c_on ? su - 2u * su2 : 0u);
+        const unsigned long long t_v = wave_sum(T.c_on ? sv - 2u * sv2 : 0u);
+        if (T.lane == 0) {
+            unsigned long long *o =
+                a.sums + (size_t)t * (kSums * kSumSlots) + (blockIdx.x & (kSumSlots - 1));
+            add_sum(o, t_sad);
+            add_sum(o + kSumSlots, t_y);
+            add_sum(o + 2 * kSumSlots, t_u);
+            add_sum(o + 3 * kSumSlots, t_v);
+        }
+    }
+    sum_prev = acc_c;
+    have_prev = true;
+}
+
+template <int BPC, bool CAREFUL>
+__device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
+                                           uint32_t (&prev0)[kRowsPerTile],
+                                           uint32_t (&prev1)[kRowsPerTile], uint32_t sum_prev,
+                                           bool have_prev)
+{
+    // time chunk of this workgroup; chunks after the first re-blur the frame before them
+    const int f_begin = uni(T.chunk * a.chunk_len);
+    const int f_end = uni(min(f_begin + a.chunk_len, a.nframes));
+    if (T.chunk > 0)
+        frame_pass<BPC, CAREFUL>(a, T, f_begin - 1, false, prev0, prev1, sum_prev, have_prev);
+    for (int t = f_begin; t < f_end; ++t)
+        frame_pass<BPC, CAREFUL>(a, T, t, true, prev0, prev1, sum_prev, have_prev);
+}
+
+template <int BPC>
+__global__ __launch_bounds__(kWave) void frames_kernel(const KernelArgs a)
+{
+    constexpr int TH = kRowsPerTile;
+    constexpr int B = Px<BPC>::kBytes;
     const int lane = threadIdx.x;
 
     // clear the other sum buffer for the next submission
     for (int i = blockIdx.x * kWave + lane; i < a.zero_n; i += gridDim.x * kWave)
         a.zero[i] = 0ull;
 
-    const int L = xcd_linear(blockIdx.x, gridDim.x);
-    const int chunk = L / a.tiles;
-    const int tile = L - chunk * a.tiles;
-    const int strip = tile / a.row_tiles;
-    const int rt = tile - strip * a.row_tiles;
-    const int s = strip * kLumaCols * a.lanes_out;  // first output column of the tile
-    const int r0 = rt * TH;                         // first output row of the tile
-    const int slot = blockIdx.x & (kSumSlots - 1);
+    Tile T;
+    const int L = uni(xcd_linear(blockIdx.x, gridDim.x));
+    T.chunk = uni(L / a.tiles);
+    T.tile = uni(L - T.chunk * a.tiles);
+    T.strip = uni(T.tile / a.row_tiles);
+    T.r0 = uni((T.tile - T.strip * a.row_tiles) * TH);  // first output row of the tile
+    const int s = uni(T.strip * kLumaCols * a.lanes_out);  // first output column of the tile
+    T.lane = lane;
     const int W = a.W, H = a.H;
+    T.rows_valid = uni(min(TH, H - T.r0));
 
-    // lane roles and column validity
-    const int c = s - kLumaCols + kLumaCols * lane;  // first luma column of this lane
-    const int need_end = min(s + kLumaCols * a.lanes_out, W) + 2;
-    const bool luma_on = lane <= a.lanes_out + 1 && c + kLumaCols > s - 2 && c < need_end;
-    const bool luma_fast = c >= 0 && c + kLumaCols <= W;
-    const bool out_lane = lane >= 1 && lane <= a.lanes_out && c < W;
-    const bool out_full = out_lane && c + kLumaCols <= W;
-    // per-column weights of the two blurred pairs: 1 in each valid 16-bit half
-    const uint32_t w0 = out_lane ? ((c < W ? 1u : 0u) | (c + 1 < W ? 0x10000u : 0u)) : 0u;
-    const uint32_t w1 = out_lane ? ((c + 2 < W ? 1u : 0u) | (c + 3 < W ? 0x10000u : 0u)) : 0u;
+    // lane roles; every load offset stays inside its row's pitch (a lane whose first column is
+    // outside [0, W) reads column 0 and its values are never used)
+    const int c = s - kLumaCols + kLumaCols * lane;
+    T.luma_off = (c >= 0 && c < W) ? (uint32_t)(c * B) : 0u;
+    T.out_lane = lane >= 1 && lane <= a.lanes_out && c < W;
+    T.w0 = T.out_lane ? ((c < W ? 1u : 0u) | (c + 1 < W ? 0x10000u : 0u)) : 0u;
+    T.w1 = T.out_lane ? ((c + 2 < W ? 1u : 0u) | (c + 3 < W ? 0x10000u : 0u)) : 0u;
+    T.left_fix = T.strip == 0 && lane == 1;
+    T.right_rem = W & 3;
+    T.right_fix = c <= W - 1 && W - 1 < c + kLumaCols && lane >= 1 && lane <= a.lanes_out;
+    if constexpr (BPC == 8) {
+        T.ym0 = (c < W ? 0xffu : 0u) | (c + 1 < W ? 0xff00u : 0u) | (c + 2 < W ? 0xff0000u : 0u) |
+                (c + 3 < W ? 0xff000000u : 0u);
+        T.ym1 = 0u;
+    } else {
+        T.ym0 = (c < W ? 0xffffu : 0u) | (c + 1 < W ? 0xffff0000u : 0u);
+        T.ym1 = (c + 2 < W ? 0xffffu : 0u) | (c + 3 < W ? 0xffff0000u : 0u);
+    }
 
-    // chroma work split: 8-bit, 32 lanes per chroma row (lanes_out / 2 dwords used), two rows per
-    // step; 10-bit, one row per step with lanes_out dwords
+    // chroma split: 8-bit, 32 lanes per chroma row with lanes_out / 2 dwords used and two rows per
+    // step (the upper half-wave takes the second); 10-bit, one row per step, lanes_out dwords
     const int cs = s / 2;  // first chroma sample of the tile
-    int ccol, crow_sub, csteps, crow_step;
-    bool c_on;
+    int ccol;
     if constexpr (BPC == 8) {
         ccol = cs + 4 * (lane & 31);
-        crow_sub = lane >> 5;
-        c_on = (lane & 31) < a.lanes_out / 2;
-        csteps = TH / 4;
-        crow_step = 2;
+        T.c_upper = lane >= 32;
+        T.c_on = (lane & 31) < a.lanes_out / 2 && ccol < a.Wc;
+        T.cm = (ccol < a.Wc ? 0xffu : 0u) | (ccol + 1 < a.Wc ? 0xff00u : 0u) |
+               (ccol + 2 < a.Wc ? 0xff0000u : 0u) | (ccol + 3 < a.Wc ? 0xff000000u : 0u);
     } else {
         ccol = cs + 2 * lane;
-        crow_sub = 0;
-        c_on = lane < a.lanes_out;
-        csteps = TH / 2;
-        crow_step = 1;
+        T.c_upper = false;
+        T.c_on = lane < a.lanes_out && ccol < a.Wc;
+        T.cm = (ccol < a.Wc ? 0xffffu : 0u) | (ccol + 1 < a.Wc ? 0xffff0000u : 0u);
     }
-    const int crow0 = r0 / 2 + crow_sub;
+    T.crow0 = uni(T.r0 / 2);
+    {
+        const uint32_t col = T.c_on ? (uint32_t)(ccol * B) : 0u;
+        const int pk[4] = {1, 4, 2, 5};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            T.coff[k] = col + (T.c_upper ? (uint32_t)a.pitch[pk[k]] : 0u);
+    }
 
-    // time chunk of this workgroup; chunks after the first re-blur the frame before them
-    const int f_begin = chunk * a.chunk_len;
-    const int f_end = min(f_begin + a.chunk_len, a.nframes);
-    const int t_start = chunk > 0 ? f_begin - 1 : f_begin;
-
+    // previous blurred tile: from the launch before, else none (chunk 0), or re-blurred by the
+    // chunk's prologue (later chunks)
     uint32_t prev0[TH], prev1[TH];
     uint32_t sum_prev = 0;
     bool have_prev = false;
-    if (chunk == 0 && a.has_prev) {
+    if (T.chunk == 0 && a.has_prev) {
         const uint2 *rin = reinterpret_cast<const uint2 *>(a.ring_in);
 #pragma unroll
         for (int i = 0; i < TH; ++i) {
-            const uint2 v = rin[(tile * TH + i) * kWave + lane];
+            const uint2 v = rin[(T.tile * TH + i) * kWave + lane];
             prev0[i] = v.x;
             prev1[i] = v.y;
-            if (r0 + i < H)
-                sum_prev = dot2u(v.y, w1, dot2u(v.x, w0, sum_prev));
+            if (i < T.rows_valid)
+                sum_prev = dot2u(v.y, T.w1, dot2u(v.x, T.w0, sum_prev));
         }
         have_prev = true;
     } else {
@@ -329,118 +550,20 @@ __global__ __launch_bounds__(kWave) void frames_kernel(const KernelArgs a)
             prev0[i] = prev1[i] = 0;
     }
 
-    for (int t = t_start; t < f_end; ++t) {
-        const bool prologue = t < f_begin;
-        const uint8_t *fp[6];
-#pragma unroll
-        for (int k = 0; k < 6; ++k)
-            fp[k] = a.table ? a.table[t].p[k] : a.base[k] + (int64_t)t * a.fstride[k];
+    // interior tiles take the lean path; tiles whose window touches a frame edge (rows or
+    // columns) or a ragged tail take the careful one
+    const bool careful = T.strip == 0 || T.strip == a.strips - 1 || T.r0 < 2 ||
+                         T.r0 + TH + 2 > H;
+    if (careful)
+        frame_loop<BPC, true>(a, T, prev0, prev1, sum_prev, have_prev);
+    else
+        frame_loop<BPC, false>(a, T, prev0, prev1, sum_prev, have_prev);
 
-        // reference luma rows r0-2 .. r0+TH+1, mirrored at the top and bottom
-        Luma R[TH + 5];
-#pragma unroll
-        for (int k = 0; k < TH + 4; ++k) {
-            const int row = mirror_clamp(r0 - 2 + k, H);
-            R[k] = load_luma<BPC>(fp[0] + (int64_t)row * a.pitch[0], c, W, luma_on, luma_fast);
-        }
-        R[TH + 4] = Luma{};
-
-        // blur, and the SAD against the previous blurred tile
-        uint32_t acc_c = 0, acc_min = 0;
-#pragma unroll
-        for (int i = 0; i < TH; ++i) {
-            uint32_t pa[4], pb[4], pc[4];
-            column_pairs<BPC>(R[i], R[i + 1], pa);      // rows i-2, i-1
-            column_pairs<BPC>(R[i + 2], R[i + 3], pb);  // rows i,   i+1
-            column_pairs<BPC>(R[i + 4], R[i + 5], pc);  // rows i+2 (i+3 has tap 0)
-            uint32_t v[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                v[b] = dot2u(pc[b], T0z, dot2u(pb[b], T21, dot2u(pa[b], T01, kVRound)));
-            const uint32_t q0 = perm(v[1], v[0], kVSel);  // V of columns c, c+1
-            const uint32_t q1 = perm(v[3], v[2], kVSel);  // V of columns c+2, c+3
-            const uint32_t ql = from_left(q1);            // V of columns c-2, c-1
-            const uint32_t qr = from_right(q0);           // V of columns c+4, c+5
-            const uint32_t h0 = dot2u(q1, T0z, dot2u(q0, T21, dot2u(ql, T01, 32768u)));
-            const uint32_t h1 = dot2u(q1, T10, dot2u(q0, T12, dot2u(ql, Tz0, 32768u)));
-            const uint32_t h2 = dot2u(qr, T0z, dot2u(q1, T21, dot2u(q0, T01, 32768u)));
-            const uint32_t h3 = dot2u(qr, T10, dot2u(q1, T12, dot2u(q0, Tz0, 32768u)));
-            const uint32_t c0 = perm(h1, h0, 0x07060302u);  // Bl of columns c, c+1
-            const uint32_t c1 = perm(h3, h2, 0x07060302u);  // Bl of columns c+2, c+3
-            if (r0 + i < H) {
-                acc_c = dot2u(c1, w1, dot2u(c0, w0, acc_c));
-                if (have_prev)
-                    acc_min = dot2u(pkmin(c1, prev1[i]), w1, dot2u(pkmin(c0, prev0[i]), w0, acc_min));
-            }
-            prev0[i] = c0;
-            prev1[i] = c1;
-        }
-
-        if (!prologue) {
-            // SSE of the luma tile
-            uint32_t sy = 0, sy2 = 0;
-#pragma unroll
-            for (int i = 0; i < TH; ++i) {
-                const int row = r0 + i;
-                if (row < H) {
-                    const Luma r = R[i + 2];
-                    const Luma d = load_dist<BPC>(fp[3] + (int64_t)row * a.pitch[3], c, W, out_lane,
-                                                  out_full, r);
-                    if (out_lane) {
-                        if constexpr (BPC == 8) {
-                            sy = dot4u(d, d, dot4u(r, r, sy));
-                            sy2 = dot4u(r, d, sy2);
-                        } else {
-                            sy = sqdiff2(r.y, d.y, sqdiff2(r.x, d.x, sy));
-                        }
-                    }
-                }
-            }
-            // SSE of the chroma tiles
-            uint32_t su = 0, su2 = 0, sv = 0, sv2 = 0;
-#pragma unroll
-            for (int k = 0; k < TH / 2; ++k) {
-                if (k < csteps) {
-                    const int row = crow0 + crow_step * k;
-                    const bool on = c_on && row < a.Hc;
-                    const int64_t ro = (int64_t)(on ? row : 0);
-                    const uint32_t ru = load_chroma<BPC>(fp[1] + ro * a.pitch[1], ccol, a.Wc, on);
-                    const uint32_t du = load_chroma<BPC>(fp[4] + ro * a.pitch[4], ccol, a.Wc, on);
-                    const uint32_t rv = load_chroma<BPC>(fp[2] + ro * a.pitch[2], ccol, a.Wc, on);
-                    const uint32_t dv = load_chroma<BPC>(fp[5] + ro * a.pitch[5], ccol, a.Wc, on);
-                    if constexpr (BPC == 8) {
-                        su = dot4u(du, du, dot4u(ru, ru, su));
-                        su2 = dot4u(ru, du, su2);
-                        sv = dot4u(dv, dv, dot4u(rv, rv, sv));
-                        sv2 = dot4u(rv, dv, sv2);
-                    } else {
-                        su = sqdiff2(ru, du, su);
-                        sv = sqdiff2(rv, dv, sv);
-                    }
-                }
-            }
-            const uint32_t sad = have_prev ? acc_c + sum_prev - 2u * acc_min : 0u;
-            const unsigned long long t_sad = wave_sum(sad);
-            const unsigned long long t_y = wave_sum(sy - 2u * sy2);
-            const unsigned long long t_u = wave_sum(su - 2u * su2);
-            const unsigned long long t_v = wave_sum(sv - 2u * sv2);
-            if (lane == 0) {
-                unsigned long long *o = a.sums + (size_t)t * (kSums * kSumSlots) + slot;
-                add_sum(o, t_sad);
-                add_sum(o + kSumSlots, t_y);
-                add_sum(o + 2 * kSumSlots, t_u);
-                add_sum(o + 3 * kSumSlots, t_v);
-            }
-        }
-        sum_prev = acc_c;
-        have_prev = true;
-    }
-
-    if (chunk == a.chunks - 1) {
+    if (T.chunk == a.chunks - 1) {
         uint2 *rout = reinterpret_cast<uint2 *>(a.ring_out);
 #pragma unroll
         for (int i = 0; i < TH; ++i)
-            rout[(tile * TH + i) * kWave + lane] = make_uint2(prev0[i], prev1[i]);
+            rout[(T.tile * TH + i) * kWave + lane] = make_uint2(prev0[i], prev1[i]);
     }
 }
 

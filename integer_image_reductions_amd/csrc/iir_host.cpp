@@ -80,6 +80,7 @@ struct iir_ctx {
     int bps = 1;  // bytes per sample
     int Wc = 0, Hc = 0;
     int lanes_out = 0, strips = 0, row_tiles = 0, tiles = 0;
+    int rows_per_tile = 16;
     int target_waves = 1024;
     int min_chunk = 4;
     int max_chunks = 1;
@@ -175,15 +176,42 @@ const uint8_t *plane_ptr(const iir_frame *ref, const iir_frame *dist, int t, int
 
 // Columns: strips of up to kMaxLanesOut output lanes (4 columns each), balanced and even so the
 // 4:2:0 chroma tile of a strip starts on a dword.
-void choose_geometry(iir_ctx *c)
+void choose_columns(iir_ctx *c)
 {
     const int dwords = (c->cfg.width + kLumaCols - 1) / kLumaCols;
     c->strips = (dwords + kMaxLanesOut - 1) / kMaxLanesOut;
     int lanes = (dwords + c->strips - 1) / c->strips;
     lanes += lanes & 1;
     c->lanes_out = std::max(2, lanes);
-    c->row_tiles = (c->cfg.height + kRowsPerTile - 1) / kRowsPerTile;
-    c->tiles = c->strips * c->row_tiles;
+}
+
+// Rows per tile: each candidate's kernel has its own register footprint and hence its own number
+// of resident wavefronts per CU. A launch whose tiles all fit at once finishes when its busiest
+// SIMD does, so the estimated cost is (wavefronts per SIMD, rounded up) x (rows + the 4 halo
+// rows each tile re-reads), times the number of rounds when they do not all fit.
+int choose_rows(iir_ctx *c, int cus, int forced)
+{
+    static const int kCandidates[] = {12, 16, 20};
+    int best = 16;
+    double best_cost = 1e300;
+    for (int th : kCandidates) {
+        if (forced && th != forced)
+            continue;
+        int per_cu = 0;
+        if (frames_occupancy(c->cfg.bpc, th, &per_cu) != hipSuccess || per_cu < 1)
+            continue;
+        const int64_t waves = (int64_t)c->strips * ((c->cfg.height + th - 1) / th);
+        const int64_t slots = (int64_t)per_cu * cus;
+        const int64_t simds = 4LL * cus;
+        const int64_t rounds = (waves + slots - 1) / slots;
+        const int64_t per_simd = (std::min(waves, slots) + simds - 1) / simds;
+        const double cost = (double)rounds * (double)per_simd * (th + 4);
+        if (cost < best_cost - 1e-9 || (cost <= best_cost + 1e-9 && th > best)) {
+            best_cost = cost;
+            best = th;
+        }
+    }
+    return best;
 }
 
 int plan_chunks(const iir_ctx *c, int nframes)
@@ -293,7 +321,7 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     const bool timing = (c->cfg.flags & IIR_FLAG_TIMING) != 0;
     if (timing)
         HIP_TRY(hipEventRecord(c->k0, c->stream));
-    HIP_TRY(launch_frames(c->cfg.bpc, a, c->stream));
+    HIP_TRY(launch_frames(c->cfg.bpc, c->rows_per_tile, a, c->stream));
     if (timing)
         HIP_TRY(hipEventRecord(c->k1, c->stream));
     c->timed = timing;
@@ -347,7 +375,10 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     c->bps = cfg->bpc == 8 ? 1 : 2;
     c->Wc = (cfg->width + 1) / 2;
     c->Hc = (cfg->height + 1) / 2;
-    choose_geometry(c);
+    choose_columns(c);
+    c->rows_per_tile = choose_rows(c, prop.multiProcessorCount, env_int("IIR_ROWS_PER_TILE", 0, 0, 64));
+    c->row_tiles = (cfg->height + c->rows_per_tile - 1) / c->rows_per_tile;
+    c->tiles = c->strips * c->row_tiles;
     c->target_waves = env_int("IIR_TARGET_WAVES", 4 * prop.multiProcessorCount, 1, 1 << 20);
     c->min_chunk = env_int("IIR_MIN_CHUNK", 4, 1, 65536);
     c->max_chunks = plan_chunks(c, cfg->max_batch);
@@ -360,7 +391,7 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     c->has_motion.assign(cfg->max_batch, 0);
     c->sums_n = (int64_t)cfg->max_batch * kSums * kSumSlots;
 
-    const size_t ring_bytes = (size_t)c->tiles * kRowsPerTile * kWave * sizeof(uint2);
+    const size_t ring_bytes = (size_t)c->tiles * c->rows_per_tile * kWave * sizeof(uint2);
     hipError_t e = hipSuccess;
     for (int i = 0; i < 2 && e == hipSuccess; ++i) {
         e = hipMalloc(&c->ring[i], ring_bytes);
@@ -501,8 +532,8 @@ IIR_API int iir_export_blur(iir_ctx *ctx, void *dst, int64_t pitch)
     if (ds.err != hipSuccess)
         return fail_hip(ds.err, "hipSetDevice");
     HIP_TRY(launch_export(ctx->ring[ctx->ring_cur], static_cast<uint16_t *>(dst), pitch,
-                          ctx->cfg.width, ctx->cfg.height, ctx->lanes_out, ctx->row_tiles,
-                          ctx->stream));
+                          ctx->cfg.width, ctx->cfg.height, ctx->lanes_out, ctx->strips,
+                          ctx->rows_per_tile, ctx->stream));
     return IIR_OK;
 }
 
@@ -528,7 +559,7 @@ IIR_API int iir_get_geometry(const iir_ctx *ctx, iir_geometry *out)
 {
     if (!ctx || !out)
         return fail(IIR_EINVAL, "NULL argument");
-    out->rows_per_tile = kRowsPerTile;
+    out->rows_per_tile = ctx->rows_per_tile;
     out->lanes_out = ctx->lanes_out;
     out->strips = ctx->strips;
     out->row_tiles = ctx->row_tiles;

@@ -11,7 +11,6 @@
 namespace iir {
 
 constexpr int kWave = 64;          // CDNA wavefront; one wavefront is one workgroup
-constexpr int kRowsPerTile = 16;   // output luma rows per tile (even, multiple of 4)
 constexpr int kMaxLanesOut = 62;   // output lanes per wavefront: lane 0 and lane lanes_out + 1
                                    // are the left and right halo lanes
 constexpr int kSumSlots = 8;       // partial slots per sum (one per XCD), added up on the host
@@ -32,7 +31,8 @@ struct KernelArgs {
     uint32_t span[6];  // readable bytes of each plane (rows * pitch), below 2^32
     const FramePtrs *table;
     // blurred reference luma of the frame before this launch (read when has_prev), and of the
-    // launch's last frame (written); tiled: uint2 at [(tile * kRowsPerTile + row) * kWave + lane]
+    // launch's last frame (written); tiled: uint2 at [(tile * TH + row) * kWave + lane], TH the
+    // launch's rows per tile
     const uint32_t *ring_in;
     uint32_t *ring_out;
     // per-frame sums [nframes][kSums][kSumSlots], zeroed before the launch
@@ -47,9 +47,12 @@ struct KernelArgs {
 };
 
 // Host-side launchers (iir_kernels.hip). Each returns the launch's hipError_t.
-hipError_t launch_frames(int bpc, const KernelArgs &a, hipStream_t stream);
+bool supported_rows_per_tile(int th);  // 12, 16 or 20
+hipError_t frames_attributes(int bpc, int th, hipFuncAttributes *attr);
+hipError_t frames_occupancy(int bpc, int th, int *waves_per_cu);
+hipError_t launch_frames(int bpc, int th, const KernelArgs &a, hipStream_t stream);
 hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
-                         int lanes_out, int row_tiles, hipStream_t stream);
+                         int lanes_out, int strips, int th, hipStream_t stream);
 hipError_t launch_probe(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream);
 
 }  // namespace iir

@@ -11,7 +11,7 @@
 // "Research-0735: CUDA motion kernel ncu hotpath analysis (576x324)": a 5x5 separable Gaussian).
 //
 // Design (MI355X-first; the CUDA tiles on the pages are prior art only):
-//   * One wavefront per workgroup owns one tile: 4 * lanes_out luma columns x kRowsPerTile rows.
+//   * One wavefront per workgroup owns one tile: 4 * lanes_out luma columns x TH rows.
 //     Lane l holds 4 adjacent luma columns; lanes 0 and lanes_out + 1 only feed the horizontal
 //     halo. Each lane slides down its columns with the whole 5-row window in registers, so every
 //     vertical value is computed exactly once and reused by the five horizontal taps through two
@@ -104,7 +104,9 @@ __device__ __forceinline__ int mirror_clamp(int i, int n)
 }
 
 // XCD-aware tile order: hardware places workgroup b on XCD b % 8; give each XCD one contiguous
-// run of the linear (chunk, strip, row tile) order. A bijection on [0, G) for any G.
+// run of the linear (chunk, row tile, strip) order. A bijection on [0, G) for any G. With strips
+// fastest, the wavefronts resident together cover whole rows of the frame, so HBM sees long
+// contiguous runs instead of a scatter of 256-byte pieces.
 __device__ __forceinline__ int xcd_linear(int b, int G)
 {
     const int x = b & 7, j = b >> 3;
@@ -112,23 +114,69 @@ __device__ __forceinline__ int xcd_linear(int b, int G)
     return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
 }
 
-// Sum of a per-lane u32 over the wavefront as u64: butterflies inside each 32-lane half (each half
-// sum stays below 2^32 for every accumulator here), then the two halves added in 64 bits.
+// Sum of a per-lane u32 over the wavefront as u64. DPP row shifts fold each row of 16 lanes into
+// its lane 15 (4 adds, no LDS round trip); the four row sums are added in 64 bits on the scalar
+// unit, so a wavefront total may exceed 2^32 while each row sum stays below it.
+template <int CTRL>
+__device__ __forceinline__ uint32_t row_shr_add(uint32_t v)
+{
+    return v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, true);
+}
+
 __device__ __forceinline__ unsigned long long wave_sum(uint32_t v)
 {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 8);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 1);
-    const uint32_t lo = __builtin_amdgcn_readlane(v, 0);
-    const uint32_t hi = __builtin_amdgcn_readlane(v, 32);
-    return (unsigned long long)lo + hi;
+    v = row_shr_add<0x111>(v);  // row_shr:1
+    v = row_shr_add<0x112>(v);  // row_shr:2
+    v = row_shr_add<0x114>(v);  // row_shr:4
+    v = row_shr_add<0x118>(v);  // row_shr:8
+    const unsigned long long r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+    const unsigned long long r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const unsigned long long r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+    const unsigned long long r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+    return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ void add_sum(unsigned long long *p, unsigned long long v)
 {
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Per-frame wavefront sums waiting for their atomics. Lane q of v[] holds queued frame q's four
+// 64-bit sums (low and high halves); a flush issues every queued
+// frame's atomics at once, one frame per lane. On gfx9 stores and atomics share the in-order
+// vmcnt counter with loads, so an atomic issued right after a frame would make the next frame's
+// first load wait for the atomic's round trip; batching keeps them off the frame loop.
+struct Pending {
+    uint32_t v[2 * kSums];
+    int first;  // frame of queue slot 0 (wave-uniform)
+    int count;  // queued frames (wave-uniform)
+};
+
+__device__ __forceinline__ void flush_sums(const KernelArgs &a, Pending &P, int lane)
+{
+    if (lane < P.count) {
+        unsigned long long *o = a.sums + (size_t)(P.first + lane) * (kSums * kSumSlots) +
+                                (blockIdx.x & (kSumSlots - 1));
+#pragma unroll
+        for (int k = 0; k < kSums; ++k)
+            add_sum(o + k * kSumSlots,
+                    ((unsigned long long)P.v[2 * k + 1] << 32) | (unsigned long long)P.v[2 * k]);
+    }
+    P.first += P.count;
+    P.count = 0;
+}
+
+__device__ __forceinline__ void push_sums(const KernelArgs &a, Pending &P, int lane,
+                                          const unsigned long long (&s)[kSums])
+{
+    const bool mine = lane == P.count;
+#pragma unroll
+    for (int k = 0; k < kSums; ++k) {
+        P.v[2 * k] = mine ? (uint32_t)s[k] : P.v[2 * k];
+        P.v[2 * k + 1] = mine ? (uint32_t)(s[k] >> 32) : P.v[2 * k + 1];
+    }
+    if (++P.count == kWave)
+        flush_sums(a, P, lane);
 }
 
 template <int BPC>
@@ -283,23 +331,70 @@ struct Tile {
     bool c_upper;                // 8-bit: lane reads the second chroma row of each step
 };
 
-// One frame of one tile: blur the reference luma (vertical pass once per column and row,
-// horizontal taps through DPP neighbours), SAD against the previous blurred tile held in
-// registers, SSE of the luma and chroma tiles, one wavefront reduction and one atomic per sum.
-// CAREFUL adds the frame-edge mirror fix-ups, ragged rows and masked tails; interior tiles (the
-// vast majority) run without any of it.
-template <int BPC, bool CAREFUL>
-__device__ __forceinline__ void frame_pass(const KernelArgs &a, const Tile &T, int t,
-                                           bool accumulate, uint32_t (&prev0)[kRowsPerTile],
-                                           uint32_t (&prev1)[kRowsPerTile], uint32_t &sum_prev,
-                                           bool &have_prev)
-{
+// The loaded samples of one frame for one tile: reference luma rows r0-2 .. r0+TH+1, distorted
+// luma rows r0 .. r0+TH-1, and the chroma dwords (ref U, dist U, ref V, dist V) of each step
+// (8-bit steps cover two chroma rows, one per half-wave).
+template <int BPC, int TH>
+struct FrameData {
     typedef typename Px<BPC>::Luma Luma;
-    constexpr int TH = kRowsPerTile;
-    constexpr uint32_t kVRound = BPC == 8 ? 128u : 32768u;
-    constexpr uint32_t kVSel = BPC == 8 ? 0x06050201u : 0x07060302u;
-    const int H = a.H;
+    static constexpr int kChromaSteps = BPC == 8 ? TH / 4 : TH / 2;
+    static constexpr int kChromaStep = BPC == 8 ? 2 : 1;
+    Luma R[TH + 4];
+    Luma D[TH];
+    uint32_t cu[kChromaSteps], du[kChromaSteps], cv[kChromaSteps], dv[kChromaSteps];
+};
 
+// LDS staging of one frame (one wavefront per workgroup, so the workgroup's LDS is the wave's):
+// each row is one dword per lane (256 bytes), filled by buffer loads that write LDS directly
+// (no VGPRs held while the load is in flight). 10-bit luma rows take two dword rows.
+template <int BPC, int TH>
+struct Stage {
+    static constexpr int kLumaDw = BPC == 8 ? 1 : 2;
+    static constexpr int kRef = 0;
+    static constexpr int kDist = (TH + 4) * kLumaDw;
+    static constexpr int kChroma = kDist + TH * kLumaDw;
+    static constexpr int kRows = kChroma + 4 * FrameData<BPC, TH>::kChromaSteps;
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Fetch one lane value into a register (STAGED false) or into LDS row `row` (STAGED true).
+template <bool STAGED>
+__device__ __forceinline__ void fetch32(Rsrc r, uint32_t voff, uint32_t soff, uint32_t &reg,
+                                        uint32_t (*lds)[kWave], int row)
+{
+    if constexpr (STAGED)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)&lds[row][0], 4, voff, soff, 0, 0);
+    else
+        reg = ld32(r, voff, soff);
+}
+
+template <int BPC, bool STAGED>
+__device__ __forceinline__ void fetch_luma(Rsrc r, uint32_t voff, uint32_t soff,
+                                           typename Px<BPC>::Luma &reg, uint32_t (*lds)[kWave],
+                                           int row)
+{
+    if constexpr (!STAGED) {
+        reg = ld_luma<BPC>(r, voff, soff);
+    } else if constexpr (BPC == 8) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)&lds[row][0], 4, voff, soff, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)&lds[2 * row][0], 4, voff, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)&lds[2 * row + 1][0], 4, voff + 4,
+                                                 soff, 0, 0);
+    }
+}
+
+// Issue every load of frame t for this tile, into registers or into the LDS stage (the distorted
+// planes and chroma only when the frame is accumulated; a chunk's prologue frame is only blurred).
+template <int BPC, int TH, bool CAREFUL, bool STAGED>
+__device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, int t,
+                                           bool accumulate, FrameData<BPC, TH> &F,
+                                           uint32_t (*lds)[kWave])
+{
+    typedef FrameData<BPC, TH> FD;
+    typedef Stage<BPC, TH> ST;
+    const int H = a.H;
     Rsrc rs[6];
     uint32_t pitch[6];
 #pragma unroll
@@ -307,60 +402,90 @@ __device__ __forceinline__ void frame_pass(const KernelArgs &a, const Tile &T, i
         rs[k] = plane_rsrc(frame_plane(a, t, k), a.span[k]);
         pitch[k] = opaque((uint32_t)a.pitch[k]);
     }
-
-    // reference luma rows r0-2 .. r0+TH+1, mirrored at the top and bottom
-    Luma R[TH + 5];
 #pragma unroll
     for (int k = 0; k < TH + 4; ++k) {
         const int row = CAREFUL ? mirror_clamp(T.r0 - 2 + k, H) : T.r0 - 2 + k;
-        R[k] = ld_luma<BPC>(rs[0], T.luma_off, (uint32_t)row * pitch[0]);
+        fetch_luma<BPC, STAGED>(rs[0], T.luma_off, (uint32_t)row * pitch[0], F.R[k], lds,
+                                ST::kRef / ST::kLumaDw + k);
     }
-    R[TH + 4] = Luma{};
-
-    // distorted luma rows of the tile (rows past the frame re-read the last row; not counted)
-    Luma D[TH];
-    if (accumulate) {
+    if (!accumulate)
+        return;
 #pragma unroll
-        for (int i = 0; i < TH; ++i) {
-            const int row = CAREFUL ? min(T.r0 + i, H - 1) : T.r0 + i;
-            D[i] = ld_luma<BPC>(rs[3], T.luma_off, (uint32_t)row * pitch[3]);
-        }
+    for (int i = 0; i < TH; ++i) {
+        // rows past the frame re-read the last row; they are not counted
+        const int row = CAREFUL ? min(T.r0 + i, H - 1) : T.r0 + i;
+        fetch_luma<BPC, STAGED>(rs[3], T.luma_off, (uint32_t)row * pitch[3], F.D[i], lds,
+                                ST::kDist / ST::kLumaDw + i);
     }
-
-    // chroma dwords of the tile: ref U, dist U, ref V, dist V; 8-bit steps cover two rows
-    constexpr int CS = BPC == 8 ? TH / 4 : TH / 2;
-    constexpr int CSTEP = BPC == 8 ? 2 : 1;
-    uint32_t cu[CS], du[CS], cv[CS], dv[CS];
-    if (accumulate) {
 #pragma unroll
-        for (int k = 0; k < CS; ++k) {
-            // the upper half-wave's row is one further down (its coff adds a pitch); at a ragged
-            // bottom every lane whose row is past the plane re-reads the last row instead
-            const int row = T.crow0 + CSTEP * k;
-            if constexpr (CAREFUL) {
-                const int rl = min(row, a.Hc - 1);
-                const bool up = T.c_upper && row + 1 < a.Hc;
-                cu[k] = ld32(rs[1], T.coff[0] - (T.c_upper && !up ? pitch[1] : 0u), (uint32_t)rl * pitch[1]);
-                du[k] = ld32(rs[4], T.coff[1] - (T.c_upper && !up ? pitch[4] : 0u), (uint32_t)rl * pitch[4]);
-                cv[k] = ld32(rs[2], T.coff[2] - (T.c_upper && !up ? pitch[2] : 0u), (uint32_t)rl * pitch[2]);
-                dv[k] = ld32(rs[5], T.coff[3] - (T.c_upper && !up ? pitch[5] : 0u), (uint32_t)rl * pitch[5]);
-            } else {
-                cu[k] = ld32(rs[1], T.coff[0], (uint32_t)row * pitch[1]);
-                du[k] = ld32(rs[4], T.coff[1], (uint32_t)row * pitch[4]);
-                cv[k] = ld32(rs[2], T.coff[2], (uint32_t)row * pitch[2]);
-                dv[k] = ld32(rs[5], T.coff[3], (uint32_t)row * pitch[5]);
-            }
-        }
+    for (int k = 0; k < FD::kChromaSteps; ++k) {
+        // the upper half-wave's row is one further down (its coff adds a pitch); at a ragged
+        // bottom every lane whose row is past the plane re-reads the last row instead
+        const int row = T.crow0 + FD::kChromaStep * k;
+        const int rl = CAREFUL ? min(row, a.Hc - 1) : row;
+        const bool back = CAREFUL && T.c_upper && row + 1 >= a.Hc;
+        const int lr = ST::kChroma + 4 * k;
+        fetch32<STAGED>(rs[1], T.coff[0] - (back ? pitch[1] : 0u), (uint32_t)rl * pitch[1], F.cu[k], lds, lr);
+        fetch32<STAGED>(rs[4], T.coff[1] - (back ? pitch[4] : 0u), (uint32_t)rl * pitch[4], F.du[k], lds, lr + 1);
+        fetch32<STAGED>(rs[2], T.coff[2] - (back ? pitch[2] : 0u), (uint32_t)rl * pitch[2], F.cv[k], lds, lr + 2);
+        fetch32<STAGED>(rs[5], T.coff[3] - (back ? pitch[5] : 0u), (uint32_t)rl * pitch[5], F.dv[k], lds, lr + 3);
     }
+}
+
+// The staged frame, from LDS into registers.
+template <int BPC, int TH>
+__device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWave], int lane,
+                                           FrameData<BPC, TH> &F)
+{
+    typedef FrameData<BPC, TH> FD;
+    typedef Stage<BPC, TH> ST;
+    auto luma = [&](int row) {
+        if constexpr (BPC == 8)
+            return lds[row][lane];
+        else
+            return u32x2{lds[2 * row][lane], lds[2 * row + 1][lane]};
+    };
+#pragma unroll
+    for (int k = 0; k < TH + 4; ++k)
+        F.R[k] = luma(ST::kRef / ST::kLumaDw + k);
+    if (!accumulate)
+        return;
+#pragma unroll
+    for (int i = 0; i < TH; ++i)
+        F.D[i] = luma(ST::kDist / ST::kLumaDw + i);
+#pragma unroll
+    for (int k = 0; k < FD::kChromaSteps; ++k) {
+        F.cu[k] = lds[ST::kChroma + 4 * k][lane];
+        F.du[k] = lds[ST::kChroma + 4 * k + 1][lane];
+        F.cv[k] = lds[ST::kChroma + 4 * k + 2][lane];
+        F.dv[k] = lds[ST::kChroma + 4 * k + 3][lane];
+    }
+}
+
+// One frame of one tile from its loaded samples: blur the reference luma (vertical pass once per
+// column and row, horizontal taps through DPP neighbours), SAD against the previous blurred tile
+// held in registers, SSE of the luma and chroma tiles, one wavefront reduction and one atomic per
+// sum. CAREFUL adds the frame-edge mirror fix-ups, ragged rows and masked tails; interior tiles
+// (the vast majority) run without any of it.
+template <int BPC, int TH, bool CAREFUL>
+__device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T, int t,
+                                              bool accumulate, const FrameData<BPC, TH> &F,
+                                              uint32_t (&prev0)[TH], uint32_t (&prev1)[TH],
+                                              uint32_t &sum_prev, bool &have_prev, Pending &P)
+{
+    typedef typename Px<BPC>::Luma Luma;
+    typedef FrameData<BPC, TH> FD;
+    constexpr uint32_t kVRound = BPC == 8 ? 128u : 32768u;
+    constexpr uint32_t kVSel = BPC == 8 ? 0x06050201u : 0x07060302u;
 
     // SSE of the chroma tiles first, which frees their registers before the blur
     uint32_t su = 0, su2 = 0, sv = 0, sv2 = 0;
     if (accumulate) {
 #pragma unroll
-        for (int k = 0; k < CS; ++k) {
-            uint32_t ru = cu[k], rdu = du[k], rv = cv[k], rdv = dv[k];
+        for (int k = 0; k < FD::kChromaSteps; ++k) {
+            uint32_t ru = F.cu[k], rdu = F.du[k], rv = F.cv[k], rdv = F.dv[k];
             if constexpr (CAREFUL) {
-                const int row = T.crow0 + CSTEP * k + (T.c_upper ? 1 : 0);
+                const int row = T.crow0 + FD::kChromaStep * k + (T.c_upper ? 1 : 0);
                 const uint32_t m = row < a.Hc ? T.cm : 0u;
                 ru &= m;
                 rdu &= m;
@@ -377,9 +502,10 @@ __device__ __forceinline__ void frame_pass(const KernelArgs &a, const Tile &T, i
 #pragma unroll
     for (int i = 0; i < TH; ++i) {
         uint32_t pa[4], pb[4], pc[4];
-        column_pairs<BPC>(R[i], R[i + 1], pa);      // rows i-2, i-1
-        column_pairs<BPC>(R[i + 2], R[i + 3], pb);  // rows i,   i+1
-        column_pairs<BPC>(R[i + 4], R[i + 5], pc);  // rows i+2 (i+3 has tap 0)
+        const Luma zero{};
+        column_pairs<BPC>(F.R[i], F.R[i + 1], pa);                            // rows i-2, i-1
+        column_pairs<BPC>(F.R[i + 2], F.R[i + 3], pb);                        // rows i,   i+1
+        column_pairs<BPC>(F.R[i + 4], i + 5 < TH + 4 ? F.R[i + 5] : zero, pc);  // rows i+2 (tap 0 on i+3)
         uint32_t v[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -416,7 +542,7 @@ __device__ __forceinline__ void frame_pass(const KernelArgs &a, const Tile &T, i
             acc_c = dot2u(c1, T.w1, dot2u(c0, T.w0, acc_c));
             acc_min = dot2u(pkmin(c1, prev1[i]), T.w1, dot2u(pkmin(c0, prev0[i]), T.w0, acc_min));
             if (accumulate) {
-                Luma r = R[i + 2], d = D[i];
+                Luma r = F.R[i + 2], d = F.D[i];
                 if constexpr (CAREFUL) {
                     r = masked<BPC>(r, T.ym0, T.ym1);
                     d = masked<BPC>(d, T.ym0, T.ym1);
@@ -430,42 +556,65 @@ __device__ __forceinline__ void frame_pass(const KernelArgs &a, const Tile &T, i
 
     if (accumulate) {
         const uint32_t sad = have_prev ? acc_c + sum_prev - 2u * acc_min : 0u;
-        const unsigned long long t_sad = wave_sum(sad);
-        const unsigned long long t_y = wave_sum(T.out_lane ? sy - 2u * sy2 : 0u);
-        const unsigned long long t_u = wave_sum(T.c_on ? su - 2u * su2 : 0u);
-        const unsigned long long t_v = wave_sum(T.c_on ? sv - 2u * sv2 : 0u);
-        if (T.lane == 0) {
-            unsigned long long *o =
-                a.sums + (size_t)t * (kSums * kSumSlots) + (blockIdx.x & (kSumSlots - 1));
-            add_sum(o, t_sad);
-            add_sum(o + kSumSlots, t_y);
-            add_sum(o + 2 * kSumSlots, t_u);
-            add_sum(o + 3 * kSumSlots, t_v);
-        }
+        const unsigned long long sums[kSums] = {wave_sum(sad),
+                                                wave_sum(T.out_lane ? sy - 2u * sy2 : 0u),
+                                                wave_sum(T.c_on ? su - 2u * su2 : 0u),
+                                                wave_sum(T.c_on ? sv - 2u * sv2 : 0u)};
+        push_sums(a, P, T.lane, sums);
     }
     sum_prev = acc_c;
     have_prev = true;
 }
 
-template <int BPC, bool CAREFUL>
+// The frames of this workgroup's time chunk. Chunks after the first start by re-blurring the
+// frame before them. STAGED keeps the next frame's loads in flight while the current one is
+// computed: the loads of frame t+1 write the wave's LDS stage (no registers held), issued as soon
+// as frame t has been read out of it.
+template <int BPC, int TH, bool CAREFUL, bool STAGED>
 __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
-                                           uint32_t (&prev0)[kRowsPerTile],
-                                           uint32_t (&prev1)[kRowsPerTile], uint32_t sum_prev,
-                                           bool have_prev)
+                                           uint32_t (&prev0)[TH], uint32_t (&prev1)[TH],
+                                           uint32_t sum_prev, bool have_prev,
+                                           uint32_t (*lds)[kWave])
 {
-    // time chunk of this workgroup; chunks after the first re-blur the frame before them
     const int f_begin = uni(T.chunk * a.chunk_len);
     const int f_end = uni(min(f_begin + a.chunk_len, a.nframes));
-    if (T.chunk > 0)
-        frame_pass<BPC, CAREFUL>(a, T, f_begin - 1, false, prev0, prev1, sum_prev, have_prev);
-    for (int t = f_begin; t < f_end; ++t)
-        frame_pass<BPC, CAREFUL>(a, T, t, true, prev0, prev1, sum_prev, have_prev);
+    const int t0 = T.chunk > 0 ? f_begin - 1 : f_begin;
+    Pending P;
+#pragma unroll
+    for (int k = 0; k < 2 * kSums; ++k)
+        P.v[k] = 0;
+    P.first = f_begin;
+    P.count = 0;
+    if constexpr (STAGED) {
+        FrameData<BPC, TH> F;
+        load_frame<BPC, TH, CAREFUL, true>(a, T, t0, t0 >= f_begin, F, lds);
+        for (int t = t0; t < f_end; ++t) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): frame t is in LDS
+            read_stage<BPC, TH>(t >= f_begin, lds, T.lane, F);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 1 < f_end)
+                load_frame<BPC, TH, CAREFUL, true>(a, T, t + 1, true, F, lds);
+            compute_frame<BPC, TH, CAREFUL>(a, T, t, t >= f_begin, F, prev0, prev1, sum_prev,
+                                            have_prev, P);
+        }
+    } else {
+        for (int t = t0; t < f_end; ++t) {
+            FrameData<BPC, TH> F;
+            load_frame<BPC, TH, CAREFUL, false>(a, T, t, t >= f_begin, F, lds);
+            compute_frame<BPC, TH, CAREFUL>(a, T, t, t >= f_begin, F, prev0, prev1, sum_prev,
+                                            have_prev, P);
+        }
+    }
+    flush_sums(a, P, T.lane);
 }
 
-template <int BPC>
-__global__ __launch_bounds__(kWave) void frames_kernel(const KernelArgs a)
+template <int BPC, int TH, bool STAGED, int WPE>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void frames_kernel(
+    const KernelArgs a)
 {
-    constexpr int TH = kRowsPerTile;
+    __shared__ uint32_t stage[STAGED ? Stage<BPC, TH>::kRows : 1][kWave];
+    static_assert(TH % 4 == 0, "tile height must be a multiple of 4 (two chroma rows per step)");
     constexpr int B = Px<BPC>::kBytes;
     const int lane = threadIdx.x;
 
@@ -477,8 +626,9 @@ __global__ __launch_bounds__(kWave) void frames_kernel(const KernelArgs a)
     const int L = uni(xcd_linear(blockIdx.x, gridDim.x));
     T.chunk = uni(L / a.tiles);
     T.tile = uni(L - T.chunk * a.tiles);
-    T.strip = uni(T.tile / a.row_tiles);
-    T.r0 = uni((T.tile - T.strip * a.row_tiles) * TH);  // first output row of the tile
+    const int rt = uni(T.tile / a.strips);
+    T.strip = uni(T.tile - rt * a.strips);
+    T.r0 = uni(rt * TH);                                   // first output row of the tile
     const int s = uni(T.strip * kLumaCols * a.lanes_out);  // first output column of the tile
     T.lane = lane;
     const int W = a.W, H = a.H;
@@ -555,9 +705,9 @@ __global__ __launch_bounds__(kWave) void frames_kernel(const KernelArgs a)
     const bool careful = T.strip == 0 || T.strip == a.strips - 1 || T.r0 < 2 ||
                          T.r0 + TH + 2 > H;
     if (careful)
-        frame_loop<BPC, true>(a, T, prev0, prev1, sum_prev, have_prev);
+        frame_loop<BPC, TH, true, STAGED>(a, T, prev0, prev1, sum_prev, have_prev, stage);
     else
-        frame_loop<BPC, false>(a, T, prev0, prev1, sum_prev, have_prev);
+        frame_loop<BPC, TH, false, STAGED>(a, T, prev0, prev1, sum_prev, have_prev, stage);
 
     if (T.chunk == a.chunks - 1) {
         uint2 *rout = reinterpret_cast<uint2 *>(a.ring_out);
@@ -569,7 +719,7 @@ __global__ __launch_bounds__(kWave) void frames_kernel(const KernelArgs a)
 
 // Tiled blurred state -> W x H uint16 plane.
 __global__ void export_kernel(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
-                              int lanes_out, int row_tiles)
+                              int lanes_out, int strips, int th)
 {
     const int pairs = (W + 1) / 2;
     const int64_t n = (int64_t)pairs * H;
@@ -582,8 +732,8 @@ __global__ void export_kernel(const uint32_t *ring, uint16_t *dst, int64_t pitch
         const int in = j - strip * sw;
         const int lane = in / kLumaCols + 1;
         const int half = (in % kLumaCols) / 2;
-        const int tile = strip * row_tiles + row / kRowsPerTile;
-        const uint32_t w = ring[(((int64_t)tile * kRowsPerTile + row % kRowsPerTile) * kWave + lane) * 2 + half];
+        const int tile = (row / th) * strips + strip;
+        const uint32_t w = ring[(((int64_t)tile * th + row % th) * kWave + lane) * 2 + half];
         uint16_t *d = reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(dst) + row * pitch);
         d[j] = (uint16_t)(w & 0xffffu);
         if (j + 1 < W)
@@ -622,25 +772,82 @@ __global__ __launch_bounds__(256) void probe_copy(const uint4 *src, uint4 *dst, 
         dst[i] = src[i];
 }
 
+typedef void (*FramesFn)(KernelArgs);
+
+#ifndef IIR_STAGE8
+#define IIR_STAGE8 1
+#endif
+#ifndef IIR_STAGE10
+#define IIR_STAGE10 0
+#endif
+#ifndef IIR_WPE12
+#define IIR_WPE12 3
+#endif
+#ifndef IIR_WPE16
+#define IIR_WPE16 2
+#endif
+#ifndef IIR_WPE20
+#define IIR_WPE20 2
+#endif
+
+// Every (bit depth, tile height) the host may pick, and whether its frames go through the LDS
+// stage.
+template <int BPC>
+FramesFn frames_fn(int th)
+{
+    constexpr bool P = BPC == 8 ? IIR_STAGE8 : IIR_STAGE10;
+    switch (th) {
+    case 12:
+        return frames_kernel<BPC, 12, P, IIR_WPE12>;
+    case 16:
+        return frames_kernel<BPC, 16, P, IIR_WPE16>;
+    case 20:
+        return frames_kernel<BPC, 20, P, IIR_WPE20>;
+    default:
+        return nullptr;
+    }
+}
+
 }  // namespace
 
-hipError_t launch_frames(int bpc, const KernelArgs &a, hipStream_t stream)
+bool supported_rows_per_tile(int th)
 {
-    const dim3 grid((unsigned)(a.tiles * a.chunks)), block(kWave);
-    if (bpc == 8)
-        hipLaunchKernelGGL(frames_kernel<8>, grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL(frames_kernel<10>, grid, block, 0, stream, a);
+    return frames_fn<8>(th) != nullptr;
+}
+
+hipError_t frames_attributes(int bpc, int th, hipFuncAttributes *attr)
+{
+    FramesFn f = bpc == 8 ? frames_fn<8>(th) : frames_fn<10>(th);
+    if (!f)
+        return hipErrorInvalidValue;
+    return hipFuncGetAttributes(attr, reinterpret_cast<const void *>(f));
+}
+
+hipError_t frames_occupancy(int bpc, int th, int *waves_per_cu)
+{
+    FramesFn f = bpc == 8 ? frames_fn<8>(th) : frames_fn<10>(th);
+    if (!f)
+        return hipErrorInvalidValue;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(waves_per_cu, reinterpret_cast<const void *>(f),
+                                                        kWave, 0);
+}
+
+hipError_t launch_frames(int bpc, int th, const KernelArgs &a, hipStream_t stream)
+{
+    FramesFn f = bpc == 8 ? frames_fn<8>(th) : frames_fn<10>(th);
+    if (!f)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(f, dim3((unsigned)(a.tiles * a.chunks)), dim3(kWave), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
-                         int lanes_out, int row_tiles, hipStream_t stream)
+                         int lanes_out, int strips, int th, hipStream_t stream)
 {
     const int64_t n = (int64_t)((W + 1) / 2) * H;
     const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 65536);
     hipLaunchKernelGGL(export_kernel, dim3(blocks), dim3(256), 0, stream, ring, dst, pitch, W, H,
-                       lanes_out, row_tiles);
+                       lanes_out, strips, th);
     return hipGetLastError();
 }
 

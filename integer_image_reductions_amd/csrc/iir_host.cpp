@@ -198,14 +198,16 @@ int choose_rows(iir_ctx *c, int cus, int forced)
         if (forced && th != forced)
             continue;
         int per_cu = 0;
-        if (frames_occupancy(c->cfg.bpc, th, &per_cu) != hipSuccess || per_cu < 1)
+        const bool generic = !fast_path_ok(c->cfg.width, c->cfg.height, th);
+        if (frames_occupancy(c->cfg.bpc, th, generic, &per_cu) != hipSuccess || per_cu < 1)
             continue;
         const int64_t waves = (int64_t)c->strips * ((c->cfg.height + th - 1) / th);
         const int64_t slots = (int64_t)per_cu * cus;
         const int64_t simds = 4LL * cus;
         const int64_t rounds = (waves + slots - 1) / slots;
         const int64_t per_simd = (std::min(waves, slots) + simds - 1) / simds;
-        const double cost = (double)rounds * (double)per_simd * (th + 4);
+        // the generic path's edge handling costs about a fifth more per row
+        const double cost = (double)rounds * (double)per_simd * (th + 4) * (generic ? 1.2 : 1.0);
         if (cost < best_cost - 1e-9 || (cost <= best_cost + 1e-9 && th > best)) {
             best_cost = cost;
             best = th;
@@ -321,7 +323,9 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     const bool timing = (c->cfg.flags & IIR_FLAG_TIMING) != 0;
     if (timing)
         HIP_TRY(hipEventRecord(c->k0, c->stream));
-    HIP_TRY(launch_frames(c->cfg.bpc, c->rows_per_tile, a, c->stream));
+    HIP_TRY(launch_frames(c->cfg.bpc, c->rows_per_tile,
+                          !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile), a,
+                          c->stream));
     if (timing)
         HIP_TRY(hipEventRecord(c->k1, c->stream));
     c->timed = timing;

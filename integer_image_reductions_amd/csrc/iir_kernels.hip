@@ -387,7 +387,7 @@ __device__ __forceinline__ void fetch_luma(Rsrc r, uint32_t voff, uint32_t soff,
 
 // Issue every load of frame t for this tile, into registers or into the LDS stage (the distorted
 // planes and chroma only when the frame is accumulated; a chunk's prologue frame is only blurred).
-template <int BPC, int TH, bool CAREFUL, bool STAGED>
+template <int BPC, int TH, bool GENERIC, bool STAGED>
 __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, int t,
                                            bool accumulate, FrameData<BPC, TH> &F,
                                            uint32_t (*lds)[kWave])
@@ -404,7 +404,9 @@ __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, i
     }
 #pragma unroll
     for (int k = 0; k < TH + 4; ++k) {
-        const int row = CAREFUL ? mirror_clamp(T.r0 - 2 + k, H) : T.r0 - 2 + k;
+        // only the two rows above and below the tile can fall outside the frame on the fast path
+        const int row = (GENERIC || k < 2 || k >= TH + 2) ? mirror_clamp(T.r0 - 2 + k, H)
+                                                          : T.r0 - 2 + k;
         fetch_luma<BPC, STAGED>(rs[0], T.luma_off, (uint32_t)row * pitch[0], F.R[k], lds,
                                 ST::kRef / ST::kLumaDw + k);
     }
@@ -413,7 +415,7 @@ __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, i
 #pragma unroll
     for (int i = 0; i < TH; ++i) {
         // rows past the frame re-read the last row; they are not counted
-        const int row = CAREFUL ? min(T.r0 + i, H - 1) : T.r0 + i;
+        const int row = GENERIC ? min(T.r0 + i, H - 1) : T.r0 + i;
         fetch_luma<BPC, STAGED>(rs[3], T.luma_off, (uint32_t)row * pitch[3], F.D[i], lds,
                                 ST::kDist / ST::kLumaDw + i);
     }
@@ -422,8 +424,8 @@ __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, i
         // the upper half-wave's row is one further down (its coff adds a pitch); at a ragged
         // bottom every lane whose row is past the plane re-reads the last row instead
         const int row = T.crow0 + FD::kChromaStep * k;
-        const int rl = CAREFUL ? min(row, a.Hc - 1) : row;
-        const bool back = CAREFUL && T.c_upper && row + 1 >= a.Hc;
+        const int rl = GENERIC ? min(row, a.Hc - 1) : row;
+        const bool back = GENERIC && T.c_upper && row + 1 >= a.Hc;
         const int lr = ST::kChroma + 4 * k;
         fetch32<STAGED>(rs[1], T.coff[0] - (back ? pitch[1] : 0u), (uint32_t)rl * pitch[1], F.cu[k], lds, lr);
         fetch32<STAGED>(rs[4], T.coff[1] - (back ? pitch[4] : 0u), (uint32_t)rl * pitch[4], F.du[k], lds, lr + 1);
@@ -465,9 +467,9 @@ __device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWav
 // One frame of one tile from its loaded samples: blur the reference luma (vertical pass once per
 // column and row, horizontal taps through DPP neighbours), SAD against the previous blurred tile
 // held in registers, SSE of the luma and chroma tiles, one wavefront reduction and one atomic per
-// sum. CAREFUL adds the frame-edge mirror fix-ups, ragged rows and masked tails; interior tiles
+// sum. GENERIC adds the frame-edge mirror fix-ups, ragged rows and masked tails; interior tiles
 // (the vast majority) run without any of it.
-template <int BPC, int TH, bool CAREFUL>
+template <int BPC, int TH, bool GENERIC>
 __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T, int t,
                                               bool accumulate, const FrameData<BPC, TH> &F,
                                               uint32_t (&prev0)[TH], uint32_t (&prev1)[TH],
@@ -484,7 +486,7 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 #pragma unroll
         for (int k = 0; k < FD::kChromaSteps; ++k) {
             uint32_t ru = F.cu[k], rdu = F.du[k], rv = F.cv[k], rdv = F.dv[k];
-            if constexpr (CAREFUL) {
+            if constexpr (GENERIC) {
                 const int row = T.crow0 + FD::kChromaStep * k + (T.c_upper ? 1 : 0);
                 const uint32_t m = row < a.Hc ? T.cm : 0u;
                 ru &= m;
@@ -513,9 +515,14 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
         uint32_t q0 = perm(v[1], v[0], kVSel);  // V of columns c, c+1
         uint32_t q1 = perm(v[3], v[2], kVSel);  // V of columns c+2, c+3
         uint32_t ql = from_left(q1);            // V of columns c-2, c-1
-        if constexpr (CAREFUL) {
+        // (V(c+2), V(c+1)): the mirror image of the lane's own columns, which stands for columns
+        // -2, -1 at the left frame edge and for W, W+1 at the right one when W % 4 == 0
+        const uint32_t mirrored = perm(q0, q1, 0x07060100u);
+        if constexpr (!GENERIC)
+            ql = T.left_fix ? mirrored : ql;
+        if constexpr (GENERIC) {
             // (V(2), V(1)) stands for columns -2, -1
-            ql = T.left_fix ? perm(q0, q1, 0x07060100u) : ql;
+            ql = T.left_fix ? mirrored : ql;
             if (T.right_rem == 1) {  // columns W, W+1 -> W-2, W-3
                 q0 = T.right_fix ? perm(ql, q0, 0x07060100u) : q0;
                 q1 = T.right_fix ? ql : q1;
@@ -526,9 +533,11 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
             }
         }
         uint32_t qr = from_right(q0);  // V of columns c+4, c+5
-        if constexpr (CAREFUL) {
+        if constexpr (!GENERIC)
+            qr = T.right_fix ? mirrored : qr;
+        if constexpr (GENERIC) {
             if (T.right_rem == 0)
-                qr = T.right_fix ? perm(q0, q1, 0x07060100u) : qr;
+                qr = T.right_fix ? mirrored : qr;
             else if (T.right_rem == 3)
                 qr = T.right_fix ? q0 : qr;
         }
@@ -538,12 +547,12 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
         const uint32_t h3 = dot2u(qr, T10, dot2u(q1, T12, dot2u(q0, Tz0, 32768u)));
         const uint32_t c0 = perm(h1, h0, 0x07060302u);  // Bl of columns c, c+1
         const uint32_t c1 = perm(h3, h2, 0x07060302u);  // Bl of columns c+2, c+3
-        if (!CAREFUL || i < T.rows_valid) {
+        if (!GENERIC || i < T.rows_valid) {
             acc_c = dot2u(c1, T.w1, dot2u(c0, T.w0, acc_c));
             acc_min = dot2u(pkmin(c1, prev1[i]), T.w1, dot2u(pkmin(c0, prev0[i]), T.w0, acc_min));
             if (accumulate) {
                 Luma r = F.R[i + 2], d = F.D[i];
-                if constexpr (CAREFUL) {
+                if constexpr (GENERIC) {
                     r = masked<BPC>(r, T.ym0, T.ym1);
                     d = masked<BPC>(d, T.ym0, T.ym1);
                 }
@@ -570,7 +579,7 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 // frame before them. STAGED keeps the next frame's loads in flight while the current one is
 // computed: the loads of frame t+1 write the wave's LDS stage (no registers held), issued as soon
 // as frame t has been read out of it.
-template <int BPC, int TH, bool CAREFUL, bool STAGED>
+template <int BPC, int TH, bool GENERIC, bool STAGED>
 __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
                                            uint32_t (&prev0)[TH], uint32_t (&prev1)[TH],
                                            uint32_t sum_prev, bool have_prev,
@@ -587,29 +596,29 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
     P.count = 0;
     if constexpr (STAGED) {
         FrameData<BPC, TH> F;
-        load_frame<BPC, TH, CAREFUL, true>(a, T, t0, t0 >= f_begin, F, lds);
+        load_frame<BPC, TH, GENERIC, true>(a, T, t0, t0 >= f_begin, F, lds);
         for (int t = t0; t < f_end; ++t) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): frame t is in LDS
             read_stage<BPC, TH>(t >= f_begin, lds, T.lane, F);
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
             __builtin_amdgcn_sched_barrier(0);
             if (t + 1 < f_end)
-                load_frame<BPC, TH, CAREFUL, true>(a, T, t + 1, true, F, lds);
-            compute_frame<BPC, TH, CAREFUL>(a, T, t, t >= f_begin, F, prev0, prev1, sum_prev,
+                load_frame<BPC, TH, GENERIC, true>(a, T, t + 1, true, F, lds);
+            compute_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F, prev0, prev1, sum_prev,
                                             have_prev, P);
         }
     } else {
         for (int t = t0; t < f_end; ++t) {
             FrameData<BPC, TH> F;
-            load_frame<BPC, TH, CAREFUL, false>(a, T, t, t >= f_begin, F, lds);
-            compute_frame<BPC, TH, CAREFUL>(a, T, t, t >= f_begin, F, prev0, prev1, sum_prev,
+            load_frame<BPC, TH, GENERIC, false>(a, T, t, t >= f_begin, F, lds);
+            compute_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F, prev0, prev1, sum_prev,
                                             have_prev, P);
         }
     }
     flush_sums(a, P, T.lane);
 }
 
-template <int BPC, int TH, bool STAGED, int WPE>
+template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void frames_kernel(
     const KernelArgs a)
 {
@@ -643,6 +652,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) vo
     T.w1 = T.out_lane ? ((c + 2 < W ? 1u : 0u) | (c + 3 < W ? 0x10000u : 0u)) : 0u;
     T.left_fix = T.strip == 0 && lane == 1;
     T.right_rem = W & 3;
+    // the lane holding column W-1 (on the fast path W % 4 == 0, so its columns end at W-1)
     T.right_fix = c <= W - 1 && W - 1 < c + kLumaCols && lane >= 1 && lane <= a.lanes_out;
     if constexpr (BPC == 8) {
         T.ym0 = (c < W ? 0xffu : 0u) | (c + 1 < W ? 0xff00u : 0u) | (c + 2 < W ? 0xff0000u : 0u) |
@@ -700,14 +710,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) vo
             prev0[i] = prev1[i] = 0;
     }
 
-    // interior tiles take the lean path; tiles whose window touches a frame edge (rows or
-    // columns) or a ragged tail take the careful one
-    const bool careful = T.strip == 0 || T.strip == a.strips - 1 || T.r0 < 2 ||
-                         T.r0 + TH + 2 > H;
-    if (careful)
-        frame_loop<BPC, TH, true, STAGED>(a, T, prev0, prev1, sum_prev, have_prev, stage);
-    else
-        frame_loop<BPC, TH, false, STAGED>(a, T, prev0, prev1, sum_prev, have_prev, stage);
+    // every tile of a launch takes the same path, so wavefronts cost the same and none trails
+    frame_loop<BPC, TH, GENERIC, STAGED>(a, T, prev0, prev1, sum_prev, have_prev, stage);
 
     if (T.chunk == a.chunks - 1) {
         uint2 *rout = reinterpret_cast<uint2 *>(a.ring_out);
@@ -790,51 +794,55 @@ typedef void (*FramesFn)(KernelArgs);
 #define IIR_WPE20 2
 #endif
 
-// Every (bit depth, tile height) the host may pick, and whether its frames go through the LDS
-// stage.
-template <int BPC>
+// Every (bit depth, tile height, path) the host may pick. The fast path needs W % 8 == 0 and
+// H % TH == 0 (no ragged tile, no partial sample group); the generic path takes any size.
+template <int BPC, bool GENERIC>
 FramesFn frames_fn(int th)
 {
     constexpr bool P = BPC == 8 ? IIR_STAGE8 : IIR_STAGE10;
     switch (th) {
     case 12:
-        return frames_kernel<BPC, 12, P, IIR_WPE12>;
+        return frames_kernel<BPC, 12, P, GENERIC, IIR_WPE12>;
     case 16:
-        return frames_kernel<BPC, 16, P, IIR_WPE16>;
+        return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16>;
     case 20:
-        return frames_kernel<BPC, 20, P, IIR_WPE20>;
+        return frames_kernel<BPC, 20, P, GENERIC, IIR_WPE20>;
     default:
         return nullptr;
     }
+}
+
+FramesFn pick(int bpc, int th, bool generic)
+{
+    if (bpc == 8)
+        return generic ? frames_fn<8, true>(th) : frames_fn<8, false>(th);
+    return generic ? frames_fn<10, true>(th) : frames_fn<10, false>(th);
 }
 
 }  // namespace
 
 bool supported_rows_per_tile(int th)
 {
-    return frames_fn<8>(th) != nullptr;
+    return pick(8, th, true) != nullptr;
 }
 
-hipError_t frames_attributes(int bpc, int th, hipFuncAttributes *attr)
+bool fast_path_ok(int W, int H, int th)
 {
-    FramesFn f = bpc == 8 ? frames_fn<8>(th) : frames_fn<10>(th);
-    if (!f)
-        return hipErrorInvalidValue;
-    return hipFuncGetAttributes(attr, reinterpret_cast<const void *>(f));
+    return W % 8 == 0 && H % th == 0;
 }
 
-hipError_t frames_occupancy(int bpc, int th, int *waves_per_cu)
+hipError_t frames_occupancy(int bpc, int th, bool generic, int *waves_per_cu)
 {
-    FramesFn f = bpc == 8 ? frames_fn<8>(th) : frames_fn<10>(th);
+    FramesFn f = pick(bpc, th, generic);
     if (!f)
         return hipErrorInvalidValue;
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(waves_per_cu, reinterpret_cast<const void *>(f),
                                                         kWave, 0);
 }
 
-hipError_t launch_frames(int bpc, int th, const KernelArgs &a, hipStream_t stream)
+hipError_t launch_frames(int bpc, int th, bool generic, const KernelArgs &a, hipStream_t stream)
 {
-    FramesFn f = bpc == 8 ? frames_fn<8>(th) : frames_fn<10>(th);
+    FramesFn f = pick(bpc, th, generic);
     if (!f)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(f, dim3((unsigned)(a.tiles * a.chunks)), dim3(kWave), 0, stream, a);

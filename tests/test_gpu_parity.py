@@ -65,6 +65,28 @@ def test_tiny_sweep(w, h, bpc):
             assert np.array_equal(_blur_np(ctx), last), f"blurred plane {kind} {w}x{h} {bpc}"
 
 
+PATH_SIZES = [(504, 36), (1000, 80), (248, 60), (8, 12), (64, 240)]
+
+
+@pytest.mark.parametrize("bpc", [8, 10])
+@pytest.mark.parametrize("th", ["12", "16", "20"])
+@pytest.mark.parametrize("w,h", PATH_SIZES, ids=[f"{w}x{h}" for w, h in PATH_SIZES])
+def test_each_tile_height_and_path(w, h, th, bpc, monkeypatch):
+    """Every tile height on sizes where the uniform fast path applies (W % 8 == 0, H a multiple of
+    the tile height) and where it does not, across several strips and row tiles."""
+    monkeypatch.setenv("IIR_ROWS_PER_TILE", th)
+    clip = synth.random_clip(w, h, bpc, 3, seed=w + h + int(th), kind="uniform")
+    ref, dist = _dev(clip)
+    _say("path", w, h, th, bpc)
+    with iir.Context(w, h, bpc, max_batch=4) as ctx:
+        assert ctx.geometry()["rows_per_tile"] == int(th)
+        sums, hm = ctx.run_clip(ref, dist)
+        blur = _blur_np(ctx)
+    want, want_hm, last = _oracle(clip, last=True)
+    _check(clip, sums, hm, want, want_hm, f"{w}x{h} th={th} bpc={bpc}")
+    assert np.array_equal(blur, last)
+
+
 @pytest.mark.parametrize("bpc", [8, 10])
 def test_streaming_equals_batch_equals_split(bpc):
     w, h = 300, 70

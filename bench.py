@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu]
 
 A step is one pass of the whole path over one batch: one iir_submit_clip of the 50-frame clip
-(resident in HBM before timing starts) and one iir_collect of its 50 results. W untimed steps, then
-K timed steps between two device synchronisations. Prints one JSON line.
+(resident in HBM before timing starts) and one iir_collect of its 50 results; step k is submitted
+before step k-1 is collected, so the host work overlaps the GPU. W untimed steps, then K timed
+steps between two device synchronisations. Prints one JSON line.
 
 roofline: the main kernel's algorithmic bytes per launch (every ref and dist sample read once,
 plus the blurred-luma state read and written once per launch) divided by its mean duration,
@@ -67,23 +68,20 @@ def load_traffic(workload: str):
 
 
 def cpu_baseline(clip, max_seconds: float = 20.0):
+    """The oracle over the leading frames of the same clip that fit `max_seconds` (the whole clip
+    when it fits), single-threaded; frames/s."""
     import oracle
-    t0 = time.perf_counter()
-    frames = 0
-    # whole clip when it fits the budget; else the leading frames that do (estimated from one)
-    est = None
     one = clip.slice(0, 1)
-    ts = time.perf_counter()
+    t0 = time.perf_counter()
     oracle.clip(one.ref, one.dist, clip.bpc)
-    est = time.perf_counter() - ts
-    n = max(1, min(clip.frames, int(max_seconds / max(est, 1e-6))))
+    per_frame = time.perf_counter() - t0
+    n = max(1, min(clip.frames, int(max_seconds / max(per_frame, 1e-6))))
     sub = clip.slice(0, n)
     t0 = time.perf_counter()
     oracle.clip(sub.ref, sub.dist, clip.bpc)
     dt = time.perf_counter() - t0
-    frames = n
-    return {"value": frames / dt, "unit": "frames/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {frames} of {clip.frames} frame pairs of the same workload, one pass, "
+    return {"value": n / dt, "unit": "frames/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {clip.frames} frame pairs of the same workload, one pass, "
                       f"single-threaded C oracle ({dt:.1f} s)"}
 
 
@@ -122,27 +120,32 @@ def main():
     F, W, H, bpc = clip.frames, clip.width, clip.height, clip.bpc
     log("uploaded", F, "frame pairs")
 
-    ctx = iir.Context(W, H, bpc, max_batch=F, timing=True)
+    # two batches in flight: step k is submitted before step k-1 is collected
+    ctx = iir.Context(W, H, bpc, max_batch=2 * F, timing=True)
     geo = ctx.geometry()
     chunks = ctx.plan_chunks(F)
-    for _ in range(args.warmup):
-        ctx.submit_clip(ref, dist)
-        ctx.collect()
+    clip_dev = ctx.prepare_clip(ref, dist)
+    for _ in range(max(args.warmup, 1)):
+        ctx.submit_prepared(clip_dev)
+        ctx.collect(F)
     torch.cuda.synchronize()
-    kms = []
+    ctx.kernel_stats(reset=True)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        ctx.submit_clip(ref, dist)
-        ctx.collect()
-        kms.append(ctx.kernel_time_ms())
+    ctx.submit_prepared(clip_dev)
+    for _ in range(args.steps - 1):
+        ctx.submit_prepared(clip_dev)
+        ctx.collect(F)
+    ctx.collect(F)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    launches, total_ms = ctx.kernel_stats()
+    assert launches == args.steps, (launches, args.steps)
     ms_step = 1000.0 * elapsed / args.steps
     frames_per_s = F * args.steps / elapsed
-    kernel_ms = float(np.mean(kms))
+    kernel_ms = total_ms / launches
     alg = algorithmic_bytes(W, H, bpc, F)
     achieved = alg / (kernel_ms * 1e-3) / 1e9
-    log(f"kernel {kernel_ms * 1e3:.1f} us/launch (median {np.median(kms) * 1e3:.1f}), "
+    log(f"kernel {kernel_ms * 1e3:.1f} us/launch (mean of {launches}), "
         f"step {ms_step * 1e3:.1f} us, {achieved:.0f} GB/s")
 
     out = {

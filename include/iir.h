@@ -80,7 +80,7 @@ typedef struct iir_config {
     int32_t height;    /* luma height, >= 3 and <= 32768 */
     int32_t bpc;       /* 8 or 10 */
     int32_t chroma;    /* IIR_CHROMA_420 */
-    int32_t max_batch; /* max frames uncollected at once (and per submission), 1..65536 */
+    int32_t max_batch; /* max frames uncollected at once, over at most 64 pending submissions */
     uint32_t flags;    /* IIR_FLAG_* */
 } iir_config;
 
@@ -124,8 +124,9 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
 /*
  * Enqueue one frame pair (asynchronous: returns before the GPU runs it). ref and dist are host
  * structs describing device planes; the planes must stay valid and unmodified until the result
- * has been collected. One kernel launch and one 32-byte-per-slot readback; no host wait.
- * Errors: IIR_EINVAL, IIR_EBUSY (max_batch frames already pending), IIR_EDEVICE.
+ * has been collected. One kernel launch and one small readback of its sums; no host wait.
+ * Errors: IIR_EINVAL, IIR_EBUSY (the pending results would exceed max_batch frames or 64
+ * submissions), IIR_EDEVICE.
  */
 IIR_API int iir_submit(iir_ctx *ctx, const iir_frame *ref, const iir_frame *dist);
 
@@ -142,10 +143,11 @@ IIR_API int iir_submit_clip(iir_ctx *ctx, const iir_frame *ref, const iir_frame 
                             int32_t nframes);
 
 /*
- * Wait once for all pending submissions and copy up to `max` results, oldest first, into the
- * HOST array `out`; *n_out receives the number copied. Results beyond `max` stay queued for the
- * next call. With nothing pending it returns IIR_OK with *n_out = 0.
- * Errors: IIR_EINVAL (null out or n_out, max < 0), IIR_EDEVICE.
+ * Copy up to `max` pending results, oldest first, into the HOST array `out`; *n_out receives the
+ * number copied. Waits once, for the submission holding the last result returned (later
+ * submissions keep running). Results beyond `max` stay queued for the next call. With nothing
+ * pending it returns IIR_OK with *n_out = 0. Errors: IIR_EINVAL (null out or n_out, max < 0),
+ * IIR_EDEVICE.
  */
 IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_out);
 
@@ -170,11 +172,18 @@ IIR_API int iir_reset(iir_ctx *ctx);
 IIR_API int iir_export_blur(iir_ctx *ctx, void *dst, int64_t pitch);
 
 /*
- * Duration in milliseconds of the main kernel of the most recent submission, from HIP events on
- * the context's stream. Needs IIR_FLAG_TIMING and a completed submission (collect first);
- * IIR_ESTATE otherwise.
+ * Duration in milliseconds of the main kernel of the most recently collected submission, from HIP
+ * events recorded around the launch on the context's stream. Needs IIR_FLAG_TIMING; IIR_ESTATE
+ * until a timed submission has been collected.
  */
 IIR_API int iir_kernel_time(iir_ctx *ctx, float *ms);
+
+/*
+ * Number of collected timed launches and their summed kernel milliseconds since create or the
+ * last reset (reset != 0 clears the counters after reading them). Needs IIR_FLAG_TIMING for
+ * non-zero counts.
+ */
+IIR_API int iir_kernel_stats(iir_ctx *ctx, int32_t reset, int64_t *launches, double *total_ms);
 
 /* Launch geometry chosen at create, for reports and tests. */
 typedef struct iir_geometry {

@@ -72,6 +72,8 @@ SIGNATURES = [
     ("iir_reset", [c_vp], ctypes.c_int),
     ("iir_export_blur", [c_vp, c_vp, c_i64], ctypes.c_int),
     ("iir_kernel_time", [c_vp, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
+    ("iir_kernel_stats", [c_vp, c_i32, ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double)],
+     ctypes.c_int),
     ("iir_get_geometry", [c_vp, ctypes.POINTER(Geometry)], ctypes.c_int),
     ("iir_plan_chunks", [c_vp, c_i32, ctypes.POINTER(c_i32)], ctypes.c_int),
     ("iir_probe_bandwidth", [c_i32, c_vp, c_i32, c_vp, c_vp, c_i64, c_i32,
@@ -229,15 +231,23 @@ class Context:
             arr[t] = frame_of([p[t] for p in planes], self.width, self.height)
         return arr, n
 
-    def submit_clip(self, ref, dist):
-        """Enqueue a clip; ref and dist are (Y, U, V) device tensors of shape (F, h, w)."""
+    def prepare_clip(self, ref, dist):
+        """Build the frame descriptors of a clip once; pass the result to submit_prepared()."""
         fr, n = self._frames(ref)
         fd, m = self._frames(dist)
         if n != m:
             raise ValueError("ref and dist have different frame counts")
+        return (fr, fd, n, ref, dist)
+
+    def submit_prepared(self, prepared):
+        fr, fd, n, ref, dist = prepared
         _check(self._lib.iir_submit_clip(self._h, fr, fd, n), "iir_submit_clip")
         self._keep.append((ref, dist))
         return n
+
+    def submit_clip(self, ref, dist):
+        """Enqueue a clip; ref and dist are (Y, U, V) device tensors of shape (F, h, w)."""
+        return self.submit_prepared(self.prepare_clip(ref, dist))
 
     def submit_frames(self, ref_frames, dist_frames):
         """Enqueue frames given as lists of (Y, U, V) 2-D device tensors (any addresses)."""
@@ -264,7 +274,8 @@ class Context:
         for i in range(got.value):
             sums[i] = (out[i].sad, out[i].sse[0], out[i].sse[1], out[i].sse[2])
             hm[i] = out[i].has_motion
-        self._keep = []
+        if len(self._keep) > 64:
+            self._keep = self._keep[-64:]
         return sums, hm
 
     def run_clip(self, ref, dist):
@@ -293,6 +304,13 @@ class Context:
         buf = torch.empty((self.height, w2 // 2), dtype=torch.int16, device=self.device)
         _check(self._lib.iir_export_blur(self._h, c_vp(buf.data_ptr()), w2), "iir_export_blur")
         return buf[:, :self.width]
+
+    def kernel_stats(self, reset: bool = False):
+        """(launches, total kernel ms) of collected timed submissions since create / last reset."""
+        n, ms = c_i64(), ctypes.c_double()
+        _check(self._lib.iir_kernel_stats(self._h, 1 if reset else 0, ctypes.byref(n),
+                                          ctypes.byref(ms)), "iir_kernel_stats")
+        return n.value, ms.value
 
     def kernel_time_ms(self) -> float:
         ms = ctypes.c_float()

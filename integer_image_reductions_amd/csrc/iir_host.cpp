@@ -92,13 +92,29 @@ struct iir_ctx {
     unsigned long long *host_sums = nullptr;  // pinned, [max_batch][kSums][kSumSlots]
     FramePtrs *table_dev = nullptr;
     FramePtrs *table_host = nullptr;  // pinned, [max_batch]
-    std::vector<int32_t> has_motion;  // per queued frame
-    int queued = 0;                   // frames submitted since the queue was last drained
-    int delivered = 0;                // of those, frames already returned by iir_collect
+    // Pending submissions, oldest first, in a ring of kMaxPending records. Their results sit in
+    // a circular region of max_batch frame slots of host_sums (and table slots), each submission
+    // contiguous, so up to max_batch frames can be in flight across several submissions.
+    struct Sub {
+        int first;       // first frame slot
+        int n;           // frames
+        int taken;       // frames already returned by iir_collect
+        bool has_prev;   // frame 0 has a previous frame
+        hipEvent_t done; // recorded after the submission's readback
+        hipEvent_t k0, k1;  // bracket the main kernel (IIR_FLAG_TIMING)
+    };
+    static constexpr int kMaxPending = 64;
+    Sub subs[kMaxPending] = {};
+    int sub_head = 0;    // oldest pending submission
+    int sub_count = 0;   // pending submissions
+    int slot_head = 0;   // next free frame slot
+    int pending = 0;     // frames submitted and not yet returned
     bool has_prev = false;            // the next frame has a previous blurred frame
     bool any_frame = false;           // ring[ring_cur] is valid
-    bool timed = false;               // k0/k1 bracket the last submission's kernel
-    hipEvent_t done = nullptr, k0 = nullptr, k1 = nullptr;
+    // kernel timing of collected submissions (IIR_FLAG_TIMING)
+    float last_ms = -1.f;
+    int64_t timed_launches = 0;
+    double timed_ms = 0.0;
 };
 
 namespace {
@@ -234,8 +250,7 @@ void release(iir_ctx *c)
     int saved = -1;
     if (hipGetDevice(&saved) == hipSuccess && saved != c->device)
         (void)hipSetDevice(c->device);
-    if (c->stream || c->done)
-        (void)hipStreamSynchronize(c->stream);
+    (void)hipStreamSynchronize(c->stream);
     for (int i = 0; i < 2; ++i) {
         if (c->ring[i])
             (void)hipFree(c->ring[i]);
@@ -248,15 +263,37 @@ void release(iir_ctx *c)
         (void)hipHostFree(c->host_sums);
     if (c->table_host)
         (void)hipHostFree(c->table_host);
-    if (c->done)
-        (void)hipEventDestroy(c->done);
-    if (c->k0)
-        (void)hipEventDestroy(c->k0);
-    if (c->k1)
-        (void)hipEventDestroy(c->k1);
+    for (auto &sub : c->subs) {
+        if (sub.done)
+            (void)hipEventDestroy(sub.done);
+        if (sub.k0)
+            (void)hipEventDestroy(sub.k0);
+        if (sub.k1)
+            (void)hipEventDestroy(sub.k1);
+    }
+
     if (saved >= 0 && saved != c->device)
         (void)hipSetDevice(saved);
     delete c;
+}
+
+// First of n contiguous free frame slots in the circular result region, or -1. Pending frames
+// occupy [first slot of the oldest submission, slot_head) modulo max_batch.
+int reserve_slots(const iir_ctx *c, int n)
+{
+    const int cap = c->cfg.max_batch;
+    if (c->sub_count >= iir_ctx::kMaxPending || c->pending + n > cap)
+        return -1;
+    if (c->sub_count == 0)
+        return 0;
+    const int tail = c->subs[c->sub_head].first;
+    const int head = c->slot_head;
+    if (head > tail || (head == tail && c->pending == 0)) {
+        if (head + n <= cap)
+            return head;
+        return n <= tail ? 0 : -1;  // wrap to the front
+    }
+    return head + n <= tail ? head : -1;
 }
 
 int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
@@ -268,9 +305,10 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     int rc = check_frames(c, ref, dist, n);
     if (rc != IIR_OK)
         return rc;
-    if (c->queued + n > c->cfg.max_batch)
-        return fail(IIR_EBUSY, "%d frames pending; %d more exceed max_batch %d",
-                    c->queued - c->delivered, n, c->cfg.max_batch);
+    const int first = reserve_slots(c, n);
+    if (first < 0)
+        return fail(IIR_EBUSY, "%d frames in %d submissions pending; %d more do not fit (max_batch %d)",
+                    c->pending, c->sub_count, n, c->cfg.max_batch);
     DeviceScope ds(c->device);
     if (ds.err != hipSuccess)
         return fail_hip(ds.err, "hipSetDevice");
@@ -287,13 +325,13 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
         a.fstride[k] = step;
     }
     if (!uniform) {
-        FramePtrs *th = c->table_host + c->queued;
+        FramePtrs *th = c->table_host + first;
         for (int t = 0; t < n; ++t)
             for (int k = 0; k < 6; ++k)
                 th[t].p[k] = plane_ptr(ref, dist, t, k);
-        HIP_TRY(hipMemcpyAsync(c->table_dev + c->queued, th, sizeof(FramePtrs) * n,
+        HIP_TRY(hipMemcpyAsync(c->table_dev + first, th, sizeof(FramePtrs) * n,
                                hipMemcpyHostToDevice, c->stream));
-        a.table = c->table_dev + c->queued;
+        a.table = c->table_dev + first;
     }
     for (int k = 0; k < 3; ++k) {
         const int64_t rows = k == 0 ? c->cfg.height : c->Hc;
@@ -321,23 +359,26 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     a.has_prev = c->has_prev ? 1 : 0;
 
     const bool timing = (c->cfg.flags & IIR_FLAG_TIMING) != 0;
+    iir_ctx::Sub &sub = c->subs[(c->sub_head + c->sub_count) % iir_ctx::kMaxPending];
     if (timing)
-        HIP_TRY(hipEventRecord(c->k0, c->stream));
+        HIP_TRY(hipEventRecord(sub.k0, c->stream));
     HIP_TRY(launch_frames(c->cfg.bpc, c->rows_per_tile,
                           !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile), a,
                           c->stream));
     if (timing)
-        HIP_TRY(hipEventRecord(c->k1, c->stream));
-    c->timed = timing;
+        HIP_TRY(hipEventRecord(sub.k1, c->stream));
     const size_t per_frame = (size_t)kSums * kSumSlots;
-    HIP_TRY(hipMemcpyAsync(c->host_sums + (size_t)c->queued * per_frame, c->sums[c->sums_cur],
+    HIP_TRY(hipMemcpyAsync(c->host_sums + (size_t)first * per_frame, c->sums[c->sums_cur],
                            sizeof(unsigned long long) * per_frame * n, hipMemcpyDeviceToHost,
                            c->stream));
-    HIP_TRY(hipEventRecord(c->done, c->stream));
-
-    for (int t = 0; t < n; ++t)
-        c->has_motion[c->queued + t] = (t > 0 || c->has_prev) ? 1 : 0;
-    c->queued += n;
+    HIP_TRY(hipEventRecord(sub.done, c->stream));
+    sub.first = first;
+    sub.n = n;
+    sub.taken = 0;
+    sub.has_prev = c->has_prev;
+    c->sub_count++;
+    c->slot_head = first + n;
+    c->pending += n;
     c->ring_cur ^= 1;
     c->sums_cur ^= 1;
     c->has_prev = true;
@@ -392,7 +433,6 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
         release(c);
         return fail(IIR_EINVAL, "frame too large for one grid");
     }
-    c->has_motion.assign(cfg->max_batch, 0);
     c->sums_n = (int64_t)cfg->max_batch * kSums * kSumSlots;
 
     const size_t ring_bytes = (size_t)c->tiles * c->rows_per_tile * kWave * sizeof(uint2);
@@ -412,11 +452,14 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
         release(c);
         return fail(IIR_ENOMEM, "allocation failed: %s", hipGetErrorString(e));
     }
-    e = hipEventCreateWithFlags(&c->done, hipEventDisableTiming);
-    if (e == hipSuccess)
-        e = hipEventCreate(&c->k0);
-    if (e == hipSuccess)
-        e = hipEventCreate(&c->k1);
+    for (auto &sub : c->subs) {
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&sub.done, hipEventDisableTiming);
+        if (e == hipSuccess && (cfg->flags & IIR_FLAG_TIMING))
+            e = hipEventCreate(&sub.k0);
+        if (e == hipSuccess && (cfg->flags & IIR_FLAG_TIMING))
+            e = hipEventCreate(&sub.k1);
+    }
     for (int i = 0; i < 2 && e == hipSuccess; ++i) {
         e = hipMemsetAsync(c->sums[i], 0, sizeof(unsigned long long) * c->sums_n, c->stream);
         if (e == hipSuccess)
@@ -448,33 +491,60 @@ IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_o
     if (!ctx || !out || !n_out || max < 0)
         return fail(IIR_EINVAL, "bad collect arguments");
     *n_out = 0;
-    if (ctx->queued == ctx->delivered)
+    const int n = std::min(max, ctx->pending);
+    if (n == 0)
         return IIR_OK;
+    // wait for the submission holding the last result returned; stream order covers the others
     {
+        int need = n, k = 0;
+        const iir_ctx::Sub *last = nullptr;
+        while (need > 0) {
+            const iir_ctx::Sub &sub = ctx->subs[(ctx->sub_head + k++) % iir_ctx::kMaxPending];
+            need -= sub.n - sub.taken;
+            last = &sub;
+        }
         DeviceScope ds(ctx->device);
         if (ds.err != hipSuccess)
             return fail_hip(ds.err, "hipSetDevice");
-        HIP_TRY(hipEventSynchronize(ctx->done));
+        HIP_TRY(hipEventSynchronize(last->done));
     }
-    const int n = std::min(max, ctx->queued - ctx->delivered);
     const size_t per_frame = (size_t)kSums * kSumSlots;
-    for (int i = 0; i < n; ++i) {
-        const int f = ctx->delivered + i;
-        const unsigned long long *s = ctx->host_sums + (size_t)f * per_frame;
-        uint64_t v[kSums] = {0, 0, 0, 0};
-        for (int k = 0; k < kSums; ++k)
-            for (int j = 0; j < kSumSlots; ++j)
-                v[k] += s[k * kSumSlots + j];
-        out[i].has_motion = ctx->has_motion[f];
-        out[i].sad = ctx->has_motion[f] ? v[0] : 0;
-        out[i].sse[0] = v[1];
-        out[i].sse[1] = v[2];
-        out[i].sse[2] = v[3];
-        out[i].reserved = 0;
+    int got = 0;
+    while (got < n) {
+        iir_ctx::Sub &sub = ctx->subs[ctx->sub_head];
+        const int take = std::min(n - got, sub.n - sub.taken);
+        for (int i = 0; i < take; ++i) {
+            const int f = sub.taken + i;
+            const unsigned long long *src = ctx->host_sums + (size_t)(sub.first + f) * per_frame;
+            uint64_t v[kSums] = {0, 0, 0, 0};
+            for (int k = 0; k < kSums; ++k)
+                for (int j = 0; j < kSumSlots; ++j)
+                    v[k] += src[k * kSumSlots + j];
+            iir_result &r = out[got + i];
+            r.has_motion = (f > 0 || sub.has_prev) ? 1 : 0;
+            r.sad = r.has_motion ? v[0] : 0;
+            r.sse[0] = v[1];
+            r.sse[1] = v[2];
+            r.sse[2] = v[3];
+            r.reserved = 0;
+        }
+        sub.taken += take;
+        got += take;
+        if (sub.taken == sub.n) {
+            float ms = 0.f;
+            if ((ctx->cfg.flags & IIR_FLAG_TIMING) &&
+                hipEventElapsedTime(&ms, sub.k0, sub.k1) == hipSuccess) {
+                ctx->last_ms = ms;
+                ctx->timed_launches++;
+                ctx->timed_ms += ms;
+            }
+            ctx->sub_head = (ctx->sub_head + 1) % iir_ctx::kMaxPending;
+            ctx->sub_count--;
+        }
     }
-    ctx->delivered += n;
-    if (ctx->delivered == ctx->queued)
-        ctx->delivered = ctx->queued = 0;
+    ctx->pending -= n;
+    if (ctx->sub_count == 0)
+        ctx->slot_head = 0;
     *n_out = n;
     return IIR_OK;
 }
@@ -484,9 +554,9 @@ IIR_API int iir_run_clip(iir_ctx *ctx, const iir_frame *ref, const iir_frame *di
 {
     if (!ctx || !out)
         return fail(IIR_EINVAL, "context or out is NULL");
-    if (ctx->queued != ctx->delivered)
+    if (ctx->pending != 0)
         return fail(IIR_ESTATE, "iir_run_clip needs an empty queue (%d results pending)",
-                    ctx->queued - ctx->delivered);
+                    ctx->pending);
     int rc = submit(ctx, ref, dist, nframes);
     if (rc != IIR_OK)
         return rc;
@@ -545,17 +615,22 @@ IIR_API int iir_kernel_time(iir_ctx *ctx, float *ms)
 {
     if (!ctx || !ms)
         return fail(IIR_EINVAL, "NULL argument");
-    if (!ctx->timed)
-        return fail(IIR_ESTATE, "no timed submission (IIR_FLAG_TIMING off or nothing submitted)");
-    DeviceScope ds(ctx->device);
-    if (ds.err != hipSuccess)
-        return fail_hip(ds.err, "hipSetDevice");
-    const hipError_t q = hipEventQuery(ctx->k1);
-    if (q == hipErrorNotReady)
-        return fail(IIR_ESTATE, "the timed submission has not completed; collect first");
-    if (q != hipSuccess)
-        return fail_hip(q, "hipEventQuery");
-    HIP_TRY(hipEventElapsedTime(ms, ctx->k0, ctx->k1));
+    if (ctx->last_ms < 0.f)
+        return fail(IIR_ESTATE, "no timed submission collected (IIR_FLAG_TIMING off, or collect first)");
+    *ms = ctx->last_ms;
+    return IIR_OK;
+}
+
+IIR_API int iir_kernel_stats(iir_ctx *ctx, int32_t reset, int64_t *launches, double *total_ms)
+{
+    if (!ctx || !launches || !total_ms)
+        return fail(IIR_EINVAL, "NULL argument");
+    *launches = ctx->timed_launches;
+    *total_ms = ctx->timed_ms;
+    if (reset) {
+        ctx->timed_launches = 0;
+        ctx->timed_ms = 0.0;
+    }
     return IIR_OK;
 }
 

@@ -77,6 +77,8 @@ def test_null_context_calls(lib):
     assert lib.iir_reset(None) == B.IIR_EINVAL
     assert lib.iir_export_blur(None, None, 0) == B.IIR_EINVAL
     assert lib.iir_kernel_time(None, ctypes.byref(ctypes.c_float())) == B.IIR_EINVAL
+    assert lib.iir_kernel_stats(None, 0, ctypes.byref(ctypes.c_int64()),
+                                ctypes.byref(ctypes.c_double())) == B.IIR_EINVAL
     assert lib.iir_get_geometry(None, ctypes.byref(B.Geometry())) == B.IIR_EINVAL
     assert lib.iir_plan_chunks(None, 1, ctypes.byref(n)) == B.IIR_EINVAL
     lib.iir_destroy(None)

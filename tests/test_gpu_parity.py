@@ -113,6 +113,35 @@ def test_streaming_equals_batch_equals_split(bpc):
         _check(clip, np.concatenate([s1, s2]), np.concatenate([h1, h2]), want, want_hm, "partial")
 
 
+def test_pipelined_submissions():
+    """Several submissions in flight; each collect waits only for what it returns, and the result
+    slots wrap around."""
+    w, h, f = 128, 36, 11
+    clip = synth.random_clip(w, h, 8, f, seed=44)
+    ref, dist = _dev(clip)
+    want, want_hm = _oracle(clip)
+    _say("pipelined")
+    got, got_hm = [], []
+    part = lambda a, b: (tuple(p[a:b] for p in ref), tuple(p[a:b] for p in dist))  # noqa: E731
+    with iir.Context(w, h, 8, max_batch=8, timing=True) as ctx:
+        ctx.submit_clip(*part(0, 3))    # slots 0-2
+        ctx.submit_clip(*part(3, 7))    # slots 3-6
+        s, hm = ctx.collect(3)
+        got.append(s); got_hm.append(hm)
+        ctx.submit_clip(*part(7, 8))    # slot 7
+        ctx.submit_clip(*part(8, 11))   # wraps to slots 0-2
+        with pytest.raises(iir.IIRError) as e:
+            ctx.submit_clip(*part(0, 1))  # 8 frames pending already
+        assert e.value.code == -5
+        s, hm = ctx.collect(2)
+        got.append(s); got_hm.append(hm)
+        s, hm = ctx.collect()
+        got.append(s); got_hm.append(hm)
+        n, ms = ctx.kernel_stats()
+        assert n == 4 and ms > 0
+    _check(clip, np.concatenate(got), np.concatenate(got_hm), want, want_hm, "pipelined")
+
+
 def test_reset_restarts_motion():
     w, h = 64, 40
     clip = synth.random_clip(w, h, 8, 4, seed=5)

@@ -1,6 +1,7 @@
 """Benchmark: frames/s of the integer motion + PSNR sums on 3840x2160 8-bit 4:2:0, one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu] [--probe]
+    python bench.py --workload c3 --traffic-from FETCH.csv WRITE.csv   (host only, see below)
 
 A step is one pass of the whole path over one batch: one iir_submit_clip of the 50-frame clip
 (resident in HBM before timing starts) and one iir_collect of its 50 results; step k is submitted
@@ -12,6 +13,10 @@ plus the blurred-luma state read and written once per launch) divided by its mea
 measured with HIP events on the context's stream, against the 8 TB/s HBM peak. traffic: HBM bytes
 per launch from the committed rocprofv3 counter summary for this workload, reported only while
 the kernel source still matches the one the counters were taken on.
+--traffic-from turns two rocprofv3 counter-collection CSVs of `bench.py --probe` runs (one with
+--pmc FETCH_SIZE, one with --pmc WRITE_SIZE) into profiles/frames_kernel_<workload>_traffic.json:
+each counter's mean KiB per main-kernel dispatch, scaled by what the same counter reads for the
+copy probe (probe_copy moves a known 1 GiB in and 1 GiB out per dispatch).
 cpu_baseline: the plain C oracle (single thread) over the same frames, on the host.
 """
 from __future__ import annotations
@@ -67,6 +72,63 @@ def load_traffic(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+PROBE_BYTES = 1 << 30
+
+
+def _counter_means(path: str, counter: str):
+    """Mean counter value (KiB) per dispatch of the main kernel and of the copy probe."""
+    import csv
+    main, copy = [], []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "frames_kernel" in r["Kernel_Name"]:
+                main.append(v)
+            elif "probe_copy" in r["Kernel_Name"]:
+                copy.append(v)
+    if not main or not copy:
+        raise SystemExit(f"{path}: no {counter} rows for frames_kernel and probe_copy")
+    return sum(main) / len(main), len(main), sum(copy) / len(copy), len(copy)
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
+    fm, fn, fc, fcn = _counter_means(fetch_csv, "FETCH_SIZE")
+    wm, wn, wc, wcn = _counter_means(write_csv, "WRITE_SIZE")
+    f_scale = PROBE_BYTES / (fc * 1024.0)
+    w_scale = PROBE_BYTES / (wc * 1024.0)
+    fetch_b, write_b = fm * 1024.0 * f_scale, wm * 1024.0 * w_scale
+    d = {
+        "workload": WORKLOADS[workload],
+        "kernel_sha256": kernel_sha(),
+        "fetch_kib_per_launch": fm, "fetch_dispatches": fn,
+        "write_kib_per_launch": wm, "write_dispatches": wn,
+        "copy_probe_bytes": PROBE_BYTES,
+        "copy_probe_fetch_kib": fc, "copy_probe_write_kib": wc,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "hbm_fetch_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": fetch_b + write_b,
+        "algorithmic_bytes_per_launch": None,
+        "commands": [
+            f"rocprofv3 --pmc {c} --output-format csv -d <dir_{c}> -o run -- python3 -u bench.py "
+            f"--workload {workload} --steps 5 --warmup 1 --no-cpu --probe"
+            for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
+            f"python bench.py --workload {workload} --traffic-from "
+            "<dir_FETCH_SIZE>/run_counter_collection.csv <dir_WRITE_SIZE>/run_counter_collection.csv"],
+    }
+    import synth
+    c = synth.CONFIGS[workload]
+    d["algorithmic_bytes_per_launch"] = algorithmic_bytes(c["width"], c["height"], c["bpc"],
+                                                          c["frames"])
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    path = os.path.join(ROOT, "profiles", f"frames_kernel_{workload}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
+    return d
+
+
 def cpu_baseline(clip, max_seconds: float = 20.0):
     """The oracle over the leading frames of the same clip that fit `max_seconds` (the whole clip
     when it fits), single-threaded; frames/s."""
@@ -93,7 +155,13 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--probe", action="store_true", help="also measure the memory ceilings")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic summary from two counter CSVs and exit")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        print(json.dumps(write_traffic(args.workload, *args.traffic_from)))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -170,7 +238,7 @@ def main():
                      "algorithmic_bytes_per_launch": alg},
     }
     if args.probe:
-        nbytes = 1 << 30
+        nbytes = PROBE_BYTES
         a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         a.fill_(1)

@@ -194,7 +194,7 @@ typedef struct iir_geometry {
     int32_t tiles;             /* strips * row_tiles */
     int32_t sum_slots;         /* partial accumulators per sum, folded on the host */
     int32_t max_chunks;        /* most time chunks one launch may split a clip into */
-    int32_t reserved;
+    int32_t group;             /* adjacent tiles (one wavefront each) per workgroup */
 } iir_geometry;
 IIR_API int iir_get_geometry(const iir_ctx *ctx, iir_geometry *out);
 

@@ -81,6 +81,7 @@ struct iir_ctx {
     int Wc = 0, Hc = 0;
     int lanes_out = 0, strips = 0, row_tiles = 0, tiles = 0;
     int rows_per_tile = 16;
+    int group = 1;  // adjacent tiles (one wavefront each) per workgroup
     int target_waves = 1024;
     int min_chunk = 4;
     int max_chunks = 1;
@@ -201,12 +202,24 @@ void choose_columns(iir_ctx *c)
     c->lanes_out = std::max(2, lanes);
 }
 
+// Wavefronts per workgroup: adjacent strips of one row of tiles run as one workgroup and step
+// through the frames together, so the 128-byte lines two neighbouring strips share are fetched
+// from HBM once and hit in the cache for the other. Needs strips % group == 0 (then tiles %
+// group == 0 too, and a workgroup never straddles two rows of tiles or two time chunks).
+int choose_group(int strips, int forced)
+{
+    if (forced > 0)
+        return (supported_group(forced) && strips % forced == 0) ? forced : 1;
+    return 1;
+}
+
 // Rows per tile: each candidate's kernel has its own register footprint and hence its own number
 // of resident wavefronts per CU. A launch whose tiles all fit at once finishes when its busiest
 // SIMD does, so the estimated cost is (wavefronts per SIMD, rounded up) x (rows + the 4 halo
 // rows each tile re-reads), times the number of rounds when they do not all fit.
 int choose_rows(iir_ctx *c, int cus, int forced)
 {
+    const int group = choose_group(c->strips, env_int("IIR_GROUP", 0, 0, 64));
     static const int kCandidates[] = {12, 16, 20};
     int best = 16;
     double best_cost = 1e300;
@@ -215,7 +228,8 @@ int choose_rows(iir_ctx *c, int cus, int forced)
             continue;
         int per_cu = 0;
         const bool generic = !fast_path_ok(c->cfg.width, c->cfg.height, th);
-        if (frames_occupancy(c->cfg.bpc, th, generic, &per_cu) != hipSuccess || per_cu < 1)
+        if (frames_occupancy(c->cfg.bpc, th, generic, group, &per_cu) != hipSuccess ||
+            per_cu < 1)
             continue;
         const int64_t waves = (int64_t)c->strips * ((c->cfg.height + th - 1) / th);
         const int64_t slots = (int64_t)per_cu * cus;
@@ -363,8 +377,8 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     if (timing)
         HIP_TRY(hipEventRecord(sub.k0, c->stream));
     HIP_TRY(launch_frames(c->cfg.bpc, c->rows_per_tile,
-                          !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile), a,
-                          c->stream));
+                          !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile), c->group,
+                          a, c->stream));
     if (timing)
         HIP_TRY(hipEventRecord(sub.k1, c->stream));
     const size_t per_frame = (size_t)kSums * kSumSlots;
@@ -424,6 +438,7 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     c->rows_per_tile = choose_rows(c, prop.multiProcessorCount, env_int("IIR_ROWS_PER_TILE", 0, 0, 64));
     c->row_tiles = (cfg->height + c->rows_per_tile - 1) / c->rows_per_tile;
     c->tiles = c->strips * c->row_tiles;
+    c->group = choose_group(c->strips, env_int("IIR_GROUP", 0, 0, 64));
     c->target_waves = env_int("IIR_TARGET_WAVES", 4 * prop.multiProcessorCount, 1, 1 << 20);
     c->min_chunk = env_int("IIR_MIN_CHUNK", 4, 1, 65536);
     c->max_chunks = plan_chunks(c, cfg->max_batch);
@@ -645,7 +660,7 @@ IIR_API int iir_get_geometry(const iir_ctx *ctx, iir_geometry *out)
     out->tiles = ctx->tiles;
     out->sum_slots = kSumSlots;
     out->max_chunks = ctx->max_chunks;
-    out->reserved = 0;
+    out->group = ctx->group;
     return IIR_OK;
 }
 

@@ -48,9 +48,12 @@ struct KernelArgs {
 
 // Host-side launchers (iir_kernels.hip). Each returns the launch's hipError_t.
 bool supported_rows_per_tile(int th);           // 12, 16 or 20
+bool supported_group(int group);                // wavefronts per workgroup: 1, 2 or 4
 bool fast_path_ok(int W, int H, int th);         // the uniform fast path applies
-hipError_t frames_occupancy(int bpc, int th, bool generic, int *waves_per_cu);
-hipError_t launch_frames(int bpc, int th, bool generic, const KernelArgs &a, hipStream_t stream);
+hipError_t frames_occupancy(int bpc, int th, bool generic, int group, int *waves_per_cu);
+// group adjacent tiles per workgroup; a.tiles must be a multiple of group
+hipError_t launch_frames(int bpc, int th, bool generic, int group, const KernelArgs &a,
+                         hipStream_t stream);
 hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
                          int lanes_out, int strips, int th, hipStream_t stream);
 hipError_t launch_probe(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream);

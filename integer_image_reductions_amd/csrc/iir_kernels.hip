@@ -83,16 +83,17 @@ __device__ __forceinline__ uint32_t pkmin(uint32_t a, uint32_t b)
                                                                   __builtin_bit_cast(u16x2, b)));
 }
 
-// lane i receives lane i-1's value (wave_shr:1); lane 0 receives 0
+// lane i receives lane i-1's value (wave_shr:1); lane 0 receives 0 (bound_ctrl, so no register
+// has to be zeroed for the lane without a source)
 __device__ __forceinline__ uint32_t from_left(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xf, 0xf, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xf, 0xf, true);
 }
 
 // lane i receives lane i+1's value (wave_shl:1); lane 63 receives 0
 __device__ __forceinline__ uint32_t from_right(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xf, 0xf, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xf, 0xf, true);
 }
 
 // whole-sample mirror into [0, n), exact for -2 <= i <= n + 1, clamped beyond (never used there)
@@ -322,7 +323,14 @@ struct Tile {
                                  // at 8 bits)
     int crow0;                   // scalar: first chroma row of the tile
     bool c_on;                   // lane reads chroma
-    // edges (careful path only)
+    // edges, fast path: the halo lane left of column 0 and the one right of column W-1 load the
+    // group next to the edge and permute it into the mirror image; only the first and last
+    // strips (edge_tile, scalar) run that permutation
+    bool edge_tile;
+    bool mirror_left;            // lane 0 of the leftmost strip: columns -2, -1 from 2, 1
+    bool mirror_right;           // lane whose first column is W: columns W, W+1 from W-2, W-3
+    uint32_t msel;               // 8-bit: the byte permutation doing the above (identity else)
+    // edges (generic path only)
     bool left_fix;               // lane 1 of the leftmost strip: mirror the columns left of 0
     bool right_fix;              // lane holding column W-1: mirror the columns right of it
     int right_rem;               // scalar: W % 4
@@ -358,30 +366,42 @@ struct Stage {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// LDS row `row` of a stage whose first row is at LDS byte address `base`. The base is passed
+// through opaque() once per frame, so each load's M0 is one scalar add instead of one of dozens
+// of precomputed addresses the compiler would otherwise keep (and spill) across the loop.
+__device__ __forceinline__ lds_void *lds_row(uint32_t base, int row)
+{
+    return (lds_void *)(uintptr_t)(base + (uint32_t)row * (kWave * 4u));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(uint32_t (*lds)[kWave])
+{
+    return (uint32_t)(uintptr_t)(lds_void *)&lds[0][0];
+}
+
 // Fetch one lane value into a register (STAGED false) or into LDS row `row` (STAGED true).
 template <bool STAGED>
 __device__ __forceinline__ void fetch32(Rsrc r, uint32_t voff, uint32_t soff, uint32_t &reg,
-                                        uint32_t (*lds)[kWave], int row)
+                                        uint32_t lds, int row)
 {
     if constexpr (STAGED)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)&lds[row][0], 4, voff, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, row), 4, voff, soff, 0, 0);
     else
         reg = ld32(r, voff, soff);
 }
 
 template <int BPC, bool STAGED>
 __device__ __forceinline__ void fetch_luma(Rsrc r, uint32_t voff, uint32_t soff,
-                                           typename Px<BPC>::Luma &reg, uint32_t (*lds)[kWave],
-                                           int row)
+                                           typename Px<BPC>::Luma &reg, uint32_t lds, int row)
 {
     if constexpr (!STAGED) {
         reg = ld_luma<BPC>(r, voff, soff);
     } else if constexpr (BPC == 8) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)&lds[row][0], 4, voff, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, row), 4, voff, soff, 0, 0);
     } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)&lds[2 * row][0], 4, voff, soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)&lds[2 * row + 1][0], 4, voff + 4,
-                                                 soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, 2 * row), 4, voff, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, 2 * row + 1), 4, voff + 4, soff,
+                                                 0, 0);
     }
 }
 
@@ -390,11 +410,12 @@ __device__ __forceinline__ void fetch_luma(Rsrc r, uint32_t voff, uint32_t soff,
 template <int BPC, int TH, bool GENERIC, bool STAGED>
 __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, int t,
                                            bool accumulate, FrameData<BPC, TH> &F,
-                                           uint32_t (*lds)[kWave])
+                                           uint32_t (*stage)[kWave])
 {
     typedef FrameData<BPC, TH> FD;
     typedef Stage<BPC, TH> ST;
     const int H = a.H;
+    const uint32_t lds = STAGED ? opaque(lds_addr(stage)) : 0u;
     Rsrc rs[6];
     uint32_t pitch[6];
 #pragma unroll
@@ -464,6 +485,25 @@ __device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWav
     }
 }
 
+// Fast path, first and last strips: turn the halo lanes' loaded groups into the mirror images
+// the horizontal taps need. Left: the group of columns 0..3 becomes (-, -, x2, x1) for columns
+// -4..-1; right: the group of columns W-4..W-1 becomes (x[W-2], x[W-3], -, -) for W..W+3.
+// Columns -4, -3, W+2 and W+3 feed no output.
+template <int BPC, int TH>
+__device__ __forceinline__ void mirror_halo(const Tile &T, FrameData<BPC, TH> &F)
+{
+#pragma unroll
+    for (int k = 0; k < TH + 4; ++k) {
+        if constexpr (BPC == 8) {
+            F.R[k] = perm(F.R[k], F.R[k], T.msel);
+        } else {
+            // (x2 | x1 << 16) from the second dword's low and the first dword's high half
+            const uint32_t m = perm(F.R[k].x, F.R[k].y, 0x07060100u);
+            F.R[k] = u32x2{T.mirror_right ? m : F.R[k].x, T.mirror_left ? m : F.R[k].y};
+        }
+    }
+}
+
 // One frame of one tile from its loaded samples: blur the reference luma (vertical pass once per
 // column and row, horizontal taps through DPP neighbours), SAD against the previous blurred tile
 // held in registers, SSE of the luma and chroma tiles, one wavefront reduction and one atomic per
@@ -471,7 +511,7 @@ __device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWav
 // (the vast majority) run without any of it.
 template <int BPC, int TH, bool GENERIC>
 __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T, int t,
-                                              bool accumulate, const FrameData<BPC, TH> &F,
+                                              bool accumulate, FrameData<BPC, TH> &F,
                                               uint32_t (&prev0)[TH], uint32_t (&prev1)[TH],
                                               uint32_t &sum_prev, bool &have_prev, Pending &P)
 {
@@ -479,6 +519,11 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
     typedef FrameData<BPC, TH> FD;
     constexpr uint32_t kVRound = BPC == 8 ? 128u : 32768u;
     constexpr uint32_t kVSel = BPC == 8 ? 0x06050201u : 0x07060302u;
+
+    if constexpr (!GENERIC) {
+        if (T.edge_tile)
+            mirror_halo<BPC, TH>(T, F);
+    }
 
     // SSE of the chroma tiles first, which frees their registers before the blur
     uint32_t su = 0, su2 = 0, sv = 0, sv2 = 0;
@@ -515,11 +560,9 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
         uint32_t q0 = perm(v[1], v[0], kVSel);  // V of columns c, c+1
         uint32_t q1 = perm(v[3], v[2], kVSel);  // V of columns c+2, c+3
         uint32_t ql = from_left(q1);            // V of columns c-2, c-1
-        // (V(c+2), V(c+1)): the mirror image of the lane's own columns, which stands for columns
-        // -2, -1 at the left frame edge and for W, W+1 at the right one when W % 4 == 0
-        const uint32_t mirrored = perm(q0, q1, 0x07060100u);
-        if constexpr (!GENERIC)
-            ql = T.left_fix ? mirrored : ql;
+        // generic path: (V(c+2), V(c+1)), the mirror image of the lane's own columns, stands for
+        // columns -2, -1 at the left frame edge and for W, W+1 at the right one when W % 4 == 0
+        const uint32_t mirrored = GENERIC ? perm(q0, q1, 0x07060100u) : 0u;
         if constexpr (GENERIC) {
             // (V(2), V(1)) stands for columns -2, -1
             ql = T.left_fix ? mirrored : ql;
@@ -533,8 +576,6 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
             }
         }
         uint32_t qr = from_right(q0);  // V of columns c+4, c+5
-        if constexpr (!GENERIC)
-            qr = T.right_fix ? mirrored : qr;
         if constexpr (GENERIC) {
             if (T.right_rem == 0)
                 qr = T.right_fix ? mirrored : qr;
@@ -579,7 +620,7 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 // frame before them. STAGED keeps the next frame's loads in flight while the current one is
 // computed: the loads of frame t+1 write the wave's LDS stage (no registers held), issued as soon
 // as frame t has been read out of it.
-template <int BPC, int TH, bool GENERIC, bool STAGED>
+template <int BPC, int TH, bool GENERIC, bool STAGED, int GROUP>
 __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
                                            uint32_t (&prev0)[TH], uint32_t (&prev1)[TH],
                                            uint32_t sum_prev, bool have_prev,
@@ -595,21 +636,31 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
     P.first = f_begin;
     P.count = 0;
     if constexpr (STAGED) {
-        FrameData<BPC, TH> F;
-        load_frame<BPC, TH, GENERIC, true>(a, T, t0, t0 >= f_begin, F, lds);
+        {
+            FrameData<BPC, TH> F;  // unused: staged loads write LDS only
+            load_frame<BPC, TH, GENERIC, true>(a, T, t0, t0 >= f_begin, F, lds);
+        }
         for (int t = t0; t < f_end; ++t) {
+            // a fresh frame per iteration: no sample register is carried around the loop
+            FrameData<BPC, TH> F;
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): frame t is in LDS
             read_stage<BPC, TH>(t >= f_begin, lds, T.lane, F);
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
+            if constexpr (GROUP > 1)
+                __builtin_amdgcn_s_barrier();  // siblings issue frame t+1 together
             __builtin_amdgcn_sched_barrier(0);
-            if (t + 1 < f_end)
-                load_frame<BPC, TH, GENERIC, true>(a, T, t + 1, true, F, lds);
+            if (t + 1 < f_end) {
+                FrameData<BPC, TH> G;  // unused: staged loads write LDS only
+                load_frame<BPC, TH, GENERIC, true>(a, T, t + 1, true, G, lds);
+            }
             compute_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F, prev0, prev1, sum_prev,
                                             have_prev, P);
         }
     } else {
         for (int t = t0; t < f_end; ++t) {
             FrameData<BPC, TH> F;
+            if constexpr (GROUP > 1)
+                __builtin_amdgcn_s_barrier();
             load_frame<BPC, TH, GENERIC, false>(a, T, t, t >= f_begin, F, lds);
             compute_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F, prev0, prev1, sum_prev,
                                             have_prev, P);
@@ -618,21 +669,25 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
     flush_sums(a, P, T.lane);
 }
 
-template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void frames_kernel(
-    const KernelArgs a)
+template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE, int GROUP>
+__global__ __launch_bounds__(kWave * GROUP) __attribute__((amdgpu_waves_per_eu(WPE))) void
+frames_kernel(const KernelArgs a)
 {
-    __shared__ uint32_t stage[STAGED ? Stage<BPC, TH>::kRows : 1][kWave];
+    __shared__ uint32_t stage[GROUP][STAGED ? Stage<BPC, TH>::kRows : 1][kWave];
     static_assert(TH % 4 == 0, "tile height must be a multiple of 4 (two chroma rows per step)");
     constexpr int B = Px<BPC>::kBytes;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uni(threadIdx.x / kWave);
 
     // clear the other sum buffer for the next submission
-    for (int i = blockIdx.x * kWave + lane; i < a.zero_n; i += gridDim.x * kWave)
+    for (int i = blockIdx.x * (kWave * GROUP) + threadIdx.x; i < a.zero_n;
+         i += gridDim.x * (kWave * GROUP))
         a.zero[i] = 0ull;
 
+    // GROUP consecutive tiles (adjacent strips) per workgroup; tiles % GROUP == 0, so a
+    // workgroup never straddles two time chunks
     Tile T;
-    const int L = uni(xcd_linear(blockIdx.x, gridDim.x));
+    const int L = uni(xcd_linear(blockIdx.x, gridDim.x) * GROUP + wave);
     T.chunk = uni(L / a.tiles);
     T.tile = uni(L - T.chunk * a.tiles);
     const int rt = uni(T.tile / a.strips);
@@ -646,11 +701,17 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) vo
     // lane roles; every load offset stays inside its row's pitch (a lane whose first column is
     // outside [0, W) reads column 0 and its values are never used)
     const int c = s - kLumaCols + kLumaCols * lane;
-    T.luma_off = (c >= 0 && c < W) ? (uint32_t)(c * B) : 0u;
+    T.luma_off = (c >= 0 && c < W) ? (uint32_t)(c * B)
+                 : (!GENERIC && c == W) ? (uint32_t)((W - kLumaCols) * B)
+                                        : 0u;
     T.out_lane = lane >= 1 && lane <= a.lanes_out && c < W;
     T.w0 = T.out_lane ? ((c < W ? 1u : 0u) | (c + 1 < W ? 0x10000u : 0u)) : 0u;
     T.w1 = T.out_lane ? ((c + 2 < W ? 1u : 0u) | (c + 3 < W ? 0x10000u : 0u)) : 0u;
     T.left_fix = T.strip == 0 && lane == 1;
+    T.edge_tile = T.strip == 0 || T.strip == a.strips - 1;
+    T.mirror_left = T.strip == 0 && lane == 0;
+    T.mirror_right = c == W;
+    T.msel = T.mirror_left ? 0x01020000u : T.mirror_right ? 0x00000102u : 0x03020100u;
     T.right_rem = W & 3;
     // the lane holding column W-1 (on the fast path W % 4 == 0, so its columns end at W-1)
     T.right_fix = c <= W - 1 && W - 1 < c + kLumaCols && lane >= 1 && lane <= a.lanes_out;
@@ -711,7 +772,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) vo
     }
 
     // every tile of a launch takes the same path, so wavefronts cost the same and none trails
-    frame_loop<BPC, TH, GENERIC, STAGED>(a, T, prev0, prev1, sum_prev, have_prev, stage);
+    frame_loop<BPC, TH, GENERIC, STAGED, GROUP>(a, T, prev0, prev1, sum_prev, have_prev,
+                                                stage[wave]);
 
     if (T.chunk == a.chunks - 1) {
         uint2 *rout = reinterpret_cast<uint2 *>(a.ring_out);
@@ -796,34 +858,54 @@ typedef void (*FramesFn)(KernelArgs);
 
 // Every (bit depth, tile height, path) the host may pick. The fast path needs W % 8 == 0 and
 // H % TH == 0 (no ragged tile, no partial sample group); the generic path takes any size.
-template <int BPC, bool GENERIC>
+template <int BPC, bool GENERIC, int GROUP>
 FramesFn frames_fn(int th)
 {
     constexpr bool P = BPC == 8 ? IIR_STAGE8 : IIR_STAGE10;
     switch (th) {
     case 12:
-        return frames_kernel<BPC, 12, P, GENERIC, IIR_WPE12>;
+        return frames_kernel<BPC, 12, P, GENERIC, IIR_WPE12, GROUP>;
     case 16:
-        return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16>;
+        return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16, GROUP>;
     case 20:
-        return frames_kernel<BPC, 20, P, GENERIC, IIR_WPE20>;
+        return frames_kernel<BPC, 20, P, GENERIC, IIR_WPE20, GROUP>;
     default:
         return nullptr;
     }
 }
 
-FramesFn pick(int bpc, int th, bool generic)
+template <int BPC, bool GENERIC>
+FramesFn frames_fn_group(int th, int group)
+{
+    switch (group) {
+    case 1:
+        return frames_fn<BPC, GENERIC, 1>(th);
+    case 2:
+        return frames_fn<BPC, GENERIC, 2>(th);
+    case 4:
+        return frames_fn<BPC, GENERIC, 4>(th);
+    default:
+        return nullptr;
+    }
+}
+
+FramesFn pick(int bpc, int th, bool generic, int group)
 {
     if (bpc == 8)
-        return generic ? frames_fn<8, true>(th) : frames_fn<8, false>(th);
-    return generic ? frames_fn<10, true>(th) : frames_fn<10, false>(th);
+        return generic ? frames_fn_group<8, true>(th, group) : frames_fn_group<8, false>(th, group);
+    return generic ? frames_fn_group<10, true>(th, group) : frames_fn_group<10, false>(th, group);
 }
 
 }  // namespace
 
 bool supported_rows_per_tile(int th)
 {
-    return pick(8, th, true) != nullptr;
+    return pick(8, th, true, 1) != nullptr;
+}
+
+bool supported_group(int group)
+{
+    return pick(8, 16, true, group) != nullptr;
 }
 
 bool fast_path_ok(int W, int H, int th)
@@ -831,21 +913,26 @@ bool fast_path_ok(int W, int H, int th)
     return W % 8 == 0 && H % th == 0;
 }
 
-hipError_t frames_occupancy(int bpc, int th, bool generic, int *waves_per_cu)
+hipError_t frames_occupancy(int bpc, int th, bool generic, int group, int *waves_per_cu)
 {
-    FramesFn f = pick(bpc, th, generic);
+    FramesFn f = pick(bpc, th, generic, group);
     if (!f)
         return hipErrorInvalidValue;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(waves_per_cu, reinterpret_cast<const void *>(f),
-                                                        kWave, 0);
+    int blocks = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &blocks, reinterpret_cast<const void *>(f), kWave * group, 0);
+    *waves_per_cu = blocks * group;
+    return e;
 }
 
-hipError_t launch_frames(int bpc, int th, bool generic, const KernelArgs &a, hipStream_t stream)
+hipError_t launch_frames(int bpc, int th, bool generic, int group, const KernelArgs &a,
+                         hipStream_t stream)
 {
-    FramesFn f = pick(bpc, th, generic);
-    if (!f)
+    FramesFn f = pick(bpc, th, generic, group);
+    if (!f || group < 1 || a.tiles % group != 0)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(f, dim3((unsigned)(a.tiles * a.chunks)), dim3(kWave), 0, stream, a);
+    hipLaunchKernelGGL(f, dim3((unsigned)(a.tiles / group * a.chunks)), dim3(kWave * group), 0,
+                       stream, a);
     return hipGetLastError();
 }
 

@@ -512,8 +512,10 @@ __device__ __forceinline__ void mirror_halo(const Tile &T, FrameData<BPC, TH> &F
 template <int BPC, int TH, bool GENERIC>
 __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T, int t,
                                               bool accumulate, FrameData<BPC, TH> &F,
-                                              uint32_t (&prev0)[TH], uint32_t (&prev1)[TH],
-                                              uint32_t &sum_prev, bool &have_prev, Pending &P)
+                                              const uint32_t (&prev0)[TH],
+                                              const uint32_t (&prev1)[TH], uint32_t (&next0)[TH],
+                                              uint32_t (&next1)[TH], uint32_t &sum_prev,
+                                              bool &have_prev, Pending &P)
 {
     typedef typename Px<BPC>::Luma Luma;
     typedef FrameData<BPC, TH> FD;
@@ -600,8 +602,8 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
                 sse_luma<BPC>(r, d, sy, sy2);
             }
         }
-        prev0[i] = c0;
-        prev1[i] = c1;
+        next0[i] = c0;
+        next1[i] = c1;
     }
 
     if (accumulate) {
@@ -619,7 +621,8 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 // The frames of this workgroup's time chunk. Chunks after the first start by re-blurring the
 // frame before them. STAGED keeps the next frame's loads in flight while the current one is
 // computed: the loads of frame t+1 write the wave's LDS stage (no registers held), issued as soon
-// as frame t has been read out of it.
+// as frame t has been read out of it. Frames go in pairs that swap the roles of two blurred-tile
+// register sets (prev -> alt -> prev), so no frame ends by copying its blurred tile back.
 template <int BPC, int TH, bool GENERIC, bool STAGED, int GROUP>
 __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
                                            uint32_t (&prev0)[TH], uint32_t (&prev1)[TH],
@@ -636,13 +639,15 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
     P.first = f_begin;
     P.count = 0;
     if constexpr (STAGED) {
-        {
-            FrameData<BPC, TH> F;  // unused: staged loads write LDS only
-            load_frame<BPC, TH, GENERIC, true>(a, T, t0, t0 >= f_begin, F, lds);
-        }
-        for (int t = t0; t < f_end; ++t) {
-            // a fresh frame per iteration: no sample register is carried around the loop
-            FrameData<BPC, TH> F;
+        FrameData<BPC, TH> F;  // unused: staged loads write LDS only
+        load_frame<BPC, TH, GENERIC, true>(a, T, t0, t0 >= f_begin, F, lds);
+    }
+    // one frame: blurred tile in (i0, i1), out to (o0, o1)
+    auto step = [&](int t, const uint32_t(&i0)[TH], const uint32_t(&i1)[TH], uint32_t(&o0)[TH],
+                    uint32_t(&o1)[TH]) {
+        // a fresh frame per step: no sample register is carried from one frame to the next
+        FrameData<BPC, TH> F;
+        if constexpr (STAGED) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): frame t is in LDS
             read_stage<BPC, TH>(t >= f_begin, lds, T.lane, F);
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
@@ -653,17 +658,25 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
                 FrameData<BPC, TH> G;  // unused: staged loads write LDS only
                 load_frame<BPC, TH, GENERIC, true>(a, T, t + 1, true, G, lds);
             }
-            compute_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F, prev0, prev1, sum_prev,
-                                            have_prev, P);
-        }
-    } else {
-        for (int t = t0; t < f_end; ++t) {
-            FrameData<BPC, TH> F;
+        } else {
             if constexpr (GROUP > 1)
                 __builtin_amdgcn_s_barrier();
             load_frame<BPC, TH, GENERIC, false>(a, T, t, t >= f_begin, F, lds);
-            compute_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F, prev0, prev1, sum_prev,
-                                            have_prev, P);
+        }
+        compute_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F, i0, i1, o0, o1, sum_prev,
+                                        have_prev, P);
+    };
+    uint32_t alt0[TH], alt1[TH];
+    for (int t = t0; t < f_end; t += 2) {
+        step(t, prev0, prev1, alt0, alt1);
+        if (t + 1 < f_end) {
+            step(t + 1, alt0, alt1, prev0, prev1);
+        } else {
+#pragma unroll
+            for (int i = 0; i < TH; ++i) {
+                prev0[i] = alt0[i];
+                prev1[i] = alt1[i];
+            }
         }
     }
     flush_sums(a, P, T.lane);

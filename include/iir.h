@@ -188,13 +188,12 @@ IIR_API int iir_kernel_stats(iir_ctx *ctx, int32_t reset, int64_t *launches, dou
 /* Launch geometry chosen at create, for reports and tests. */
 typedef struct iir_geometry {
     int32_t rows_per_tile;     /* output luma rows per wavefront tile */
-    int32_t lanes_out;         /* output lanes per wavefront (4 luma columns each) */
-    int32_t strips;            /* tiles across */
+    int32_t lanes_out;         /* output lanes per wavefront (4 luma columns each): 64 */
+    int32_t strips;            /* tiles across: ceil(W / 256) */
     int32_t row_tiles;         /* tiles down */
     int32_t tiles;             /* strips * row_tiles */
     int32_t sum_slots;         /* partial accumulators per sum, folded on the host */
     int32_t max_chunks;        /* most time chunks one launch may split a clip into */
-    int32_t group;             /* adjacent tiles (one wavefront each) per workgroup */
 } iir_geometry;
 IIR_API int iir_get_geometry(const iir_ctx *ctx, iir_geometry *out);
 

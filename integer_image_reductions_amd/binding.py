@@ -48,7 +48,7 @@ class Scores(ctypes.Structure):
 class Geometry(ctypes.Structure):
     _fields_ = [("rows_per_tile", c_i32), ("lanes_out", c_i32), ("strips", c_i32),
                 ("row_tiles", c_i32), ("tiles", c_i32), ("sum_slots", c_i32),
-                ("max_chunks", c_i32), ("group", c_i32)]
+                ("max_chunks", c_i32)]
 
 
 class IIRError(RuntimeError):

@@ -81,7 +81,6 @@ struct iir_ctx {
     int Wc = 0, Hc = 0;
     int lanes_out = 0, strips = 0, row_tiles = 0, tiles = 0;
     int rows_per_tile = 16;
-    int group = 1;  // adjacent tiles (one wavefront each) per workgroup
     int target_waves = 1024;
     int min_chunk = 4;
     int max_chunks = 1;
@@ -191,26 +190,12 @@ const uint8_t *plane_ptr(const iir_frame *ref, const iir_frame *dist, int t, int
     return static_cast<const uint8_t *>(k < 3 ? ref[t].plane[k].data : dist[t].plane[k - 3].data);
 }
 
-// Columns: strips of up to kMaxLanesOut output lanes (4 columns each), balanced and even so the
-// 4:2:0 chroma tile of a strip starts on a dword.
+// Columns: strips of kStripCols luma columns, each starting on a 256-column boundary, so a
+// wavefront's rows are whole aligned cache lines that no other wavefront loads.
 void choose_columns(iir_ctx *c)
 {
-    const int dwords = (c->cfg.width + kLumaCols - 1) / kLumaCols;
-    c->strips = (dwords + kMaxLanesOut - 1) / kMaxLanesOut;
-    int lanes = (dwords + c->strips - 1) / c->strips;
-    lanes += lanes & 1;
-    c->lanes_out = std::max(2, lanes);
-}
-
-// Wavefronts per workgroup: adjacent strips of one row of tiles run as one workgroup and step
-// through the frames together, so the 128-byte lines two neighbouring strips share are fetched
-// from HBM once and hit in the cache for the other. Needs strips % group == 0 (then tiles %
-// group == 0 too, and a workgroup never straddles two rows of tiles or two time chunks).
-int choose_group(int strips, int forced)
-{
-    if (forced > 0)
-        return (supported_group(forced) && strips % forced == 0) ? forced : 1;
-    return 1;
+    c->strips = (c->cfg.width + kStripCols - 1) / kStripCols;
+    c->lanes_out = kWave;
 }
 
 // Rows per tile: each candidate's kernel has its own register footprint and hence its own number
@@ -219,7 +204,6 @@ int choose_group(int strips, int forced)
 // rows each tile re-reads), times the number of rounds when they do not all fit.
 int choose_rows(iir_ctx *c, int cus, int forced)
 {
-    const int group = choose_group(c->strips, env_int("IIR_GROUP", 0, 0, 64));
     static const int kCandidates[] = {12, 16, 20};
     int best = 16;
     double best_cost = 1e300;
@@ -228,7 +212,7 @@ int choose_rows(iir_ctx *c, int cus, int forced)
             continue;
         int per_cu = 0;
         const bool generic = !fast_path_ok(c->cfg.width, c->cfg.height, th);
-        if (frames_occupancy(c->cfg.bpc, th, generic, group, &per_cu) != hipSuccess ||
+        if (frames_occupancy(c->cfg.bpc, th, generic, &per_cu) != hipSuccess ||
             per_cu < 1)
             continue;
         const int64_t waves = (int64_t)c->strips * ((c->cfg.height + th - 1) / th);
@@ -363,7 +347,6 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     a.H = c->cfg.height;
     a.Wc = c->Wc;
     a.Hc = c->Hc;
-    a.lanes_out = c->lanes_out;
     a.strips = c->strips;
     a.row_tiles = c->row_tiles;
     a.tiles = c->tiles;
@@ -377,8 +360,8 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     if (timing)
         HIP_TRY(hipEventRecord(sub.k0, c->stream));
     HIP_TRY(launch_frames(c->cfg.bpc, c->rows_per_tile,
-                          !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile), c->group,
-                          a, c->stream));
+                          !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile), a,
+                          c->stream));
     if (timing)
         HIP_TRY(hipEventRecord(sub.k1, c->stream));
     const size_t per_frame = (size_t)kSums * kSumSlots;
@@ -438,7 +421,6 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     c->rows_per_tile = choose_rows(c, prop.multiProcessorCount, env_int("IIR_ROWS_PER_TILE", 0, 0, 64));
     c->row_tiles = (cfg->height + c->rows_per_tile - 1) / c->rows_per_tile;
     c->tiles = c->strips * c->row_tiles;
-    c->group = choose_group(c->strips, env_int("IIR_GROUP", 0, 0, 64));
     c->target_waves = env_int("IIR_TARGET_WAVES", 4 * prop.multiProcessorCount, 1, 1 << 20);
     c->min_chunk = env_int("IIR_MIN_CHUNK", 4, 1, 65536);
     c->max_chunks = plan_chunks(c, cfg->max_batch);
@@ -621,7 +603,7 @@ IIR_API int iir_export_blur(iir_ctx *ctx, void *dst, int64_t pitch)
     if (ds.err != hipSuccess)
         return fail_hip(ds.err, "hipSetDevice");
     HIP_TRY(launch_export(ctx->ring[ctx->ring_cur], static_cast<uint16_t *>(dst), pitch,
-                          ctx->cfg.width, ctx->cfg.height, ctx->lanes_out, ctx->strips,
+                          ctx->cfg.width, ctx->cfg.height, ctx->strips,
                           ctx->rows_per_tile, ctx->stream));
     return IIR_OK;
 }
@@ -660,7 +642,6 @@ IIR_API int iir_get_geometry(const iir_ctx *ctx, iir_geometry *out)
     out->tiles = ctx->tiles;
     out->sum_slots = kSumSlots;
     out->max_chunks = ctx->max_chunks;
-    out->group = ctx->group;
     return IIR_OK;
 }
 

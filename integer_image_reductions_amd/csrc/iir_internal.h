@@ -11,11 +11,10 @@
 namespace iir {
 
 constexpr int kWave = 64;          // CDNA wavefront; one wavefront is one workgroup
-constexpr int kMaxLanesOut = 62;   // output lanes per wavefront: lane 0 and lane lanes_out + 1
-                                   // are the left and right halo lanes
 constexpr int kSumSlots = 8;       // partial slots per sum (one per XCD), added up on the host
 constexpr int kSums = 4;           // SAD, SSE_Y, SSE_U, SSE_V
 constexpr int kLumaCols = 4;       // luma columns per lane
+constexpr int kStripCols = kWave * kLumaCols;  // luma columns per tile (one per 4 per lane)
 
 // Device pointers of one frame pair: ref Y, U, V, then dist Y, U, V.
 struct FramePtrs {
@@ -41,21 +40,18 @@ struct KernelArgs {
     unsigned long long *zero;
     int32_t zero_n;
     int32_t W, H, Wc, Hc;
-    int32_t lanes_out, strips, row_tiles, tiles;
+    int32_t strips, row_tiles, tiles;
     int32_t nframes, chunks, chunk_len;
     int32_t has_prev;
 };
 
 // Host-side launchers (iir_kernels.hip). Each returns the launch's hipError_t.
 bool supported_rows_per_tile(int th);           // 12, 16 or 20
-bool supported_group(int group);                // wavefronts per workgroup: 1, 2 or 4
 bool fast_path_ok(int W, int H, int th);         // the uniform fast path applies
-hipError_t frames_occupancy(int bpc, int th, bool generic, int group, int *waves_per_cu);
-// group adjacent tiles per workgroup; a.tiles must be a multiple of group
-hipError_t launch_frames(int bpc, int th, bool generic, int group, const KernelArgs &a,
-                         hipStream_t stream);
+hipError_t frames_occupancy(int bpc, int th, bool generic, int *waves_per_cu);
+hipError_t launch_frames(int bpc, int th, bool generic, const KernelArgs &a, hipStream_t stream);
 hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
-                         int lanes_out, int strips, int th, hipStream_t stream);
+                         int strips, int th, hipStream_t stream);
 hipError_t launch_probe(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream);
 
 }  // namespace iir

@@ -11,11 +11,16 @@
 // "Research-0735: CUDA motion kernel ncu hotpath analysis (576x324)": a 5x5 separable Gaussian).
 //
 // Design (MI355X-first; the CUDA tiles on the pages are prior art only):
-//   * One wavefront per workgroup owns one tile: 4 * lanes_out luma columns x TH rows.
-//     Lane l holds 4 adjacent luma columns; lanes 0 and lanes_out + 1 only feed the horizontal
-//     halo. Each lane slides down its columns with the whole 5-row window in registers, so every
-//     vertical value is computed exactly once and reused by the five horizontal taps through two
-//     DPP lane shifts per row (no LDS round trip, no barrier).
+//   * One wavefront per workgroup owns one tile: 256 luma columns x TH rows, its rows starting
+//     on a 256-column boundary, so every row a wavefront loads is whole, aligned cache lines that
+//     no other wavefront touches (chroma: 128 samples per row). Lane l holds luma columns
+//     4l .. 4l+3 of the tile. Each lane slides down its columns with the whole 5-row window in
+//     registers, so every vertical value is computed exactly once and reused by the five
+//     horizontal taps through two DPP lane shifts per row (no LDS round trip, no barrier).
+//   * The two columns left and right of the tile (horizontal halo) arrive transposed: one load
+//     per frame gives lane k the halo samples of tile row k-2 (lanes 0-31 the left side, lanes
+//     32-63 the right side), their vertical pass runs once per frame across lanes, and each row
+//     hands the result to lane 0 and lane 63 with two readlanes.
 //   * The separable filter runs on packed 16-bit pairs: v_perm_b32 builds (row r, row r+1) pairs
 //     per column, v_dot2_u32_u16 applies two taps per instruction with the rounding constant as
 //     the accumulator, and v_perm_b32 extracts the 16-bit result of a byte-aligned shift. 10-bit
@@ -94,6 +99,20 @@ __device__ __forceinline__ uint32_t from_left(uint32_t v)
 __device__ __forceinline__ uint32_t from_right(uint32_t v)
 {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xf, 0xf, true);
+}
+
+// As from_left / from_right, but the lane without a source keeps `edge` (bound_ctrl off: the DPP
+// leaves that lane's old value). A select around a plain shift would let the compiler run the
+// shift with that lane masked off, and a DPP read from a masked-off lane returns 0 to its
+// neighbour.
+__device__ __forceinline__ uint32_t from_left_or(uint32_t v, uint32_t edge)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)edge, (int)v, 0x138, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ uint32_t from_right_or(uint32_t v, uint32_t edge)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)edge, (int)v, 0x130, 0xf, 0xf, false);
 }
 
 // whole-sample mirror into [0, n), exact for -2 <= i <= n + 1, clamped beyond (never used there)
@@ -323,15 +342,17 @@ struct Tile {
                                  // at 8 bits)
     int crow0;                   // scalar: first chroma row of the tile
     bool c_on;                   // lane reads chroma
-    // edges, fast path: the halo lane left of column 0 and the one right of column W-1 load the
-    // group next to the edge and permute it into the mirror image; only the first and last
-    // strips (edge_tile, scalar) run that permutation
-    bool edge_tile;
-    bool mirror_left;            // lane 0 of the leftmost strip: columns -2, -1 from 2, 1
+    // horizontal halo, transposed: lane k of each half-wave loads 8 bytes of reference luma row
+    // r0 - 2 + (k mod 32) around the tile's left (lanes 0-31) or right (lanes 32-63) edge;
+    // hsel picks the two halo columns out of them as a 16-bit pair, mirrored at a frame edge
+    uint32_t hvoff;              // byte offset of the lane's halo load in the plane
+    uint32_t hsel;               // byte permutation: (column -2, column -1) or (+256, +257)
+    // right frame edge inside the last strip (W % 256 != 0), fast path: the lane whose first
+    // column is W loads the group before it and permutes it into the mirror image
+    bool edge_tile;              // scalar: the last strip, with W inside it
     bool mirror_right;           // lane whose first column is W: columns W, W+1 from W-2, W-3
     uint32_t msel;               // 8-bit: the byte permutation doing the above (identity else)
     // edges (generic path only)
-    bool left_fix;               // lane 1 of the leftmost strip: mirror the columns left of 0
     bool right_fix;              // lane holding column W-1: mirror the columns right of it
     int right_rem;               // scalar: W % 4
     uint32_t ym0, ym1;           // luma sample masks for SSE (valid columns)
@@ -347,9 +368,11 @@ struct FrameData {
     typedef typename Px<BPC>::Luma Luma;
     static constexpr int kChromaSteps = BPC == 8 ? TH / 4 : TH / 2;
     static constexpr int kChromaStep = BPC == 8 ? 2 : 1;
+    static_assert(TH + 4 <= kWave / 2, "the transposed halo gives each tile row one lane per side");
     Luma R[TH + 4];
     Luma D[TH];
     uint32_t cu[kChromaSteps], du[kChromaSteps], cv[kChromaSteps], dv[kChromaSteps];
+    u32x2 HL;  // the lane's 8 halo bytes (see Tile::hvoff)
 };
 
 // LDS staging of one frame (one wavefront per workgroup, so the workgroup's LDS is the wave's):
@@ -361,7 +384,8 @@ struct Stage {
     static constexpr int kRef = 0;
     static constexpr int kDist = (TH + 4) * kLumaDw;
     static constexpr int kChroma = kDist + TH * kLumaDw;
-    static constexpr int kRows = kChroma + 4 * FrameData<BPC, TH>::kChromaSteps;
+    static constexpr int kHalo = kChroma + 4 * FrameData<BPC, TH>::kChromaSteps;  // two rows
+    static constexpr int kRows = kHalo + 2;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -431,6 +455,7 @@ __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, i
         fetch_luma<BPC, STAGED>(rs[0], T.luma_off, (uint32_t)row * pitch[0], F.R[k], lds,
                                 ST::kRef / ST::kLumaDw + k);
     }
+    fetch_luma<10, STAGED>(rs[0], T.hvoff, 0u, F.HL, lds, ST::kHalo / 2);
     if (!accumulate)
         return;
 #pragma unroll
@@ -471,6 +496,7 @@ __device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWav
 #pragma unroll
     for (int k = 0; k < TH + 4; ++k)
         F.R[k] = luma(ST::kRef / ST::kLumaDw + k);
+    F.HL = u32x2{lds[ST::kHalo][lane], lds[ST::kHalo + 1][lane]};
     if (!accumulate)
         return;
 #pragma unroll
@@ -485,10 +511,10 @@ __device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWav
     }
 }
 
-// Fast path, first and last strips: turn the halo lanes' loaded groups into the mirror images
-// the horizontal taps need. Left: the group of columns 0..3 becomes (-, -, x2, x1) for columns
-// -4..-1; right: the group of columns W-4..W-1 becomes (x[W-2], x[W-3], -, -) for W..W+3.
-// Columns -4, -3, W+2 and W+3 feed no output.
+// Fast path, last strip with the frame's right edge inside it: the lane whose first column is W
+// loaded the group of columns W-4..W-1; it becomes (x[W-2], x[W-3], -, -) for columns W..W+3,
+// the mirror image the horizontal taps of the lane before it need. Columns W+2 and W+3 feed no
+// output.
 template <int BPC, int TH>
 __device__ __forceinline__ void mirror_halo(const Tile &T, FrameData<BPC, TH> &F)
 {
@@ -497,11 +523,33 @@ __device__ __forceinline__ void mirror_halo(const Tile &T, FrameData<BPC, TH> &F
         if constexpr (BPC == 8) {
             F.R[k] = perm(F.R[k], F.R[k], T.msel);
         } else {
-            // (x2 | x1 << 16) from the second dword's low and the first dword's high half
+            // (x[W-2] | x[W-3] << 16) from the second dword's low and the first dword's high half
             const uint32_t m = perm(F.R[k].x, F.R[k].y, 0x07060100u);
-            F.R[k] = u32x2{T.mirror_right ? m : F.R[k].x, T.mirror_left ? m : F.R[k].y};
+            F.R[k] = u32x2{T.mirror_right ? m : F.R[k].x, F.R[k].y};
         }
     }
+}
+
+// Vertical pass of the transposed halo. Lane k holds the two halo columns of tile row k - 2 (of
+// its side) as a 16-bit pair; rows k-2 .. k+2 come from the lanes around it. Lane i + 2 returns
+// the vertical values of output row i for the left side, lane i + 34 for the right side.
+template <int BPC>
+__device__ __forceinline__ uint32_t halo_vertical(u32x2 h, uint32_t hsel)
+{
+    constexpr uint32_t kVRound = BPC == 8 ? 128u : 32768u;
+    constexpr uint32_t kVSel = BPC == 8 ? 0x06050201u : 0x07060302u;
+    uint32_t x0 = perm(h.y, h.x, hsel);
+    if constexpr (BPC == 10)
+        x0 = scale64(x0);
+    const uint32_t m1 = from_left(x0), m2 = from_left(m1);    // rows k-1, k-2
+    const uint32_t p1 = from_right(x0), p2 = from_right(p1);  // rows k+1, k+2
+    const uint32_t va = dot2u(p2 & 0xffffu, T0z,
+                              dot2u(perm(p1, x0, 0x05040100u), T21,
+                                    dot2u(perm(m1, m2, 0x05040100u), T01, kVRound)));
+    const uint32_t vb = dot2u(p2 >> 16, T0z,
+                              dot2u(perm(p1, x0, 0x07060302u), T21,
+                                    dot2u(perm(m1, m2, 0x07060302u), T01, kVRound)));
+    return perm(vb, va, kVSel);
 }
 
 // One frame of one tile from its loaded samples: blur the reference luma (vertical pass once per
@@ -526,6 +574,7 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
         if (T.edge_tile)
             mirror_halo<BPC, TH>(T, F);
     }
+    const uint32_t hv = halo_vertical<BPC>(F.HL, T.hsel);
 
     // SSE of the chroma tiles first, which frees their registers before the blur
     uint32_t su = 0, su2 = 0, sv = 0, sv2 = 0;
@@ -561,13 +610,13 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
             v[b] = dot2u(pc[b], T0z, dot2u(pb[b], T21, dot2u(pa[b], T01, kVRound)));
         uint32_t q0 = perm(v[1], v[0], kVSel);  // V of columns c, c+1
         uint32_t q1 = perm(v[3], v[2], kVSel);  // V of columns c+2, c+3
-        uint32_t ql = from_left(q1);            // V of columns c-2, c-1
+        // V of columns c-2, c-1: the lane to the left, or the left halo for lane 0
+        const uint32_t hl = (uint32_t)__builtin_amdgcn_readlane((int)hv, i + 2);
+        uint32_t ql = from_left_or(q1, hl);
         // generic path: (V(c+2), V(c+1)), the mirror image of the lane's own columns, stands for
-        // columns -2, -1 at the left frame edge and for W, W+1 at the right one when W % 4 == 0
+        // columns W, W+1 at the right frame edge when W % 4 == 0
         const uint32_t mirrored = GENERIC ? perm(q0, q1, 0x07060100u) : 0u;
         if constexpr (GENERIC) {
-            // (V(2), V(1)) stands for columns -2, -1
-            ql = T.left_fix ? mirrored : ql;
             if (T.right_rem == 1) {  // columns W, W+1 -> W-2, W-3
                 q0 = T.right_fix ? perm(ql, q0, 0x07060100u) : q0;
                 q1 = T.right_fix ? ql : q1;
@@ -577,7 +626,9 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
                 q1 = T.right_fix ? perm(q0, q1, 0x07060100u) : q1;
             }
         }
-        uint32_t qr = from_right(q0);  // V of columns c+4, c+5
+        // V of columns c+4, c+5: the lane to the right, or the right halo for lane 63
+        const uint32_t hr = (uint32_t)__builtin_amdgcn_readlane((int)hv, i + kWave / 2 + 2);
+        uint32_t qr = from_right_or(q0, hr);
         if constexpr (GENERIC) {
             if (T.right_rem == 0)
                 qr = T.right_fix ? mirrored : qr;
@@ -623,7 +674,7 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 // computed: the loads of frame t+1 write the wave's LDS stage (no registers held), issued as soon
 // as frame t has been read out of it. Frames go in pairs that swap the roles of two blurred-tile
 // register sets (prev -> alt -> prev), so no frame ends by copying its blurred tile back.
-template <int BPC, int TH, bool GENERIC, bool STAGED, int GROUP>
+template <int BPC, int TH, bool GENERIC, bool STAGED>
 __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
                                            uint32_t (&prev0)[TH], uint32_t (&prev1)[TH],
                                            uint32_t sum_prev, bool have_prev,
@@ -651,16 +702,12 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): frame t is in LDS
             read_stage<BPC, TH>(t >= f_begin, lds, T.lane, F);
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
-            if constexpr (GROUP > 1)
-                __builtin_amdgcn_s_barrier();  // siblings issue frame t+1 together
             __builtin_amdgcn_sched_barrier(0);
             if (t + 1 < f_end) {
                 FrameData<BPC, TH> G;  // unused: staged loads write LDS only
                 load_frame<BPC, TH, GENERIC, true>(a, T, t + 1, true, G, lds);
             }
         } else {
-            if constexpr (GROUP > 1)
-                __builtin_amdgcn_s_barrier();
             load_frame<BPC, TH, GENERIC, false>(a, T, t, t >= f_begin, F, lds);
         }
         compute_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F, i0, i1, o0, o1, sum_prev,
@@ -682,52 +729,46 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
     flush_sums(a, P, T.lane);
 }
 
-template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE, int GROUP>
-__global__ __launch_bounds__(kWave * GROUP) __attribute__((amdgpu_waves_per_eu(WPE))) void
+template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void
 frames_kernel(const KernelArgs a)
 {
-    __shared__ uint32_t stage[GROUP][STAGED ? Stage<BPC, TH>::kRows : 1][kWave];
+    __shared__ uint32_t stage[STAGED ? Stage<BPC, TH>::kRows : 1][kWave];
     static_assert(TH % 4 == 0, "tile height must be a multiple of 4 (two chroma rows per step)");
     constexpr int B = Px<BPC>::kBytes;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = uni(threadIdx.x / kWave);
+    const int lane = threadIdx.x;
 
     // clear the other sum buffer for the next submission
-    for (int i = blockIdx.x * (kWave * GROUP) + threadIdx.x; i < a.zero_n;
-         i += gridDim.x * (kWave * GROUP))
+    for (int i = blockIdx.x * kWave + threadIdx.x; i < a.zero_n; i += gridDim.x * kWave)
         a.zero[i] = 0ull;
 
-    // GROUP consecutive tiles (adjacent strips) per workgroup; tiles % GROUP == 0, so a
-    // workgroup never straddles two time chunks
     Tile T;
-    const int L = uni(xcd_linear(blockIdx.x, gridDim.x) * GROUP + wave);
+    const int L = uni(xcd_linear(blockIdx.x, gridDim.x));
     T.chunk = uni(L / a.tiles);
     T.tile = uni(L - T.chunk * a.tiles);
     const int rt = uni(T.tile / a.strips);
     T.strip = uni(T.tile - rt * a.strips);
-    T.r0 = uni(rt * TH);                                   // first output row of the tile
-    const int s = uni(T.strip * kLumaCols * a.lanes_out);  // first output column of the tile
+    T.r0 = uni(rt * TH);                     // first output row of the tile
+    const int s = uni(T.strip * kStripCols);  // first column of the tile
     T.lane = lane;
     const int W = a.W, H = a.H;
     T.rows_valid = uni(min(TH, H - T.r0));
 
     // lane roles; every load offset stays inside its row's pitch (a lane whose first column is
     // outside [0, W) reads column 0 and its values are never used)
-    const int c = s - kLumaCols + kLumaCols * lane;
-    T.luma_off = (c >= 0 && c < W) ? (uint32_t)(c * B)
+    const int c = s + kLumaCols * lane;
+    T.luma_off = c < W ? (uint32_t)(c * B)
                  : (!GENERIC && c == W) ? (uint32_t)((W - kLumaCols) * B)
                                         : 0u;
-    T.out_lane = lane >= 1 && lane <= a.lanes_out && c < W;
-    T.w0 = T.out_lane ? ((c < W ? 1u : 0u) | (c + 1 < W ? 0x10000u : 0u)) : 0u;
-    T.w1 = T.out_lane ? ((c + 2 < W ? 1u : 0u) | (c + 3 < W ? 0x10000u : 0u)) : 0u;
-    T.left_fix = T.strip == 0 && lane == 1;
-    T.edge_tile = T.strip == 0 || T.strip == a.strips - 1;
-    T.mirror_left = T.strip == 0 && lane == 0;
+    T.out_lane = c < W;
+    T.w0 = (c < W ? 1u : 0u) | (c + 1 < W ? 0x10000u : 0u);
+    T.w1 = (c + 2 < W ? 1u : 0u) | (c + 3 < W ? 0x10000u : 0u);
+    T.edge_tile = T.strip == a.strips - 1 && W % kStripCols != 0;
     T.mirror_right = c == W;
-    T.msel = T.mirror_left ? 0x01020000u : T.mirror_right ? 0x00000102u : 0x03020100u;
+    T.msel = T.mirror_right ? 0x00000102u : 0x03020100u;
     T.right_rem = W & 3;
     // the lane holding column W-1 (on the fast path W % 4 == 0, so its columns end at W-1)
-    T.right_fix = c <= W - 1 && W - 1 < c + kLumaCols && lane >= 1 && lane <= a.lanes_out;
+    T.right_fix = c <= W - 1 && W - 1 < c + kLumaCols;
     if constexpr (BPC == 8) {
         T.ym0 = (c < W ? 0xffu : 0u) | (c + 1 < W ? 0xff00u : 0u) | (c + 2 < W ? 0xff0000u : 0u) |
                 (c + 3 < W ? 0xff000000u : 0u);
@@ -737,20 +778,54 @@ frames_kernel(const KernelArgs a)
         T.ym1 = (c + 2 < W ? 0xffffu : 0u) | (c + 3 < W ? 0xffff0000u : 0u);
     }
 
-    // chroma split: 8-bit, 32 lanes per chroma row with lanes_out / 2 dwords used and two rows per
-    // step (the upper half-wave takes the second); 10-bit, one row per step, lanes_out dwords
+    // transposed horizontal halo: 8 bytes of row r0 - 2 + k per lane, inside the row's pitch.
+    // Selectors give (column a, column b) as a 16-bit pair: 8-bit picks bytes (0x0c = zero),
+    // 10-bit picks 16-bit samples.
+    {
+        const int k = min(lane & (kWave / 2 - 1), TH + 3);
+        const int hrow = mirror_clamp(T.r0 - 2 + k, H);
+        const int e = s + kStripCols;  // first column right of the tile
+        int col;
+        uint32_t sel;
+        if (lane < kWave / 2) {
+            if (T.strip == 0) {  // columns -2, -1 mirror 2, 1
+                col = 0;
+                sel = BPC == 8 ? 0x0c010c02u : 0x03020504u;
+            } else {  // columns s-2, s-1
+                col = s - 4;
+                sel = BPC == 8 ? 0x0c030c02u : 0x07060504u;
+            }
+        } else if (e < W - 1) {  // columns e, e+1
+            col = BPC == 8 ? e - 4 : e;
+            sel = BPC == 8 ? 0x0c050c04u : 0x03020100u;
+        } else if (e == W - 1) {  // column e, then e+1 = W mirrors W-2 = e-1
+            col = BPC == 8 ? e - 4 : e - 2;
+            sel = BPC == 8 ? 0x0c030c04u : 0x03020504u;
+        } else if (e == W) {  // columns W, W+1 mirror W-2, W-3
+            col = BPC == 8 ? W - 8 : W - 4;
+            sel = BPC == 8 ? 0x0c050c06u : 0x03020504u;
+        } else {  // the frame ends inside the tile: unused
+            col = 0;
+            sel = 0u;
+        }
+        T.hvoff = (uint32_t)(col * B) + (uint32_t)hrow * (uint32_t)a.pitch[0];
+        T.hsel = sel;
+    }
+
+    // chroma split: 8-bit, 32 lanes (one dword each) per chroma row and two rows per step (the
+    // upper half-wave takes the second); 10-bit, one row per step, 64 dwords
     const int cs = s / 2;  // first chroma sample of the tile
     int ccol;
     if constexpr (BPC == 8) {
         ccol = cs + 4 * (lane & 31);
         T.c_upper = lane >= 32;
-        T.c_on = (lane & 31) < a.lanes_out / 2 && ccol < a.Wc;
+        T.c_on = ccol < a.Wc;
         T.cm = (ccol < a.Wc ? 0xffu : 0u) | (ccol + 1 < a.Wc ? 0xff00u : 0u) |
                (ccol + 2 < a.Wc ? 0xff0000u : 0u) | (ccol + 3 < a.Wc ? 0xff000000u : 0u);
     } else {
         ccol = cs + 2 * lane;
         T.c_upper = false;
-        T.c_on = lane < a.lanes_out && ccol < a.Wc;
+        T.c_on = ccol < a.Wc;
         T.cm = (ccol < a.Wc ? 0xffffu : 0u) | (ccol + 1 < a.Wc ? 0xffff0000u : 0u);
     }
     T.crow0 = uni(T.r0 / 2);
@@ -785,8 +860,7 @@ frames_kernel(const KernelArgs a)
     }
 
     // every tile of a launch takes the same path, so wavefronts cost the same and none trails
-    frame_loop<BPC, TH, GENERIC, STAGED, GROUP>(a, T, prev0, prev1, sum_prev, have_prev,
-                                                stage[wave]);
+    frame_loop<BPC, TH, GENERIC, STAGED>(a, T, prev0, prev1, sum_prev, have_prev, stage);
 
     if (T.chunk == a.chunks - 1) {
         uint2 *rout = reinterpret_cast<uint2 *>(a.ring_out);
@@ -798,7 +872,7 @@ frames_kernel(const KernelArgs a)
 
 // Tiled blurred state -> W x H uint16 plane.
 __global__ void export_kernel(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
-                              int lanes_out, int strips, int th)
+                              int strips, int th)
 {
     const int pairs = (W + 1) / 2;
     const int64_t n = (int64_t)pairs * H;
@@ -806,10 +880,9 @@ __global__ void export_kernel(const uint32_t *ring, uint16_t *dst, int64_t pitch
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int row = (int)(idx / pairs);
         const int j = 2 * (int)(idx - (int64_t)row * pairs);
-        const int sw = kLumaCols * lanes_out;
-        const int strip = j / sw;
-        const int in = j - strip * sw;
-        const int lane = in / kLumaCols + 1;
+        const int strip = j / kStripCols;
+        const int in = j - strip * kStripCols;
+        const int lane = in / kLumaCols;
         const int half = (in % kLumaCols) / 2;
         const int tile = (row / th) * strips + strip;
         const uint32_t w = ring[(((int64_t)tile * th + row % th) * kWave + lane) * 2 + half];
@@ -871,54 +944,34 @@ typedef void (*FramesFn)(KernelArgs);
 
 // Every (bit depth, tile height, path) the host may pick. The fast path needs W % 8 == 0 and
 // H % TH == 0 (no ragged tile, no partial sample group); the generic path takes any size.
-template <int BPC, bool GENERIC, int GROUP>
+template <int BPC, bool GENERIC>
 FramesFn frames_fn(int th)
 {
     constexpr bool P = BPC == 8 ? IIR_STAGE8 : IIR_STAGE10;
     switch (th) {
     case 12:
-        return frames_kernel<BPC, 12, P, GENERIC, IIR_WPE12, GROUP>;
+        return frames_kernel<BPC, 12, P, GENERIC, IIR_WPE12>;
     case 16:
-        return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16, GROUP>;
+        return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16>;
     case 20:
-        return frames_kernel<BPC, 20, P, GENERIC, IIR_WPE20, GROUP>;
+        return frames_kernel<BPC, 20, P, GENERIC, IIR_WPE20>;
     default:
         return nullptr;
     }
 }
 
-template <int BPC, bool GENERIC>
-FramesFn frames_fn_group(int th, int group)
-{
-    switch (group) {
-    case 1:
-        return frames_fn<BPC, GENERIC, 1>(th);
-    case 2:
-        return frames_fn<BPC, GENERIC, 2>(th);
-    case 4:
-        return frames_fn<BPC, GENERIC, 4>(th);
-    default:
-        return nullptr;
-    }
-}
-
-FramesFn pick(int bpc, int th, bool generic, int group)
+FramesFn pick(int bpc, int th, bool generic)
 {
     if (bpc == 8)
-        return generic ? frames_fn_group<8, true>(th, group) : frames_fn_group<8, false>(th, group);
-    return generic ? frames_fn_group<10, true>(th, group) : frames_fn_group<10, false>(th, group);
+        return generic ? frames_fn<8, true>(th) : frames_fn<8, false>(th);
+    return generic ? frames_fn<10, true>(th) : frames_fn<10, false>(th);
 }
 
 }  // namespace
 
 bool supported_rows_per_tile(int th)
 {
-    return pick(8, th, true, 1) != nullptr;
-}
-
-bool supported_group(int group)
-{
-    return pick(8, 16, true, group) != nullptr;
+    return pick(8, th, true) != nullptr;
 }
 
 bool fast_path_ok(int W, int H, int th)
@@ -926,36 +979,34 @@ bool fast_path_ok(int W, int H, int th)
     return W % 8 == 0 && H % th == 0;
 }
 
-hipError_t frames_occupancy(int bpc, int th, bool generic, int group, int *waves_per_cu)
+hipError_t frames_occupancy(int bpc, int th, bool generic, int *waves_per_cu)
 {
-    FramesFn f = pick(bpc, th, generic, group);
+    FramesFn f = pick(bpc, th, generic);
     if (!f)
         return hipErrorInvalidValue;
     int blocks = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &blocks, reinterpret_cast<const void *>(f), kWave * group, 0);
-    *waves_per_cu = blocks * group;
+        &blocks, reinterpret_cast<const void *>(f), kWave, 0);
+    *waves_per_cu = blocks;
     return e;
 }
 
-hipError_t launch_frames(int bpc, int th, bool generic, int group, const KernelArgs &a,
-                         hipStream_t stream)
+hipError_t launch_frames(int bpc, int th, bool generic, const KernelArgs &a, hipStream_t stream)
 {
-    FramesFn f = pick(bpc, th, generic, group);
-    if (!f || group < 1 || a.tiles % group != 0)
+    FramesFn f = pick(bpc, th, generic);
+    if (!f)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(f, dim3((unsigned)(a.tiles / group * a.chunks)), dim3(kWave * group), 0,
-                       stream, a);
+    hipLaunchKernelGGL(f, dim3((unsigned)(a.tiles * a.chunks)), dim3(kWave), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
-                         int lanes_out, int strips, int th, hipStream_t stream)
+                         int strips, int th, hipStream_t stream)
 {
     const int64_t n = (int64_t)((W + 1) / 2) * H;
     const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 65536);
     hipLaunchKernelGGL(export_kernel, dim3(blocks), dim3(256), 0, stream, ring, dst, pitch, W, H,
-                       lanes_out, strips, th);
+                       strips, th);
     return hipGetLastError();
 }
 

@@ -46,7 +46,8 @@ def _check(clip, sums, hm, want, want_hm, what):
 
 
 TINY = [(3, 3), (4, 7), (9, 5), (17, 23), (5, 64), (64, 5), (70, 3), (33, 18), (131, 17),
-        (250, 40), (255, 33), (258, 35), (500, 17), (1283, 723)]
+        (250, 40), (255, 33), (256, 5), (257, 9), (258, 35), (259, 6), (260, 4), (500, 17),
+        (513, 7), (1283, 723)]
 
 
 @pytest.mark.parametrize("bpc", [8, 10])
@@ -65,7 +66,10 @@ def test_tiny_sweep(w, h, bpc):
             assert np.array_equal(_blur_np(ctx), last), f"blurred plane {kind} {w}x{h} {bpc}"
 
 
-PATH_SIZES = [(504, 36), (1000, 80), (248, 60), (8, 12), (64, 240)]
+# 256-column strips: right frame edge at a strip boundary (512, 768), inside the last strip
+# (504, 1000, 248, 8, 64), one column past a boundary (257, 513), ragged rows (512x50)
+PATH_SIZES = [(504, 36), (1000, 80), (248, 60), (8, 12), (64, 240), (512, 48), (768, 60),
+              (257, 40), (513, 24), (512, 50)]
 
 
 @pytest.mark.parametrize("bpc", [8, 10])

@@ -375,17 +375,34 @@ struct FrameData {
     u32x2 HL;  // the lane's 8 halo bytes (see Tile::hvoff)
 };
 
-// LDS staging of one frame (one wavefront per workgroup, so the workgroup's LDS is the wave's):
-// each row is one dword per lane (256 bytes), filled by buffer loads that write LDS directly
-// (no VGPRs held while the load is in flight). 10-bit luma rows take two dword rows.
-template <int BPC, int TH>
+// LDS staging of one 8-bit frame (one wavefront per workgroup, so the workgroup's LDS is the
+// wave's), in rows of 256 bytes (one dword per lane). Loads write LDS directly, 16 bytes per
+// lane, so one instruction moves 1 KB: four luma rows of the tile (16 lanes per row) or eight
+// chroma rows (8 lanes per row). A chroma LDS row holds two chroma rows, the second for the
+// upper half-wave, which is the order the chroma SSE steps read them in.
+template <int TH>
 struct Stage {
-    static constexpr int kLumaDw = BPC == 8 ? 1 : 2;
+    static constexpr int kRefLoads = (TH + 4) / 4;    // 16-byte loads of reference luma
+    static constexpr int kDistLoads = TH / 4;         // of distorted luma
+    static constexpr int kChromaLoads = (TH + 15) / 16;  // per chroma plane (8 rows each)
+    static constexpr int kChromaRows = 4 * kChromaLoads;  // LDS rows per chroma plane
     static constexpr int kRef = 0;
-    static constexpr int kDist = (TH + 4) * kLumaDw;
-    static constexpr int kChroma = kDist + TH * kLumaDw;
-    static constexpr int kHalo = kChroma + 4 * FrameData<BPC, TH>::kChromaSteps;  // two rows
+    static constexpr int kDist = TH + 4;
+    static constexpr int kChroma = kDist + TH;      // planes ref U, dist U, ref V, dist V
+    static constexpr int kHalo = kChroma + 4 * kChromaRows;  // two rows
     static constexpr int kRows = kHalo + 2;
+    static_assert(TH % 4 == 0, "whole 16-byte luma loads");
+};
+
+// Per-lane byte offsets of a tile's staged loads, fixed for the whole launch: one per reference
+// luma load (rows mirrored at the frame's top and bottom edges), the distorted luma's and the
+// four chroma planes' (their rows advance through the scalar offset). Rows past the bottom of a
+// plane fall outside its buffer range and read as zero; they are never counted.
+template <int TH>
+struct StageOffsets {
+    uint32_t ref[Stage<TH>::kRefLoads];
+    uint32_t dist;
+    uint32_t chroma[4];
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -429,17 +446,16 @@ __device__ __forceinline__ void fetch_luma(Rsrc r, uint32_t voff, uint32_t soff,
     }
 }
 
-// Issue every load of frame t for this tile, into registers or into the LDS stage (the distorted
-// planes and chroma only when the frame is accumulated; a chunk's prologue frame is only blurred).
-template <int BPC, int TH, bool GENERIC, bool STAGED>
+// Issue every load of frame t for this tile into registers (the distorted planes and chroma only
+// when the frame is accumulated; a chunk's prologue frame is only blurred).
+template <int BPC, int TH, bool GENERIC>
 __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, int t,
-                                           bool accumulate, FrameData<BPC, TH> &F,
-                                           uint32_t (*stage)[kWave])
+                                           bool accumulate, FrameData<BPC, TH> &F)
 {
     typedef FrameData<BPC, TH> FD;
-    typedef Stage<BPC, TH> ST;
+    constexpr bool STAGED = false;
     const int H = a.H;
-    const uint32_t lds = STAGED ? opaque(lds_addr(stage)) : 0u;
+    const uint32_t lds = 0u;
     Rsrc rs[6];
     uint32_t pitch[6];
 #pragma unroll
@@ -452,18 +468,16 @@ __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, i
         // only the two rows above and below the tile can fall outside the frame on the fast path
         const int row = (GENERIC || k < 2 || k >= TH + 2) ? mirror_clamp(T.r0 - 2 + k, H)
                                                           : T.r0 - 2 + k;
-        fetch_luma<BPC, STAGED>(rs[0], T.luma_off, (uint32_t)row * pitch[0], F.R[k], lds,
-                                ST::kRef / ST::kLumaDw + k);
+        fetch_luma<BPC, STAGED>(rs[0], T.luma_off, (uint32_t)row * pitch[0], F.R[k], lds, 0);
     }
-    fetch_luma<10, STAGED>(rs[0], T.hvoff, 0u, F.HL, lds, ST::kHalo / 2);
+    fetch_luma<10, STAGED>(rs[0], T.hvoff, 0u, F.HL, lds, 0);
     if (!accumulate)
         return;
 #pragma unroll
     for (int i = 0; i < TH; ++i) {
         // rows past the frame re-read the last row; they are not counted
         const int row = GENERIC ? min(T.r0 + i, H - 1) : T.r0 + i;
-        fetch_luma<BPC, STAGED>(rs[3], T.luma_off, (uint32_t)row * pitch[3], F.D[i], lds,
-                                ST::kDist / ST::kLumaDw + i);
+        fetch_luma<BPC, STAGED>(rs[3], T.luma_off, (uint32_t)row * pitch[3], F.D[i], lds, 0);
     }
 #pragma unroll
     for (int k = 0; k < FD::kChromaSteps; ++k) {
@@ -472,7 +486,7 @@ __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, i
         const int row = T.crow0 + FD::kChromaStep * k;
         const int rl = GENERIC ? min(row, a.Hc - 1) : row;
         const bool back = GENERIC && T.c_upper && row + 1 >= a.Hc;
-        const int lr = ST::kChroma + 4 * k;
+        const int lr = 0;
         fetch32<STAGED>(rs[1], T.coff[0] - (back ? pitch[1] : 0u), (uint32_t)rl * pitch[1], F.cu[k], lds, lr);
         fetch32<STAGED>(rs[4], T.coff[1] - (back ? pitch[4] : 0u), (uint32_t)rl * pitch[4], F.du[k], lds, lr + 1);
         fetch32<STAGED>(rs[2], T.coff[2] - (back ? pitch[2] : 0u), (uint32_t)rl * pitch[2], F.cv[k], lds, lr + 2);
@@ -480,34 +494,68 @@ __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, i
     }
 }
 
-// The staged frame, from LDS into registers.
-template <int BPC, int TH>
-__device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWave], int lane,
-                                           FrameData<BPC, TH> &F)
+// Issue every load of 8-bit frame t for this tile into the wavefront's LDS stage: 16 bytes per
+// lane per instruction, the reference luma and its halo always, the distorted luma and chroma
+// when the frame is accumulated.
+template <int TH>
+__device__ __forceinline__ void load_frame_staged(const KernelArgs &a, const Tile &T,
+                                                  const StageOffsets<TH> &O, int t,
+                                                  bool accumulate, uint32_t (*stage)[kWave])
 {
-    typedef FrameData<BPC, TH> FD;
-    typedef Stage<BPC, TH> ST;
-    auto luma = [&](int row) {
-        if constexpr (BPC == 8)
-            return lds[row][lane];
-        else
-            return u32x2{lds[2 * row][lane], lds[2 * row + 1][lane]};
+    typedef Stage<TH> ST;
+    const uint32_t lds = opaque(lds_addr(stage));
+    auto dma16 = [&](Rsrc r, int lds_row0, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, lds_row0), 16, voff, soff, 0, 0);
     };
+    const Rsrc ry = plane_rsrc(frame_plane(a, t, 0), a.span[0]);
+#pragma unroll
+    for (int q = 0; q < ST::kRefLoads; ++q)
+        dma16(ry, ST::kRef + 4 * q, O.ref[q], 0u);
+    // transposed halo: two 4-byte loads per lane (lane k of each half-wave: tile row k - 2)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, lds_row(lds, ST::kHalo), 4, T.hvoff, 0u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, lds_row(lds, ST::kHalo + 1), 4, T.hvoff + 4u, 0u,
+                                             0, 0);
+    if (!accumulate)
+        return;
+    const Rsrc rd = plane_rsrc(frame_plane(a, t, 3), a.span[3]);
+    const uint32_t pd = opaque((uint32_t)a.pitch[3]);
+#pragma unroll
+    for (int q = 0; q < ST::kDistLoads; ++q)
+        dma16(rd, ST::kDist + 4 * q, O.dist, (uint32_t)(T.r0 + 4 * q) * pd);
+    constexpr int pk[4] = {1, 4, 2, 5};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const Rsrc rc = plane_rsrc(frame_plane(a, t, pk[p]), a.span[pk[p]]);
+        const uint32_t pc = opaque((uint32_t)a.pitch[pk[p]]);
+#pragma unroll
+        for (int q = 0; q < ST::kChromaLoads; ++q)
+            dma16(rc, ST::kChroma + p * ST::kChromaRows + 4 * q, O.chroma[p],
+                  (uint32_t)(T.crow0 + 8 * q) * pc);
+    }
+}
+
+// The staged 8-bit frame, from LDS into registers.
+template <int TH>
+__device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWave], int lane,
+                                           FrameData<8, TH> &F)
+{
+    typedef FrameData<8, TH> FD;
+    typedef Stage<TH> ST;
 #pragma unroll
     for (int k = 0; k < TH + 4; ++k)
-        F.R[k] = luma(ST::kRef / ST::kLumaDw + k);
+        F.R[k] = lds[ST::kRef + k][lane];
     F.HL = u32x2{lds[ST::kHalo][lane], lds[ST::kHalo + 1][lane]};
     if (!accumulate)
         return;
 #pragma unroll
     for (int i = 0; i < TH; ++i)
-        F.D[i] = luma(ST::kDist / ST::kLumaDw + i);
+        F.D[i] = lds[ST::kDist + i][lane];
 #pragma unroll
     for (int k = 0; k < FD::kChromaSteps; ++k) {
-        F.cu[k] = lds[ST::kChroma + 4 * k][lane];
-        F.du[k] = lds[ST::kChroma + 4 * k + 1][lane];
-        F.cv[k] = lds[ST::kChroma + 4 * k + 2][lane];
-        F.dv[k] = lds[ST::kChroma + 4 * k + 3][lane];
+        F.cu[k] = lds[ST::kChroma + k][lane];
+        F.du[k] = lds[ST::kChroma + ST::kChromaRows + k][lane];
+        F.cv[k] = lds[ST::kChroma + 2 * ST::kChromaRows + k][lane];
+        F.dv[k] = lds[ST::kChroma + 3 * ST::kChromaRows + k][lane];
     }
 }
 
@@ -515,12 +563,16 @@ __device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWav
 // loaded the group of columns W-4..W-1; it becomes (x[W-2], x[W-3], -, -) for columns W..W+3,
 // the mirror image the horizontal taps of the lane before it need. Columns W+2 and W+3 feed no
 // output.
-template <int BPC, int TH>
+template <int BPC, int TH, bool STAGED>
 __device__ __forceinline__ void mirror_halo(const Tile &T, FrameData<BPC, TH> &F)
 {
 #pragma unroll
     for (int k = 0; k < TH + 4; ++k) {
-        if constexpr (BPC == 8) {
+        if constexpr (STAGED) {
+            // staged rows hold the lane's own columns W..W+3; the group W-4..W-1 comes from the
+            // lane to the left (every lane runs the shift; only the edge lane's selector uses it)
+            F.R[k] = perm(from_left(F.R[k]), F.R[k], T.msel);
+        } else if constexpr (BPC == 8) {
             F.R[k] = perm(F.R[k], F.R[k], T.msel);
         } else {
             // (x[W-2] | x[W-3] << 16) from the second dword's low and the first dword's high half
@@ -557,7 +609,7 @@ __device__ __forceinline__ uint32_t halo_vertical(u32x2 h, uint32_t hsel)
 // held in registers, SSE of the luma and chroma tiles, one wavefront reduction and one atomic per
 // sum. GENERIC adds the frame-edge mirror fix-ups, ragged rows and masked tails; interior tiles
 // (the vast majority) run without any of it.
-template <int BPC, int TH, bool GENERIC>
+template <int BPC, int TH, bool GENERIC, bool ROWSTAGE>
 __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T, int t,
                                               bool accumulate, FrameData<BPC, TH> &F,
                                               const uint32_t (&prev0)[TH],
@@ -572,7 +624,7 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 
     if constexpr (!GENERIC) {
         if (T.edge_tile)
-            mirror_halo<BPC, TH>(T, F);
+            mirror_halo<BPC, TH, ROWSTAGE>(T, F);
     }
     const uint32_t hv = halo_vertical<BPC>(F.HL, T.hsel);
 
@@ -676,9 +728,9 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 // register sets (prev -> alt -> prev), so no frame ends by copying its blurred tile back.
 template <int BPC, int TH, bool GENERIC, bool STAGED>
 __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
-                                           uint32_t (&prev0)[TH], uint32_t (&prev1)[TH],
-                                           uint32_t sum_prev, bool have_prev,
-                                           uint32_t (*lds)[kWave])
+                                           const StageOffsets<TH> &O, uint32_t (&prev0)[TH],
+                                           uint32_t (&prev1)[TH], uint32_t sum_prev,
+                                           bool have_prev, uint32_t (*lds)[kWave])
 {
     const int f_begin = uni(T.chunk * a.chunk_len);
     const int f_end = uni(min(f_begin + a.chunk_len, a.nframes));
@@ -689,29 +741,29 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
         P.v[k] = 0;
     P.first = f_begin;
     P.count = 0;
-    if constexpr (STAGED) {
-        FrameData<BPC, TH> F;  // unused: staged loads write LDS only
-        load_frame<BPC, TH, GENERIC, true>(a, T, t0, t0 >= f_begin, F, lds);
-    }
+    if constexpr (STAGED)
+        load_frame_staged<TH>(a, T, O, t0, t0 >= f_begin, lds);
     // one frame: blurred tile in (i0, i1), out to (o0, o1)
     auto step = [&](int t, const uint32_t(&i0)[TH], const uint32_t(&i1)[TH], uint32_t(&o0)[TH],
                     uint32_t(&o1)[TH]) {
         // a fresh frame per step: no sample register is carried from one frame to the next
         FrameData<BPC, TH> F;
         if constexpr (STAGED) {
+            // raised priority from the wait to the last load issued: a wavefront whose frame has
+            // landed reads it out and refills the memory pipe ahead of its SIMD's computing waves
+            __builtin_amdgcn_s_setprio(3);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): frame t is in LDS
-            read_stage<BPC, TH>(t >= f_begin, lds, T.lane, F);
+            read_stage<TH>(t >= f_begin, lds, T.lane, F);
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
             __builtin_amdgcn_sched_barrier(0);
-            if (t + 1 < f_end) {
-                FrameData<BPC, TH> G;  // unused: staged loads write LDS only
-                load_frame<BPC, TH, GENERIC, true>(a, T, t + 1, true, G, lds);
-            }
+            if (t + 1 < f_end)
+                load_frame_staged<TH>(a, T, O, t + 1, true, lds);
+            __builtin_amdgcn_s_setprio(0);
         } else {
-            load_frame<BPC, TH, GENERIC, false>(a, T, t, t >= f_begin, F, lds);
+            load_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F);
         }
-        compute_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F, i0, i1, o0, o1, sum_prev,
-                                        have_prev, P);
+        compute_frame<BPC, TH, GENERIC, STAGED>(a, T, t, t >= f_begin, F, i0, i1, o0, o1,
+                                                sum_prev, have_prev, P);
     };
     uint32_t alt0[TH], alt1[TH];
     for (int t = t0; t < f_end; t += 2) {
@@ -733,8 +785,9 @@ template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void
 frames_kernel(const KernelArgs a)
 {
-    __shared__ uint32_t stage[STAGED ? Stage<BPC, TH>::kRows : 1][kWave];
+    __shared__ uint32_t stage[STAGED ? Stage<TH>::kRows : 1][kWave];
     static_assert(TH % 4 == 0, "tile height must be a multiple of 4 (two chroma rows per step)");
+    static_assert(!STAGED || BPC == 8, "LDS staging is laid out for 8-bit samples");
     constexpr int B = Px<BPC>::kBytes;
     const int lane = threadIdx.x;
 
@@ -765,7 +818,9 @@ frames_kernel(const KernelArgs a)
     T.w1 = (c + 2 < W ? 1u : 0u) | (c + 3 < W ? 0x10000u : 0u);
     T.edge_tile = T.strip == a.strips - 1 && W % kStripCols != 0;
     T.mirror_right = c == W;
-    T.msel = T.mirror_right ? 0x00000102u : 0x03020100u;
+    // byte permutation building columns W, W+1 from W-2, W-3: staged, from the left neighbour's
+    // group (the perm's high operand); else from the lane's own reload of W-4..W-1
+    T.msel = T.mirror_right ? (STAGED ? 0x04040506u : 0x00000102u) : 0x03020100u;
     T.right_rem = W & 3;
     // the lane holding column W-1 (on the fast path W % 4 == 0, so its columns end at W-1)
     T.right_fix = c <= W - 1 && W - 1 < c + kLumaCols;
@@ -860,7 +915,23 @@ frames_kernel(const KernelArgs a)
     }
 
     // every tile of a launch takes the same path, so wavefronts cost the same and none trails
-    frame_loop<BPC, TH, GENERIC, STAGED>(a, T, prev0, prev1, sum_prev, have_prev, stage);
+    // staged: per-lane offsets of the 16-byte loads (16 lanes per luma row, 8 per chroma row)
+    StageOffsets<TH> O;
+    if constexpr (STAGED) {
+#pragma unroll
+        for (int q = 0; q < Stage<TH>::kRefLoads; ++q) {
+            const int row = mirror_clamp(T.r0 - 2 + 4 * q + (lane >> 4), H);
+            O.ref[q] = (uint32_t)(s + 16 * (lane & 15)) + (uint32_t)row * (uint32_t)a.pitch[0];
+        }
+        O.dist = (uint32_t)(s + 16 * (lane & 15)) + (uint32_t)(lane >> 4) * (uint32_t)a.pitch[3];
+        const int pk[4] = {1, 4, 2, 5};
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            O.chroma[p] = (uint32_t)(s / 2 + 16 * (lane & 7)) +
+                          (uint32_t)(lane >> 3) * (uint32_t)a.pitch[pk[p]];
+    }
+
+    frame_loop<BPC, TH, GENERIC, STAGED>(a, T, O, prev0, prev1, sum_prev, have_prev, stage);
 
     if (T.chunk == a.chunks - 1) {
         uint2 *rout = reinterpret_cast<uint2 *>(a.ring_out);

@@ -342,11 +342,15 @@ struct Tile {
                                  // at 8 bits)
     int crow0;                   // scalar: first chroma row of the tile
     bool c_on;                   // lane reads chroma
-    // horizontal halo, transposed: lane k of each half-wave loads 8 bytes of reference luma row
+    // horizontal halo, transposed: lane k of each half-wave loads bytes of reference luma row
     // r0 - 2 + (k mod 32) around the tile's left (lanes 0-31) or right (lanes 32-63) edge;
-    // hsel picks the two halo columns out of them as a 16-bit pair, mirrored at a frame edge
+    // hsel picks the two halo columns out of a dword of them as a 16-bit pair, mirrored at a
+    // frame edge. Registers: 8 bytes at hvoff. Staged: the aligned 16 bytes at hvoff go to LDS
+    // and the dword hlds (LDS dword index) is read back.
     uint32_t hvoff;              // byte offset of the lane's halo load in the plane
     uint32_t hsel;               // byte permutation: (column -2, column -1) or (+256, +257)
+    uint32_t hlds;               // staged: LDS dword index of the lane's halo dword
+    bool halo_fix;               // staged, generic: lane 63 when column e+1 = W mirrors e-1
     // right frame edge inside the last strip (W % 256 != 0), fast path: the lane whose first
     // column is W loads the group before it and permutes it into the mirror image
     bool edge_tile;              // scalar: the last strip, with W inside it
@@ -389,8 +393,8 @@ struct Stage {
     static constexpr int kRef = 0;
     static constexpr int kDist = TH + 4;
     static constexpr int kChroma = kDist + TH;      // planes ref U, dist U, ref V, dist V
-    static constexpr int kHalo = kChroma + 4 * kChromaRows;  // two rows
-    static constexpr int kRows = kHalo + 2;
+    static constexpr int kHalo = kChroma + 4 * kChromaRows;  // four rows: 16 bytes per lane
+    static constexpr int kRows = kHalo + 4;
     static_assert(TH % 4 == 0, "whole 16-byte luma loads");
 };
 
@@ -511,10 +515,8 @@ __device__ __forceinline__ void load_frame_staged(const KernelArgs &a, const Til
 #pragma unroll
     for (int q = 0; q < ST::kRefLoads; ++q)
         dma16(ry, ST::kRef + 4 * q, O.ref[q], 0u);
-    // transposed halo: two 4-byte loads per lane (lane k of each half-wave: tile row k - 2)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, lds_row(lds, ST::kHalo), 4, T.hvoff, 0u, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, lds_row(lds, ST::kHalo + 1), 4, T.hvoff + 4u, 0u,
-                                             0, 0);
+    // transposed halo: one aligned 16-byte load per lane (lane k of each half-wave: tile row k-2)
+    dma16(ry, ST::kHalo, T.hvoff, 0u);
     if (!accumulate)
         return;
     const Rsrc rd = plane_rsrc(frame_plane(a, t, 3), a.span[3]);
@@ -537,14 +539,14 @@ __device__ __forceinline__ void load_frame_staged(const KernelArgs &a, const Til
 // The staged 8-bit frame, from LDS into registers.
 template <int TH>
 __device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWave], int lane,
-                                           FrameData<8, TH> &F)
+                                           uint32_t hlds, FrameData<8, TH> &F)
 {
     typedef FrameData<8, TH> FD;
     typedef Stage<TH> ST;
 #pragma unroll
     for (int k = 0; k < TH + 4; ++k)
         F.R[k] = lds[ST::kRef + k][lane];
-    F.HL = u32x2{lds[ST::kHalo][lane], lds[ST::kHalo + 1][lane]};
+    F.HL = u32x2{(&lds[0][0])[hlds], 0u};
     if (!accumulate)
         return;
 #pragma unroll
@@ -681,6 +683,8 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
         // V of columns c+4, c+5: the lane to the right, or the right halo for lane 63
         const uint32_t hr = (uint32_t)__builtin_amdgcn_readlane((int)hv, i + kWave / 2 + 2);
         uint32_t qr = from_right_or(q0, hr);
+        if constexpr (GENERIC && ROWSTAGE)
+            qr = T.halo_fix ? perm(q1, qr, 0x07060100u) : qr;  // (V(e), V(e-1))
         if constexpr (GENERIC) {
             if (T.right_rem == 0)
                 qr = T.right_fix ? mirrored : qr;
@@ -753,7 +757,7 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
             // landed reads it out and refills the memory pipe ahead of its SIMD's computing waves
             __builtin_amdgcn_s_setprio(3);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): frame t is in LDS
-            read_stage<TH>(t >= f_begin, lds, T.lane, F);
+            read_stage<TH>(t >= f_begin, lds, T.lane, T.hlds, F);
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
             __builtin_amdgcn_sched_barrier(0);
             if (t + 1 < f_end)
@@ -865,6 +869,35 @@ frames_kernel(const KernelArgs a)
         }
         T.hvoff = (uint32_t)(col * B) + (uint32_t)hrow * (uint32_t)a.pitch[0];
         T.hsel = sel;
+        T.hlds = 0u;
+        T.halo_fix = false;
+        if constexpr (STAGED) {
+            // 16-byte aligned chunks: left, the chunk ending at s (its last dword holds columns
+            // s-4..s-1) or at the frame edge the first chunk (columns 0..3); right, the chunk
+            // starting at e, or the one ending at W when the frame ends at e
+            int chunk, dw;
+            if (lane < kWave / 2) {
+                chunk = T.strip == 0 ? 0 : s - 16;
+                dw = T.strip == 0 ? 0 : 3;
+                sel = T.strip == 0 ? 0x0c010c02u : 0x0c030c02u;
+            } else if (e < W) {
+                chunk = e;
+                dw = 0;
+                sel = 0x0c010c00u;  // columns e, e+1 (e+1 = W is fixed up by halo_fix)
+            } else if (e == W) {
+                chunk = W - 16;
+                dw = 3;
+                sel = 0x0c010c02u;
+            } else {
+                chunk = 0;
+                dw = 0;
+                sel = 0u;
+            }
+            T.hvoff = (uint32_t)chunk + (uint32_t)hrow * (uint32_t)a.pitch[0];
+            T.hsel = sel;
+            T.hlds = (uint32_t)(Stage<TH>::kHalo * kWave + 4 * lane + dw);
+            T.halo_fix = lane == kWave - 1 && e == W - 1;
+        }
     }
 
     // chroma split: 8-bit, 32 lanes (one dword each) per chroma row and two rows per step (the

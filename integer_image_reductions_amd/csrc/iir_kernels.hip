@@ -223,18 +223,27 @@ __device__ __forceinline__ Rsrc plane_rsrc(const uint8_t *p, uint32_t bytes)
                                              0x00020000);
 }
 
+// Cache policy of a load (the buffer instructions' cache-policy operand): kKeep allocates in L2
+// normally; kStream sets the non-temporal bit, so the line is among the first L2 evicts. Samples
+// only this wavefront reads (distorted luma, chroma) stream; reference luma rows, which the
+// vertically and horizontally neighbouring tiles also read as their halo, are kept so that the
+// second reader finds them in L2.
+constexpr int kKeep = 0;
+constexpr int kStream = 2;
+
+template <int POL = kKeep>
 __device__ __forceinline__ uint32_t ld32(Rsrc r, uint32_t voff, uint32_t soff)
 {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, POL);
 }
 
-template <int BPC>
+template <int BPC, int POL = kKeep>
 __device__ __forceinline__ typename Px<BPC>::Luma ld_luma(Rsrc r, uint32_t voff, uint32_t soff)
 {
     if constexpr (BPC == 8) {
-        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, POL);
     } else {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, POL);
         return u32x2{v[0], v[1]};
     }
 }
@@ -424,32 +433,6 @@ __device__ __forceinline__ uint32_t lds_addr(uint32_t (*lds)[kWave])
     return (uint32_t)(uintptr_t)(lds_void *)&lds[0][0];
 }
 
-// Fetch one lane value into a register (STAGED false) or into LDS row `row` (STAGED true).
-template <bool STAGED>
-__device__ __forceinline__ void fetch32(Rsrc r, uint32_t voff, uint32_t soff, uint32_t &reg,
-                                        uint32_t lds, int row)
-{
-    if constexpr (STAGED)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, row), 4, voff, soff, 0, 0);
-    else
-        reg = ld32(r, voff, soff);
-}
-
-template <int BPC, bool STAGED>
-__device__ __forceinline__ void fetch_luma(Rsrc r, uint32_t voff, uint32_t soff,
-                                           typename Px<BPC>::Luma &reg, uint32_t lds, int row)
-{
-    if constexpr (!STAGED) {
-        reg = ld_luma<BPC>(r, voff, soff);
-    } else if constexpr (BPC == 8) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, row), 4, voff, soff, 0, 0);
-    } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, 2 * row), 4, voff, soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, 2 * row + 1), 4, voff + 4, soff,
-                                                 0, 0);
-    }
-}
-
 // Issue every load of frame t for this tile into registers (the distorted planes and chroma only
 // when the frame is accumulated; a chunk's prologue frame is only blurred).
 template <int BPC, int TH, bool GENERIC>
@@ -457,9 +440,7 @@ __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, i
                                            bool accumulate, FrameData<BPC, TH> &F)
 {
     typedef FrameData<BPC, TH> FD;
-    constexpr bool STAGED = false;
     const int H = a.H;
-    const uint32_t lds = 0u;
     Rsrc rs[6];
     uint32_t pitch[6];
 #pragma unroll
@@ -472,16 +453,16 @@ __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, i
         // only the two rows above and below the tile can fall outside the frame on the fast path
         const int row = (GENERIC || k < 2 || k >= TH + 2) ? mirror_clamp(T.r0 - 2 + k, H)
                                                           : T.r0 - 2 + k;
-        fetch_luma<BPC, STAGED>(rs[0], T.luma_off, (uint32_t)row * pitch[0], F.R[k], lds, 0);
+        F.R[k] = ld_luma<BPC>(rs[0], T.luma_off, (uint32_t)row * pitch[0]);
     }
-    fetch_luma<10, STAGED>(rs[0], T.hvoff, 0u, F.HL, lds, 0);
+    F.HL = ld_luma<10>(rs[0], T.hvoff, 0u);
     if (!accumulate)
         return;
 #pragma unroll
     for (int i = 0; i < TH; ++i) {
         // rows past the frame re-read the last row; they are not counted
         const int row = GENERIC ? min(T.r0 + i, H - 1) : T.r0 + i;
-        fetch_luma<BPC, STAGED>(rs[3], T.luma_off, (uint32_t)row * pitch[3], F.D[i], lds, 0);
+        F.D[i] = ld_luma<BPC, kStream>(rs[3], T.luma_off, (uint32_t)row * pitch[3]);
     }
 #pragma unroll
     for (int k = 0; k < FD::kChromaSteps; ++k) {
@@ -490,11 +471,10 @@ __device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, i
         const int row = T.crow0 + FD::kChromaStep * k;
         const int rl = GENERIC ? min(row, a.Hc - 1) : row;
         const bool back = GENERIC && T.c_upper && row + 1 >= a.Hc;
-        const int lr = 0;
-        fetch32<STAGED>(rs[1], T.coff[0] - (back ? pitch[1] : 0u), (uint32_t)rl * pitch[1], F.cu[k], lds, lr);
-        fetch32<STAGED>(rs[4], T.coff[1] - (back ? pitch[4] : 0u), (uint32_t)rl * pitch[4], F.du[k], lds, lr + 1);
-        fetch32<STAGED>(rs[2], T.coff[2] - (back ? pitch[2] : 0u), (uint32_t)rl * pitch[2], F.cv[k], lds, lr + 2);
-        fetch32<STAGED>(rs[5], T.coff[3] - (back ? pitch[5] : 0u), (uint32_t)rl * pitch[5], F.dv[k], lds, lr + 3);
+        F.cu[k] = ld32<kStream>(rs[1], T.coff[0] - (back ? pitch[1] : 0u), (uint32_t)rl * pitch[1]);
+        F.du[k] = ld32<kStream>(rs[4], T.coff[1] - (back ? pitch[4] : 0u), (uint32_t)rl * pitch[4]);
+        F.cv[k] = ld32<kStream>(rs[2], T.coff[2] - (back ? pitch[2] : 0u), (uint32_t)rl * pitch[2]);
+        F.dv[k] = ld32<kStream>(rs[5], T.coff[3] - (back ? pitch[5] : 0u), (uint32_t)rl * pitch[5]);
     }
 }
 
@@ -509,7 +489,12 @@ __device__ __forceinline__ void load_frame_staged(const KernelArgs &a, const Til
     typedef Stage<TH> ST;
     const uint32_t lds = opaque(lds_addr(stage));
     auto dma16 = [&](Rsrc r, int lds_row0, uint32_t voff, uint32_t soff) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, lds_row0), 16, voff, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, lds_row0), 16, voff, soff, 0,
+                                                 kKeep);
+    };
+    auto dma16_stream = [&](Rsrc r, int lds_row0, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, lds_row0), 16, voff, soff, 0,
+                                                 kStream);
     };
     const Rsrc ry = plane_rsrc(frame_plane(a, t, 0), a.span[0]);
 #pragma unroll
@@ -523,7 +508,7 @@ __device__ __forceinline__ void load_frame_staged(const KernelArgs &a, const Til
     const uint32_t pd = opaque((uint32_t)a.pitch[3]);
 #pragma unroll
     for (int q = 0; q < ST::kDistLoads; ++q)
-        dma16(rd, ST::kDist + 4 * q, O.dist, (uint32_t)(T.r0 + 4 * q) * pd);
+        dma16_stream(rd, ST::kDist + 4 * q, O.dist, (uint32_t)(T.r0 + 4 * q) * pd);
     constexpr int pk[4] = {1, 4, 2, 5};
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -531,8 +516,8 @@ __device__ __forceinline__ void load_frame_staged(const KernelArgs &a, const Til
         const uint32_t pc = opaque((uint32_t)a.pitch[pk[p]]);
 #pragma unroll
         for (int q = 0; q < ST::kChromaLoads; ++q)
-            dma16(rc, ST::kChroma + p * ST::kChromaRows + 4 * q, O.chroma[p],
-                  (uint32_t)(T.crow0 + 8 * q) * pc);
+            dma16_stream(rc, ST::kChroma + p * ST::kChromaRows + 4 * q, O.chroma[p],
+                         (uint32_t)(T.crow0 + 8 * q) * pc);
     }
 }
 

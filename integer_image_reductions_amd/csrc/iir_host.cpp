@@ -2,10 +2,10 @@
 // queue and the score derivation. All device work goes to the gfx950 kernels in iir_kernels.hip.
 //
 // Per submission the context enqueues, on the caller's stream: (only for a non-uniformly strided
-// clip) one host-to-device copy of the frame table, one kernel launch, one device-to-host copy of
-// the per-frame sums into pinned memory and one event; iir_collect waits on that event once
-// ("ADR-1380: The CUDA SpEED twins are device-resident ...", Decision: submit on the picture's
-// stream, read the small result back behind an event, collect waits once). Everything is allocated
+// clip) one host-to-device copy of the frame table, one kernel launch, whose last workgroup writes
+// the per-frame totals into pinned host memory, and one event; iir_collect waits on that event
+// once ("ADR-1380: The CUDA SpEED twins are device-resident ...", Decision: submit on the
+// picture's stream, read the small result back behind an event, collect waits once). Everything is allocated
 // in iir_create ("Making it fast: three rounds on one pipeline", Round 2: no allocation or free on
 // the hot path).
 #include <hip/hip_runtime.h>
@@ -86,10 +86,12 @@ struct iir_ctx {
     int max_chunks = 1;
     uint32_t *ring[2] = {nullptr, nullptr};
     int ring_cur = 0;  // ring[ring_cur] holds the blurred state of the last submitted frame
-    unsigned long long *sums[2] = {nullptr, nullptr};
-    int sums_cur = 0;  // the next submission accumulates into sums[sums_cur]
+    unsigned long long *sums = nullptr;       // device, [max_batch][kSums][kSumSlots], zero
+                                              // between launches (each launch re-zeroes it)
+    unsigned int *arrivals = nullptr;         // device, finished-workgroup counter, zero
     int64_t sums_n = 0;
-    unsigned long long *host_sums = nullptr;  // pinned, [max_batch][kSums][kSumSlots]
+    unsigned long long *host_sums = nullptr;  // pinned coherent, [max_batch][kSums] totals
+    unsigned long long *host_sums_dev = nullptr;  // the same memory as the device sees it
     FramePtrs *table_dev = nullptr;
     FramePtrs *table_host = nullptr;  // pinned, [max_batch]
     // Pending submissions, oldest first, in a ring of kMaxPending records. Their results sit in
@@ -249,12 +251,13 @@ void release(iir_ctx *c)
     if (hipGetDevice(&saved) == hipSuccess && saved != c->device)
         (void)hipSetDevice(c->device);
     (void)hipStreamSynchronize(c->stream);
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 2; ++i)
         if (c->ring[i])
             (void)hipFree(c->ring[i]);
-        if (c->sums[i])
-            (void)hipFree(c->sums[i]);
-    }
+    if (c->sums)
+        (void)hipFree(c->sums);
+    if (c->arrivals)
+        (void)hipFree(c->arrivals);
     if (c->table_dev)
         (void)hipFree(c->table_dev);
     if (c->host_sums)
@@ -340,9 +343,9 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     }
     a.ring_in = c->ring[c->ring_cur];
     a.ring_out = c->ring[c->ring_cur ^ 1];
-    a.sums = c->sums[c->sums_cur];
-    a.zero = c->sums[c->sums_cur ^ 1];
-    a.zero_n = (int32_t)c->sums_n;
+    a.sums = c->sums;
+    a.publish = c->host_sums_dev + (size_t)first * kSums;
+    a.arrivals = c->arrivals;
     a.W = c->cfg.width;
     a.H = c->cfg.height;
     a.Wc = c->Wc;
@@ -362,13 +365,9 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     HIP_TRY(launch_frames(c->cfg.bpc, c->rows_per_tile,
                           !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile), a,
                           c->stream));
-    if (timing)
-        HIP_TRY(hipEventRecord(sub.k1, c->stream));
-    const size_t per_frame = (size_t)kSums * kSumSlots;
-    HIP_TRY(hipMemcpyAsync(c->host_sums + (size_t)first * per_frame, c->sums[c->sums_cur],
-                           sizeof(unsigned long long) * per_frame * n, hipMemcpyDeviceToHost,
-                           c->stream));
-    HIP_TRY(hipEventRecord(sub.done, c->stream));
+    // the kernel itself writes the totals to host_sums; one event marks the end (with timing,
+    // the event that closes the kernel's timed interval)
+    HIP_TRY(hipEventRecord(timing ? sub.k1 : sub.done, c->stream));
     sub.first = first;
     sub.n = n;
     sub.taken = 0;
@@ -377,7 +376,6 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     c->slot_head = first + n;
     c->pending += n;
     c->ring_cur ^= 1;
-    c->sums_cur ^= 1;
     c->has_prev = true;
     c->any_frame = true;
     return IIR_OK;
@@ -434,15 +432,19 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
 
     const size_t ring_bytes = (size_t)c->tiles * c->rows_per_tile * kWave * sizeof(uint2);
     hipError_t e = hipSuccess;
-    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+    for (int i = 0; i < 2 && e == hipSuccess; ++i)
         e = hipMalloc(&c->ring[i], ring_bytes);
-        if (e == hipSuccess)
-            e = hipMalloc(&c->sums[i], sizeof(unsigned long long) * c->sums_n);
-    }
+    if (e == hipSuccess)
+        e = hipMalloc(&c->sums, sizeof(unsigned long long) * c->sums_n);
+    if (e == hipSuccess)
+        e = hipMalloc(&c->arrivals, sizeof(unsigned int));
     if (e == hipSuccess)
         e = hipMalloc(&c->table_dev, sizeof(FramePtrs) * cfg->max_batch);
     if (e == hipSuccess)
-        e = hipHostMalloc(&c->host_sums, sizeof(unsigned long long) * c->sums_n, hipHostMallocDefault);
+        e = hipHostMalloc(&c->host_sums, sizeof(unsigned long long) * cfg->max_batch * kSums,
+                          hipHostMallocCoherent | hipHostMallocMapped);
+    if (e == hipSuccess)
+        e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->host_sums_dev), c->host_sums, 0);
     if (e == hipSuccess)
         e = hipHostMalloc(&c->table_host, sizeof(FramePtrs) * cfg->max_batch, hipHostMallocDefault);
     if (e != hipSuccess) {
@@ -457,11 +459,12 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
         if (e == hipSuccess && (cfg->flags & IIR_FLAG_TIMING))
             e = hipEventCreate(&sub.k1);
     }
-    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
-        e = hipMemsetAsync(c->sums[i], 0, sizeof(unsigned long long) * c->sums_n, c->stream);
-        if (e == hipSuccess)
-            e = hipMemsetAsync(c->ring[i], 0, ring_bytes, c->stream);
-    }
+    if (e == hipSuccess)
+        e = hipMemsetAsync(c->sums, 0, sizeof(unsigned long long) * c->sums_n, c->stream);
+    if (e == hipSuccess)
+        e = hipMemsetAsync(c->arrivals, 0, sizeof(unsigned int), c->stream);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i)
+        e = hipMemsetAsync(c->ring[i], 0, ring_bytes, c->stream);
     if (e == hipSuccess)
         e = hipStreamSynchronize(c->stream);
     if (e != hipSuccess) {
@@ -503,20 +506,15 @@ IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_o
         DeviceScope ds(ctx->device);
         if (ds.err != hipSuccess)
             return fail_hip(ds.err, "hipSetDevice");
-        HIP_TRY(hipEventSynchronize(last->done));
+        HIP_TRY(hipEventSynchronize((ctx->cfg.flags & IIR_FLAG_TIMING) ? last->k1 : last->done));
     }
-    const size_t per_frame = (size_t)kSums * kSumSlots;
     int got = 0;
     while (got < n) {
         iir_ctx::Sub &sub = ctx->subs[ctx->sub_head];
         const int take = std::min(n - got, sub.n - sub.taken);
         for (int i = 0; i < take; ++i) {
             const int f = sub.taken + i;
-            const unsigned long long *src = ctx->host_sums + (size_t)(sub.first + f) * per_frame;
-            uint64_t v[kSums] = {0, 0, 0, 0};
-            for (int k = 0; k < kSums; ++k)
-                for (int j = 0; j < kSumSlots; ++j)
-                    v[k] += src[k * kSumSlots + j];
+            const volatile unsigned long long *v = ctx->host_sums + (size_t)(sub.first + f) * kSums;
             iir_result &r = out[got + i];
             r.has_motion = (f > 0 || sub.has_prev) ? 1 : 0;
             r.sad = r.has_motion ? v[0] : 0;

@@ -34,11 +34,13 @@ struct KernelArgs {
     // launch's rows per tile
     const uint32_t *ring_in;
     uint32_t *ring_out;
-    // per-frame sums [nframes][kSums][kSumSlots], zeroed before the launch
+    // per-frame partial sums [nframes][kSums][kSumSlots], zero at launch; the launch's last
+    // workgroup folds the slots, writes the totals to `publish` and zeroes them again
     unsigned long long *sums;
-    // the other sum buffer, cleared here for the next submission
-    unsigned long long *zero;
-    int32_t zero_n;
+    // host-visible [nframes][kSums] totals of this launch (pinned host memory)
+    unsigned long long *publish;
+    // workgroups of this launch that have finished, zero at launch (the last one resets it)
+    unsigned int *arrivals;
     int32_t W, H, Wc, Hc;
     int32_t strips, row_tiles, tiles;
     int32_t nframes, chunks, chunk_len;

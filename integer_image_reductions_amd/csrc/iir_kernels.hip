@@ -770,6 +770,41 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
     flush_sums(a, P, T.lane);
 }
 
+// The launch's last workgroup to finish (counted with one device-scope atomic per workgroup)
+// folds the kSumSlots partial sums of every frame, writes the totals straight to the
+// caller-visible pinned buffer and zeroes the partial sums and the counter for the next launch.
+// No workgroup waits for another, and no separate readback copy follows the kernel. Ordering:
+// the sum atomics are device-scope read-modify-writes; each workgroup waits until its own have
+// completed (vmcnt(0)) before counting itself, and the last one reads them back with
+// device-scope atomic loads after an acquire fence. A release fence per workgroup would write
+// back every XCD's L2 once per workgroup, which costs far more than the copy it replaces.
+__device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane)
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this workgroup's sum atomics completed
+    unsigned int arrived = 0;
+    if (lane == 0)
+        arrived = __hip_atomic_fetch_add(a.arrivals, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    arrived = (unsigned int)uni((int)arrived);
+    if (arrived != gridDim.x - 1u)
+        return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const int n = a.nframes * kSums;
+    for (int i = lane; i < n; i += kWave) {
+        unsigned long long *slot = a.sums + (size_t)i * kSumSlots;
+        unsigned long long total = 0;
+#pragma unroll
+        for (int j = 0; j < kSumSlots; ++j) {
+            total += __hip_atomic_load(slot + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(slot + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __hip_atomic_store(a.publish + i, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    if (lane == 0)
+        __hip_atomic_store(a.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+}
+
 template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void
 frames_kernel(const KernelArgs a)
@@ -779,10 +814,6 @@ frames_kernel(const KernelArgs a)
     static_assert(!STAGED || BPC == 8, "LDS staging is laid out for 8-bit samples");
     constexpr int B = Px<BPC>::kBytes;
     const int lane = threadIdx.x;
-
-    // clear the other sum buffer for the next submission
-    for (int i = blockIdx.x * kWave + threadIdx.x; i < a.zero_n; i += gridDim.x * kWave)
-        a.zero[i] = 0ull;
 
     Tile T;
     const int L = uni(xcd_linear(blockIdx.x, gridDim.x));
@@ -957,6 +988,8 @@ frames_kernel(const KernelArgs a)
         for (int i = 0; i < TH; ++i)
             rout[(T.tile * TH + i) * kWave + lane] = make_uint2(prev0[i], prev1[i]);
     }
+
+    publish_if_last(a, lane);
 }
 
 // Tiled blurred state -> W x H uint16 plane.

@@ -789,20 +789,39 @@ __device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane)
     if (arrived != gridDim.x - 1u)
         return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // kPer totals per lane per pass, all of their slot loads issued before any is added, so a
+    // pass costs one memory round trip (a 64-frame launch is one pass)
+    constexpr int kPer = 4;
     const int n = a.nframes * kSums;
-    for (int i = lane; i < n; i += kWave) {
-        unsigned long long *slot = a.sums + (size_t)i * kSumSlots;
-        unsigned long long total = 0;
+    for (int base = 0; base < n; base += kPer * kWave) {
+        unsigned long long v[kPer][kSumSlots];
 #pragma unroll
-        for (int j = 0; j < kSumSlots; ++j) {
-            total += __hip_atomic_load(slot + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(slot + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int q = 0; q < kPer; ++q) {
+            const int i = min(base + q * kWave + lane, n - 1);
+#pragma unroll
+            for (int j = 0; j < kSumSlots; ++j)
+                v[q][j] = __hip_atomic_load(a.sums + (size_t)i * kSumSlots + j, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
         }
-        __hip_atomic_store(a.publish + i, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int i = base + q * kWave + lane;
+            if (i < n) {
+                unsigned long long total = 0;
+#pragma unroll
+                for (int j = 0; j < kSumSlots; ++j) {
+                    total += v[q][j];
+                    __hip_atomic_store(a.sums + (size_t)i * kSumSlots + j, 0ull,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __hip_atomic_store(a.publish + i, total, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+        }
     }
     if (lane == 0)
         __hip_atomic_store(a.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+    // the end of the kernel releases these stores to the host before its completion signal
 }
 
 template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE>
@@ -982,14 +1001,15 @@ frames_kernel(const KernelArgs a)
 
     frame_loop<BPC, TH, GENERIC, STAGED>(a, T, O, prev0, prev1, sum_prev, have_prev, stage);
 
+    // counted before the state write, so the count waits only for this workgroup's sum atomics
+    publish_if_last(a, lane);
+
     if (T.chunk == a.chunks - 1) {
         uint2 *rout = reinterpret_cast<uint2 *>(a.ring_out);
 #pragma unroll
         for (int i = 0; i < TH; ++i)
             rout[(T.tile * TH + i) * kWave + lane] = make_uint2(prev0[i], prev1[i]);
     }
-
-    publish_if_last(a, lane);
 }
 
 // Tiled blurred state -> W x H uint16 plane.

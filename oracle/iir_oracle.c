@@ -248,3 +248,99 @@ int iiro_scores(int32_t w, int32_t h, int32_t bpc, const uint64_t sums[4], int32
     }
     return IIRO_OK;
 }
+
+/*
+ * Luma moments of one plane ("ADR-1392: CUDA motion, PSNR and moment kernels add one atomic per
+ * block ...", Decision 6 and Consequences: the moment kernel sums the reference and distorted
+ * luma and their squares into four accumulators; float_moment reports their means). out receives
+ * {sum x, sum x^2} over the plane, exact 64-bit integers.
+ */
+int iiro_moments(const void *plane, int64_t pitch, int32_t w, int32_t h, int32_t bpc,
+                 uint64_t out[2])
+{
+    if (!plane || !out || bad_dims(w, h, bpc))
+        return IIRO_EINVAL;
+    if (check_range(plane, pitch, w, h, bpc))
+        return IIRO_ERANGE;
+    uint64_t s1 = 0, s2 = 0;
+    for (int64_t i = 0; i < h; ++i)
+        for (int64_t j = 0; j < w; ++j) {
+            const uint64_t x = (uint64_t)sample(plane, pitch, i, j, bpc);
+            s1 += x;
+            s2 += x * x;
+        }
+    out[0] = s1;
+    out[1] = s2;
+    return IIRO_OK;
+}
+
+/*
+ * Second motion score of each frame of a clip ("ADR-1392", Consequences lists the motion2
+ * output; the pages give no formula, so this is the reading): frame t's motion2 is the smaller
+ * of its own motion and the next frame's, and the clip's last frame keeps its own motion.
+ */
+int iiro_motion2(const double *motion, int32_t n, double *out)
+{
+    if (!motion || !out || n < 1)
+        return IIRO_EINVAL;
+    for (int32_t t = 0; t < n; ++t) {
+        const double a = motion[t];
+        const double b = t + 1 < n ? motion[t + 1] : a;
+        out[t] = b < a ? b : a;
+    }
+    return IIRO_OK;
+}
+
+/*
+ * Clip aggregates (reading; the pages name aggregate PSNR outputs without a formula): for plane c
+ * the aggregate PSNR is 10 log10(peak^2 / MSE_c) with MSE_c the clip's total squared error over
+ * its total sample count (+infinity when the total is 0); the mean motion and mean motion2 are
+ * the plain averages of the per-frame scores (frame 0 of a clip without a previous frame scores
+ * 0). sums holds n x 4 {SAD, SSE_Y, SSE_U, SSE_V}; out = {apsnr_y, apsnr_u, apsnr_v,
+ * mean_motion, mean_motion2}.
+ */
+int iiro_aggregate(int32_t w, int32_t h, int32_t bpc, const uint64_t *sums,
+                   const int32_t *has_motion, int32_t n, double out[5])
+{
+    if (!sums || !has_motion || !out || n < 1 || bad_dims(w, h, bpc))
+        return IIRO_EINVAL;
+    double *motion = (double *)malloc(sizeof(double) * (size_t)n);
+    double *motion2 = (double *)malloc(sizeof(double) * (size_t)n);
+    if (!motion || !motion2) {
+        free(motion);
+        free(motion2);
+        return IIRO_ENOMEM;
+    }
+    uint64_t total[3] = {0, 0, 0};
+    for (int32_t t = 0; t < n; ++t) {
+        double s[7];
+        int rc = iiro_scores(w, h, bpc, sums + 4 * (int64_t)t, has_motion[t], s);
+        if (rc) {
+            free(motion);
+            free(motion2);
+            return rc;
+        }
+        motion[t] = s[0];
+        for (int c = 0; c < 3; ++c)
+            total[c] += sums[4 * (int64_t)t + 1 + c];
+    }
+    iiro_motion2(motion, n, motion2);
+    const double npx[3] = {(double)w * (double)h, (double)((w + 1) / 2) * (double)((h + 1) / 2),
+                           (double)((w + 1) / 2) * (double)((h + 1) / 2)};
+    const double peak = (double)(((int64_t)1 << bpc) - 1);
+    const double peak_sq = peak * peak;
+    for (int c = 0; c < 3; ++c) {
+        const double mse = (double)total[c] / ((double)n * npx[c]);
+        out[c] = total[c] == 0 ? INFINITY : 10.0 * log10(peak_sq / mse);
+    }
+    double m1 = 0.0, m2 = 0.0;
+    for (int32_t t = 0; t < n; ++t) {
+        m1 += motion[t];
+        m2 += motion2[t];
+    }
+    out[3] = m1 / (double)n;
+    out[4] = m2 / (double)n;
+    free(motion);
+    free(motion2);
+    return IIRO_OK;
+}

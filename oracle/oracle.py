@@ -85,8 +85,11 @@ class OracleLib:
         lib.iiro_sad.argtypes = [vp, vp, i32, i32, vp]
         lib.iiro_clip.argtypes = [vp] * 6 + [i32, i32, i32, i32, vp, vp, vp, vp]
         lib.iiro_scores.argtypes = [i32, i32, i32, vp, i32, vp]
+        lib.iiro_moments.argtypes = [vp, i64, i32, i32, i32, vp]
+        lib.iiro_motion2.argtypes = [vp, i32, vp]
+        lib.iiro_aggregate.argtypes = [i32, i32, i32, vp, vp, i32, vp]
         for f in (lib.iiro_taps, lib.iiro_sse, lib.iiro_blur, lib.iiro_sad, lib.iiro_clip,
-                  lib.iiro_scores):
+                  lib.iiro_scores, lib.iiro_moments, lib.iiro_motion2, lib.iiro_aggregate):
             f.restype = ctypes.c_int
         self.path = path
         self._lib = lib
@@ -163,6 +166,29 @@ class OracleLib:
         return {"motion": float(out[0]), "mse": [float(x) for x in out[1:4]],
                 "psnr": [float(x) for x in out[4:7]]}
 
+    def moments(self, plane: np.ndarray, bpc: int):
+        """(sum x, sum x^2) of one plane."""
+        p = _plane(plane, bpc)
+        out = np.zeros(2, dtype=np.uint64)
+        _check(self._lib.iiro_moments(_ptr(p), p.strides[0], p.shape[1], p.shape[0], bpc,
+                                      _ptr(out)), "moments")
+        return int(out[0]), int(out[1])
+
+    def motion2(self, motion) -> np.ndarray:
+        m = np.ascontiguousarray(np.asarray(motion, dtype=np.float64).reshape(-1))
+        out = np.zeros_like(m)
+        _check(self._lib.iiro_motion2(_ptr(m), m.size, _ptr(out)), "motion2")
+        return out
+
+    def aggregate(self, w: int, h: int, bpc: int, sums, has_motion) -> dict:
+        s = np.ascontiguousarray(np.asarray(sums, dtype=np.uint64).reshape(-1, 4))
+        hm = np.ascontiguousarray(np.asarray(has_motion, dtype=np.int32).reshape(-1))
+        out = np.zeros(5, dtype=np.float64)
+        _check(self._lib.iiro_aggregate(w, h, bpc, _ptr(s), _ptr(hm), s.shape[0], _ptr(out)),
+               "aggregate")
+        return {"apsnr": [float(x) for x in out[:3]], "mean_motion": float(out[3]),
+                "mean_motion2": float(out[4])}
+
 
 def default() -> OracleLib:
     """The real oracle, built on first use if the library is missing or stale."""
@@ -198,3 +224,15 @@ def clip(ref, dist, bpc, prev_blur=None, want_last_blur=False):
 
 def scores(w, h, bpc, sums, has_motion):
     return default().scores(w, h, bpc, sums, has_motion)
+
+
+def moments(plane, bpc):
+    return default().moments(plane, bpc)
+
+
+def motion2(motion):
+    return default().motion2(motion)
+
+
+def aggregate(w, h, bpc, sums, has_motion):
+    return default().aggregate(w, h, bpc, sums, has_motion)

@@ -345,4 +345,71 @@ def pin_rejects_out_of_range(o):
         raise AssertionError("a 10-bit sample of 1024 was accepted")
 
 
+# ---------------------------------------------------------------------------------------------
+# luma moments, motion2 and clip aggregates (readings: the pages name these outputs only)
+
+
+def pin_moments_brute_force(o):
+    """sum x and sum x^2 against Python integers over random, checkerboard and 0/max planes."""
+    for bpc in (8, 10):
+        for i, x in enumerate(_planes(bpc, 41 + bpc)):
+            v = [int(a) for a in x.reshape(-1)]
+            assert o.moments(x, bpc) == (sum(v), sum(a * a for a in v)), (bpc, i, x.shape)
+
+
+def pin_moments_closed_form(o):
+    """A flat plane of value c: N c and N c^2; a bit-depth step (x4) scales them by 4 and 16."""
+    for bpc in (8, 10):
+        for c in (0, 1, 200, (1 << bpc) - 1):
+            x = np.full((7, 9), c, dtype=np.uint8 if bpc == 8 else np.uint16)
+            assert o.moments(x, bpc) == (63 * c, 63 * c * c), (bpc, c)
+    x = _rng(4).integers(0, 256, size=(13, 17)).astype(np.uint8)
+    s1, s2 = o.moments(x, 8)
+    assert o.moments((x.astype(np.uint16) * 4), 10) == (4 * s1, 16 * s2)
+
+
+def pin_motion2_properties(o):
+    """Each value is one of its two inputs and no larger than either; the last frame keeps its
+    own motion; an increasing clip keeps its motions, a decreasing one takes the next frame's."""
+    r = _rng(8)
+    for n in (1, 2, 5, 40):
+        m = r.random(n) * 10.0
+        m2 = o.motion2(m)
+        for t in range(n):
+            nxt = m[t + 1] if t + 1 < n else m[t]
+            assert m2[t] in (m[t], nxt) and m2[t] <= m[t] and m2[t] <= nxt, (n, t)
+        assert m2[-1] == m[-1]
+    inc = np.arange(1.0, 9.0)
+    assert np.array_equal(o.motion2(inc), inc)
+    dec = inc[::-1].copy()
+    assert np.array_equal(o.motion2(dec)[:-1], dec[1:]) and o.motion2(dec)[-1] == dec[-1]
+
+
+def pin_aggregate(o):
+    """Aggregate PSNR is the PSNR of the clip's mean MSE: equal frames give the frame PSNR, and
+    it lies between the per-frame PSNRs; zero error gives +inf; the mean motions average the
+    per-frame scores of the per-frame function."""
+    w, h, bpc = 6, 4, 8
+    sums = [[0, 24, 6, 6]] * 3
+    agg = o.aggregate(w, h, bpc, sums, [0, 1, 1])
+    frame = o.scores(w, h, bpc, sums[0], 1)
+    assert np.allclose(agg["apsnr"], frame["psnr"], rtol=0, atol=1e-12)
+    r = _rng(12)
+    sums = [[int(r.integers(0, 1 << 20))] + [int(r.integers(1, 5000)) for _ in range(3)]
+            for _ in range(7)]
+    hm = [0] + [1] * 6
+    agg = o.aggregate(w, h, bpc, sums, hm)
+    per = [o.scores(w, h, bpc, s, m) for s, m in zip(sums, hm)]
+    for c in range(3):
+        ps = [p["psnr"][c] for p in per]
+        assert min(ps) - 1e-12 <= agg["apsnr"][c] <= max(ps) + 1e-12
+        mean_mse = sum(p["mse"][c] for p in per) / len(per)
+        assert abs(agg["apsnr"][c] - 10.0 * math.log10(255.0 ** 2 / mean_mse)) < 1e-9
+    mot = [p["motion"] for p in per]
+    assert abs(agg["mean_motion"] - sum(mot) / 7) < 1e-15
+    assert abs(agg["mean_motion2"] - sum(o.motion2(mot)) / 7) < 1e-15
+    zero = o.aggregate(w, h, bpc, [[0, 0, 0, 0]] * 2, [0, 1])
+    assert all(math.isinf(v) for v in zero["apsnr"])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -39,6 +39,14 @@ MUTANTS = [
     ("psnr_uses_sse", "10.0 * log10(peak * peak / mse)", "10.0 * log10(peak * peak / (double)sums[1 + c])"),
     ("range_check_off", "if (sample(plane, pitch, i, j, bpc) > maxv)",
      "if (sample(plane, pitch, i, j, bpc) > maxv + 1)"),
+    ("moment_not_squared", "s2 += x * x;", "s2 += x;"),
+    ("motion2_max", "out[t] = b < a ? b : a;", "out[t] = b > a ? b : a;"),
+    ("motion2_previous_frame", "const double b = t + 1 < n ? motion[t + 1] : a;",
+     "const double b = t > 0 ? motion[t - 1] : a;"),
+    ("apsnr_mean_of_psnr_count", "const double mse = (double)total[c] / ((double)n * npx[c]);",
+     "const double mse = (double)total[c] / npx[c];"),
+    ("apsnr_peak_not_squared", "const double peak_sq = peak * peak;", "const double peak_sq = peak;"),
+    ("mean_motion_skips_first", "m1 += motion[t];", "m1 += t ? motion[t] : motion[1 % n];"),
 ]
 
 

@@ -1,6 +1,7 @@
 """Benchmark: frames/s of the integer motion + PSNR sums on 3840x2160 8-bit 4:2:0, one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu] [--probe]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--moments] [--no-cpu]
+                    [--probe]
     python bench.py --workload c3 --traffic-from FETCH.csv WRITE.csv   (host only, see below)
 
 A step is one pass of the whole path over one batch: one iir_submit_clip of the 50-frame clip
@@ -18,6 +19,9 @@ the kernel source still matches the one the counters were taken on.
 each counter's mean KiB per main-kernel dispatch, scaled by what the same counter reads for the
 copy probe (probe_copy moves a known 1 GiB in and 1 GiB out per dispatch).
 cpu_baseline: the plain C oracle (single thread) over the same frames, on the host.
+--moments runs the same workload with the luma moments summed in the same pass (IIR_FLAG_MOMENTS):
+the bytes moved are the same, the arithmetic per sample grows; its traffic summary is kept under
+the workload name with a _moments suffix.
 """
 from __future__ import annotations
 
@@ -93,14 +97,16 @@ def _counter_means(path: str, counter: str):
     return sum(main) / len(main), len(main), sum(copy) / len(copy), len(copy)
 
 
-def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
+def write_traffic(workload: str, moments: bool, fetch_csv: str, write_csv: str) -> dict:
     fm, fn, fc, fcn = _counter_means(fetch_csv, "FETCH_SIZE")
     wm, wn, wc, wcn = _counter_means(write_csv, "WRITE_SIZE")
     f_scale = PROBE_BYTES / (fc * 1024.0)
     w_scale = PROBE_BYTES / (wc * 1024.0)
     fetch_b, write_b = fm * 1024.0 * f_scale, wm * 1024.0 * w_scale
+    wl = workload + ("_moments" if moments else "")
+    flag = " --moments" if moments else ""
     d = {
-        "workload": WORKLOADS[workload],
+        "workload": WORKLOADS[workload] + (" + luma moments" if moments else ""),
         "kernel_sha256": kernel_sha(),
         "fetch_kib_per_launch": fm, "fetch_dispatches": fn,
         "write_kib_per_launch": wm, "write_dispatches": wn,
@@ -112,9 +118,9 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
         "algorithmic_bytes_per_launch": None,
         "commands": [
             f"rocprofv3 --pmc {c} --output-format csv -d <dir_{c}> -o run -- python3 -u bench.py "
-            f"--workload {workload} --steps 5 --warmup 1 --no-cpu --probe"
+            f"--workload {workload}{flag} --steps 5 --warmup 1 --no-cpu --probe"
             for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
-            f"python bench.py --workload {workload} --traffic-from "
+            f"python bench.py --workload {workload}{flag} --traffic-from "
             "<dir_FETCH_SIZE>/run_counter_collection.csv <dir_WRITE_SIZE>/run_counter_collection.csv"],
     }
     import synth
@@ -122,25 +128,34 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
     d["algorithmic_bytes_per_launch"] = algorithmic_bytes(c["width"], c["height"], c["bpc"],
                                                           c["frames"])
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    path = os.path.join(ROOT, "profiles", f"frames_kernel_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"frames_kernel_{wl}_traffic.json")
     with open(path, "w") as f:
         json.dump(d, f, indent=1)
         f.write("\n")
     return d
 
 
-def cpu_baseline(clip, max_seconds: float = 20.0):
+def cpu_baseline(clip, max_seconds: float = 20.0, moments: bool = False):
     """The oracle over the leading frames of the same clip that fit `max_seconds` (the whole clip
-    when it fits), single-threaded; frames/s."""
+    when it fits), single-threaded; frames/s. With moments, also the oracle's luma moments of
+    every ref and dist frame."""
     import oracle
+
+    def run(c):
+        oracle.clip(c.ref, c.dist, clip.bpc)
+        if moments:
+            for t in range(c.frames):
+                oracle.moments(c.ref[0][t], clip.bpc)
+                oracle.moments(c.dist[0][t], clip.bpc)
+
     one = clip.slice(0, 1)
     t0 = time.perf_counter()
-    oracle.clip(one.ref, one.dist, clip.bpc)
+    run(one)
     per_frame = time.perf_counter() - t0
     n = max(1, min(clip.frames, int(max_seconds / max(per_frame, 1e-6))))
     sub = clip.slice(0, n)
     t0 = time.perf_counter()
-    oracle.clip(sub.ref, sub.dist, clip.bpc)
+    run(sub)
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "frames/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} of {clip.frames} frame pairs of the same workload, one pass, "
@@ -153,14 +168,17 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--moments", action="store_true",
+                    help="also sum the luma moments in the same pass (IIR_FLAG_MOMENTS)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--probe", action="store_true", help="also measure the memory ceilings")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic summary from two counter CSVs and exit")
     args = ap.parse_args()
 
+    wl = args.workload + ("_moments" if args.moments else "")
     if args.traffic_from:
-        print(json.dumps(write_traffic(args.workload, *args.traffic_from)))
+        print(json.dumps(write_traffic(args.workload, args.moments, *args.traffic_from)))
         return
 
     if args.gpus != 1:
@@ -189,7 +207,7 @@ def main():
     log("uploaded", F, "frame pairs")
 
     # two batches in flight: step k is submitted before step k-1 is collected
-    ctx = iir.Context(W, H, bpc, max_batch=2 * F, timing=True)
+    ctx = iir.Context(W, H, bpc, max_batch=2 * F, timing=True, moments=args.moments)
     geo = ctx.geometry()
     chunks = ctx.plan_chunks(F)
     clip_dev = ctx.prepare_clip(ref, dist)
@@ -229,11 +247,13 @@ def main():
         "vs_baseline": None,
         "dtype": "u8" if bpc == 8 else "u16",
         "data": "synthetic (seeded value-noise clip of the workload's shape; see synth.py)",
-        "config": {"workload": WORKLOADS[args.workload], "width": W, "height": H, "bpc": bpc,
+        "config": {"workload": WORKLOADS[args.workload] + (" + luma moments" if args.moments
+                                                           else ""),
+                   "width": W, "height": H, "bpc": bpc,
                    "frames_per_step": F, "chroma": "4:2:0", "tiles": geo["tiles"],
                    "time_chunks": chunks, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(args.workload),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(wl),
                      "kernel": "frames_kernel", "kernel_us": kernel_ms * 1e3,
                      "algorithmic_bytes_per_launch": alg},
     }
@@ -252,7 +272,7 @@ def main():
     ctx.close()
     if not args.no_cpu:
         log("cpu baseline")
-        out["cpu_baseline"] = cpu_baseline(clip)
+        out["cpu_baseline"] = cpu_baseline(clip, moments=args.moments)
     print(json.dumps(out), flush=True)
 
 

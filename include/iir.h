@@ -12,6 +12,10 @@
  *           mirror and round-half-up are this library's readings where the pages give no numbers.
  *   SSE[c]  sum over plane c in {Y, U, V} of (ref - dist)^2 ("ADR-1392", Context and Decision 2).
  *
+ * Optionally (IIR_FLAG_MOMENTS) four more: the sums and sums of squares of the reference and the
+ * distorted luma, in the same pass. Clip-level scores (iir_motion2, iir_aggregate_of) are host
+ * functions of the per-frame results.
+ *
  * Every sum is computed exactly in integers, so the order of the reduction does not matter
  * ("ADR-1392", Context: the sums are order-independent). Derived doubles (iir_scores_of) are
  * computed on the host.
@@ -53,6 +57,12 @@ enum {
 
 /* iir_config.flags */
 #define IIR_FLAG_TIMING 1u /* record HIP events around each main kernel launch (iir_kernel_time) */
+/*
+ * Also sum the luma moments of every frame pair in the same pass (iir_result.moment): the sums
+ * and sums of squares of the reference and distorted luma, the four accumulators of the moment
+ * kernel ("ADR-1392", Context, and Decision 6).
+ */
+#define IIR_FLAG_MOMENTS 2u
 
 /*
  * One plane of one frame. data is a DEVICE pointer, pitch is the distance between rows in bytes.
@@ -86,11 +96,14 @@ typedef struct iir_config {
 
 /*
  * Exact sums of one frame pair. has_motion is 0 for the first frame after iir_create or iir_reset
- * (there is no previous blurred frame; sad is then 0) and 1 otherwise.
+ * (there is no previous blurred frame; sad is then 0) and 1 otherwise. moment = {sum of ref Y,
+ * sum of dist Y, sum of ref Y^2, sum of dist Y^2} over the luma plane with IIR_FLAG_MOMENTS, else
+ * all 0.
  */
 typedef struct iir_result {
     uint64_t sad;
     uint64_t sse[3];
+    uint64_t moment[4];
     int32_t has_motion;
     int32_t reserved;
 } iir_result;
@@ -98,16 +111,36 @@ typedef struct iir_result {
 /*
  * Scores derived from one iir_result on the host in IEEE double ("ADR-1392", Consequences names
  * the psnr_*, mse_* and motion outputs; the formulas are this library's readings):
- *   motion  = sad / (256 * W * H)   (mean absolute blurred difference in 8-bit units; 0 when
- *                                    has_motion is 0)
- *   mse[c]  = sse[c] / (W_c * H_c)
- *   psnr[c] = 10 * log10(peak^2 / mse[c]), peak = 2^bpc - 1; +infinity when sse[c] == 0.
+ *   motion    = sad / (256 * W * H)   (mean absolute blurred difference in 8-bit units; 0 when
+ *                                      has_motion is 0)
+ *   mse[c]    = sse[c] / (W_c * H_c)
+ *   psnr[c]   = 10 * log10(peak^2 / mse[c]), peak = 2^bpc - 1; +infinity when sse[c] == 0
+ *   moment[k] = result moment[k] / (W * H): the first and second moments of ref and dist luma
+ *               (0 unless the result came from a context with IIR_FLAG_MOMENTS).
  */
 typedef struct iir_scores {
     double motion;
     double mse[3];
     double psnr[3];
+    double moment[4];
 } iir_scores;
+
+/*
+ * Clip aggregates of n consecutive results (pure host code; "ADR-1392", Consequences names the
+ * apsnr_* and integer_motion2 outputs without formulas, so these are this library's readings):
+ *   sse[c]       = the clip's total squared error of plane c (exact)
+ *   apsnr[c]     = 10 * log10(peak^2 / (sse[c] / (n * W_c * H_c))); +infinity when sse[c] == 0
+ *   mean_motion  = the mean of the frames' motion scores (iir_scores.motion)
+ *   mean_motion2 = the mean of the frames' motion2 scores (iir_motion2)
+ */
+typedef struct iir_aggregate {
+    uint64_t sse[3];
+    double apsnr[3];
+    double mean_motion;
+    double mean_motion2;
+    int32_t frames;
+    int32_t reserved;
+} iir_aggregate;
 
 typedef struct iir_ctx iir_ctx;
 
@@ -160,6 +193,18 @@ IIR_API int iir_run_clip(iir_ctx *ctx, const iir_frame *ref, const iir_frame *di
 
 /* Derive the scores of one result for a configuration (pure host code). Errors: IIR_EINVAL. */
 IIR_API int iir_scores_of(const iir_config *cfg, const iir_result *r, iir_scores *s);
+
+/*
+ * Second motion score of each of n consecutive frames from their motion scores (reading of the
+ * integer_motion2 output named by "ADR-1392", Consequences): motion2[t] = min(motion[t],
+ * motion[t + 1]); the last frame keeps its own motion. motion2 may alias motion. Errors:
+ * IIR_EINVAL (NULL array, n < 1).
+ */
+IIR_API int iir_motion2(const double *motion, int32_t n, double *motion2);
+
+/* Aggregate n >= 1 consecutive results of one clip (see iir_aggregate). Errors: IIR_EINVAL. */
+IIR_API int iir_aggregate_of(const iir_config *cfg, const iir_result *r, int32_t n,
+                             iir_aggregate *out);
 
 /* Forget the previous frame: the next submitted frame gets has_motion = 0. Enqueues nothing. */
 IIR_API int iir_reset(iir_ctx *ctx);

@@ -5,10 +5,13 @@ this package is its Python binding. Import is cheap: the library loads on first 
 """
 from .binding import (  # noqa: F401
     IIR_CHROMA_420,
+    IIR_FLAG_MOMENTS,
     IIR_FLAG_TIMING,
     LIB_PATH,
     PLANE_ALIGN,
     SIGNATURES,
+    aggregate,
+    motion2,
     Context,
     IIRError,
     frame_of,

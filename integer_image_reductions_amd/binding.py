@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libiir.so")
 IIR_OK, IIR_EINVAL, IIR_ENODEV, IIR_ENOMEM, IIR_EDEVICE, IIR_EBUSY, IIR_ESTATE = 0, -1, -2, -3, -4, -5, -6
 IIR_CHROMA_420 = 420
 IIR_FLAG_TIMING = 1
+IIR_FLAG_MOMENTS = 2
 PLANE_ALIGN = 16  # bytes: plane data and pitch must be multiples of this
 
 c_i32, c_i64, c_u32, c_u64, c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
@@ -37,12 +38,19 @@ class Config(ctypes.Structure):
 
 
 class Result(ctypes.Structure):
-    _fields_ = [("sad", c_u64), ("sse", c_u64 * 3), ("has_motion", c_i32), ("reserved", c_i32)]
+    _fields_ = [("sad", c_u64), ("sse", c_u64 * 3), ("moment", c_u64 * 4), ("has_motion", c_i32),
+                ("reserved", c_i32)]
 
 
 class Scores(ctypes.Structure):
     _fields_ = [("motion", ctypes.c_double), ("mse", ctypes.c_double * 3),
-                ("psnr", ctypes.c_double * 3)]
+                ("psnr", ctypes.c_double * 3), ("moment", ctypes.c_double * 4)]
+
+
+class Aggregate(ctypes.Structure):
+    _fields_ = [("sse", c_u64 * 3), ("apsnr", ctypes.c_double * 3),
+                ("mean_motion", ctypes.c_double), ("mean_motion2", ctypes.c_double),
+                ("frames", c_i32), ("reserved", c_i32)]
 
 
 class Geometry(ctypes.Structure):
@@ -69,6 +77,10 @@ SIGNATURES = [
                       ctypes.POINTER(Result)], ctypes.c_int),
     ("iir_scores_of", [ctypes.POINTER(Config), ctypes.POINTER(Result), ctypes.POINTER(Scores)],
      ctypes.c_int),
+    ("iir_motion2", [ctypes.POINTER(ctypes.c_double), c_i32, ctypes.POINTER(ctypes.c_double)],
+     ctypes.c_int),
+    ("iir_aggregate_of", [ctypes.POINTER(Config), ctypes.POINTER(Result), c_i32,
+                          ctypes.POINTER(Aggregate)], ctypes.c_int),
     ("iir_reset", [c_vp], ctypes.c_int),
     ("iir_export_blur", [c_vp, c_vp, c_i64], ctypes.c_int),
     ("iir_kernel_time", [c_vp, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
@@ -162,7 +174,7 @@ class Context:
     """One library context (iir_ctx): a frame geometry, a device and a stream."""
 
     def __init__(self, width: int, height: int, bpc: int, max_batch: int = 64, device=None,
-                 stream=None, timing: bool = False):
+                 stream=None, timing: bool = False, moments: bool = False):
         torch = _torch()
         lib = load_library()
         self._lib = lib
@@ -170,7 +182,9 @@ class Context:
         self.device = dev
         self.stream = stream if stream is not None else torch.cuda.current_stream(dev)
         self.config = Config(width, height, bpc, IIR_CHROMA_420, max_batch,
-                             IIR_FLAG_TIMING if timing else 0)
+                             (IIR_FLAG_TIMING if timing else 0) |
+                             (IIR_FLAG_MOMENTS if moments else 0))
+        self.moments = bool(moments)
         h = c_vp()
         _check(lib.iir_create(ctypes.byref(self.config), dev.index, c_vp(self.stream.cuda_stream),
                               ctypes.byref(h)), "iir_create")
@@ -262,21 +276,30 @@ class Context:
         self._keep.append((ref_frames, dist_frames))
         return n
 
+    def _unpack(self, out, n):
+        cols = 8 if self.moments else 4
+        sums = np.zeros((n, cols), dtype=np.uint64)
+        hm = np.zeros(n, dtype=np.int32)
+        for i in range(n):
+            r = out[i]
+            row = [r.sad, r.sse[0], r.sse[1], r.sse[2]]
+            if self.moments:
+                row += list(r.moment)
+            sums[i] = row
+            hm[i] = r.has_motion
+        return sums, hm
+
     def collect(self, max_results: int = 1 << 20):
-        """Wait for pending work; returns (sums (n, 4) uint64 [SAD, SSE_Y, SSE_U, SSE_V],
-        has_motion (n,) int32)."""
+        """Wait for pending work; returns (sums (n, 4) uint64 [SAD, SSE_Y, SSE_U, SSE_V] -- (n, 8)
+        with moments, adding [sum ref Y, sum dist Y, sum ref Y^2, sum dist Y^2] --, has_motion
+        (n,) int32)."""
         n_cap = min(max_results, self.config.max_batch)
         out = (Result * n_cap)()
         got = c_i32()
         _check(self._lib.iir_collect(self._h, out, n_cap, ctypes.byref(got)), "iir_collect")
-        sums = np.zeros((got.value, 4), dtype=np.uint64)
-        hm = np.zeros(got.value, dtype=np.int32)
-        for i in range(got.value):
-            sums[i] = (out[i].sad, out[i].sse[0], out[i].sse[1], out[i].sse[2])
-            hm[i] = out[i].has_motion
         if len(self._keep) > 64:
             self._keep = self._keep[-64:]
-        return sums, hm
+        return self._unpack(out, got.value)
 
     def run_clip(self, ref, dist):
         """Submit a clip and wait for its sums; same return as collect()."""
@@ -286,12 +309,7 @@ class Context:
             raise ValueError("ref and dist have different frame counts")
         out = (Result * n)()
         _check(self._lib.iir_run_clip(self._h, fr, fd, n, out), "iir_run_clip")
-        sums = np.zeros((n, 4), dtype=np.uint64)
-        hm = np.zeros(n, dtype=np.int32)
-        for i in range(n):
-            sums[i] = (out[i].sad, out[i].sse[0], out[i].sse[1], out[i].sse[2])
-            hm[i] = out[i].has_motion
-        return sums, hm
+        return self._unpack(out, n)
 
     def reset(self):
         _check(self._lib.iir_reset(self._h), "iir_reset")
@@ -318,16 +336,50 @@ class Context:
         return ms.value
 
 
+def _result(row, has_motion) -> Result:
+    r = Result()
+    row = [int(v) for v in row]
+    r.sad, r.sse[0], r.sse[1], r.sse[2] = row[:4]
+    for k, v in enumerate(row[4:8]):
+        r.moment[k] = v
+    r.has_motion = int(has_motion)
+    return r
+
+
 def scores(width: int, height: int, bpc: int, sums, has_motion: int) -> dict:
-    """iir_scores_of for one result: {motion, mse[3], psnr[3]}."""
+    """iir_scores_of for one result row (4 sums, or 8 with moments): {motion, mse[3], psnr[3],
+    moment[4]}."""
     lib = load_library()
     cfg = Config(width, height, bpc, IIR_CHROMA_420, 1, 0)
-    r = Result()
-    r.sad, r.sse[0], r.sse[1], r.sse[2] = (int(v) for v in sums)
-    r.has_motion = int(has_motion)
+    r = _result(sums, has_motion)
     s = Scores()
     _check(lib.iir_scores_of(ctypes.byref(cfg), ctypes.byref(r), ctypes.byref(s)), "iir_scores_of")
-    return {"motion": s.motion, "mse": list(s.mse), "psnr": list(s.psnr)}
+    return {"motion": s.motion, "mse": list(s.mse), "psnr": list(s.psnr),
+            "moment": list(s.moment)}
+
+
+def motion2(motion) -> np.ndarray:
+    """iir_motion2: each frame's second motion score from the clip's motion scores."""
+    lib = load_library()
+    m = np.ascontiguousarray(motion, dtype=np.float64)
+    out = np.empty_like(m)
+    dp = ctypes.POINTER(ctypes.c_double)
+    _check(lib.iir_motion2(m.ctypes.data_as(dp), m.size, out.ctypes.data_as(dp)), "iir_motion2")
+    return out
+
+
+def aggregate(width: int, height: int, bpc: int, sums, has_motion) -> dict:
+    """iir_aggregate_of over a clip's results: {sse[3], apsnr[3], mean_motion, mean_motion2}."""
+    lib = load_library()
+    n = len(sums)
+    cfg = Config(width, height, bpc, IIR_CHROMA_420, 1, 0)
+    arr = (Result * n)()
+    for i in range(n):
+        arr[i] = _result(sums[i], has_motion[i])
+    a = Aggregate()
+    _check(lib.iir_aggregate_of(ctypes.byref(cfg), arr, n, ctypes.byref(a)), "iir_aggregate_of")
+    return {"sse": [int(v) for v in a.sse], "apsnr": list(a.apsnr), "mean_motion": a.mean_motion,
+            "mean_motion2": a.mean_motion2}
 
 
 def probe_bandwidth(mode: int, src, dst, iters: int = 20, stream=None) -> float:

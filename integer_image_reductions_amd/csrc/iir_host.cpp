@@ -84,13 +84,15 @@ struct iir_ctx {
     int target_waves = 1024;
     int min_chunk = 4;
     int max_chunks = 1;
+    bool moments = false;  // IIR_FLAG_MOMENTS: the kernels also sum the luma moments
+    int nsums = kSums;     // 64-bit sums per frame: kSums, or kMaxSums with moments
     uint32_t *ring[2] = {nullptr, nullptr};
     int ring_cur = 0;  // ring[ring_cur] holds the blurred state of the last submitted frame
-    unsigned long long *sums = nullptr;       // device, [max_batch][kSums][kSumSlots], zero
+    unsigned long long *sums = nullptr;       // device, [max_batch][nsums][kSumSlots], zero
                                               // between launches (each launch re-zeroes it)
     unsigned int *arrivals = nullptr;         // device, finished-workgroup counter, zero
     int64_t sums_n = 0;
-    unsigned long long *host_sums = nullptr;  // pinned coherent, [max_batch][kSums] totals
+    unsigned long long *host_sums = nullptr;  // pinned coherent, [max_batch][nsums] totals
     unsigned long long *host_sums_dev = nullptr;  // the same memory as the device sees it
     FramePtrs *table_dev = nullptr;
     FramePtrs *table_host = nullptr;  // pinned, [max_batch]
@@ -142,7 +144,7 @@ int check_config(const iir_config *c)
         return fail(IIR_EINVAL, "frame size %dx%d outside 3..32768", c->width, c->height);
     if (c->max_batch < 1 || c->max_batch > 65536)
         return fail(IIR_EINVAL, "max_batch %d outside 1..65536", c->max_batch);
-    if (c->flags & ~IIR_FLAG_TIMING)
+    if (c->flags & ~(IIR_FLAG_TIMING | IIR_FLAG_MOMENTS))
         return fail(IIR_EINVAL, "unknown flags 0x%x", c->flags);
     return IIR_OK;
 }
@@ -214,7 +216,7 @@ int choose_rows(iir_ctx *c, int cus, int forced)
             continue;
         int per_cu = 0;
         const bool generic = !fast_path_ok(c->cfg.width, c->cfg.height, th);
-        if (frames_occupancy(c->cfg.bpc, th, generic, &per_cu) != hipSuccess ||
+        if (frames_occupancy(c->cfg.bpc, th, generic, c->moments, &per_cu) != hipSuccess ||
             per_cu < 1)
             continue;
         const int64_t waves = (int64_t)c->strips * ((c->cfg.height + th - 1) / th);
@@ -344,7 +346,7 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     a.ring_in = c->ring[c->ring_cur];
     a.ring_out = c->ring[c->ring_cur ^ 1];
     a.sums = c->sums;
-    a.publish = c->host_sums_dev + (size_t)first * kSums;
+    a.publish = c->host_sums_dev + (size_t)first * c->nsums;
     a.arrivals = c->arrivals;
     a.W = c->cfg.width;
     a.H = c->cfg.height;
@@ -363,8 +365,8 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     if (timing)
         HIP_TRY(hipEventRecord(sub.k0, c->stream));
     HIP_TRY(launch_frames(c->cfg.bpc, c->rows_per_tile,
-                          !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile), a,
-                          c->stream));
+                          !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile),
+                          c->moments, a, c->stream));
     // the kernel itself writes the totals to host_sums; one event marks the end (with timing,
     // the event that closes the kernel's timed interval)
     HIP_TRY(hipEventRecord(timing ? sub.k1 : sub.done, c->stream));
@@ -415,6 +417,8 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     c->bps = cfg->bpc == 8 ? 1 : 2;
     c->Wc = (cfg->width + 1) / 2;
     c->Hc = (cfg->height + 1) / 2;
+    c->moments = (cfg->flags & IIR_FLAG_MOMENTS) != 0;
+    c->nsums = c->moments ? kMaxSums : kSums;
     choose_columns(c);
     c->rows_per_tile = choose_rows(c, prop.multiProcessorCount, env_int("IIR_ROWS_PER_TILE", 0, 0, 64));
     c->row_tiles = (cfg->height + c->rows_per_tile - 1) / c->rows_per_tile;
@@ -428,7 +432,7 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
         release(c);
         return fail(IIR_EINVAL, "frame too large for one grid");
     }
-    c->sums_n = (int64_t)cfg->max_batch * kSums * kSumSlots;
+    c->sums_n = (int64_t)cfg->max_batch * c->nsums * kSumSlots;
 
     const size_t ring_bytes = (size_t)c->tiles * c->rows_per_tile * kWave * sizeof(uint2);
     hipError_t e = hipSuccess;
@@ -441,7 +445,7 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     if (e == hipSuccess)
         e = hipMalloc(&c->table_dev, sizeof(FramePtrs) * cfg->max_batch);
     if (e == hipSuccess)
-        e = hipHostMalloc(&c->host_sums, sizeof(unsigned long long) * cfg->max_batch * kSums,
+        e = hipHostMalloc(&c->host_sums, sizeof(unsigned long long) * cfg->max_batch * c->nsums,
                           hipHostMallocCoherent | hipHostMallocMapped);
     if (e == hipSuccess)
         e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->host_sums_dev), c->host_sums, 0);
@@ -514,13 +518,16 @@ IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_o
         const int take = std::min(n - got, sub.n - sub.taken);
         for (int i = 0; i < take; ++i) {
             const int f = sub.taken + i;
-            const volatile unsigned long long *v = ctx->host_sums + (size_t)(sub.first + f) * kSums;
+            const volatile unsigned long long *v =
+                ctx->host_sums + (size_t)(sub.first + f) * ctx->nsums;
             iir_result &r = out[got + i];
             r.has_motion = (f > 0 || sub.has_prev) ? 1 : 0;
             r.sad = r.has_motion ? v[0] : 0;
             r.sse[0] = v[1];
             r.sse[1] = v[2];
             r.sse[2] = v[3];
+            for (int k = 0; k < kMoments; ++k)
+                r.moment[k] = ctx->moments ? v[kSums + k] : 0;
             r.reserved = 0;
         }
         sub.taken += take;
@@ -577,6 +584,56 @@ IIR_API int iir_scores_of(const iir_config *cfg, const iir_result *r, iir_scores
         s->mse[c] = mse;
         s->psnr[c] = r->sse[c] == 0 ? INFINITY : 10.0 * std::log10(peak * peak / mse);
     }
+    for (int k = 0; k < 4; ++k)
+        s->moment[k] = (double)r->moment[k] / n_luma;
+    return IIR_OK;
+}
+
+IIR_API int iir_motion2(const double *motion, int32_t n, double *motion2)
+{
+    if (!motion || !motion2 || n < 1)
+        return fail(IIR_EINVAL, "motion2 needs two non-NULL arrays and n >= 1");
+    // in place is allowed: frame t reads motion[t + 1] before anything overwrites it
+    for (int32_t t = 0; t < n; ++t) {
+        const double own = motion[t];
+        const double next = t + 1 < n ? motion[t + 1] : own;
+        motion2[t] = std::min(own, next);
+    }
+    return IIR_OK;
+}
+
+IIR_API int iir_aggregate_of(const iir_config *cfg, const iir_result *r, int32_t n,
+                             iir_aggregate *out)
+{
+    if (!cfg || !r || !out || n < 1)
+        return fail(IIR_EINVAL, "aggregate needs a config, n >= 1 results and an output");
+    if ((cfg->bpc != 8 && cfg->bpc != 10) || cfg->width < 1 || cfg->height < 1)
+        return fail(IIR_EINVAL, "bad configuration");
+    const double n_luma = (double)cfg->width * (double)cfg->height;
+    const double n_chroma = (double)((cfg->width + 1) / 2) * (double)((cfg->height + 1) / 2);
+    const double peak = (double)((1 << cfg->bpc) - 1);
+    uint64_t total[3] = {0, 0, 0};
+    double sum_motion = 0.0, sum_motion2 = 0.0;
+    double prev = 0.0;  // motion of frame t - 1 while frame t is read
+    for (int32_t t = 0; t < n; ++t) {
+        const double m = r[t].has_motion ? (double)r[t].sad / (256.0 * n_luma) : 0.0;
+        for (int c = 0; c < 3; ++c)
+            total[c] += r[t].sse[c];
+        sum_motion += m;
+        if (t > 0)
+            sum_motion2 += std::min(prev, m);  // motion2 of frame t - 1
+        prev = m;
+    }
+    sum_motion2 += prev;  // the last frame keeps its own motion
+    for (int c = 0; c < 3; ++c) {
+        out->sse[c] = total[c];
+        const double mse = (double)total[c] / ((double)n * (c == 0 ? n_luma : n_chroma));
+        out->apsnr[c] = total[c] == 0 ? INFINITY : 10.0 * std::log10(peak * peak / mse);
+    }
+    out->mean_motion = sum_motion / (double)n;
+    out->mean_motion2 = sum_motion2 / (double)n;
+    out->frames = n;
+    out->reserved = 0;
     return IIR_OK;
 }
 

@@ -13,6 +13,8 @@ namespace iir {
 constexpr int kWave = 64;          // CDNA wavefront; one wavefront is one workgroup
 constexpr int kSumSlots = 8;       // partial slots per sum (one per XCD), added up on the host
 constexpr int kSums = 4;           // SAD, SSE_Y, SSE_U, SSE_V
+constexpr int kMoments = 4;        // optional: sum ref Y, sum dist Y, sum ref Y^2, sum dist Y^2
+constexpr int kMaxSums = kSums + kMoments;
 constexpr int kLumaCols = 4;       // luma columns per lane
 constexpr int kStripCols = kWave * kLumaCols;  // luma columns per tile (one per 4 per lane)
 
@@ -34,10 +36,11 @@ struct KernelArgs {
     // launch's rows per tile
     const uint32_t *ring_in;
     uint32_t *ring_out;
-    // per-frame partial sums [nframes][kSums][kSumSlots], zero at launch; the launch's last
-    // workgroup folds the slots, writes the totals to `publish` and zeroes them again
+    // per-frame partial sums [nframes][S][kSumSlots], S = kSums, or kMaxSums when the launch
+    // also sums the luma moments; zero at launch; the launch's last workgroup folds the slots,
+    // writes the totals to `publish` and zeroes them again
     unsigned long long *sums;
-    // host-visible [nframes][kSums] totals of this launch (pinned host memory)
+    // host-visible [nframes][S] totals of this launch (pinned host memory)
     unsigned long long *publish;
     // workgroups of this launch that have finished, zero at launch (the last one resets it)
     unsigned int *arrivals;
@@ -50,8 +53,10 @@ struct KernelArgs {
 // Host-side launchers (iir_kernels.hip). Each returns the launch's hipError_t.
 bool supported_rows_per_tile(int th);           // 12, 16 or 20
 bool fast_path_ok(int W, int H, int th);         // the uniform fast path applies
-hipError_t frames_occupancy(int bpc, int th, bool generic, int *waves_per_cu);
-hipError_t launch_frames(int bpc, int th, bool generic, const KernelArgs &a, hipStream_t stream);
+// `moments`: the launch also sums the luma moments (S = kMaxSums)
+hipError_t frames_occupancy(int bpc, int th, bool generic, bool moments, int *waves_per_cu);
+hipError_t launch_frames(int bpc, int th, bool generic, bool moments, const KernelArgs &a,
+                         hipStream_t stream);
 hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
                          int strips, int th, hipStream_t stream);
 hipError_t launch_probe(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream);

@@ -161,24 +161,26 @@ __device__ __forceinline__ void add_sum(unsigned long long *p, unsigned long lon
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Per-frame wavefront sums waiting for their atomics. Lane q of v[] holds queued frame q's four
-// 64-bit sums (low and high halves); a flush issues every queued
-// frame's atomics at once, one frame per lane. On gfx9 stores and atomics share the in-order
+// Per-frame wavefront sums waiting for their atomics. Lane q of v[] holds queued frame q's NS
+// 64-bit sums (low and high halves); a flush issues every queued frame's atomics at once, one
+// frame per lane. On gfx9 stores and atomics share the in-order
 // vmcnt counter with loads, so an atomic issued right after a frame would make the next frame's
 // first load wait for the atomic's round trip; batching keeps them off the frame loop.
+template <int NS>
 struct Pending {
-    uint32_t v[2 * kSums];
+    uint32_t v[2 * NS];
     int first;  // frame of queue slot 0 (wave-uniform)
     int count;  // queued frames (wave-uniform)
 };
 
-__device__ __forceinline__ void flush_sums(const KernelArgs &a, Pending &P, int lane)
+template <int NS>
+__device__ __forceinline__ void flush_sums(const KernelArgs &a, Pending<NS> &P, int lane)
 {
     if (lane < P.count) {
-        unsigned long long *o = a.sums + (size_t)(P.first + lane) * (kSums * kSumSlots) +
+        unsigned long long *o = a.sums + (size_t)(P.first + lane) * (NS * kSumSlots) +
                                 (blockIdx.x & (kSumSlots - 1));
 #pragma unroll
-        for (int k = 0; k < kSums; ++k)
+        for (int k = 0; k < NS; ++k)
             add_sum(o + k * kSumSlots,
                     ((unsigned long long)P.v[2 * k + 1] << 32) | (unsigned long long)P.v[2 * k]);
     }
@@ -186,12 +188,13 @@ __device__ __forceinline__ void flush_sums(const KernelArgs &a, Pending &P, int 
     P.count = 0;
 }
 
-__device__ __forceinline__ void push_sums(const KernelArgs &a, Pending &P, int lane,
-                                          const unsigned long long (&s)[kSums])
+template <int NS>
+__device__ __forceinline__ void push_sums(const KernelArgs &a, Pending<NS> &P, int lane,
+                                          const unsigned long long (&s)[NS])
 {
     const bool mine = lane == P.count;
 #pragma unroll
-    for (int k = 0; k < kSums; ++k) {
+    for (int k = 0; k < NS; ++k) {
         P.v[2 * k] = mine ? (uint32_t)s[k] : P.v[2 * k];
         P.v[2 * k + 1] = mine ? (uint32_t)(s[k] >> 32) : P.v[2 * k + 1];
     }
@@ -322,6 +325,29 @@ __device__ __forceinline__ void sse_chroma(uint32_t r, uint32_t d, uint32_t &s, 
         s2 = dot4u(r, d, s2);
     } else {
         s = sqdiff2(r, d, s);
+    }
+}
+
+// Luma moments of one sample group: m1 += samples, m2 += squares, for ref (r) and dist (d), and
+// the cross term x += r . d, from which the squared error is m2r + m2d - 2x (8-bit). At 10 bits
+// the squared error keeps its own difference-square sum in x.
+template <int BPC>
+__device__ __forceinline__ void moments_luma(typename Px<BPC>::Luma r, typename Px<BPC>::Luma d,
+                                             uint32_t &m1r, uint32_t &m1d, uint32_t &m2r,
+                                             uint32_t &m2d, uint32_t &x)
+{
+    if constexpr (BPC == 8) {
+        m1r = dot4u(r, 0x01010101u, m1r);
+        m1d = dot4u(d, 0x01010101u, m1d);
+        m2r = dot4u(r, r, m2r);
+        m2d = dot4u(d, d, m2d);
+        x = dot4u(r, d, x);
+    } else {
+        m1r = dot2u(r.y, 0x00010001u, dot2u(r.x, 0x00010001u, m1r));
+        m1d = dot2u(d.y, 0x00010001u, dot2u(d.x, 0x00010001u, m1d));
+        m2r = dot2u(r.y, r.y, dot2u(r.x, r.x, m2r));
+        m2d = dot2u(d.y, d.y, dot2u(d.x, d.x, m2d));
+        x = sqdiff2(r.y, d.y, sqdiff2(r.x, d.x, x));
     }
 }
 
@@ -595,14 +621,15 @@ __device__ __forceinline__ uint32_t halo_vertical(u32x2 h, uint32_t hsel)
 // column and row, horizontal taps through DPP neighbours), SAD against the previous blurred tile
 // held in registers, SSE of the luma and chroma tiles, one wavefront reduction and one atomic per
 // sum. GENERIC adds the frame-edge mirror fix-ups, ragged rows and masked tails; interior tiles
-// (the vast majority) run without any of it.
-template <int BPC, int TH, bool GENERIC, bool ROWSTAGE>
+// (the vast majority) run without any of it. MOM also sums the luma moments of ref and dist.
+template <int BPC, int TH, bool GENERIC, bool ROWSTAGE, bool MOM>
 __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T, int t,
                                               bool accumulate, FrameData<BPC, TH> &F,
                                               const uint32_t (&prev0)[TH],
                                               const uint32_t (&prev1)[TH], uint32_t (&next0)[TH],
                                               uint32_t (&next1)[TH], uint32_t &sum_prev,
-                                              bool &have_prev, Pending &P)
+                                              bool &have_prev,
+                                              Pending<MOM ? kMaxSums : kSums> &P)
 {
     typedef typename Px<BPC>::Luma Luma;
     typedef FrameData<BPC, TH> FD;
@@ -636,6 +663,7 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 
     // blur, SAD against the previous blurred tile, and SSE of the luma rows as they go by
     uint32_t acc_c = 0, acc_min = 0, sy = 0, sy2 = 0;
+    uint32_t m1r = 0, m1d = 0, m2r = 0, m2d = 0;
 #pragma unroll
     for (int i = 0; i < TH; ++i) {
         uint32_t pa[4], pb[4], pc[4];
@@ -691,7 +719,10 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
                     r = masked<BPC>(r, T.ym0, T.ym1);
                     d = masked<BPC>(d, T.ym0, T.ym1);
                 }
-                sse_luma<BPC>(r, d, sy, sy2);
+                if constexpr (MOM)
+                    moments_luma<BPC>(r, d, m1r, m1d, m2r, m2d, sy2);
+                else
+                    sse_luma<BPC>(r, d, sy, sy2);
             }
         }
         next0[i] = c0;
@@ -700,11 +731,31 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 
     if (accumulate) {
         const uint32_t sad = have_prev ? acc_c + sum_prev - 2u * acc_min : 0u;
-        const unsigned long long sums[kSums] = {wave_sum(sad),
-                                                wave_sum(T.out_lane ? sy - 2u * sy2 : 0u),
-                                                wave_sum(T.c_on ? su - 2u * su2 : 0u),
-                                                wave_sum(T.c_on ? sv - 2u * sv2 : 0u)};
-        push_sums(a, P, T.lane, sums);
+        // squared luma error: 8-bit sy + sy2 hold sum r^2 + d^2 and sum r d; with moments the
+        // squares are apart (m2r, m2d); 10-bit keeps the difference squares in sy (sy2 with MOM)
+        uint32_t ey;
+        if constexpr (BPC == 8)
+            ey = (MOM ? m2r + m2d : sy) - 2u * sy2;
+        else
+            ey = MOM ? sy2 : sy;
+        if constexpr (MOM) {
+            const unsigned long long sums[kMaxSums] = {
+                wave_sum(sad),
+                wave_sum(T.out_lane ? ey : 0u),
+                wave_sum(T.c_on ? su - 2u * su2 : 0u),
+                wave_sum(T.c_on ? sv - 2u * sv2 : 0u),
+                wave_sum(T.out_lane ? m1r : 0u),
+                wave_sum(T.out_lane ? m1d : 0u),
+                wave_sum(T.out_lane ? m2r : 0u),
+                wave_sum(T.out_lane ? m2d : 0u)};
+            push_sums(a, P, T.lane, sums);
+        } else {
+            const unsigned long long sums[kSums] = {wave_sum(sad),
+                                                    wave_sum(T.out_lane ? ey : 0u),
+                                                    wave_sum(T.c_on ? su - 2u * su2 : 0u),
+                                                    wave_sum(T.c_on ? sv - 2u * sv2 : 0u)};
+            push_sums(a, P, T.lane, sums);
+        }
     }
     sum_prev = acc_c;
     have_prev = true;
@@ -715,7 +766,7 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 // computed: the loads of frame t+1 write the wave's LDS stage (no registers held), issued as soon
 // as frame t has been read out of it. Frames go in pairs that swap the roles of two blurred-tile
 // register sets (prev -> alt -> prev), so no frame ends by copying its blurred tile back.
-template <int BPC, int TH, bool GENERIC, bool STAGED>
+template <int BPC, int TH, bool GENERIC, bool STAGED, bool MOM>
 __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
                                            const StageOffsets<TH> &O, uint32_t (&prev0)[TH],
                                            uint32_t (&prev1)[TH], uint32_t sum_prev,
@@ -724,9 +775,10 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
     const int f_begin = uni(T.chunk * a.chunk_len);
     const int f_end = uni(min(f_begin + a.chunk_len, a.nframes));
     const int t0 = T.chunk > 0 ? f_begin - 1 : f_begin;
-    Pending P;
+    constexpr int NS = MOM ? kMaxSums : kSums;
+    Pending<NS> P;
 #pragma unroll
-    for (int k = 0; k < 2 * kSums; ++k)
+    for (int k = 0; k < 2 * NS; ++k)
         P.v[k] = 0;
     P.first = f_begin;
     P.count = 0;
@@ -751,8 +803,8 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
         } else {
             load_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F);
         }
-        compute_frame<BPC, TH, GENERIC, STAGED>(a, T, t, t >= f_begin, F, i0, i1, o0, o1,
-                                                sum_prev, have_prev, P);
+        compute_frame<BPC, TH, GENERIC, STAGED, MOM>(a, T, t, t >= f_begin, F, i0, i1, o0, o1,
+                                                     sum_prev, have_prev, P);
     };
     uint32_t alt0[TH], alt1[TH];
     for (int t = t0; t < f_end; t += 2) {
@@ -771,13 +823,14 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
 }
 
 // The launch's last workgroup to finish (counted with one device-scope atomic per workgroup)
-// folds the kSumSlots partial sums of every frame, writes the totals straight to the
+// folds the kSumSlots partial sums of each of the NS sums of every frame, writes the totals straight to the
 // caller-visible pinned buffer and zeroes the partial sums and the counter for the next launch.
 // No workgroup waits for another, and no separate readback copy follows the kernel. Ordering:
 // the sum atomics are device-scope read-modify-writes; each workgroup waits until its own have
 // completed (vmcnt(0)) before counting itself, and the last one reads them back with
 // device-scope atomic loads after an acquire fence. A release fence per workgroup would write
 // back every XCD's L2 once per workgroup, which costs far more than the copy it replaces.
+template <int NS>
 __device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane)
 {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this workgroup's sum atomics completed
@@ -792,7 +845,7 @@ __device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane)
     // kPer totals per lane per pass, all of their slot loads issued before any is added, so a
     // pass costs one memory round trip (a 64-frame launch is one pass)
     constexpr int kPer = 4;
-    const int n = a.nframes * kSums;
+    const int n = a.nframes * NS;
     for (int base = 0; base < n; base += kPer * kWave) {
         unsigned long long v[kPer][kSumSlots];
 #pragma unroll
@@ -824,7 +877,7 @@ __device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane)
     // the end of the kernel releases these stores to the host before its completion signal
 }
 
-template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE>
+template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE, bool MOM>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void
 frames_kernel(const KernelArgs a)
 {
@@ -999,10 +1052,10 @@ frames_kernel(const KernelArgs a)
                           (uint32_t)(lane >> 3) * (uint32_t)a.pitch[pk[p]];
     }
 
-    frame_loop<BPC, TH, GENERIC, STAGED>(a, T, O, prev0, prev1, sum_prev, have_prev, stage);
+    frame_loop<BPC, TH, GENERIC, STAGED, MOM>(a, T, O, prev0, prev1, sum_prev, have_prev, stage);
 
     // counted before the state write, so the count waits only for this workgroup's sum atomics
-    publish_if_last(a, lane);
+    publish_if_last<MOM ? kMaxSums : kSums>(a, lane);
 
     if (T.chunk == a.chunks - 1) {
         uint2 *rout = reinterpret_cast<uint2 *>(a.ring_out);
@@ -1086,34 +1139,40 @@ typedef void (*FramesFn)(KernelArgs);
 
 // Every (bit depth, tile height, path) the host may pick. The fast path needs W % 8 == 0 and
 // H % TH == 0 (no ragged tile, no partial sample group); the generic path takes any size.
-template <int BPC, bool GENERIC>
+template <int BPC, bool GENERIC, bool MOM>
 FramesFn frames_fn(int th)
 {
     constexpr bool P = BPC == 8 ? IIR_STAGE8 : IIR_STAGE10;
     switch (th) {
     case 12:
-        return frames_kernel<BPC, 12, P, GENERIC, IIR_WPE12>;
+        return frames_kernel<BPC, 12, P, GENERIC, IIR_WPE12, MOM>;
     case 16:
-        return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16>;
+        return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16, MOM>;
     case 20:
-        return frames_kernel<BPC, 20, P, GENERIC, IIR_WPE20>;
+        return frames_kernel<BPC, 20, P, GENERIC, IIR_WPE20, MOM>;
     default:
         return nullptr;
     }
 }
 
-FramesFn pick(int bpc, int th, bool generic)
+template <bool MOM>
+FramesFn pick_depth(int bpc, int th, bool generic)
 {
     if (bpc == 8)
-        return generic ? frames_fn<8, true>(th) : frames_fn<8, false>(th);
-    return generic ? frames_fn<10, true>(th) : frames_fn<10, false>(th);
+        return generic ? frames_fn<8, true, MOM>(th) : frames_fn<8, false, MOM>(th);
+    return generic ? frames_fn<10, true, MOM>(th) : frames_fn<10, false, MOM>(th);
+}
+
+FramesFn pick(int bpc, int th, bool generic, bool moments)
+{
+    return moments ? pick_depth<true>(bpc, th, generic) : pick_depth<false>(bpc, th, generic);
 }
 
 }  // namespace
 
 bool supported_rows_per_tile(int th)
 {
-    return pick(8, th, true) != nullptr;
+    return pick(8, th, true, false) != nullptr;
 }
 
 bool fast_path_ok(int W, int H, int th)
@@ -1121,9 +1180,9 @@ bool fast_path_ok(int W, int H, int th)
     return W % 8 == 0 && H % th == 0;
 }
 
-hipError_t frames_occupancy(int bpc, int th, bool generic, int *waves_per_cu)
+hipError_t frames_occupancy(int bpc, int th, bool generic, bool moments, int *waves_per_cu)
 {
-    FramesFn f = pick(bpc, th, generic);
+    FramesFn f = pick(bpc, th, generic, moments);
     if (!f)
         return hipErrorInvalidValue;
     int blocks = 0;
@@ -1133,9 +1192,10 @@ hipError_t frames_occupancy(int bpc, int th, bool generic, int *waves_per_cu)
     return e;
 }
 
-hipError_t launch_frames(int bpc, int th, bool generic, const KernelArgs &a, hipStream_t stream)
+hipError_t launch_frames(int bpc, int th, bool generic, bool moments, const KernelArgs &a,
+                         hipStream_t stream)
 {
-    FramesFn f = pick(bpc, th, generic);
+    FramesFn f = pick(bpc, th, generic, moments);
     if (!f)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(f, dim3((unsigned)(a.tiles * a.chunks)), dim3(kWave), 0, stream, a);

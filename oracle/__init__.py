@@ -9,12 +9,15 @@ from .oracle import (  # noqa: F401
     SOURCE,
     OracleError,
     OracleLib,
+    aggregate,
     blur,
     build,
     clip,
     compile_source,
     default,
     library_path,
+    moments,
+    motion2,
     sad,
     scores,
     sse,

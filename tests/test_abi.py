@@ -121,3 +121,59 @@ def test_scores_match_oracle(bpc):
             for c in range(3):
                 assert _close(a["mse"][c], b["mse"][c])
                 assert _close(a["psnr"][c], b["psnr"][c])
+
+
+def test_clip_functions_reject(lib):
+    dp = ctypes.POINTER(ctypes.c_double)
+    m = (ctypes.c_double * 2)()
+    assert lib.iir_motion2(None, 2, m) == B.IIR_EINVAL
+    assert lib.iir_motion2(m, 0, m) == B.IIR_EINVAL
+    assert lib.iir_motion2(ctypes.cast(m, dp), 2, None) == B.IIR_EINVAL
+    cfg = B.Config(8, 8, 8, 420, 1, 0)
+    r, a = (B.Result * 1)(), B.Aggregate()
+    assert lib.iir_aggregate_of(None, r, 1, ctypes.byref(a)) == B.IIR_EINVAL
+    assert lib.iir_aggregate_of(ctypes.byref(cfg), r, 0, ctypes.byref(a)) == B.IIR_EINVAL
+    assert lib.iir_aggregate_of(ctypes.byref(cfg), r, 1, None) == B.IIR_EINVAL
+    bad = B.Config(8, 8, 9, 420, 1, 0)
+    assert lib.iir_aggregate_of(ctypes.byref(bad), r, 1, ctypes.byref(a)) == B.IIR_EINVAL
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 17, 300])
+def test_motion2_matches_oracle(n):
+    """The library's motion2 equals the oracle's exactly (min is exact), ties and zeros included."""
+    r = np.random.default_rng(n)
+    m = r.random(n) * 20.0
+    m[r.random(n) < 0.3] = 0.0
+    if n > 3:
+        m[2] = m[3]
+    assert np.array_equal(iir.motion2(m), oracle.motion2(m))
+
+
+@pytest.mark.parametrize("bpc", [8, 10])
+@pytest.mark.parametrize("n", [1, 2, 5, 64])
+def test_aggregate_matches_oracle(bpc, n):
+    """Clip aggregates: totals exact, apsnr and the motion means within 1e-12 relative of the
+    oracle, also with a plane whose error is zero on every frame (+infinity)."""
+    r = np.random.default_rng(100 * bpc + n)
+    for w, h in ((3840, 2160), (576, 324), (5, 3)):
+        sums = r.integers(0, 2 ** 40, size=(n, 4)).astype(np.uint64)
+        hm = np.ones(n, np.int32)
+        hm[0] = int(r.integers(0, 2))
+        if n > 1:
+            sums[:, 2] = 0
+        a = iir.aggregate(w, h, bpc, sums, hm)
+        b = oracle.aggregate(w, h, bpc, sums, hm)
+        assert a["sse"] == [int(sums[:, c + 1].sum()) for c in range(3)]
+        for c in range(3):
+            assert _close(a["apsnr"][c], b["apsnr"][c])
+        assert _close(a["mean_motion"], b["mean_motion"])
+        assert _close(a["mean_motion2"], b["mean_motion2"])
+
+
+def test_scores_moments():
+    """moment[k] of the scores is the k-th luma moment sum over W * H samples."""
+    w, h = 37, 19
+    row = [5, 1, 2, 3, 4 * w * h, 7 * w * h, 16 * w * h, 49 * w * h]
+    s = iir.scores(w, h, 8, row, 1)
+    assert s["moment"] == [4.0, 7.0, 16.0, 49.0]
+    assert iir.scores(w, h, 8, row[:4], 1)["moment"] == [0.0, 0.0, 0.0, 0.0]

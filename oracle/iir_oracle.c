@@ -39,9 +39,10 @@
  * (tap values, rounding, mirror) are not fixed by the pages: agreement with the pages on those is
  * parity unpinned; the pins fix that this file computes exactly what the readings say.
  *
- * Planes: 4:2:0, luma W x H, chroma ceil(W/2) x ceil(H/2). 8-bit samples are uint8, 10-bit samples
- * are little-endian uint16 in [0, 1023]. Every function returns 0 on success and a negative value
- * on bad arguments or on a sample outside [0, 2^bpc - 1].
+ * Planes: 4:2:0, luma W x H, chroma ceil(W/2) x ceil(H/2). 8-bit samples are uint8; 9- to 16-bit
+ * samples are little-endian uint16 in [0, 2^bpc - 1] ("ADR-1392", Consequences checks the outputs
+ * at 8, 10 and 16 bits). Every function returns 0 on success and a negative value on bad
+ * arguments or on a sample outside [0, 2^bpc - 1].
  */
 #include <math.h>
 #include <stdint.h>
@@ -101,7 +102,7 @@ static int check_range(const void *plane, int64_t pitch, int32_t w, int32_t h, i
 
 static int bad_dims(int32_t w, int32_t h, int32_t bpc)
 {
-    return (bpc != 8 && bpc != 10) || w < 1 || h < 1;
+    return bpc < 8 || bpc > 16 || w < 1 || h < 1;
 }
 
 /* Sum of squared differences of one plane. */

@@ -61,9 +61,9 @@ def _check(rc: int, what: str):
 def _dtype(bpc: int):
     if bpc == 8:
         return np.uint8
-    if bpc == 10:
+    if 9 <= bpc <= 16:
         return np.uint16
-    raise OracleError(f"bpc must be 8 or 10, got {bpc}")
+    raise OracleError(f"bpc must be 8 to 16, got {bpc}")
 
 
 def _plane(a: np.ndarray, bpc: int) -> np.ndarray:

@@ -18,6 +18,7 @@ import numpy as np
 import scipy.ndimage as ndi
 
 TAPS = (3571, 16004, 26386, 16004, 3571)
+DEPTHS = (8, 10, 12, 16)  # every storage path: uint8, and uint16 at 10, 12 and the full 16 bits
 SIZES = [(3, 3), (4, 7), (9, 5), (17, 23), (32, 32), (5, 64), (70, 3)]
 
 
@@ -79,7 +80,7 @@ def pin_taps(o):
 
 
 def pin_blur_brute_force(o):
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         for i, x in enumerate(_planes(bpc, 11 + bpc)):
             got, want = o.blur(x, bpc), brute_force_blur(x, bpc)
             assert np.array_equal(got, want), (bpc, i, x.shape)
@@ -93,14 +94,14 @@ def pin_blur_brute_force_large(o):
 
 
 def pin_blur_scipy(o):
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         for i, x in enumerate(_planes(bpc, 23 + bpc)):
             assert np.array_equal(o.blur(x, bpc), scipy_blur(x, bpc)), (bpc, i, x.shape)
 
 
 def pin_blur_constant(o):
     """A flat plane stays flat, scaled to 16 bits: c * 2^(16 - bpc)."""
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         for c in (0, 1, 77, (1 << bpc) - 1):
             for h, w in ((3, 3), (6, 16), (11, 4)):
                 x = np.full((h, w), c, dtype=np.uint8 if bpc == 8 else np.uint16)
@@ -152,7 +153,7 @@ def pin_blur_step(o):
 def pin_blur_mirror_edges(o):
     """A step placed one column from the left edge: the mirror makes column -1 equal column 1, so
     output column 0 sees (x1, x1... ) = the mirrored neighbours, which differs from clamping."""
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         peak = (1 << bpc) - 1
         x = np.zeros((5, 8), dtype=np.uint8 if bpc == 8 else np.uint16)
         x[:, 1] = peak  # column 1 bright: mirrored into column -1
@@ -168,7 +169,7 @@ def pin_blur_mirror_edges(o):
 
 
 def pin_blur_flip(o):
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         for x in _planes(bpc, 41 + bpc):
             b = o.blur(x, bpc)
             assert np.array_equal(o.blur(np.ascontiguousarray(x[::-1]), bpc), b[::-1])
@@ -177,7 +178,7 @@ def pin_blur_flip(o):
 
 def pin_blur_range_and_linearity(o):
     r = _rng(3)
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         peak = (1 << bpc) - 1
         dt = np.uint8 if bpc == 8 else np.uint16
         for h, w in ((3, 3), (12, 19), (40, 7)):
@@ -190,15 +191,20 @@ def pin_blur_range_and_linearity(o):
 
 
 def pin_blur_bit_depth(o):
-    """10-bit blur of 4x equals the 8-bit blur of x: floor((4a + 512)/1024) = floor((a + 128)/256)."""
+    """The blur of x * 2^(bpc - 8) at bpc bits equals the 8-bit blur of x: the vertical sum and its
+    rounding term both scale by 2^(bpc - 8), so floor((s a + s 128) / (s 256)) = floor((a + 128) /
+    256) with s = 2^(bpc - 8); the horizontal pass then sees the same values."""
     for x in _planes(8, 59):
-        assert np.array_equal(o.blur((x.astype(np.uint16) * 4), 10), o.blur(x, 8))
+        b8 = o.blur(x, 8)
+        for bpc in (9, 10, 12, 16):
+            xs = x.astype(np.uint16) << (bpc - 8)
+            assert np.array_equal(o.blur(xs, bpc), b8), bpc
 
 
 def pin_blur_error_bound(o):
     """The integer result is within 1 of the exact real-valued 2-D filter scaled to 16 bits."""
     g = np.array(TAPS, dtype=np.float64) / 65536.0
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         for x in _planes(bpc, 61 + bpc):
             h, w = x.shape
             xp = np.pad(x.astype(np.float64), 2, mode="reflect")
@@ -225,7 +231,7 @@ def pin_blur_translation(o):
 
 def pin_sse_brute_force(o):
     r = _rng(13)
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         peak = (1 << bpc) - 1
         dt = np.uint8 if bpc == 8 else np.uint16
         for h, w in SIZES + [(1, 1), (1, 9), (8, 1)]:
@@ -237,8 +243,22 @@ def pin_sse_brute_force(o):
             assert o.sse(a, a, bpc) == 0
 
 
+def pin_sse_bit_depth(o):
+    """Scaling both planes by 2^(bpc - 8) scales the squared error by 4^(bpc - 8); at 16 bits a
+    full-scale difference squares to 65535^2, which needs more than 32 bits once two are added."""
+    r = _rng(19)
+    a = r.integers(0, 256, size=(9, 14)).astype(np.uint8)
+    b = r.integers(0, 256, size=(9, 14)).astype(np.uint8)
+    e8 = o.sse(a, b, 8)
+    for bpc in (10, 12, 16):
+        s = 1 << (bpc - 8)
+        assert o.sse(a.astype(np.uint16) * s, b.astype(np.uint16) * s, bpc) == e8 * s * s, bpc
+    full = np.full((2, 3), 65535, dtype=np.uint16)
+    assert o.sse(full, np.zeros_like(full), 16) == 6 * 65535 ** 2
+
+
 def pin_sse_constant(o):
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         dt = np.uint8 if bpc == 8 else np.uint16
         a = np.full((6, 16), 100, dtype=dt)
         b = np.full((6, 16), 103, dtype=dt)
@@ -272,7 +292,8 @@ def _tiny_clip(bpc, f, h, w, seed):
 
 def pin_clip_composition(o):
     """Per frame: SSE of each plane by brute force, SAD of brute-force blurs of consecutive frames."""
-    for bpc, (f, h, w) in ((8, (4, 7, 9)), (10, (3, 5, 6)), (8, (3, 3, 3)), (8, (2, 11, 4))):
+    for bpc, (f, h, w) in ((8, (4, 7, 9)), (10, (3, 5, 6)), (8, (3, 3, 3)), (8, (2, 11, 4)),
+                           (12, (3, 6, 5)), (16, (3, 5, 7))):
         ref, dist = _tiny_clip(bpc, f, h, w, 100 + h)
         sums, hm = o.clip(ref, dist, bpc)
         assert list(hm) == [0] + [1] * (f - 1)
@@ -300,7 +321,7 @@ def pin_clip_split(o):
 
 def pin_clip_constant_motion(o):
     """Constant frames c then c + d: SAD = N |d| 2^(16 - bpc), so motion = |d| (8-bit units)."""
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         dt = np.uint8 if bpc == 8 else np.uint16
         h, w = 6, 16
         hc, wc = 3, 8
@@ -316,7 +337,7 @@ def pin_clip_constant_motion(o):
 
 def pin_scores(o):
     """PSNR of a constant difference d is 10 log10(peak^2 / d^2); zero error gives +inf."""
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         peak = (1 << bpc) - 1
         w, h = 8, 6
         n, nc = 48, 12
@@ -336,13 +357,14 @@ def pin_scores(o):
 
 
 def pin_rejects_out_of_range(o):
-    x = np.full((4, 4), 1024, dtype=np.uint16)
-    try:
-        o.blur(x, 10)
-    except Exception:
-        pass
-    else:
-        raise AssertionError("a 10-bit sample of 1024 was accepted")
+    for bpc in (10, 12):
+        x = np.full((4, 4), 1 << bpc, dtype=np.uint16)
+        try:
+            o.blur(x, bpc)
+        except Exception:
+            pass
+        else:
+            raise AssertionError(f"a {bpc}-bit sample of {1 << bpc} was accepted")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -351,7 +373,7 @@ def pin_rejects_out_of_range(o):
 
 def pin_moments_brute_force(o):
     """sum x and sum x^2 against Python integers over random, checkerboard and 0/max planes."""
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         for i, x in enumerate(_planes(bpc, 41 + bpc)):
             v = [int(a) for a in x.reshape(-1)]
             assert o.moments(x, bpc) == (sum(v), sum(a * a for a in v)), (bpc, i, x.shape)
@@ -359,13 +381,14 @@ def pin_moments_brute_force(o):
 
 def pin_moments_closed_form(o):
     """A flat plane of value c: N c and N c^2; a bit-depth step (x4) scales them by 4 and 16."""
-    for bpc in (8, 10):
+    for bpc in DEPTHS:
         for c in (0, 1, 200, (1 << bpc) - 1):
             x = np.full((7, 9), c, dtype=np.uint8 if bpc == 8 else np.uint16)
             assert o.moments(x, bpc) == (63 * c, 63 * c * c), (bpc, c)
     x = _rng(4).integers(0, 256, size=(13, 17)).astype(np.uint8)
     s1, s2 = o.moments(x, 8)
     assert o.moments((x.astype(np.uint16) * 4), 10) == (4 * s1, 16 * s2)
+    assert o.moments((x.astype(np.uint16) * 256), 16) == (256 * s1, 65536 * s2)
 
 
 def pin_motion2_properties(o):

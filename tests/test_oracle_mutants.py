@@ -47,6 +47,10 @@ MUTANTS = [
      "const double mse = (double)total[c] / npx[c];"),
     ("apsnr_peak_not_squared", "const double peak_sq = peak * peak;", "const double peak_sq = peak;"),
     ("mean_motion_skips_first", "m1 += motion[t];", "m1 += t ? motion[t] : motion[1 % n];"),
+    ("sample_signed_16", "uint16_t v;\n    memcpy", "int16_t v;\n    memcpy"),
+    ("sse_32bit_total", "    uint64_t s = 0;\n    for (int64_t i = 0; i < h; ++i)\n        for (int64_t j = 0; j < w; ++j) {\n            int64_t d",
+     "    uint32_t s = 0;\n    for (int64_t i = 0; i < h; ++i)\n        for (int64_t j = 0; j < w; ++j) {\n            int64_t d"),
+    ("moments_32bit_squares", "uint64_t s1 = 0, s2 = 0;", "uint64_t s1 = 0; uint32_t s2 = 0;"),
 ]
 
 

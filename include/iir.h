@@ -1,7 +1,7 @@
 /*
  * iir.h -- C ABI of the integer motion + PSNR library for AMD MI355X (gfx950).
  *
- * Per frame pair of an 8- or 10-bit planar 4:2:0 video, the library returns four exact 64-bit sums:
+ * Per frame pair of an 8- to 16-bit planar 4:2:0 video, the library returns four exact 64-bit sums:
  *
  *   SAD     sum over the luma plane of |Bl_t - Bl_(t-1)|, where Bl is the reference luma after a
  *           5-tap separable fixed-point Gaussian blur with mirrored edges: the vertical pass is
@@ -66,7 +66,8 @@ enum {
 
 /*
  * One plane of one frame. data is a DEVICE pointer, pitch is the distance between rows in bytes.
- * Samples are uint8 (bpc 8) or little-endian uint16 holding 0..1023 (bpc 10). data and pitch must
+ * Samples are uint8 (bpc 8) or little-endian uint16 holding 0..2^bpc - 1 (bpc 9 to 16; the pages
+ * check their outputs at 8, 10 and 16 bits, "ADR-1392", Consequences). data and pitch must
  * both be multiples of 16 bytes, pitch >= width * bytes-per-sample, and height * pitch < 2^32.
  * The whole height * pitch bytes must be readable device memory (the kernels load whole 16-byte
  * aligned groups, which may reach past the last column of a row up to its pitch; those bytes never
@@ -88,7 +89,7 @@ typedef struct iir_frame {
 typedef struct iir_config {
     int32_t width;     /* luma width, >= 3 and <= 32768 */
     int32_t height;    /* luma height, >= 3 and <= 32768 */
-    int32_t bpc;       /* 8 or 10 */
+    int32_t bpc;       /* bit depth, 8 to 16 */
     int32_t chroma;    /* IIR_CHROMA_420 */
     int32_t max_batch; /* max frames uncollected at once, over at most 64 pending submissions */
     uint32_t flags;    /* IIR_FLAG_* */

@@ -136,8 +136,8 @@ int check_config(const iir_config *c)
 {
     if (!c)
         return fail(IIR_EINVAL, "config is NULL");
-    if (c->bpc != 8 && c->bpc != 10)
-        return fail(IIR_EINVAL, "bpc must be 8 or 10, got %d", c->bpc);
+    if (c->bpc < 8 || c->bpc > 16)
+        return fail(IIR_EINVAL, "bpc must be 8 to 16, got %d", c->bpc);
     if (c->chroma != IIR_CHROMA_420)
         return fail(IIR_EINVAL, "only 4:2:0 (chroma = %d) is supported", IIR_CHROMA_420);
     if (c->width < 3 || c->height < 3 || c->width > 32768 || c->height > 32768)
@@ -359,6 +359,7 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     a.chunks = plan_chunks(c, n);
     a.chunk_len = (n + a.chunks - 1) / a.chunks;
     a.has_prev = c->has_prev ? 1 : 0;
+    a.shift = c->cfg.bpc == 8 ? 0 : 16 - c->cfg.bpc;
 
     const bool timing = (c->cfg.flags & IIR_FLAG_TIMING) != 0;
     iir_ctx::Sub &sub = c->subs[(c->sub_head + c->sub_count) % iir_ctx::kMaxPending];
@@ -573,7 +574,7 @@ IIR_API int iir_scores_of(const iir_config *cfg, const iir_result *r, iir_scores
 {
     if (!cfg || !r || !s)
         return fail(IIR_EINVAL, "NULL argument");
-    if ((cfg->bpc != 8 && cfg->bpc != 10) || cfg->width < 1 || cfg->height < 1)
+    if (cfg->bpc < 8 || cfg->bpc > 16 || cfg->width < 1 || cfg->height < 1)
         return fail(IIR_EINVAL, "bad configuration");
     const double n_luma = (double)cfg->width * (double)cfg->height;
     const double n_chroma = (double)((cfg->width + 1) / 2) * (double)((cfg->height + 1) / 2);
@@ -607,7 +608,7 @@ IIR_API int iir_aggregate_of(const iir_config *cfg, const iir_result *r, int32_t
 {
     if (!cfg || !r || !out || n < 1)
         return fail(IIR_EINVAL, "aggregate needs a config, n >= 1 results and an output");
-    if ((cfg->bpc != 8 && cfg->bpc != 10) || cfg->width < 1 || cfg->height < 1)
+    if (cfg->bpc < 8 || cfg->bpc > 16 || cfg->width < 1 || cfg->height < 1)
         return fail(IIR_EINVAL, "bad configuration");
     const double n_luma = (double)cfg->width * (double)cfg->height;
     const double n_chroma = (double)((cfg->width + 1) / 2) * (double)((cfg->height + 1) / 2);

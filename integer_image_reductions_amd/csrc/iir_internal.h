@@ -48,6 +48,7 @@ struct KernelArgs {
     int32_t strips, row_tiles, tiles;
     int32_t nframes, chunks, chunk_len;
     int32_t has_prev;
+    int32_t shift;  // 16-bit samples: 16 - bit depth, the left shift that scales them to 16 bits
 };
 
 // Host-side launchers (iir_kernels.hip). Each returns the launch's hipError_t.

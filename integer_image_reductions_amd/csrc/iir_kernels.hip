@@ -37,6 +37,7 @@
 //   * Workgroup ids are remapped so each XCD (and its L2) gets a contiguous run of vertically
 //     adjacent tiles, which share their halo rows.
 #include <algorithm>
+#include <type_traits>
 
 #include "iir_internal.h"
 
@@ -156,6 +157,18 @@ __device__ __forceinline__ unsigned long long wave_sum(uint32_t v)
     return (r0 + r1) + (r2 + r3);
 }
 
+// Wavefront sum of per-lane 64-bit values below 2^40 (the squares of 16-bit samples): the low 24
+// bits and the rest are summed apart, each fitting the 32-bit lanes of wave_sum.
+__device__ __forceinline__ unsigned long long wave_sum_sq(unsigned long long v)
+{
+    return wave_sum((uint32_t)v & 0xffffffu) + (wave_sum((uint32_t)(v >> 24)) << 24);
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_sq(uint32_t v)
+{
+    return wave_sum(v);
+}
+
 __device__ __forceinline__ void add_sum(unsigned long long *p, unsigned long long v)
 {
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -214,6 +227,14 @@ struct Px<10> {
     typedef u32x2 Luma;  // 4 luma samples, 2 per dword
     static constexpr int kBytes = 2;
 };
+// 16-bit storage at any depth from 9 to 16 bits other than 10: samples are scaled to 16 bits by a
+// runtime shift, and squares are summed per lane in 64 bits (two 16-bit squares overflow 32)
+template <>
+struct Px<16> : Px<10> {};
+
+// Per-lane accumulator of squares: 32 bits up to 10-bit samples, 64 bits beyond.
+template <int BPC>
+using Sq = typename std::conditional<BPC == 16, unsigned long long, uint32_t>::type;
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
@@ -282,10 +303,24 @@ __device__ __forceinline__ uint32_t scale64(uint32_t v)
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, v) << 6);
 }
 
+// 16-bit samples of bit depth bpc scaled to 16 bits (shift 16 - bpc): 10-bit by the constant,
+// other depths by the launch's shift. The vertical pass then rounds and shifts by 16 at every
+// depth: (sum g x 2^s + 2^15) >> 16 = (sum g x + 2^(bpc-1)) >> bpc with s = 16 - bpc.
+template <int BPC>
+__device__ __forceinline__ uint32_t to16(uint32_t v, uint32_t shift)
+{
+    if constexpr (BPC == 10)
+        return scale64(v);
+    else
+        return __builtin_bit_cast(uint32_t,
+                                  __builtin_bit_cast(u16x2, v) << (u16x2){(unsigned short)shift,
+                                                                          (unsigned short)shift});
+}
+
 // (row a, row b) 16-bit pairs of the lane's 4 columns, the vertical filter's operands.
 template <int BPC>
 __device__ __forceinline__ void column_pairs(typename Px<BPC>::Luma a, typename Px<BPC>::Luma b,
-                                             uint32_t p[4])
+                                             uint32_t p[4], uint32_t shift)
 {
     if constexpr (BPC == 8) {
         p[0] = perm(b, a, 0x0c040c00u);
@@ -293,9 +328,9 @@ __device__ __forceinline__ void column_pairs(typename Px<BPC>::Luma a, typename 
         p[2] = perm(b, a, 0x0c060c02u);
         p[3] = perm(b, a, 0x0c070c03u);
     } else {
-        // 10-bit samples scaled by 64 (still < 2^16): the vertical shift by 10 becomes >> 16
-        const uint32_t ax = scale64(a.x), ay = scale64(a.y);
-        const uint32_t bx = scale64(b.x), by = scale64(b.y);
+        // samples scaled to 16 bits (10-bit: by 64): the vertical shift by bpc becomes >> 16
+        const uint32_t ax = to16<BPC>(a.x, shift), ay = to16<BPC>(a.y, shift);
+        const uint32_t bx = to16<BPC>(b.x, shift), by = to16<BPC>(b.y, shift);
         p[0] = perm(bx, ax, 0x05040100u);
         p[1] = perm(bx, ax, 0x07060302u);
         p[2] = perm(by, ay, 0x05040100u);
@@ -303,51 +338,76 @@ __device__ __forceinline__ void column_pairs(typename Px<BPC>::Luma a, typename 
     }
 }
 
+// |a - b| of both unsigned 16-bit halves
+__device__ __forceinline__ uint32_t absdiff16x2(uint32_t a, uint32_t b)
+{
+    const u16x2 x = __builtin_bit_cast(u16x2, a), y = __builtin_bit_cast(u16x2, b);
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_elementwise_max(x, y) - __builtin_elementwise_min(x, y));
+}
+
+// acc + the squares of both 16-bit halves of v (each square < 2^32, the sum needs 64 bits)
+__device__ __forceinline__ unsigned long long sq16x2(uint32_t v, unsigned long long acc)
+{
+    const uint32_t lo = v & 0xffffu, hi = v >> 16;
+    return acc + (unsigned long long)(lo * lo) + (unsigned long long)(hi * hi);
+}
+
 // Squared-error accumulation of one luma group (4 samples) or one chroma dword. 8-bit keeps
-// sum(r^2 + d^2) in s and sum(r d) in s2; 10-bit keeps the sum of squared differences in s.
+// sum(r^2 + d^2) in s and sum(r d) in s2; deeper samples keep the sum of squared differences
+// in s (32 bits up to 10-bit samples, 64 bits beyond) and leave s2 alone.
 template <int BPC>
 __device__ __forceinline__ void sse_luma(typename Px<BPC>::Luma r, typename Px<BPC>::Luma d,
-                                         uint32_t &s, uint32_t &s2)
+                                         Sq<BPC> &s, uint32_t &s2)
 {
     if constexpr (BPC == 8) {
         s = dot4u(d, d, dot4u(r, r, s));
         s2 = dot4u(r, d, s2);
-    } else {
+    } else if constexpr (BPC == 10) {
         s = sqdiff2(r.y, d.y, sqdiff2(r.x, d.x, s));
+    } else {
+        s = sq16x2(absdiff16x2(r.y, d.y), sq16x2(absdiff16x2(r.x, d.x), s));
     }
 }
 
 template <int BPC>
-__device__ __forceinline__ void sse_chroma(uint32_t r, uint32_t d, uint32_t &s, uint32_t &s2)
+__device__ __forceinline__ void sse_chroma(uint32_t r, uint32_t d, Sq<BPC> &s, uint32_t &s2)
 {
     if constexpr (BPC == 8) {
         s = dot4u(d, d, dot4u(r, r, s));
         s2 = dot4u(r, d, s2);
-    } else {
+    } else if constexpr (BPC == 10) {
         s = sqdiff2(r, d, s);
+    } else {
+        s = sq16x2(absdiff16x2(r, d), s);
     }
 }
 
-// Luma moments of one sample group: m1 += samples, m2 += squares, for ref (r) and dist (d), and
-// the cross term x += r . d, from which the squared error is m2r + m2d - 2x (8-bit). At 10 bits
-// the squared error keeps its own difference-square sum in x.
+// Luma moments of one sample group: m1 += samples, m2 += squares, for ref (r) and dist (d). The
+// squared error goes where sse_luma puts it: at 8 bits only the cross term s2 += r . d is added
+// (the error is m2r + m2d - 2 s2), deeper samples add their difference squares to s.
 template <int BPC>
 __device__ __forceinline__ void moments_luma(typename Px<BPC>::Luma r, typename Px<BPC>::Luma d,
-                                             uint32_t &m1r, uint32_t &m1d, uint32_t &m2r,
-                                             uint32_t &m2d, uint32_t &x)
+                                             uint32_t &m1r, uint32_t &m1d, Sq<BPC> &m2r,
+                                             Sq<BPC> &m2d, Sq<BPC> &s, uint32_t &s2)
 {
     if constexpr (BPC == 8) {
         m1r = dot4u(r, 0x01010101u, m1r);
         m1d = dot4u(d, 0x01010101u, m1d);
         m2r = dot4u(r, r, m2r);
         m2d = dot4u(d, d, m2d);
-        x = dot4u(r, d, x);
+        s2 = dot4u(r, d, s2);
     } else {
         m1r = dot2u(r.y, 0x00010001u, dot2u(r.x, 0x00010001u, m1r));
         m1d = dot2u(d.y, 0x00010001u, dot2u(d.x, 0x00010001u, m1d));
-        m2r = dot2u(r.y, r.y, dot2u(r.x, r.x, m2r));
-        m2d = dot2u(d.y, d.y, dot2u(d.x, d.x, m2d));
-        x = sqdiff2(r.y, d.y, sqdiff2(r.x, d.x, x));
+        if constexpr (BPC == 10) {
+            m2r = dot2u(r.y, r.y, dot2u(r.x, r.x, m2r));
+            m2d = dot2u(d.y, d.y, dot2u(d.x, d.x, m2d));
+        } else {
+            m2r = sq16x2(r.y, sq16x2(r.x, m2r));
+            m2d = sq16x2(d.y, sq16x2(d.x, m2d));
+        }
+        sse_luma<BPC>(r, d, s, s2);
     }
 }
 
@@ -599,13 +659,13 @@ __device__ __forceinline__ void mirror_halo(const Tile &T, FrameData<BPC, TH> &F
 // its side) as a 16-bit pair; rows k-2 .. k+2 come from the lanes around it. Lane i + 2 returns
 // the vertical values of output row i for the left side, lane i + 34 for the right side.
 template <int BPC>
-__device__ __forceinline__ uint32_t halo_vertical(u32x2 h, uint32_t hsel)
+__device__ __forceinline__ uint32_t halo_vertical(u32x2 h, uint32_t hsel, uint32_t shift)
 {
     constexpr uint32_t kVRound = BPC == 8 ? 128u : 32768u;
     constexpr uint32_t kVSel = BPC == 8 ? 0x06050201u : 0x07060302u;
     uint32_t x0 = perm(h.y, h.x, hsel);
-    if constexpr (BPC == 10)
-        x0 = scale64(x0);
+    if constexpr (BPC != 8)
+        x0 = to16<BPC>(x0, shift);
     const uint32_t m1 = from_left(x0), m2 = from_left(m1);    // rows k-1, k-2
     const uint32_t p1 = from_right(x0), p2 = from_right(p1);  // rows k+1, k+2
     const uint32_t va = dot2u(p2 & 0xffffu, T0z,
@@ -640,10 +700,12 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
         if (T.edge_tile)
             mirror_halo<BPC, TH, ROWSTAGE>(T, F);
     }
-    const uint32_t hv = halo_vertical<BPC>(F.HL, T.hsel);
+    const uint32_t shift = (uint32_t)a.shift;
+    const uint32_t hv = halo_vertical<BPC>(F.HL, T.hsel, shift);
 
     // SSE of the chroma tiles first, which frees their registers before the blur
-    uint32_t su = 0, su2 = 0, sv = 0, sv2 = 0;
+    Sq<BPC> su = 0, sv = 0;
+    uint32_t su2 = 0, sv2 = 0;
     if (accumulate) {
 #pragma unroll
         for (int k = 0; k < FD::kChromaSteps; ++k) {
@@ -662,15 +724,16 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
     }
 
     // blur, SAD against the previous blurred tile, and SSE of the luma rows as they go by
-    uint32_t acc_c = 0, acc_min = 0, sy = 0, sy2 = 0;
-    uint32_t m1r = 0, m1d = 0, m2r = 0, m2d = 0;
+    uint32_t acc_c = 0, acc_min = 0, sy2 = 0, m1r = 0, m1d = 0;
+    Sq<BPC> sy = 0, m2r = 0, m2d = 0;
 #pragma unroll
     for (int i = 0; i < TH; ++i) {
         uint32_t pa[4], pb[4], pc[4];
         const Luma zero{};
-        column_pairs<BPC>(F.R[i], F.R[i + 1], pa);                            // rows i-2, i-1
-        column_pairs<BPC>(F.R[i + 2], F.R[i + 3], pb);                        // rows i,   i+1
-        column_pairs<BPC>(F.R[i + 4], i + 5 < TH + 4 ? F.R[i + 5] : zero, pc);  // rows i+2 (tap 0 on i+3)
+        column_pairs<BPC>(F.R[i], F.R[i + 1], pa, shift);      // rows i-2, i-1
+        column_pairs<BPC>(F.R[i + 2], F.R[i + 3], pb, shift);  // rows i,   i+1
+        column_pairs<BPC>(F.R[i + 4], i + 5 < TH + 4 ? F.R[i + 5] : zero, pc,
+                          shift);  // rows i+2 (tap 0 on i+3)
         uint32_t v[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -720,7 +783,7 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
                     d = masked<BPC>(d, T.ym0, T.ym1);
                 }
                 if constexpr (MOM)
-                    moments_luma<BPC>(r, d, m1r, m1d, m2r, m2d, sy2);
+                    moments_luma<BPC>(r, d, m1r, m1d, m2r, m2d, sy, sy2);
                 else
                     sse_luma<BPC>(r, d, sy, sy2);
             }
@@ -731,29 +794,31 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 
     if (accumulate) {
         const uint32_t sad = have_prev ? acc_c + sum_prev - 2u * acc_min : 0u;
-        // squared luma error: 8-bit sy + sy2 hold sum r^2 + d^2 and sum r d; with moments the
-        // squares are apart (m2r, m2d); 10-bit keeps the difference squares in sy (sy2 with MOM)
-        uint32_t ey;
-        if constexpr (BPC == 8)
+        // squared errors: 8-bit sy (or, with moments, m2r + m2d) holds sum r^2 + d^2 and sy2
+        // sum r d; deeper samples keep the difference squares in sy (su, sv likewise)
+        Sq<BPC> ey = sy, eu = su, ev = sv;
+        if constexpr (BPC == 8) {
             ey = (MOM ? m2r + m2d : sy) - 2u * sy2;
-        else
-            ey = MOM ? sy2 : sy;
+            eu = su - 2u * su2;
+            ev = sv - 2u * sv2;
+        }
+        const Sq<BPC> zero = 0;
         if constexpr (MOM) {
             const unsigned long long sums[kMaxSums] = {
                 wave_sum(sad),
-                wave_sum(T.out_lane ? ey : 0u),
-                wave_sum(T.c_on ? su - 2u * su2 : 0u),
-                wave_sum(T.c_on ? sv - 2u * sv2 : 0u),
+                wave_sum_sq(T.out_lane ? ey : zero),
+                wave_sum_sq(T.c_on ? eu : zero),
+                wave_sum_sq(T.c_on ? ev : zero),
                 wave_sum(T.out_lane ? m1r : 0u),
                 wave_sum(T.out_lane ? m1d : 0u),
-                wave_sum(T.out_lane ? m2r : 0u),
-                wave_sum(T.out_lane ? m2d : 0u)};
+                wave_sum_sq(T.out_lane ? m2r : zero),
+                wave_sum_sq(T.out_lane ? m2d : zero)};
             push_sums(a, P, T.lane, sums);
         } else {
             const unsigned long long sums[kSums] = {wave_sum(sad),
-                                                    wave_sum(T.out_lane ? ey : 0u),
-                                                    wave_sum(T.c_on ? su - 2u * su2 : 0u),
-                                                    wave_sum(T.c_on ? sv - 2u * sv2 : 0u)};
+                                                    wave_sum_sq(T.out_lane ? ey : zero),
+                                                    wave_sum_sq(T.c_on ? eu : zero),
+                                                    wave_sum_sq(T.c_on ? ev : zero)};
             push_sums(a, P, T.lane, sums);
         }
     }
@@ -1155,12 +1220,18 @@ FramesFn frames_fn(int th)
     }
 }
 
+// 8-bit and 10-bit samples have kernels of their own; every other depth up to 16 bits takes the
+// 16-bit one with the launch's scale shift
 template <bool MOM>
 FramesFn pick_depth(int bpc, int th, bool generic)
 {
     if (bpc == 8)
         return generic ? frames_fn<8, true, MOM>(th) : frames_fn<8, false, MOM>(th);
-    return generic ? frames_fn<10, true, MOM>(th) : frames_fn<10, false, MOM>(th);
+    if (bpc == 10)
+        return generic ? frames_fn<10, true, MOM>(th) : frames_fn<10, false, MOM>(th);
+    if (bpc >= 9 && bpc <= 16)
+        return generic ? frames_fn<16, true, MOM>(th) : frames_fn<16, false, MOM>(th);
+    return nullptr;
 }
 
 FramesFn pick(int bpc, int th, bool generic, bool moments)

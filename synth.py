@@ -13,6 +13,8 @@ Five named workloads, shaped like the pages' clips (the clips themselves are not
   c4  3840x2160 10-bit, 50 pairs  c3's reference times 4, dist = 8x8 block mean + noise sigma 8
   c5  960x544   8-bit, 301 frames breathing sinusoid (amplitude 20, period 40 frames) + noise
                                   sigma 2, dist sigma 4
+  c6  3840x2160 16-bit, 50 pairs  not one of the pages' clips: the 16-bit storage path at the 4K
+                                  shape; every plane of c4 times 64 plus uniform noise in 0..63
 
 Chroma (not described for the workloads, so fixed here): reference U is the rounded mean of each
 2x2 luma block (edge rows/columns replicated for odd sizes), reference V is (peak - U), and the
@@ -55,6 +57,7 @@ CONFIGS = {
     "c3": dict(width=3840, height=2160, bpc=8, frames=50, seed=303),
     "c4": dict(width=3840, height=2160, bpc=10, frames=50, seed=303, noise_seed=404),
     "c5": dict(width=960, height=544, bpc=8, frames=301, seed=505),
+    "c6": dict(width=3840, height=2160, bpc=16, frames=50, seed=303, noise_seed=404, low_seed=606),
 }
 
 
@@ -215,6 +218,16 @@ def _c5(f, seed):
     return w, h, bpc, ref, dist
 
 
+def _c6(f, seed, noise_seed, low_seed):
+    w, h, _, ref, dist = _c4(f, seed, noise_seed)
+    rng = np.random.default_rng(low_seed)
+    for planes in (ref, dist):
+        for p in planes:
+            for t in range(f):
+                p[t] = (p[t] << 6) | rng.integers(0, 64, size=p[t].shape, dtype=np.uint16)
+    return w, h, 16, ref, dist
+
+
 def make_clip(name: str, frames: int | None = None) -> Clip:
     """Build a named workload; ``frames`` truncates it (the first frames are the same either way)."""
     cfg = CONFIGS[name]
@@ -229,6 +242,8 @@ def make_clip(name: str, frames: int | None = None) -> Clip:
         w, h, bpc, ref, dist = _c3(f, cfg["seed"])
     elif name == "c4":
         w, h, bpc, ref, dist = _c4(f, cfg["seed"], cfg["noise_seed"])
+    elif name == "c6":
+        w, h, bpc, ref, dist = _c6(f, cfg["seed"], cfg["noise_seed"], cfg["low_seed"])
     else:
         w, h, bpc, ref, dist = _c5(f, cfg["seed"])
     return Clip(name, w, h, bpc, tuple(ref), tuple(dist))

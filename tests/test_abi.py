@@ -45,7 +45,7 @@ def _create(lib, **kw):
     return lib.iir_create(ctypes.byref(cfg), kw.get("device", 0), None, ctypes.byref(h))
 
 
-@pytest.mark.parametrize("kw", [dict(bpc=9), dict(bpc=16), dict(chroma=444), dict(w=2),
+@pytest.mark.parametrize("kw", [dict(bpc=7), dict(bpc=17), dict(chroma=444), dict(w=2),
                                 dict(h=2), dict(w=40000), dict(max_batch=0),
                                 dict(max_batch=70000), dict(flags=8)])
 def test_create_rejects_bad_config(lib, kw):
@@ -95,8 +95,9 @@ def test_probe_rejects_bad_arguments(lib):
 def test_scores_of_rejects(lib):
     r, s = B.Result(), B.Scores()
     assert lib.iir_scores_of(None, ctypes.byref(r), ctypes.byref(s)) == B.IIR_EINVAL
-    cfg = B.Config(8, 8, 12, 420, 1, 0)
-    assert lib.iir_scores_of(ctypes.byref(cfg), ctypes.byref(r), ctypes.byref(s)) == B.IIR_EINVAL
+    for bpc in (7, 17):
+        cfg = B.Config(8, 8, bpc, 420, 1, 0)
+        assert lib.iir_scores_of(ctypes.byref(cfg), ctypes.byref(r), ctypes.byref(s)) == B.IIR_EINVAL
 
 
 def _close(a, b):
@@ -105,7 +106,7 @@ def _close(a, b):
     return abs(a - b) <= 1e-12 * max(abs(a), abs(b), 1e-300)
 
 
-@pytest.mark.parametrize("bpc", [8, 10])
+@pytest.mark.parametrize("bpc", [8, 10, 12, 16])
 def test_scores_match_oracle(bpc):
     """Host score derivation in the library equals the oracle's within 1e-12 relative."""
     r = np.random.default_rng(bpc)
@@ -134,7 +135,7 @@ def test_clip_functions_reject(lib):
     assert lib.iir_aggregate_of(None, r, 1, ctypes.byref(a)) == B.IIR_EINVAL
     assert lib.iir_aggregate_of(ctypes.byref(cfg), r, 0, ctypes.byref(a)) == B.IIR_EINVAL
     assert lib.iir_aggregate_of(ctypes.byref(cfg), r, 1, None) == B.IIR_EINVAL
-    bad = B.Config(8, 8, 9, 420, 1, 0)
+    bad = B.Config(8, 8, 17, 420, 1, 0)
     assert lib.iir_aggregate_of(ctypes.byref(bad), r, 1, ctypes.byref(a)) == B.IIR_EINVAL
 
 
@@ -149,7 +150,7 @@ def test_motion2_matches_oracle(n):
     assert np.array_equal(iir.motion2(m), oracle.motion2(m))
 
 
-@pytest.mark.parametrize("bpc", [8, 10])
+@pytest.mark.parametrize("bpc", [8, 10, 16])
 @pytest.mark.parametrize("n", [1, 2, 5, 64])
 def test_aggregate_matches_oracle(bpc, n):
     """Clip aggregates: totals exact, apsnr and the motion means within 1e-12 relative of the

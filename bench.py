@@ -36,7 +36,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "integer_image_reductions_amd", "csrc", "iir_kernels.hip")
+# the frames kernel's sources: its templates and the units that instantiate them
+KERNEL_SRCS = [os.path.join(ROOT, "integer_image_reductions_amd", "csrc", n) for n in
+               ("iir_frames.h", "iir_frames_8.hip", "iir_frames_10.hip", "iir_frames_16.hip")]
 
 WORKLOADS = {
     "c3": "3840x2160 8-bit 4:2:0, 50 frame pairs, motion SAD + Y/U/V SSE",
@@ -44,6 +46,8 @@ WORKLOADS = {
     "c2": "1920x1080 8-bit 4:2:0, 48 frame pairs, motion SAD + Y/U/V SSE",
     "c1": "576x324 8-bit 4:2:0, 10 frame pairs, motion SAD + Y/U/V SSE",
     "c5": "960x544 8-bit 4:2:0, 301-frame resident clip, motion SAD + Y/U/V SSE",
+    "c6": "3840x2160 16-bit 4:2:0 (uint16), 50 frame pairs, motion SAD + Y/U/V SSE "
+          "(the 16-bit path at the 4K shape; not one of the pages' clips)",
 }
 
 
@@ -52,8 +56,11 @@ def log(*a):
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def algorithmic_bytes(w: int, h: int, bpc: int, frames: int) -> int:

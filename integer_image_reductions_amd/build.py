@@ -19,7 +19,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libiir.so")
-SOURCES = [os.path.join(CSRC, "iir_kernels.hip"), os.path.join(CSRC, "iir_host.cpp")]
+# one translation unit per sample type of the frames kernel, so they compile in parallel
+SOURCES = [os.path.join(CSRC, n) for n in
+           ("iir_frames_8.hip", "iir_frames_10.hip", "iir_frames_16.hip", "iir_kernels.hip",
+            "iir_host.cpp")]
+HEADERS = [os.path.join(CSRC, n) for n in ("iir_frames.h", "iir_internal.h")]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: never emit packed fp32 VALU ops (the kernels are integer-only anyway).
@@ -36,26 +40,47 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile libiir.so; always recompiles."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *COMMON, "-shared", *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libiir.so")
+    """Compile libiir.so; always recompiles (every source in parallel, then one link)."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    with tempfile.TemporaryDirectory(prefix="iir_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
+        cmds = [[hipcc(), *COMMON, "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+        workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+        with ThreadPoolExecutor(workers) as pool:
+            results = list(pool.map(lambda c: (c, subprocess.run(c, capture_output=True,
+                                                                  text=True)), cmds))
+        for cmd, r in results:
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            if r.returncode != 0:
+                sys.stderr.write(r.stdout + r.stderr)
+                raise RuntimeError("hipcc failed building libiir.so")
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = [hipcc(), *COMMON, "-shared", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed linking libiir.so")
     os.replace(tmp, LIB)
     return LIB
 
 
-def assembly(out_dir: str) -> str:
-    """Write the gfx950 assembly of the kernels (for resource and instruction checks)."""
+def assembly(out_dir: str) -> list:
+    """Write the gfx950 assembly of every kernel source (for resource and instruction checks)."""
     os.makedirs(out_dir, exist_ok=True)
-    out = os.path.join(out_dir, "iir_kernels-gfx950.s")
-    cmd = [hipcc(), *COMMON, "--cuda-device-only", "-S", SOURCES[0], "-o", out]
-    subprocess.run(cmd, check=True, capture_output=True, text=True)
-    return out
+    outs = []
+    for src in SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        out = os.path.join(out_dir, os.path.basename(src)[:-4] + "-gfx950.s")
+        cmd = [hipcc(), *COMMON, "--cuda-device-only", "-S", src, "-o", out]
+        subprocess.run(cmd, check=True, capture_output=True, text=True)
+        outs.append(out)
+    return outs
 
 
 def main():

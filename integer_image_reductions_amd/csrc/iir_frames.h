@@ -1,0 +1,1172 @@
+// iir_frames.h -- the gfx950 frames kernel (templates) for the integer motion (blurred-luma SAD)
+// and PSNR (per-plane SSE) sums of 4:2:0 video. Each iir_frames_*.hip translation unit
+// instantiates the kernels of one sample type; iir_kernels.hip picks among them.
+//
+// What is computed (readings stated in include/iir.h):
+//   V[i][j]  = (sum_k g_k x[m(i+k-2)][j] + 2^(bpc-1)) >> bpc            vertical pass
+//   Bl[i][j] = (sum_l g_l V[i][m(j+l-2)] + 2^15) >> 16                  horizontal pass
+//   SAD_t    = sum |Bl_t - Bl_(t-1)|,  SSE_c = sum (ref_c - dist_c)^2
+// with g = (3571, 16004, 26386, 16004, 3571) and m the whole-sample mirror ("ADR-1392: CUDA
+// motion, PSNR and moment kernels add one atomic per block ...", Decision 4: vertical pass once per
+// output row and column, rounded by the bit depth, then five horizontal taps shifted by 16;
+// "Research-0735: CUDA motion kernel ncu hotpath analysis (576x324)": a 5x5 separable Gaussian).
+//
+// Design (MI355X-first; the CUDA tiles on the pages are prior art only):
+//   * One wavefront per workgroup owns one tile: 256 luma columns x TH rows, its rows starting
+//     on a 256-column boundary, so every row a wavefront loads is whole, aligned cache lines that
+//     no other wavefront touches (chroma: 128 samples per row). Lane l holds luma columns
+//     4l .. 4l+3 of the tile. Each lane slides down its columns with the whole 5-row window in
+//     registers, so every vertical value is computed exactly once and reused by the five
+//     horizontal taps through two DPP lane shifts per row (no LDS round trip, no barrier).
+//   * The two columns left and right of the tile (horizontal halo) arrive transposed: one load
+//     per frame gives lane k the halo samples of tile row k-2 (lanes 0-31 the left side, lanes
+//     32-63 the right side), their vertical pass runs once per frame across lanes, and each row
+//     hands the result to lane 0 and lane 63 with two readlanes.
+//   * The separable filter runs on packed 16-bit pairs: v_perm_b32 builds (row r, row r+1) pairs
+//     per column, v_dot2_u32_u16 applies two taps per instruction with the rounding constant as
+//     the accumulator, and v_perm_b32 extracts the 16-bit result of a byte-aligned shift. 10-bit
+//     input is pre-scaled by 64 so its vertical shift (10) also becomes a 16-bit byte shift.
+//   * SAD on packed blurred pairs: |a - b| = a + b - 2 min(a, b), with sum(b) kept from the
+//     previous frame, so each pair costs one v_pk_min_u16 and two v_dot2 accumulations.
+//   * SSE: 8-bit as sum(r^2 + d^2) - 2 sum(r d) with v_dot4_u32_u8 (exact in 32-bit modular
+//     arithmetic, since the true per-lane value is far below 2^32); 10-bit as v_pk_sub_i16 then
+//     v_dot2_i32_i16 of the difference with itself.
+//   * A workgroup loops over the frames of its time chunk, keeping the previous blurred tile in
+//     registers; the blurred state crosses launches through a small tiled plane (ring).
+//   * Per frame, per workgroup: one 64-bit atomic per sum ("ADR-1392", Decision 1), into one of
+//     kSumSlots partial slots chosen by XCD; the host adds the slots.
+//   * Workgroup ids are remapped so each XCD (and its L2) gets a contiguous run of vertically
+//     adjacent tiles, which share their halo rows.
+#pragma once
+
+#include <algorithm>
+#include <type_traits>
+
+#include "iir_internal.h"
+
+namespace iir {
+namespace {
+
+constexpr uint32_t G0 = 3571, G1 = 16004, G2 = 26386;
+static_assert(2 * G0 + 2 * G1 + G2 == 65536u, "taps must sum to 2^16 so flat planes stay flat");
+
+// (lo, hi) 16-bit tap pairs for v_dot2_u32_u16
+constexpr uint32_t T01 = G0 | (G1 << 16);
+constexpr uint32_t T21 = G2 | (G1 << 16);
+constexpr uint32_t T0z = G0;
+constexpr uint32_t Tz0 = G0 << 16;
+constexpr uint32_t T12 = G1 | (G2 << 16);
+constexpr uint32_t T10 = G1 | (G0 << 16);
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t dot2u(uint32_t a, uint32_t b, uint32_t c)
+{
+    return __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b), c,
+                                  false);
+}
+
+__device__ __forceinline__ uint32_t dot4u(uint32_t a, uint32_t b, uint32_t c)
+{
+    return __builtin_amdgcn_udot4(a, b, c, false);
+}
+
+// square of the packed signed 16-bit difference a - b, summed over both halves, added to c
+__device__ __forceinline__ uint32_t sqdiff2(uint32_t a, uint32_t b, uint32_t c)
+{
+    const i16x2 d = __builtin_bit_cast(i16x2, a) - __builtin_bit_cast(i16x2, b);
+    return (uint32_t)__builtin_amdgcn_sdot2(d, d, (int)c, false);
+}
+
+// byte permute of the 8-byte value {hi:lo}: selector bytes 0-3 pick lo, 4-7 pick hi, 12 gives 0
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ uint32_t pkmin(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+// lane i receives lane i-1's value (wave_shr:1); lane 0 receives 0 (bound_ctrl, so no register
+// has to be zeroed for the lane without a source)
+__device__ __forceinline__ uint32_t from_left(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xf, 0xf, true);
+}
+
+// lane i receives lane i+1's value (wave_shl:1); lane 63 receives 0
+__device__ __forceinline__ uint32_t from_right(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xf, 0xf, true);
+}
+
+// As from_left / from_right, but the lane without a source keeps `edge` (bound_ctrl off: the DPP
+// leaves that lane's old value). A select around a plain shift would let the compiler run the
+// shift with that lane masked off, and a DPP read from a masked-off lane returns 0 to its
+// neighbour.
+__device__ __forceinline__ uint32_t from_left_or(uint32_t v, uint32_t edge)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)edge, (int)v, 0x138, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ uint32_t from_right_or(uint32_t v, uint32_t edge)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)edge, (int)v, 0x130, 0xf, 0xf, false);
+}
+
+// whole-sample mirror into [0, n), exact for -2 <= i <= n + 1, clamped beyond (never used there)
+__device__ __forceinline__ int mirror_clamp(int i, int n)
+{
+    i = i < 0 ? -i : i;
+    i = i >= n ? 2 * n - 2 - i : i;
+    return min(max(i, 0), n - 1);
+}
+
+// XCD-aware tile order: hardware places workgroup b on XCD b % 8; give each XCD one contiguous
+// run of the linear (chunk, row tile, strip) order. A bijection on [0, G) for any G. With strips
+// fastest, the wavefronts resident together cover whole rows of the frame, so HBM sees long
+// contiguous runs instead of a scatter of 256-byte pieces.
+__device__ __forceinline__ int xcd_linear(int b, int G)
+{
+    const int x = b & 7, j = b >> 3;
+    const int q = G >> 3, r = G & 7;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+}
+
+// Sum of a per-lane u32 over the wavefront as u64. DPP row shifts fold each row of 16 lanes into
+// its lane 15 (4 adds, no LDS round trip); the four row sums are added in 64 bits on the scalar
+// unit, so a wavefront total may exceed 2^32 while each row sum stays below it.
+template <int CTRL>
+__device__ __forceinline__ uint32_t row_shr_add(uint32_t v)
+{
+    return v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, true);
+}
+
+__device__ __forceinline__ unsigned long long wave_sum(uint32_t v)
+{
+    v = row_shr_add<0x111>(v);  // row_shr:1
+    v = row_shr_add<0x112>(v);  // row_shr:2
+    v = row_shr_add<0x114>(v);  // row_shr:4
+    v = row_shr_add<0x118>(v);  // row_shr:8
+    const unsigned long long r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+    const unsigned long long r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const unsigned long long r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+    const unsigned long long r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Wavefront sum of per-lane 64-bit values below 2^40 (the squares of 16-bit samples): the low 24
+// bits and the rest are summed apart, each fitting the 32-bit lanes of wave_sum.
+__device__ __forceinline__ unsigned long long wave_sum_sq(unsigned long long v)
+{
+    return wave_sum((uint32_t)v & 0xffffffu) + (wave_sum((uint32_t)(v >> 24)) << 24);
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_sq(uint32_t v)
+{
+    return wave_sum(v);
+}
+
+__device__ __forceinline__ void add_sum(unsigned long long *p, unsigned long long v)
+{
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Per-frame wavefront sums waiting for their atomics. Lane q of v[] holds queued frame q's NS
+// 64-bit sums (low and high halves); a flush issues every queued frame's atomics at once, one
+// frame per lane. On gfx9 stores and atomics share the in-order
+// vmcnt counter with loads, so an atomic issued right after a frame would make the next frame's
+// first load wait for the atomic's round trip; batching keeps them off the frame loop.
+template <int NS>
+struct Pending {
+    uint32_t v[2 * NS];
+    int first;  // frame of queue slot 0 (wave-uniform)
+    int count;  // queued frames (wave-uniform)
+};
+
+template <int NS>
+__device__ __forceinline__ void flush_sums(const KernelArgs &a, Pending<NS> &P, int lane)
+{
+    if (lane < P.count) {
+        unsigned long long *o = a.sums + (size_t)(P.first + lane) * (NS * kSumSlots) +
+                                (blockIdx.x & (kSumSlots - 1));
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+            add_sum(o + k * kSumSlots,
+                    ((unsigned long long)P.v[2 * k + 1] << 32) | (unsigned long long)P.v[2 * k]);
+    }
+    P.first += P.count;
+    P.count = 0;
+}
+
+template <int NS>
+__device__ __forceinline__ void push_sums(const KernelArgs &a, Pending<NS> &P, int lane,
+                                          const unsigned long long (&s)[NS])
+{
+    const bool mine = lane == P.count;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        P.v[2 * k] = mine ? (uint32_t)s[k] : P.v[2 * k];
+        P.v[2 * k + 1] = mine ? (uint32_t)(s[k] >> 32) : P.v[2 * k + 1];
+    }
+    if (++P.count == kWave)
+        flush_sums(a, P, lane);
+}
+
+template <int BPC>
+struct Px;
+template <>
+struct Px<8> {
+    typedef uint32_t Luma;  // 4 luma samples
+    static constexpr int kBytes = 1;
+};
+template <>
+struct Px<10> {
+    typedef u32x2 Luma;  // 4 luma samples, 2 per dword
+    static constexpr int kBytes = 2;
+};
+// 16-bit storage at any depth from 9 to 16 bits other than 10: samples are scaled to 16 bits by a
+// runtime shift, and squares are summed per lane in 64 bits (two 16-bit squares overflow 32)
+template <>
+struct Px<16> : Px<10> {};
+
+// Per-lane accumulator of squares: 32 bits up to 10-bit samples, 64 bits beyond.
+template <int BPC>
+using Sq = typename std::conditional<BPC == 16, unsigned long long, uint32_t>::type;
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// A buffer resource over one plane: base in SGPRs, `bytes` as its range. Loads then take the
+// row offset in an SGPR (soffset) and the lane's column offset in one VGPR (voffset), so no
+// per-row VALU address arithmetic and no 64-bit address registers are needed.
+__device__ __forceinline__ Rsrc plane_rsrc(const uint8_t *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Cache policy of a load (the buffer instructions' cache-policy operand): kKeep allocates in L2
+// normally; kStream sets the non-temporal bit, so the line is among the first L2 evicts. Samples
+// only this wavefront reads (distorted luma, chroma) stream; reference luma rows, which the
+// vertically and horizontally neighbouring tiles also read as their halo, are kept so that the
+// second reader finds them in L2.
+constexpr int kKeep = 0;
+constexpr int kStream = 2;
+
+template <int POL = kKeep>
+__device__ __forceinline__ uint32_t ld32(Rsrc r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, POL);
+}
+
+template <int BPC, int POL = kKeep>
+__device__ __forceinline__ typename Px<BPC>::Luma ld_luma(Rsrc r, uint32_t voff, uint32_t soff)
+{
+    if constexpr (BPC == 8) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, POL);
+    } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, POL);
+        return u32x2{v[0], v[1]};
+    }
+}
+
+__device__ __forceinline__ int uni(int v)
+{
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+// A value the compiler must treat as changed on every frame, so per-row products of it are not
+// hoisted out of the frame loop into dozens of live scalar registers.
+__device__ __forceinline__ uint32_t opaque(uint32_t v)
+{
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
+// Plane k of frame t (wave-uniform; scalar loads when it comes from the frame table).
+__device__ __forceinline__ const uint8_t *frame_plane(const KernelArgs &a, int t, int k)
+{
+    if (a.table) {
+        typedef __attribute__((address_space(4))) const FramePtrs cFramePtrs;
+        const cFramePtrs *tb = (const cFramePtrs *)(uintptr_t)a.table;
+        return tb[t].p[k];
+    }
+    return a.base[k] + (int64_t)t * a.fstride[k];
+}
+
+// Both 16-bit halves of v shifted left by 6. Takes the dword by value: __builtin_bit_cast must
+// not be applied to a vector element expression such as a.y (clang reads element 0 there).
+__device__ __forceinline__ uint32_t scale64(uint32_t v)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, v) << 6);
+}
+
+// 16-bit samples of bit depth bpc scaled to 16 bits (shift 16 - bpc): 10-bit by the constant,
+// other depths by the launch's shift. The vertical pass then rounds and shifts by 16 at every
+// depth: (sum g x 2^s + 2^15) >> 16 = (sum g x + 2^(bpc-1)) >> bpc with s = 16 - bpc.
+template <int BPC>
+__device__ __forceinline__ uint32_t to16(uint32_t v, uint32_t shift)
+{
+    if constexpr (BPC == 10)
+        return scale64(v);
+    else
+        return __builtin_bit_cast(uint32_t,
+                                  __builtin_bit_cast(u16x2, v) << (u16x2){(unsigned short)shift,
+                                                                          (unsigned short)shift});
+}
+
+// (row a, row b) 16-bit pairs of the lane's 4 columns, the vertical filter's operands.
+template <int BPC>
+__device__ __forceinline__ void column_pairs(typename Px<BPC>::Luma a, typename Px<BPC>::Luma b,
+                                             uint32_t p[4], uint32_t shift)
+{
+    if constexpr (BPC == 8) {
+        p[0] = perm(b, a, 0x0c040c00u);
+        p[1] = perm(b, a, 0x0c050c01u);
+        p[2] = perm(b, a, 0x0c060c02u);
+        p[3] = perm(b, a, 0x0c070c03u);
+    } else {
+        // samples scaled to 16 bits (10-bit: by 64): the vertical shift by bpc becomes >> 16
+        const uint32_t ax = to16<BPC>(a.x, shift), ay = to16<BPC>(a.y, shift);
+        const uint32_t bx = to16<BPC>(b.x, shift), by = to16<BPC>(b.y, shift);
+        p[0] = perm(bx, ax, 0x05040100u);
+        p[1] = perm(bx, ax, 0x07060302u);
+        p[2] = perm(by, ay, 0x05040100u);
+        p[3] = perm(by, ay, 0x07060302u);
+    }
+}
+
+// |a - b| of both unsigned 16-bit halves
+__device__ __forceinline__ uint32_t absdiff16x2(uint32_t a, uint32_t b)
+{
+    const u16x2 x = __builtin_bit_cast(u16x2, a), y = __builtin_bit_cast(u16x2, b);
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_elementwise_max(x, y) - __builtin_elementwise_min(x, y));
+}
+
+// acc + the squares of both 16-bit halves of v (each square < 2^32, the sum needs 64 bits)
+__device__ __forceinline__ unsigned long long sq16x2(uint32_t v, unsigned long long acc)
+{
+    const uint32_t lo = v & 0xffffu, hi = v >> 16;
+    return acc + (unsigned long long)(lo * lo) + (unsigned long long)(hi * hi);
+}
+
+// Squared-error accumulation of one luma group (4 samples) or one chroma dword. 8-bit keeps
+// sum(r^2 + d^2) in s and sum(r d) in s2; deeper samples keep the sum of squared differences
+// in s (32 bits up to 10-bit samples, 64 bits beyond) and leave s2 alone.
+template <int BPC>
+__device__ __forceinline__ void sse_luma(typename Px<BPC>::Luma r, typename Px<BPC>::Luma d,
+                                         Sq<BPC> &s, uint32_t &s2)
+{
+    if constexpr (BPC == 8) {
+        s = dot4u(d, d, dot4u(r, r, s));
+        s2 = dot4u(r, d, s2);
+    } else if constexpr (BPC == 10) {
+        s = sqdiff2(r.y, d.y, sqdiff2(r.x, d.x, s));
+    } else {
+        s = sq16x2(absdiff16x2(r.y, d.y), sq16x2(absdiff16x2(r.x, d.x), s));
+    }
+}
+
+template <int BPC>
+__device__ __forceinline__ void sse_chroma(uint32_t r, uint32_t d, Sq<BPC> &s, uint32_t &s2)
+{
+    if constexpr (BPC == 8) {
+        s = dot4u(d, d, dot4u(r, r, s));
+        s2 = dot4u(r, d, s2);
+    } else if constexpr (BPC == 10) {
+        s = sqdiff2(r, d, s);
+    } else {
+        s = sq16x2(absdiff16x2(r, d), s);
+    }
+}
+
+// Luma moments of one sample group: m1 += samples, m2 += squares, for ref (r) and dist (d). The
+// squared error goes where sse_luma puts it: at 8 bits only the cross term s2 += r . d is added
+// (the error is m2r + m2d - 2 s2), deeper samples add their difference squares to s.
+template <int BPC>
+__device__ __forceinline__ void moments_luma(typename Px<BPC>::Luma r, typename Px<BPC>::Luma d,
+                                             uint32_t &m1r, uint32_t &m1d, Sq<BPC> &m2r,
+                                             Sq<BPC> &m2d, Sq<BPC> &s, uint32_t &s2)
+{
+    if constexpr (BPC == 8) {
+        m1r = dot4u(r, 0x01010101u, m1r);
+        m1d = dot4u(d, 0x01010101u, m1d);
+        m2r = dot4u(r, r, m2r);
+        m2d = dot4u(d, d, m2d);
+        s2 = dot4u(r, d, s2);
+    } else {
+        m1r = dot2u(r.y, 0x00010001u, dot2u(r.x, 0x00010001u, m1r));
+        m1d = dot2u(d.y, 0x00010001u, dot2u(d.x, 0x00010001u, m1d));
+        if constexpr (BPC == 10) {
+            m2r = dot2u(r.y, r.y, dot2u(r.x, r.x, m2r));
+            m2d = dot2u(d.y, d.y, dot2u(d.x, d.x, m2d));
+        } else {
+            m2r = sq16x2(r.y, sq16x2(r.x, m2r));
+            m2d = sq16x2(d.y, sq16x2(d.x, m2d));
+        }
+        sse_luma<BPC>(r, d, s, s2);
+    }
+}
+
+// r with the samples outside a per-lane validity mask cleared
+template <int BPC>
+__device__ __forceinline__ typename Px<BPC>::Luma masked(typename Px<BPC>::Luma r, uint32_t m0,
+                                                         uint32_t m1)
+{
+    if constexpr (BPC == 8) {
+        return r & m0;
+    } else {
+        return u32x2{r.x & m0, r.y & m1};
+    }
+}
+
+// Everything one wavefront knows about its tile, fixed for the whole launch. Scalars are
+// wave-uniform (kept in SGPRs); the rest are per lane.
+struct Tile {
+    int tile, chunk, strip, r0;  // scalar
+    int rows_valid;              // scalar: output rows of the tile inside the frame
+    int lane;
+    uint32_t luma_off;           // byte offset of the lane's 4 luma samples in a row
+    uint32_t w0, w1;             // 16-bit weights of the lane's blurred pairs (1 = valid column)
+    bool out_lane;               // lane owns output columns
+    uint32_t coff[4];            // byte offsets of the lane's chroma dword in ref U, dist U,
+                                 // ref V, dist V (column, plus one row for the upper half-wave
+                                 // at 8 bits)
+    int crow0;                   // scalar: first chroma row of the tile
+    bool c_on;                   // lane reads chroma
+    // horizontal halo, transposed: lane k of each half-wave loads bytes of reference luma row
+    // r0 - 2 + (k mod 32) around the tile's left (lanes 0-31) or right (lanes 32-63) edge;
+    // hsel picks the two halo columns out of a dword of them as a 16-bit pair, mirrored at a
+    // frame edge. Registers: 8 bytes at hvoff. Staged: the aligned 16 bytes at hvoff go to LDS
+    // and the dword hlds (LDS dword index) is read back.
+    uint32_t hvoff;              // byte offset of the lane's halo load in the plane
+    uint32_t hsel;               // byte permutation: (column -2, column -1) or (+256, +257)
+    uint32_t hlds;               // staged: LDS dword index of the lane's halo dword
+    bool halo_fix;               // staged, generic: lane 63 when column e+1 = W mirrors e-1
+    // right frame edge inside the last strip (W % 256 != 0), fast path: the lane whose first
+    // column is W loads the group before it and permutes it into the mirror image
+    bool edge_tile;              // scalar: the last strip, with W inside it
+    bool mirror_right;           // lane whose first column is W: columns W, W+1 from W-2, W-3
+    uint32_t msel;               // 8-bit: the byte permutation doing the above (identity else)
+    // edges (generic path only)
+    bool right_fix;              // lane holding column W-1: mirror the columns right of it
+    int right_rem;               // scalar: W % 4
+    uint32_t ym0, ym1;           // luma sample masks for SSE (valid columns)
+    uint32_t cm;                 // chroma sample mask for SSE (valid columns)
+    bool c_upper;                // 8-bit: lane reads the second chroma row of each step
+};
+
+// The loaded samples of one frame for one tile: reference luma rows r0-2 .. r0+TH+1, distorted
+// luma rows r0 .. r0+TH-1, and the chroma dwords (ref U, dist U, ref V, dist V) of each step
+// (8-bit steps cover two chroma rows, one per half-wave).
+template <int BPC, int TH>
+struct FrameData {
+    typedef typename Px<BPC>::Luma Luma;
+    static constexpr int kChromaSteps = BPC == 8 ? TH / 4 : TH / 2;
+    static constexpr int kChromaStep = BPC == 8 ? 2 : 1;
+    static_assert(TH + 4 <= kWave / 2, "the transposed halo gives each tile row one lane per side");
+    Luma R[TH + 4];
+    Luma D[TH];
+    uint32_t cu[kChromaSteps], du[kChromaSteps], cv[kChromaSteps], dv[kChromaSteps];
+    u32x2 HL;  // the lane's 8 halo bytes (see Tile::hvoff)
+};
+
+// LDS staging of one 8-bit frame (one wavefront per workgroup, so the workgroup's LDS is the
+// wave's), in rows of 256 bytes (one dword per lane). Loads write LDS directly, 16 bytes per
+// lane, so one instruction moves 1 KB: four luma rows of the tile (16 lanes per row) or eight
+// chroma rows (8 lanes per row). A chroma LDS row holds two chroma rows, the second for the
+// upper half-wave, which is the order the chroma SSE steps read them in.
+template <int TH>
+struct Stage {
+    static constexpr int kRefLoads = (TH + 4) / 4;    // 16-byte loads of reference luma
+    static constexpr int kDistLoads = TH / 4;         // of distorted luma
+    static constexpr int kChromaLoads = (TH + 15) / 16;  // per chroma plane (8 rows each)
+    static constexpr int kChromaRows = 4 * kChromaLoads;  // LDS rows per chroma plane
+    static constexpr int kRef = 0;
+    static constexpr int kDist = TH + 4;
+    static constexpr int kChroma = kDist + TH;      // planes ref U, dist U, ref V, dist V
+    static constexpr int kHalo = kChroma + 4 * kChromaRows;  // four rows: 16 bytes per lane
+    static constexpr int kRows = kHalo + 4;
+    static_assert(TH % 4 == 0, "whole 16-byte luma loads");
+};
+
+// Per-lane byte offsets of a tile's staged loads, fixed for the whole launch: one per reference
+// luma load (rows mirrored at the frame's top and bottom edges), the distorted luma's and the
+// four chroma planes' (their rows advance through the scalar offset). Rows past the bottom of a
+// plane fall outside its buffer range and read as zero; they are never counted.
+template <int TH>
+struct StageOffsets {
+    uint32_t ref[Stage<TH>::kRefLoads];
+    uint32_t dist;
+    uint32_t chroma[4];
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS row `row` of a stage whose first row is at LDS byte address `base`. The base is passed
+// through opaque() once per frame, so each load's M0 is one scalar add instead of one of dozens
+// of precomputed addresses the compiler would otherwise keep (and spill) across the loop.
+__device__ __forceinline__ lds_void *lds_row(uint32_t base, int row)
+{
+    return (lds_void *)(uintptr_t)(base + (uint32_t)row * (kWave * 4u));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(uint32_t (*lds)[kWave])
+{
+    return (uint32_t)(uintptr_t)(lds_void *)&lds[0][0];
+}
+
+// Issue every load of frame t for this tile into registers (the distorted planes and chroma only
+// when the frame is accumulated; a chunk's prologue frame is only blurred).
+template <int BPC, int TH, bool GENERIC>
+__device__ __forceinline__ void load_frame(const KernelArgs &a, const Tile &T, int t,
+                                           bool accumulate, FrameData<BPC, TH> &F)
+{
+    typedef FrameData<BPC, TH> FD;
+    const int H = a.H;
+    Rsrc rs[6];
+    uint32_t pitch[6];
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+        rs[k] = plane_rsrc(frame_plane(a, t, k), a.span[k]);
+        pitch[k] = opaque((uint32_t)a.pitch[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < TH + 4; ++k) {
+        // only the two rows above and below the tile can fall outside the frame on the fast path
+        const int row = (GENERIC || k < 2 || k >= TH + 2) ? mirror_clamp(T.r0 - 2 + k, H)
+                                                          : T.r0 - 2 + k;
+        F.R[k] = ld_luma<BPC>(rs[0], T.luma_off, (uint32_t)row * pitch[0]);
+    }
+    F.HL = ld_luma<10>(rs[0], T.hvoff, 0u);
+    if (!accumulate)
+        return;
+#pragma unroll
+    for (int i = 0; i < TH; ++i) {
+        // rows past the frame re-read the last row; they are not counted
+        const int row = GENERIC ? min(T.r0 + i, H - 1) : T.r0 + i;
+        F.D[i] = ld_luma<BPC, kStream>(rs[3], T.luma_off, (uint32_t)row * pitch[3]);
+    }
+#pragma unroll
+    for (int k = 0; k < FD::kChromaSteps; ++k) {
+        // the upper half-wave's row is one further down (its coff adds a pitch); at a ragged
+        // bottom every lane whose row is past the plane re-reads the last row instead
+        const int row = T.crow0 + FD::kChromaStep * k;
+        const int rl = GENERIC ? min(row, a.Hc - 1) : row;
+        const bool back = GENERIC && T.c_upper && row + 1 >= a.Hc;
+        F.cu[k] = ld32<kStream>(rs[1], T.coff[0] - (back ? pitch[1] : 0u), (uint32_t)rl * pitch[1]);
+        F.du[k] = ld32<kStream>(rs[4], T.coff[1] - (back ? pitch[4] : 0u), (uint32_t)rl * pitch[4]);
+        F.cv[k] = ld32<kStream>(rs[2], T.coff[2] - (back ? pitch[2] : 0u), (uint32_t)rl * pitch[2]);
+        F.dv[k] = ld32<kStream>(rs[5], T.coff[3] - (back ? pitch[5] : 0u), (uint32_t)rl * pitch[5]);
+    }
+}
+
+// Issue every load of 8-bit frame t for this tile into the wavefront's LDS stage: 16 bytes per
+// lane per instruction, the reference luma and its halo always, the distorted luma and chroma
+// when the frame is accumulated.
+template <int TH>
+__device__ __forceinline__ void load_frame_staged(const KernelArgs &a, const Tile &T,
+                                                  const StageOffsets<TH> &O, int t,
+                                                  bool accumulate, uint32_t (*stage)[kWave])
+{
+    typedef Stage<TH> ST;
+    const uint32_t lds = opaque(lds_addr(stage));
+    auto dma16 = [&](Rsrc r, int lds_row0, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, lds_row0), 16, voff, soff, 0,
+                                                 kKeep);
+    };
+    auto dma16_stream = [&](Rsrc r, int lds_row0, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row(lds, lds_row0), 16, voff, soff, 0,
+                                                 kStream);
+    };
+    const Rsrc ry = plane_rsrc(frame_plane(a, t, 0), a.span[0]);
+#pragma unroll
+    for (int q = 0; q < ST::kRefLoads; ++q)
+        dma16(ry, ST::kRef + 4 * q, O.ref[q], 0u);
+    // transposed halo: one aligned 16-byte load per lane (lane k of each half-wave: tile row k-2)
+    dma16(ry, ST::kHalo, T.hvoff, 0u);
+    if (!accumulate)
+        return;
+    const Rsrc rd = plane_rsrc(frame_plane(a, t, 3), a.span[3]);
+    const uint32_t pd = opaque((uint32_t)a.pitch[3]);
+#pragma unroll
+    for (int q = 0; q < ST::kDistLoads; ++q)
+        dma16_stream(rd, ST::kDist + 4 * q, O.dist, (uint32_t)(T.r0 + 4 * q) * pd);
+    constexpr int pk[4] = {1, 4, 2, 5};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const Rsrc rc = plane_rsrc(frame_plane(a, t, pk[p]), a.span[pk[p]]);
+        const uint32_t pc = opaque((uint32_t)a.pitch[pk[p]]);
+#pragma unroll
+        for (int q = 0; q < ST::kChromaLoads; ++q)
+            dma16_stream(rc, ST::kChroma + p * ST::kChromaRows + 4 * q, O.chroma[p],
+                         (uint32_t)(T.crow0 + 8 * q) * pc);
+    }
+}
+
+// The staged 8-bit frame, from LDS into registers.
+template <int TH>
+__device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWave], int lane,
+                                           uint32_t hlds, FrameData<8, TH> &F)
+{
+    typedef FrameData<8, TH> FD;
+    typedef Stage<TH> ST;
+#pragma unroll
+    for (int k = 0; k < TH + 4; ++k)
+        F.R[k] = lds[ST::kRef + k][lane];
+    F.HL = u32x2{(&lds[0][0])[hlds], 0u};
+    if (!accumulate)
+        return;
+#pragma unroll
+    for (int i = 0; i < TH; ++i)
+        F.D[i] = lds[ST::kDist + i][lane];
+#pragma unroll
+    for (int k = 0; k < FD::kChromaSteps; ++k) {
+        F.cu[k] = lds[ST::kChroma + k][lane];
+        F.du[k] = lds[ST::kChroma + ST::kChromaRows + k][lane];
+        F.cv[k] = lds[ST::kChroma + 2 * ST::kChromaRows + k][lane];
+        F.dv[k] = lds[ST::kChroma + 3 * ST::kChromaRows + k][lane];
+    }
+}
+
+// Fast path, last strip with the frame's right edge inside it: the lane whose first column is W
+// loaded the group of columns W-4..W-1; it becomes (x[W-2], x[W-3], -, -) for columns W..W+3,
+// the mirror image the horizontal taps of the lane before it need. Columns W+2 and W+3 feed no
+// output.
+template <int BPC, int TH, bool STAGED>
+__device__ __forceinline__ void mirror_halo(const Tile &T, FrameData<BPC, TH> &F)
+{
+#pragma unroll
+    for (int k = 0; k < TH + 4; ++k) {
+        if constexpr (STAGED) {
+            // staged rows hold the lane's own columns W..W+3; the group W-4..W-1 comes from the
+            // lane to the left (every lane runs the shift; only the edge lane's selector uses it)
+            F.R[k] = perm(from_left(F.R[k]), F.R[k], T.msel);
+        } else if constexpr (BPC == 8) {
+            F.R[k] = perm(F.R[k], F.R[k], T.msel);
+        } else {
+            // (x[W-2] | x[W-3] << 16) from the second dword's low and the first dword's high half
+            const uint32_t m = perm(F.R[k].x, F.R[k].y, 0x07060100u);
+            F.R[k] = u32x2{T.mirror_right ? m : F.R[k].x, F.R[k].y};
+        }
+    }
+}
+
+// Vertical pass of the transposed halo. Lane k holds the two halo columns of tile row k - 2 (of
+// its side) as a 16-bit pair; rows k-2 .. k+2 come from the lanes around it. Lane i + 2 returns
+// the vertical values of output row i for the left side, lane i + 34 for the right side.
+template <int BPC>
+__device__ __forceinline__ uint32_t halo_vertical(u32x2 h, uint32_t hsel, uint32_t shift)
+{
+    constexpr uint32_t kVRound = BPC == 8 ? 128u : 32768u;
+    constexpr uint32_t kVSel = BPC == 8 ? 0x06050201u : 0x07060302u;
+    uint32_t x0 = perm(h.y, h.x, hsel);
+    if constexpr (BPC != 8)
+        x0 = to16<BPC>(x0, shift);
+    const uint32_t m1 = from_left(x0), m2 = from_left(m1);    // rows k-1, k-2
+    const uint32_t p1 = from_right(x0), p2 = from_right(p1);  // rows k+1, k+2
+    const uint32_t va = dot2u(p2 & 0xffffu, T0z,
+                              dot2u(perm(p1, x0, 0x05040100u), T21,
+                                    dot2u(perm(m1, m2, 0x05040100u), T01, kVRound)));
+    const uint32_t vb = dot2u(p2 >> 16, T0z,
+                              dot2u(perm(p1, x0, 0x07060302u), T21,
+                                    dot2u(perm(m1, m2, 0x07060302u), T01, kVRound)));
+    return perm(vb, va, kVSel);
+}
+
+// One frame of one tile from its loaded samples: blur the reference luma (vertical pass once per
+// column and row, horizontal taps through DPP neighbours), SAD against the previous blurred tile
+// held in registers, SSE of the luma and chroma tiles, one wavefront reduction and one atomic per
+// sum. GENERIC adds the frame-edge mirror fix-ups, ragged rows and masked tails; interior tiles
+// (the vast majority) run without any of it. MOM also sums the luma moments of ref and dist.
+template <int BPC, int TH, bool GENERIC, bool ROWSTAGE, bool MOM>
+__device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T, int t,
+                                              bool accumulate, FrameData<BPC, TH> &F,
+                                              const uint32_t (&prev0)[TH],
+                                              const uint32_t (&prev1)[TH], uint32_t (&next0)[TH],
+                                              uint32_t (&next1)[TH], uint32_t &sum_prev,
+                                              bool &have_prev,
+                                              Pending<MOM ? kMaxSums : kSums> &P)
+{
+    typedef typename Px<BPC>::Luma Luma;
+    typedef FrameData<BPC, TH> FD;
+    constexpr uint32_t kVRound = BPC == 8 ? 128u : 32768u;
+    constexpr uint32_t kVSel = BPC == 8 ? 0x06050201u : 0x07060302u;
+
+    if constexpr (!GENERIC) {
+        if (T.edge_tile)
+            mirror_halo<BPC, TH, ROWSTAGE>(T, F);
+    }
+    const uint32_t shift = (uint32_t)a.shift;
+    const uint32_t hv = halo_vertical<BPC>(F.HL, T.hsel, shift);
+
+    // SSE of the chroma tiles first, which frees their registers before the blur
+    Sq<BPC> su = 0, sv = 0;
+    uint32_t su2 = 0, sv2 = 0;
+    if (accumulate) {
+#pragma unroll
+        for (int k = 0; k < FD::kChromaSteps; ++k) {
+            uint32_t ru = F.cu[k], rdu = F.du[k], rv = F.cv[k], rdv = F.dv[k];
+            if constexpr (GENERIC) {
+                const int row = T.crow0 + FD::kChromaStep * k + (T.c_upper ? 1 : 0);
+                const uint32_t m = row < a.Hc ? T.cm : 0u;
+                ru &= m;
+                rdu &= m;
+                rv &= m;
+                rdv &= m;
+            }
+            sse_chroma<BPC>(ru, rdu, su, su2);
+            sse_chroma<BPC>(rv, rdv, sv, sv2);
+        }
+    }
+
+    // blur, SAD against the previous blurred tile, and SSE of the luma rows as they go by
+    uint32_t acc_c = 0, acc_min = 0, sy2 = 0, m1r = 0, m1d = 0;
+    Sq<BPC> sy = 0, m2r = 0, m2d = 0;
+#pragma unroll
+    for (int i = 0; i < TH; ++i) {
+        uint32_t pa[4], pb[4], pc[4];
+        const Luma zero{};
+        column_pairs<BPC>(F.R[i], F.R[i + 1], pa, shift);      // rows i-2, i-1
+        column_pairs<BPC>(F.R[i + 2], F.R[i + 3], pb, shift);  // rows i,   i+1
+        column_pairs<BPC>(F.R[i + 4], i + 5 < TH + 4 ? F.R[i + 5] : zero, pc,
+                          shift);  // rows i+2 (tap 0 on i+3)
+        uint32_t v[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            v[b] = dot2u(pc[b], T0z, dot2u(pb[b], T21, dot2u(pa[b], T01, kVRound)));
+        uint32_t q0 = perm(v[1], v[0], kVSel);  // V of columns c, c+1
+        uint32_t q1 = perm(v[3], v[2], kVSel);  // V of columns c+2, c+3
+        // V of columns c-2, c-1: the lane to the left, or the left halo for lane 0
+        const uint32_t hl = (uint32_t)__builtin_amdgcn_readlane((int)hv, i + 2);
+        uint32_t ql = from_left_or(q1, hl);
+        // generic path: (V(c+2), V(c+1)), the mirror image of the lane's own columns, stands for
+        // columns W, W+1 at the right frame edge when W % 4 == 0
+        const uint32_t mirrored = GENERIC ? perm(q0, q1, 0x07060100u) : 0u;
+        if constexpr (GENERIC) {
+            if (T.right_rem == 1) {  // columns W, W+1 -> W-2, W-3
+                q0 = T.right_fix ? perm(ql, q0, 0x07060100u) : q0;
+                q1 = T.right_fix ? ql : q1;
+            } else if (T.right_rem == 2) {
+                q1 = T.right_fix ? perm(ql, q0, 0x07060100u) : q1;
+            } else if (T.right_rem == 3) {
+                q1 = T.right_fix ? perm(q0, q1, 0x07060100u) : q1;
+            }
+        }
+        // V of columns c+4, c+5: the lane to the right, or the right halo for lane 63
+        const uint32_t hr = (uint32_t)__builtin_amdgcn_readlane((int)hv, i + kWave / 2 + 2);
+        uint32_t qr = from_right_or(q0, hr);
+        if constexpr (GENERIC && ROWSTAGE)
+            qr = T.halo_fix ? perm(q1, qr, 0x07060100u) : qr;  // (V(e), V(e-1))
+        if constexpr (GENERIC) {
+            if (T.right_rem == 0)
+                qr = T.right_fix ? mirrored : qr;
+            else if (T.right_rem == 3)
+                qr = T.right_fix ? q0 : qr;
+        }
+        const uint32_t h0 = dot2u(q1, T0z, dot2u(q0, T21, dot2u(ql, T01, 32768u)));
+        const uint32_t h1 = dot2u(q1, T10, dot2u(q0, T12, dot2u(ql, Tz0, 32768u)));
+        const uint32_t h2 = dot2u(qr, T0z, dot2u(q1, T21, dot2u(q0, T01, 32768u)));
+        const uint32_t h3 = dot2u(qr, T10, dot2u(q1, T12, dot2u(q0, Tz0, 32768u)));
+        const uint32_t c0 = perm(h1, h0, 0x07060302u);  // Bl of columns c, c+1
+        const uint32_t c1 = perm(h3, h2, 0x07060302u);  // Bl of columns c+2, c+3
+        if (!GENERIC || i < T.rows_valid) {
+            acc_c = dot2u(c1, T.w1, dot2u(c0, T.w0, acc_c));
+            acc_min = dot2u(pkmin(c1, prev1[i]), T.w1, dot2u(pkmin(c0, prev0[i]), T.w0, acc_min));
+            if (accumulate) {
+                Luma r = F.R[i + 2], d = F.D[i];
+                if constexpr (GENERIC) {
+                    r = masked<BPC>(r, T.ym0, T.ym1);
+                    d = masked<BPC>(d, T.ym0, T.ym1);
+                }
+                if constexpr (MOM)
+                    moments_luma<BPC>(r, d, m1r, m1d, m2r, m2d, sy, sy2);
+                else
+                    sse_luma<BPC>(r, d, sy, sy2);
+            }
+        }
+        next0[i] = c0;
+        next1[i] = c1;
+    }
+
+    if (accumulate) {
+        const uint32_t sad = have_prev ? acc_c + sum_prev - 2u * acc_min : 0u;
+        // squared errors: 8-bit sy (or, with moments, m2r + m2d) holds sum r^2 + d^2 and sy2
+        // sum r d; deeper samples keep the difference squares in sy (su, sv likewise)
+        Sq<BPC> ey = sy, eu = su, ev = sv;
+        if constexpr (BPC == 8) {
+            ey = (MOM ? m2r + m2d : sy) - 2u * sy2;
+            eu = su - 2u * su2;
+            ev = sv - 2u * sv2;
+        }
+        const Sq<BPC> zero = 0;
+        if constexpr (MOM) {
+            const unsigned long long sums[kMaxSums] = {
+                wave_sum(sad),
+                wave_sum_sq(T.out_lane ? ey : zero),
+                wave_sum_sq(T.c_on ? eu : zero),
+                wave_sum_sq(T.c_on ? ev : zero),
+                wave_sum(T.out_lane ? m1r : 0u),
+                wave_sum(T.out_lane ? m1d : 0u),
+                wave_sum_sq(T.out_lane ? m2r : zero),
+                wave_sum_sq(T.out_lane ? m2d : zero)};
+            push_sums(a, P, T.lane, sums);
+        } else {
+            const unsigned long long sums[kSums] = {wave_sum(sad),
+                                                    wave_sum_sq(T.out_lane ? ey : zero),
+                                                    wave_sum_sq(T.c_on ? eu : zero),
+                                                    wave_sum_sq(T.c_on ? ev : zero)};
+            push_sums(a, P, T.lane, sums);
+        }
+    }
+    sum_prev = acc_c;
+    have_prev = true;
+}
+
+// The frames of this workgroup's time chunk. Chunks after the first start by re-blurring the
+// frame before them. STAGED keeps the next frame's loads in flight while the current one is
+// computed: the loads of frame t+1 write the wave's LDS stage (no registers held), issued as soon
+// as frame t has been read out of it. Frames go in pairs that swap the roles of two blurred-tile
+// register sets (prev -> alt -> prev), so no frame ends by copying its blurred tile back.
+template <int BPC, int TH, bool GENERIC, bool STAGED, bool MOM>
+__device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
+                                           const StageOffsets<TH> &O, uint32_t (&prev0)[TH],
+                                           uint32_t (&prev1)[TH], uint32_t sum_prev,
+                                           bool have_prev, uint32_t (*lds)[kWave])
+{
+    const int f_begin = uni(T.chunk * a.chunk_len);
+    const int f_end = uni(min(f_begin + a.chunk_len, a.nframes));
+    const int t0 = T.chunk > 0 ? f_begin - 1 : f_begin;
+    constexpr int NS = MOM ? kMaxSums : kSums;
+    Pending<NS> P;
+#pragma unroll
+    for (int k = 0; k < 2 * NS; ++k)
+        P.v[k] = 0;
+    P.first = f_begin;
+    P.count = 0;
+    if constexpr (STAGED)
+        load_frame_staged<TH>(a, T, O, t0, t0 >= f_begin, lds);
+    // one frame: blurred tile in (i0, i1), out to (o0, o1)
+    auto step = [&](int t, const uint32_t(&i0)[TH], const uint32_t(&i1)[TH], uint32_t(&o0)[TH],
+                    uint32_t(&o1)[TH]) {
+        // a fresh frame per step: no sample register is carried from one frame to the next
+        FrameData<BPC, TH> F;
+        if constexpr (STAGED) {
+            // raised priority from the wait to the last load issued: a wavefront whose frame has
+            // landed reads it out and refills the memory pipe ahead of its SIMD's computing waves
+            __builtin_amdgcn_s_setprio(3);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): frame t is in LDS
+            read_stage<TH>(t >= f_begin, lds, T.lane, T.hlds, F);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 1 < f_end)
+                load_frame_staged<TH>(a, T, O, t + 1, true, lds);
+            __builtin_amdgcn_s_setprio(0);
+        } else {
+            load_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F);
+        }
+        compute_frame<BPC, TH, GENERIC, STAGED, MOM>(a, T, t, t >= f_begin, F, i0, i1, o0, o1,
+                                                     sum_prev, have_prev, P);
+    };
+    uint32_t alt0[TH], alt1[TH];
+    for (int t = t0; t < f_end; t += 2) {
+        step(t, prev0, prev1, alt0, alt1);
+        if (t + 1 < f_end) {
+            step(t + 1, alt0, alt1, prev0, prev1);
+        } else {
+#pragma unroll
+            for (int i = 0; i < TH; ++i) {
+                prev0[i] = alt0[i];
+                prev1[i] = alt1[i];
+            }
+        }
+    }
+    flush_sums(a, P, T.lane);
+}
+
+// The launch's last workgroup to finish (counted with one device-scope atomic per workgroup)
+// folds the kSumSlots partial sums of each of the NS sums of every frame, writes the totals straight to the
+// caller-visible pinned buffer and zeroes the partial sums and the counter for the next launch.
+// No workgroup waits for another, and no separate readback copy follows the kernel. Ordering:
+// the sum atomics are device-scope read-modify-writes; each workgroup waits until its own have
+// completed (vmcnt(0)) before counting itself, and the last one reads them back with
+// device-scope atomic loads after an acquire fence. A release fence per workgroup would write
+// back every XCD's L2 once per workgroup, which costs far more than the copy it replaces.
+template <int NS>
+__device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane)
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this workgroup's sum atomics completed
+    unsigned int arrived = 0;
+    if (lane == 0)
+        arrived = __hip_atomic_fetch_add(a.arrivals, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    arrived = (unsigned int)uni((int)arrived);
+    if (arrived != gridDim.x - 1u)
+        return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // kPer totals per lane per pass, all of their slot loads issued before any is added, so a
+    // pass costs one memory round trip (a 64-frame launch is one pass)
+    constexpr int kPer = 4;
+    const int n = a.nframes * NS;
+    for (int base = 0; base < n; base += kPer * kWave) {
+        unsigned long long v[kPer][kSumSlots];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int i = min(base + q * kWave + lane, n - 1);
+#pragma unroll
+            for (int j = 0; j < kSumSlots; ++j)
+                v[q][j] = __hip_atomic_load(a.sums + (size_t)i * kSumSlots + j, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int i = base + q * kWave + lane;
+            if (i < n) {
+                unsigned long long total = 0;
+#pragma unroll
+                for (int j = 0; j < kSumSlots; ++j) {
+                    total += v[q][j];
+                    __hip_atomic_store(a.sums + (size_t)i * kSumSlots + j, 0ull,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __hip_atomic_store(a.publish + i, total, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+        }
+    }
+    if (lane == 0)
+        __hip_atomic_store(a.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the end of the kernel releases these stores to the host before its completion signal
+}
+
+template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE, bool MOM>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void
+frames_kernel(const KernelArgs a)
+{
+    __shared__ uint32_t stage[STAGED ? Stage<TH>::kRows : 1][kWave];
+    static_assert(TH % 4 == 0, "tile height must be a multiple of 4 (two chroma rows per step)");
+    static_assert(!STAGED || BPC == 8, "LDS staging is laid out for 8-bit samples");
+    constexpr int B = Px<BPC>::kBytes;
+    const int lane = threadIdx.x;
+
+    Tile T;
+    const int L = uni(xcd_linear(blockIdx.x, gridDim.x));
+    T.chunk = uni(L / a.tiles);
+    T.tile = uni(L - T.chunk * a.tiles);
+    const int rt = uni(T.tile / a.strips);
+    T.strip = uni(T.tile - rt * a.strips);
+    T.r0 = uni(rt * TH);                     // first output row of the tile
+    const int s = uni(T.strip * kStripCols);  // first column of the tile
+    T.lane = lane;
+    const int W = a.W, H = a.H;
+    T.rows_valid = uni(min(TH, H - T.r0));
+
+    // lane roles; every load offset stays inside its row's pitch (a lane whose first column is
+    // outside [0, W) reads column 0 and its values are never used)
+    const int c = s + kLumaCols * lane;
+    T.luma_off = c < W ? (uint32_t)(c * B)
+                 : (!GENERIC && c == W) ? (uint32_t)((W - kLumaCols) * B)
+                                        : 0u;
+    T.out_lane = c < W;
+    T.w0 = (c < W ? 1u : 0u) | (c + 1 < W ? 0x10000u : 0u);
+    T.w1 = (c + 2 < W ? 1u : 0u) | (c + 3 < W ? 0x10000u : 0u);
+    T.edge_tile = T.strip == a.strips - 1 && W % kStripCols != 0;
+    T.mirror_right = c == W;
+    // byte permutation building columns W, W+1 from W-2, W-3: staged, from the left neighbour's
+    // group (the perm's high operand); else from the lane's own reload of W-4..W-1
+    T.msel = T.mirror_right ? (STAGED ? 0x04040506u : 0x00000102u) : 0x03020100u;
+    T.right_rem = W & 3;
+    // the lane holding column W-1 (on the fast path W % 4 == 0, so its columns end at W-1)
+    T.right_fix = c <= W - 1 && W - 1 < c + kLumaCols;
+    if constexpr (BPC == 8) {
+        T.ym0 = (c < W ? 0xffu : 0u) | (c + 1 < W ? 0xff00u : 0u) | (c + 2 < W ? 0xff0000u : 0u) |
+                (c + 3 < W ? 0xff000000u : 0u);
+        T.ym1 = 0u;
+    } else {
+        T.ym0 = (c < W ? 0xffffu : 0u) | (c + 1 < W ? 0xffff0000u : 0u);
+        T.ym1 = (c + 2 < W ? 0xffffu : 0u) | (c + 3 < W ? 0xffff0000u : 0u);
+    }
+
+    // transposed horizontal halo: 8 bytes of row r0 - 2 + k per lane, inside the row's pitch.
+    // Selectors give (column a, column b) as a 16-bit pair: 8-bit picks bytes (0x0c = zero),
+    // 10-bit picks 16-bit samples.
+    {
+        const int k = min(lane & (kWave / 2 - 1), TH + 3);
+        const int hrow = mirror_clamp(T.r0 - 2 + k, H);
+        const int e = s + kStripCols;  // first column right of the tile
+        int col;
+        uint32_t sel;
+        if (lane < kWave / 2) {
+            if (T.strip == 0) {  // columns -2, -1 mirror 2, 1
+                col = 0;
+                sel = BPC == 8 ? 0x0c010c02u : 0x03020504u;
+            } else {  // columns s-2, s-1
+                col = s - 4;
+                sel = BPC == 8 ? 0x0c030c02u : 0x07060504u;
+            }
+        } else if (e < W - 1) {  // columns e, e+1
+            col = BPC == 8 ? e - 4 : e;
+            sel = BPC == 8 ? 0x0c050c04u : 0x03020100u;
+        } else if (e == W - 1) {  // column e, then e+1 = W mirrors W-2 = e-1
+            col = BPC == 8 ? e - 4 : e - 2;
+            sel = BPC == 8 ? 0x0c030c04u : 0x03020504u;
+        } else if (e == W) {  // columns W, W+1 mirror W-2, W-3
+            col = BPC == 8 ? W - 8 : W - 4;
+            sel = BPC == 8 ? 0x0c050c06u : 0x03020504u;
+        } else {  // the frame ends inside the tile: unused
+            col = 0;
+            sel = 0u;
+        }
+        T.hvoff = (uint32_t)(col * B) + (uint32_t)hrow * (uint32_t)a.pitch[0];
+        T.hsel = sel;
+        T.hlds = 0u;
+        T.halo_fix = false;
+        if constexpr (STAGED) {
+            // 16-byte aligned chunks: left, the chunk ending at s (its last dword holds columns
+            // s-4..s-1) or at the frame edge the first chunk (columns 0..3); right, the chunk
+            // starting at e, or the one ending at W when the frame ends at e
+            int chunk, dw;
+            if (lane < kWave / 2) {
+                chunk = T.strip == 0 ? 0 : s - 16;
+                dw = T.strip == 0 ? 0 : 3;
+                sel = T.strip == 0 ? 0x0c010c02u : 0x0c030c02u;
+            } else if (e < W) {
+                chunk = e;
+                dw = 0;
+                sel = 0x0c010c00u;  // columns e, e+1 (e+1 = W is fixed up by halo_fix)
+            } else if (e == W) {
+                chunk = W - 16;
+                dw = 3;
+                sel = 0x0c010c02u;
+            } else {
+                chunk = 0;
+                dw = 0;
+                sel = 0u;
+            }
+            T.hvoff = (uint32_t)chunk + (uint32_t)hrow * (uint32_t)a.pitch[0];
+            T.hsel = sel;
+            T.hlds = (uint32_t)(Stage<TH>::kHalo * kWave + 4 * lane + dw);
+            T.halo_fix = lane == kWave - 1 && e == W - 1;
+        }
+    }
+
+    // chroma split: 8-bit, 32 lanes (one dword each) per chroma row and two rows per step (the
+    // upper half-wave takes the second); 10-bit, one row per step, 64 dwords
+    const int cs = s / 2;  // first chroma sample of the tile
+    int ccol;
+    if constexpr (BPC == 8) {
+        ccol = cs + 4 * (lane & 31);
+        T.c_upper = lane >= 32;
+        T.c_on = ccol < a.Wc;
+        T.cm = (ccol < a.Wc ? 0xffu : 0u) | (ccol + 1 < a.Wc ? 0xff00u : 0u) |
+               (ccol + 2 < a.Wc ? 0xff0000u : 0u) | (ccol + 3 < a.Wc ? 0xff000000u : 0u);
+    } else {
+        ccol = cs + 2 * lane;
+        T.c_upper = false;
+        T.c_on = ccol < a.Wc;
+        T.cm = (ccol < a.Wc ? 0xffffu : 0u) | (ccol + 1 < a.Wc ? 0xffff0000u : 0u);
+    }
+    T.crow0 = uni(T.r0 / 2);
+    {
+        const uint32_t col = T.c_on ? (uint32_t)(ccol * B) : 0u;
+        const int pk[4] = {1, 4, 2, 5};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            T.coff[k] = col + (T.c_upper ? (uint32_t)a.pitch[pk[k]] : 0u);
+    }
+
+    // previous blurred tile: from the launch before, else none (chunk 0), or re-blurred by the
+    // chunk's prologue (later chunks)
+    uint32_t prev0[TH], prev1[TH];
+    uint32_t sum_prev = 0;
+    bool have_prev = false;
+    if (T.chunk == 0 && a.has_prev) {
+        const uint2 *rin = reinterpret_cast<const uint2 *>(a.ring_in);
+#pragma unroll
+        for (int i = 0; i < TH; ++i) {
+            const uint2 v = rin[(T.tile * TH + i) * kWave + lane];
+            prev0[i] = v.x;
+            prev1[i] = v.y;
+            if (i < T.rows_valid)
+                sum_prev = dot2u(v.y, T.w1, dot2u(v.x, T.w0, sum_prev));
+        }
+        have_prev = true;
+    } else {
+#pragma unroll
+        for (int i = 0; i < TH; ++i)
+            prev0[i] = prev1[i] = 0;
+    }
+
+    // every tile of a launch takes the same path, so wavefronts cost the same and none trails
+    // staged: per-lane offsets of the 16-byte loads (16 lanes per luma row, 8 per chroma row)
+    StageOffsets<TH> O;
+    if constexpr (STAGED) {
+#pragma unroll
+        for (int q = 0; q < Stage<TH>::kRefLoads; ++q) {
+            const int row = mirror_clamp(T.r0 - 2 + 4 * q + (lane >> 4), H);
+            O.ref[q] = (uint32_t)(s + 16 * (lane & 15)) + (uint32_t)row * (uint32_t)a.pitch[0];
+        }
+        O.dist = (uint32_t)(s + 16 * (lane & 15)) + (uint32_t)(lane >> 4) * (uint32_t)a.pitch[3];
+        const int pk[4] = {1, 4, 2, 5};
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            O.chroma[p] = (uint32_t)(s / 2 + 16 * (lane & 7)) +
+                          (uint32_t)(lane >> 3) * (uint32_t)a.pitch[pk[p]];
+    }
+
+    frame_loop<BPC, TH, GENERIC, STAGED, MOM>(a, T, O, prev0, prev1, sum_prev, have_prev, stage);
+
+    // counted before the state write, so the count waits only for this workgroup's sum atomics
+    publish_if_last<MOM ? kMaxSums : kSums>(a, lane);
+
+    if (T.chunk == a.chunks - 1) {
+        uint2 *rout = reinterpret_cast<uint2 *>(a.ring_out);
+#pragma unroll
+        for (int i = 0; i < TH; ++i)
+            rout[(T.tile * TH + i) * kWave + lane] = make_uint2(prev0[i], prev1[i]);
+    }
+}
+
+
+#ifndef IIR_STAGE8
+#define IIR_STAGE8 1
+#endif
+#ifndef IIR_STAGE10
+#define IIR_STAGE10 0
+#endif
+#ifndef IIR_WPE12
+#define IIR_WPE12 3
+#endif
+#ifndef IIR_WPE16
+#define IIR_WPE16 2
+#endif
+#ifndef IIR_WPE20
+#define IIR_WPE20 2
+#endif
+
+// Every (bit depth, tile height, path) the host may pick. The fast path needs W % 8 == 0 and
+// H % TH == 0 (no ragged tile, no partial sample group); the generic path takes any size.
+template <int BPC, bool GENERIC, bool MOM>
+FramesFn frames_fn(int th)
+{
+    constexpr bool P = BPC == 8 ? IIR_STAGE8 : IIR_STAGE10;
+    switch (th) {
+    case 12:
+        return frames_kernel<BPC, 12, P, GENERIC, IIR_WPE12, MOM>;
+    case 16:
+        return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16, MOM>;
+    case 20:
+        return frames_kernel<BPC, 20, P, GENERIC, IIR_WPE20, MOM>;
+    default:
+        return nullptr;
+    }
+}
+
+}  // namespace
+}  // namespace iir

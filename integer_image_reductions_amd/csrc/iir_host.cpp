@@ -1,5 +1,6 @@
 // iir_host.cpp -- the C ABI of include/iir.h: argument checks, context lifetime, the submission
-// queue and the score derivation. All device work goes to the gfx950 kernels in iir_kernels.hip.
+// queue and the score derivation. All device work goes to the gfx950 kernels (iir_frames.h and
+// iir_kernels.hip).
 //
 // Per submission the context enqueues, on the caller's stream: (only for a non-uniformly strided
 // clip) one host-to-device copy of the frame table, one kernel launch, whose last workgroup writes

@@ -1,6 +1,6 @@
 // iir_internal.h -- the contract between the host library (iir_host.cpp) and the gfx950 kernels
-// (iir_kernels.hip): tile geometry constants and the one argument struct every launch takes by
-// value. One header for both sides, so the host sizes grids and buffers with the numbers the
+// (iir_frames.h, iir_frames_*.hip, iir_kernels.hip): tile geometry constants and the one argument
+// struct every launch takes by value. One header for both sides, so the host sizes grids and buffers with the numbers the
 // kernels assume ("ADR-1392: CUDA motion, PSNR and moment kernels add one atomic per block ...",
 // Decision 2 keeps the PSNR block geometry in one header shared by the kernel and its dispatch).
 #pragma once
@@ -50,6 +50,13 @@ struct KernelArgs {
     int32_t has_prev;
     int32_t shift;  // 16-bit samples: 16 - bit depth, the left shift that scales them to 16 bits
 };
+
+// The frames kernel of one configuration, or nullptr: one function per sample type, each in its
+// own translation unit (iir_frames_8.hip, iir_frames_10.hip, iir_frames_16.hip).
+typedef void (*FramesFn)(KernelArgs);
+FramesFn frames_pick_8(int th, bool generic, bool moments);
+FramesFn frames_pick_10(int th, bool generic, bool moments);
+FramesFn frames_pick_16(int th, bool generic, bool moments);
 
 // Host-side launchers (iir_kernels.hip). Each returns the launch's hipError_t.
 bool supported_rows_per_tile(int th);           // 12, 16 or 20

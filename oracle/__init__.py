@@ -13,8 +13,10 @@ from .oracle import (  # noqa: F401
     blur,
     build,
     clip,
+    clip_v2,
     compile_source,
     default,
+    diff_blur,
     library_path,
     moments,
     motion2,

@@ -27,6 +27,15 @@
  *    sum of |Bl_t - Bl_(t-1)| over the luma plane of the reference video, for every frame that has
  *    a previous frame; the first frame of a clip without a previous frame has no SAD (0, flagged).
  *
+ *  - Motion v2, difference first ("ADR-1392", Decision 4: the kernel stages prev - cur and runs
+ *    the separable filter on it, vertical pass rounded by the bit depth, horizontal by 16;
+ *    "Larger motion tiles ..." alternative: the horizontal sum needs 33 bits): the same taps and
+ *    mirror on the signed difference D = prev - cur of consecutive reference luma frames. The
+ *    shifts of negative sums are read as floor (arithmetic shifts), with the same half-divisor
+ *    added first; SAD2 = sum of |F| over the plane.
+ *      V2[i][j] = floor((sum_k g_k D[m(i+k-2, H)][j] + 2^(bpc-1)) / 2^bpc)
+ *      F[i][j]  = floor((sum_l g_l V2[i][m(j+l-2, W)] + 2^15) / 2^16)
+ *
  *  - Derived scores (host doubles; "ADR-1392", Consequences lists psnr_*, mse_* and the motion
  *    scores): motion = SAD / (256 W H); mse_c = SSE_c / (W_c H_c); psnr_c = 10 log10(peak^2 / mse_c)
  *    with peak = 2^bpc - 1, +inf when SSE_c = 0. Build with -ffp-contract=off.
@@ -226,6 +235,94 @@ int iiro_clip(const void *ry, const void *ru, const void *rv, const void *dy, co
         memcpy(last_blur, prev, sizeof(uint16_t) * (size_t)n);
     free(prev);
     free(cur);
+    return rc;
+}
+
+/* floor(x / 2^s) for any sign of x, written out rather than left to the shift of a negative */
+static int64_t floor_shift(int64_t x, int s)
+{
+    const int64_t d = (int64_t)1 << s;
+    return x >= 0 ? x / d : -((-x + d - 1) / d);
+}
+
+/*
+ * Motion v2 filter of one frame pair: out (w x h int32, row pitch out_pitch elements) receives F,
+ * the separable filter of prev - cur with floor rounding. prev and cur share `pitch`.
+ */
+int iiro_diff_blur(const void *prev, const void *cur, int64_t pitch, int32_t w, int32_t h,
+                   int32_t bpc, int32_t *out, int64_t out_pitch)
+{
+    if (!prev || !cur || !out || bad_dims(w, h, bpc) || w < 3 || h < 3 || out_pitch < w)
+        return IIRO_EINVAL;
+    if (check_range(prev, pitch, w, h, bpc) || check_range(cur, pitch, w, h, bpc))
+        return IIRO_ERANGE;
+    int32_t g[5];
+    if (iiro_taps(g))
+        return IIRO_EINVAL;
+    int64_t *v = (int64_t *)malloc(sizeof(int64_t) * (size_t)w * (size_t)h);
+    if (!v)
+        return IIRO_ENOMEM;
+    /* vertical pass on the difference, floor after adding half of 2^bpc */
+    for (int64_t i = 0; i < h; ++i)
+        for (int64_t j = 0; j < w; ++j) {
+            int64_t acc = 0;
+            for (int k = 0; k < 5; ++k) {
+                const int64_t r = mirror(i + k - 2, h);
+                acc += (int64_t)g[k] * (sample(prev, pitch, r, j, bpc) - sample(cur, pitch, r, j, bpc));
+            }
+            v[i * w + j] = floor_shift(acc + ((int64_t)1 << (bpc - 1)), bpc);
+        }
+    /* horizontal pass, floor after adding 2^15 */
+    for (int64_t i = 0; i < h; ++i)
+        for (int64_t j = 0; j < w; ++j) {
+            int64_t acc = 0;
+            for (int l = 0; l < 5; ++l)
+                acc += (int64_t)g[l] * v[i * w + mirror(j + l - 2, w)];
+            out[i * out_pitch + j] = (int32_t)floor_shift(acc + 32768, 16);
+        }
+    free(v);
+    return IIRO_OK;
+}
+
+/*
+ * A clip with motion v2: like iiro_clip, but out[4 t] is SAD2 of frames t - 1 and t (sum |F|).
+ * prev_luma, when not NULL, is the reference luma of the frame before the clip (w x h samples,
+ * contiguous), so frame 0 also has a SAD2.
+ */
+int iiro_clip_v2(const void *ry, const void *ru, const void *rv, const void *dy, const void *du,
+                 const void *dv, int32_t nframes, int32_t w, int32_t h, int32_t bpc,
+                 const void *prev_luma, uint64_t *out, int32_t *has_motion)
+{
+    if (!ry || !ru || !rv || !dy || !du || !dv || !out || !has_motion || nframes < 1 ||
+        bad_dims(w, h, bpc) || w < 3 || h < 3)
+        return IIRO_EINVAL;
+    const int64_t bps = bpc == 8 ? 1 : 2;
+    const int32_t wc = (w + 1) / 2, hc = (h + 1) / 2;
+    const int64_t ybytes = (int64_t)w * h * bps, cbytes = (int64_t)wc * hc * bps;
+    int32_t *f = (int32_t *)malloc(sizeof(int32_t) * (size_t)w * (size_t)h);
+    if (!f)
+        return IIRO_ENOMEM;
+    int rc = IIRO_OK;
+    for (int64_t t = 0; t < nframes && rc == IIRO_OK; ++t) {
+        const uint8_t *fy = (const uint8_t *)ry + t * ybytes, *gy = (const uint8_t *)dy + t * ybytes;
+        const uint8_t *fu = (const uint8_t *)ru + t * cbytes, *gu = (const uint8_t *)du + t * cbytes;
+        const uint8_t *fv = (const uint8_t *)rv + t * cbytes, *gv = (const uint8_t *)dv + t * cbytes;
+        const void *before = t > 0 ? (const void *)(fy - ybytes) : prev_luma;
+        uint64_t *o = out + 4 * t;
+        rc = iiro_sse(fy, w * bps, gy, w * bps, w, h, bpc, &o[1]);
+        if (!rc)
+            rc = iiro_sse(fu, wc * bps, gu, wc * bps, wc, hc, bpc, &o[2]);
+        if (!rc)
+            rc = iiro_sse(fv, wc * bps, gv, wc * bps, wc, hc, bpc, &o[3]);
+        o[0] = 0;
+        has_motion[t] = before != NULL;
+        if (!rc && before) {
+            rc = iiro_diff_blur(before, fy, w * bps, w, h, bpc, f, w);
+            for (int64_t n = 0; !rc && n < (int64_t)w * h; ++n)
+                o[0] += (uint64_t)(f[n] < 0 ? -(int64_t)f[n] : (int64_t)f[n]);
+        }
+    }
+    free(f);
     return rc;
 }
 

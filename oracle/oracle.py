@@ -88,8 +88,11 @@ class OracleLib:
         lib.iiro_moments.argtypes = [vp, i64, i32, i32, i32, vp]
         lib.iiro_motion2.argtypes = [vp, i32, vp]
         lib.iiro_aggregate.argtypes = [i32, i32, i32, vp, vp, i32, vp]
+        lib.iiro_diff_blur.argtypes = [vp, vp, i64, i32, i32, i32, vp, i64]
+        lib.iiro_clip_v2.argtypes = [vp] * 6 + [i32, i32, i32, i32, vp, vp, vp]
         for f in (lib.iiro_taps, lib.iiro_sse, lib.iiro_blur, lib.iiro_sad, lib.iiro_clip,
-                  lib.iiro_scores, lib.iiro_moments, lib.iiro_motion2, lib.iiro_aggregate):
+                  lib.iiro_scores, lib.iiro_moments, lib.iiro_motion2, lib.iiro_aggregate,
+                  lib.iiro_diff_blur, lib.iiro_clip_v2):
             f.restype = ctypes.c_int
         self.path = path
         self._lib = lib
@@ -159,6 +162,43 @@ class OracleLib:
             return out, hm, last
         return out, hm
 
+    def diff_blur(self, prev: np.ndarray, cur: np.ndarray, bpc: int) -> np.ndarray:
+        """Motion v2 filter F of prev - cur, an (H, W) int32 array."""
+        p, c = _plane(prev, bpc), _plane(cur, bpc)
+        if p.shape != c.shape or p.strides != c.strides:
+            raise OracleError("prev and cur must be planes of one shape")
+        h, w = p.shape
+        out = np.zeros((h, w), dtype=np.int32)
+        _check(self._lib.iiro_diff_blur(_ptr(p), _ptr(c), p.strides[0], w, h, bpc, _ptr(out), w),
+               "diff_blur")
+        return out
+
+    def clip_v2(self, ref, dist, bpc: int, prev_luma: np.ndarray | None = None):
+        """Run a clip with motion v2: (sums (F, 4) uint64 {SAD2, SSE_Y, SSE_U, SSE_V},
+        has_motion). prev_luma is the reference luma of the frame before the clip, if any."""
+        dt = _dtype(bpc)
+        planes = [np.ascontiguousarray(p) for p in (*ref, *dist)]
+        for p in planes:
+            if p.dtype != dt or p.ndim != 3:
+                raise OracleError("clip planes must be 3-D arrays of the bit depth's dtype")
+        f, h, w = planes[0].shape
+        hc, wc = (h + 1) // 2, (w + 1) // 2
+        for i, p in enumerate(planes):
+            want = (f, h, w) if i % 3 == 0 else (f, hc, wc)
+            if p.shape != want:
+                raise OracleError(f"plane {i} has shape {p.shape}, expected {want}")
+        pl = None
+        if prev_luma is not None:
+            pl = np.ascontiguousarray(prev_luma)
+            if pl.dtype != dt or pl.shape != (h, w):
+                raise OracleError("prev_luma must be an (H, W) plane of the bit depth's dtype")
+        out = np.zeros((f, 4), dtype=np.uint64)
+        hm = np.zeros(f, dtype=np.int32)
+        _check(self._lib.iiro_clip_v2(*[_ptr(p) for p in planes], f, w, h, bpc,
+                                      _ptr(pl) if pl is not None else None, _ptr(out), _ptr(hm)),
+               "clip_v2")
+        return out, hm
+
     def scores(self, w: int, h: int, bpc: int, sums, has_motion: int) -> dict:
         s = np.ascontiguousarray(np.asarray(sums, dtype=np.uint64).reshape(4))
         out = np.zeros(7, dtype=np.float64)
@@ -224,6 +264,14 @@ def clip(ref, dist, bpc, prev_blur=None, want_last_blur=False):
 
 def scores(w, h, bpc, sums, has_motion):
     return default().scores(w, h, bpc, sums, has_motion)
+
+
+def diff_blur(prev, cur, bpc):
+    return default().diff_blur(prev, cur, bpc)
+
+
+def clip_v2(ref, dist, bpc, prev_luma=None):
+    return default().clip_v2(ref, dist, bpc, prev_luma)
 
 
 def moments(plane, bpc):

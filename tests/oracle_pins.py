@@ -435,4 +435,105 @@ def pin_aggregate(o):
     assert all(math.isinf(v) for v in zero["apsnr"])
 
 
+# ---------------------------------------------------------------------------------------------
+# motion v2: the filter of the difference prev - cur (floor shifts)
+
+
+def brute_force_diff_blur(prev: np.ndarray, cur: np.ndarray, bpc: int) -> np.ndarray:
+    """25 multiply-adds per output on D = prev - cur with numpy's floor division (//) for both
+    rounded shifts and numpy's 'reflect' padding for the mirror."""
+    h, w = prev.shape
+    d = np.pad(prev.astype(np.int64) - cur.astype(np.int64), 2, mode="reflect")
+    g = np.array(TAPS, dtype=np.int64)
+    out = np.zeros((h, w), dtype=np.int64)
+    for l in range(5):
+        v = np.zeros((h, w), dtype=np.int64)
+        for k in range(5):
+            v += g[k] * d[k:k + h, l:l + w]
+        out += g[l] * ((v + (1 << (bpc - 1))) // (1 << bpc))
+    return (out + 32768) // 65536
+
+
+def scipy_diff_blur(prev: np.ndarray, cur: np.ndarray, bpc: int) -> np.ndarray:
+    g = np.array(TAPS, dtype=np.float64)
+    d = prev.astype(np.int64) - cur.astype(np.int64)
+    v = ndi.correlate1d(d, g, axis=0, mode="mirror").astype(np.int64)
+    v = np.floor_divide(v + (1 << (bpc - 1)), 1 << bpc)
+    b = ndi.correlate1d(v, g, axis=1, mode="mirror").astype(np.int64)
+    return np.floor_divide(b + 32768, 65536)
+
+
+def _pairs(bpc, seed):
+    a, b = _planes(bpc, seed), _planes(bpc, seed + 1)
+    return list(zip(a, b))
+
+
+def pin_diff_blur_brute_force(o):
+    for bpc in (8, 10, 12):
+        for i, (p, c) in enumerate(_pairs(bpc, 71 + bpc)):
+            assert np.array_equal(o.diff_blur(p, c, bpc), brute_force_diff_blur(p, c, bpc)), \
+                (bpc, i, p.shape)
+
+
+def pin_diff_blur_scipy(o):
+    for bpc in (8, 10):
+        for i, (p, c) in enumerate(_pairs(bpc, 83 + bpc)):
+            assert np.array_equal(o.diff_blur(p, c, bpc), scipy_diff_blur(p, c, bpc)), (bpc, i)
+
+
+def pin_diff_blur_constant(o):
+    """Flat frames c + d then c: every output is d 2^(16 - bpc), of either sign."""
+    for bpc in (8, 10):
+        dt = np.uint8 if bpc == 8 else np.uint16
+        for c0, d in ((100, 3), (100, -7), (0, 255), (255, -255)):
+            if bpc == 10:
+                c0, d = c0 * 4, d * 4
+            p = np.full((6, 9), c0 + d, dt)
+            c = np.full((6, 9), c0, dt)
+            assert np.all(o.diff_blur(p, c, bpc) == d * (1 << (16 - bpc))), (bpc, c0, d)
+        x = _planes(bpc, 5)[0]
+        assert not o.diff_blur(x, x, bpc).any()
+
+
+def pin_diff_blur_bounds(o):
+    """Within 1 of the exact real filter of prev - cur scaled to 16 bits; within 3 of the
+    difference of the two blurred frames; swapping the frames negates the result up to 1."""
+    g = np.array(TAPS, dtype=np.float64) / 65536.0
+    for bpc in (8, 10):
+        for p, c in _pairs(bpc, 97 + bpc):
+            h, w = p.shape
+            f = o.diff_blur(p, c, bpc).astype(np.int64)
+            dp = np.pad(p.astype(np.float64) - c.astype(np.float64), 2, mode="reflect")
+            exact = np.zeros((h, w))
+            for k in range(5):
+                for l in range(5):
+                    exact += g[k] * g[l] * dp[k:k + h, l:l + w]
+            assert np.abs(f - exact * (1 << (16 - bpc))).max() <= 1.0
+            blurred = o.blur(p, bpc).astype(np.int64) - o.blur(c, bpc).astype(np.int64)
+            assert np.abs(f - blurred).max() <= 3
+            assert np.abs(f + o.diff_blur(c, p, bpc).astype(np.int64)).max() <= 1
+
+
+def pin_clip_v2_composition(o):
+    """Per frame: SSE by brute force, SAD2 = sum |F| of the brute-force filter of the previous and
+    the current reference luma; a clip split in two with the first part's last luma as prev_luma
+    equals the whole clip."""
+    for bpc, (f, h, w) in ((8, (4, 7, 9)), (10, (3, 5, 6)), (8, (3, 3, 3))):
+        ref, dist = _tiny_clip(bpc, f, h, w, 300 + h)
+        sums, hm = o.clip_v2(ref, dist, bpc)
+        assert list(hm) == [0] + [1] * (f - 1)
+        for t in range(f):
+            for p in range(3):
+                d = ref[p][t].astype(np.int64) - dist[p][t].astype(np.int64)
+                assert int(sums[t, 1 + p]) == int((d * d).sum())
+            want = 0 if t == 0 else int(np.abs(brute_force_diff_blur(ref[0][t - 1], ref[0][t],
+                                                                      bpc)).sum())
+            assert int(sums[t, 0]) == want, (bpc, t)
+        a, ha = o.clip_v2(tuple(q[:2] for q in ref), tuple(q[:2] for q in dist), bpc)
+        b, hb = o.clip_v2(tuple(q[2:] for q in ref), tuple(q[2:] for q in dist), bpc,
+                          prev_luma=ref[0][1])
+        assert np.array_equal(np.concatenate([a, b]), sums)
+        assert list(ha) + list(hb) == [0] + [1] * (f - 1)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

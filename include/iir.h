@@ -63,6 +63,15 @@ enum {
  * kernel ("ADR-1392", Context, and Decision 6).
  */
 #define IIR_FLAG_MOMENTS 2u
+/*
+ * Motion v2 instead of the blurred-frame SAD (8- and 10-bit only): iir_result.sad becomes
+ * SAD2 = sum over the luma plane of |F|, F the same separable filter applied to the difference
+ * prev - cur of consecutive reference luma frames, with both rounded shifts taken as floor
+ * ("ADR-1392", Decision 4: the kernel stages prev - cur and filters it separably). The context
+ * then keeps the last reference luma frame instead of the blurred one; iir_export_blur is not
+ * available (IIR_ESTATE).
+ */
+#define IIR_FLAG_MOTION_V2 4u
 
 /*
  * One plane of one frame. data is a DEVICE pointer, pitch is the distance between rows in bytes.
@@ -213,7 +222,8 @@ IIR_API int iir_reset(iir_ctx *ctx);
 /*
  * Write the blurred reference luma of the most recently submitted frame as a W x H uint16 plane
  * into the DEVICE buffer dst (row pitch `pitch` bytes, >= 2 W, multiple of 4), enqueued on the
- * context's stream. IIR_ESTATE if no frame has been submitted since create/reset.
+ * context's stream. IIR_ESTATE if no frame has been submitted since create/reset, or with
+ * IIR_FLAG_MOTION_V2 (which keeps no blurred frame).
  */
 IIR_API int iir_export_blur(iir_ctx *ctx, void *dst, int64_t pitch);
 

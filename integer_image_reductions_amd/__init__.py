@@ -6,6 +6,7 @@ this package is its Python binding. Import is cheap: the library loads on first 
 from .binding import (  # noqa: F401
     IIR_CHROMA_420,
     IIR_FLAG_MOMENTS,
+    IIR_FLAG_MOTION_V2,
     IIR_FLAG_TIMING,
     LIB_PATH,
     PLANE_ALIGN,

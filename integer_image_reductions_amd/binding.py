@@ -18,6 +18,7 @@ IIR_OK, IIR_EINVAL, IIR_ENODEV, IIR_ENOMEM, IIR_EDEVICE, IIR_EBUSY, IIR_ESTATE =
 IIR_CHROMA_420 = 420
 IIR_FLAG_TIMING = 1
 IIR_FLAG_MOMENTS = 2
+IIR_FLAG_MOTION_V2 = 4
 PLANE_ALIGN = 16  # bytes: plane data and pitch must be multiples of this
 
 c_i32, c_i64, c_u32, c_u64, c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
@@ -174,7 +175,8 @@ class Context:
     """One library context (iir_ctx): a frame geometry, a device and a stream."""
 
     def __init__(self, width: int, height: int, bpc: int, max_batch: int = 64, device=None,
-                 stream=None, timing: bool = False, moments: bool = False):
+                 stream=None, timing: bool = False, moments: bool = False,
+                 motion_v2: bool = False):
         torch = _torch()
         lib = load_library()
         self._lib = lib
@@ -183,7 +185,8 @@ class Context:
         self.stream = stream if stream is not None else torch.cuda.current_stream(dev)
         self.config = Config(width, height, bpc, IIR_CHROMA_420, max_batch,
                              (IIR_FLAG_TIMING if timing else 0) |
-                             (IIR_FLAG_MOMENTS if moments else 0))
+                             (IIR_FLAG_MOMENTS if moments else 0) |
+                             (IIR_FLAG_MOTION_V2 if motion_v2 else 0))
         self.moments = bool(moments)
         h = c_vp()
         _check(lib.iir_create(ctypes.byref(self.config), dev.index, c_vp(self.stream.cuda_stream),

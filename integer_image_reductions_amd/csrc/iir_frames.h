@@ -640,21 +640,58 @@ __device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWav
 // the mirror image the horizontal taps of the lane before it need. Columns W+2 and W+3 feed no
 // output.
 template <int BPC, int TH, bool STAGED>
-__device__ __forceinline__ void mirror_halo(const Tile &T, FrameData<BPC, TH> &F)
+__device__ __forceinline__ void mirror_rows(const Tile &T, typename Px<BPC>::Luma (&R)[TH + 4])
 {
 #pragma unroll
     for (int k = 0; k < TH + 4; ++k) {
         if constexpr (STAGED) {
             // staged rows hold the lane's own columns W..W+3; the group W-4..W-1 comes from the
             // lane to the left (every lane runs the shift; only the edge lane's selector uses it)
-            F.R[k] = perm(from_left(F.R[k]), F.R[k], T.msel);
+            R[k] = perm(from_left(R[k]), R[k], T.msel);
         } else if constexpr (BPC == 8) {
-            F.R[k] = perm(F.R[k], F.R[k], T.msel);
+            R[k] = perm(R[k], R[k], T.msel);
         } else {
             // (x[W-2] | x[W-3] << 16) from the second dword's low and the first dword's high half
-            const uint32_t m = perm(F.R[k].x, F.R[k].y, 0x07060100u);
-            F.R[k] = u32x2{T.mirror_right ? m : F.R[k].x, F.R[k].y};
+            const uint32_t m = perm(R[k].x, R[k].y, 0x07060100u);
+            R[k] = u32x2{T.mirror_right ? m : R[k].x, R[k].y};
         }
+    }
+}
+
+template <int BPC, int TH, bool STAGED>
+__device__ __forceinline__ void mirror_halo(const Tile &T, FrameData<BPC, TH> &F)
+{
+    mirror_rows<BPC, TH, STAGED>(T, F.R);
+}
+
+// Register-path source of the lane's two horizontal halo columns: the first column `col` of an
+// 8-byte load of the halo row and the byte permutation `sel` that makes the 16-bit pair of them
+// (8-bit: bytes, 0x0c = zero; 16-bit samples: halves), mirrored at the frame edges.
+template <int BPC>
+__device__ __forceinline__ void halo_source(int lane, int strip, int s, int W, int &col,
+                                            uint32_t &sel)
+{
+    const int e = s + kStripCols;  // first column right of the tile
+    if (lane < kWave / 2) {
+        if (strip == 0) {  // columns -2, -1 mirror 2, 1
+            col = 0;
+            sel = BPC == 8 ? 0x0c010c02u : 0x03020504u;
+        } else {  // columns s-2, s-1
+            col = s - 4;
+            sel = BPC == 8 ? 0x0c030c02u : 0x07060504u;
+        }
+    } else if (e < W - 1) {  // columns e, e+1
+        col = BPC == 8 ? e - 4 : e;
+        sel = BPC == 8 ? 0x0c050c04u : 0x03020100u;
+    } else if (e == W - 1) {  // column e, then e+1 = W mirrors W-2 = e-1
+        col = BPC == 8 ? e - 4 : e - 2;
+        sel = BPC == 8 ? 0x0c030c04u : 0x03020504u;
+    } else if (e == W) {  // columns W, W+1 mirror W-2, W-3
+        col = BPC == 8 ? W - 8 : W - 4;
+        sel = BPC == 8 ? 0x0c050c06u : 0x03020504u;
+    } else {  // the frame ends inside the tile: unused
+        col = 0;
+        sel = 0u;
     }
 }
 
@@ -678,6 +715,210 @@ __device__ __forceinline__ uint32_t halo_vertical(u32x2 h, uint32_t hsel, uint32
                               dot2u(perm(p1, x0, 0x07060302u), T21,
                                     dot2u(perm(m1, m2, 0x07060302u), T01, kVRound)));
     return perm(vb, va, kVSel);
+}
+
+// Squared error of the frame's chroma tiles (8-bit: sums of squares in su/sv and cross terms in
+// su2/sv2; deeper samples: difference squares in su/sv).
+template <int BPC, int TH, bool GENERIC>
+__device__ __forceinline__ void chroma_sse(const KernelArgs &a, const Tile &T,
+                                           const FrameData<BPC, TH> &F, Sq<BPC> &su, uint32_t &su2,
+                                           Sq<BPC> &sv, uint32_t &sv2)
+{
+    typedef FrameData<BPC, TH> FD;
+#pragma unroll
+    for (int k = 0; k < FD::kChromaSteps; ++k) {
+        uint32_t ru = F.cu[k], rdu = F.du[k], rv = F.cv[k], rdv = F.dv[k];
+        if constexpr (GENERIC) {
+            const int row = T.crow0 + FD::kChromaStep * k + (T.c_upper ? 1 : 0);
+            const uint32_t m = row < a.Hc ? T.cm : 0u;
+            ru &= m;
+            rdu &= m;
+            rv &= m;
+            rdv &= m;
+        }
+        sse_chroma<BPC>(ru, rdu, su, su2);
+        sse_chroma<BPC>(rv, rdv, sv, sv2);
+    }
+}
+
+// Per-lane accumulators of the luma and chroma statistics of one frame.
+template <int BPC>
+struct FrameStats {
+    Sq<BPC> sy = 0, su = 0, sv = 0, m2r = 0, m2d = 0;
+    uint32_t sy2 = 0, su2 = 0, sv2 = 0, m1r = 0, m1d = 0;
+};
+
+// Squared error (and moments) of output row i's luma samples.
+template <int BPC, int TH, bool GENERIC, bool MOM>
+__device__ __forceinline__ void luma_row_stats(const Tile &T, const FrameData<BPC, TH> &F, int i,
+                                               FrameStats<BPC> &S)
+{
+    typename Px<BPC>::Luma r = F.R[i + 2], d = F.D[i];
+    if constexpr (GENERIC) {
+        r = masked<BPC>(r, T.ym0, T.ym1);
+        d = masked<BPC>(d, T.ym0, T.ym1);
+    }
+    if constexpr (MOM)
+        moments_luma<BPC>(r, d, S.m1r, S.m1d, S.m2r, S.m2d, S.sy, S.sy2);
+    else
+        sse_luma<BPC>(r, d, S.sy, S.sy2);
+}
+
+// One wavefront reduction per sum of the frame, queued for the frame's atomics.
+template <int BPC, bool MOM>
+__device__ __forceinline__ void push_frame_sums(const KernelArgs &a, const Tile &T,
+                                                Pending<MOM ? kMaxSums : kSums> &P, uint32_t sad,
+                                                const FrameStats<BPC> &S)
+{
+    // squared errors: 8-bit sy (or, with moments, m2r + m2d) holds sum r^2 + d^2 and sy2
+    // sum r d; deeper samples keep the difference squares in sy (su, sv likewise)
+    Sq<BPC> ey = S.sy, eu = S.su, ev = S.sv;
+    if constexpr (BPC == 8) {
+        ey = (MOM ? S.m2r + S.m2d : S.sy) - 2u * S.sy2;
+        eu = S.su - 2u * S.su2;
+        ev = S.sv - 2u * S.sv2;
+    }
+    const Sq<BPC> zero = 0;
+    if constexpr (MOM) {
+        const unsigned long long sums[kMaxSums] = {
+            wave_sum(sad),
+            wave_sum_sq(T.out_lane ? ey : zero),
+            wave_sum_sq(T.c_on ? eu : zero),
+            wave_sum_sq(T.c_on ? ev : zero),
+            wave_sum(T.out_lane ? S.m1r : 0u),
+            wave_sum(T.out_lane ? S.m1d : 0u),
+            wave_sum_sq(T.out_lane ? S.m2r : zero),
+            wave_sum_sq(T.out_lane ? S.m2d : zero)};
+        push_sums(a, P, T.lane, sums);
+    } else {
+        const unsigned long long sums[kSums] = {wave_sum(sad),
+                                                wave_sum_sq(T.out_lane ? ey : zero),
+                                                wave_sum_sq(T.c_on ? eu : zero),
+                                                wave_sum_sq(T.c_on ? ev : zero)};
+        push_sums(a, P, T.lane, sums);
+    }
+}
+
+// The horizontal neighbours of one row's packed vertical values. q0, q1 hold the lane's columns
+// (c, c+1) and (c+2, c+3) as 16-bit pairs; ql receives (c-2, c-1) from the lane to the left or,
+// for lane 0, the left halo hl; qr receives (c+4, c+5) from the lane to the right or, for lane
+// 63, the right halo hr. The generic path then mirrors the columns past the right frame edge.
+template <bool GENERIC, bool ROWSTAGE>
+__device__ __forceinline__ void neighbours(const Tile &T, uint32_t hl, uint32_t hr, uint32_t &q0,
+                                           uint32_t &q1, uint32_t &ql, uint32_t &qr)
+{
+    ql = from_left_or(q1, hl);
+    // generic path: (V(c+2), V(c+1)), the mirror image of the lane's own columns, stands for
+    // columns W, W+1 at the right frame edge when W % 4 == 0
+    const uint32_t mirrored = GENERIC ? perm(q0, q1, 0x07060100u) : 0u;
+    if constexpr (GENERIC) {
+        if (T.right_rem == 1) {  // columns W, W+1 -> W-2, W-3
+            q0 = T.right_fix ? perm(ql, q0, 0x07060100u) : q0;
+            q1 = T.right_fix ? ql : q1;
+        } else if (T.right_rem == 2) {
+            q1 = T.right_fix ? perm(ql, q0, 0x07060100u) : q1;
+        } else if (T.right_rem == 3) {
+            q1 = T.right_fix ? perm(q0, q1, 0x07060100u) : q1;
+        }
+    }
+    qr = from_right_or(q0, hr);
+    if constexpr (GENERIC && ROWSTAGE)
+        qr = T.halo_fix ? perm(q1, qr, 0x07060100u) : qr;  // (V(e), V(e-1))
+    if constexpr (GENERIC) {
+        if (T.right_rem == 0)
+            qr = T.right_fix ? mirrored : qr;
+        else if (T.right_rem == 3)
+            qr = T.right_fix ? q0 : qr;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Motion v2: the separable filter applied to the difference prev - cur of consecutive reference
+// luma frames ("ADR-1392", Decision 4: the kernel stages prev - cur, runs the vertical pass once,
+// rounded by the bit depth, then the five horizontal taps shifted by 16). Shifts of negative
+// sums floor. The vertical value V of a difference needs 17 bits, so it travels split into its
+// high part Vh = floor(V / 256) (a signed 16-bit lane) and its low byte Vl = V mod 256; the
+// horizontal sum, 33 bits wide ("ADR-1392", the alternative of 32-bit horizontal sums), is then
+// the exact combination of two 32-bit sums A = sum g Vh and B = sum g Vl:
+//   floor((256 A + B + 2^15) / 2^16) = floor((A + floor((B + 2^15) / 2^8)) / 2^8).
+
+// signed 16-bit pair dot product, accumulated in 32 bits
+__device__ __forceinline__ int32_t dot2s(uint32_t a, uint32_t b, int32_t c)
+{
+    return __builtin_amdgcn_sdot2(__builtin_bit_cast(i16x2, a), __builtin_bit_cast(i16x2, b), c,
+                                  false);
+}
+
+// a - b of both 16-bit halves (each difference fits a signed 16-bit lane)
+__device__ __forceinline__ uint32_t sub16x2(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, a) - __builtin_bit_cast(i16x2, b));
+}
+
+// prev - cur of one row's 4 samples as two signed 16-bit pairs: columns (c, c+1), (c+2, c+3)
+template <int BPC>
+__device__ __forceinline__ u32x2 diff_row(typename Px<BPC>::Luma p, typename Px<BPC>::Luma r)
+{
+    if constexpr (BPC == 8) {
+        return u32x2{sub16x2(perm(0u, p, 0x0c010c00u), perm(0u, r, 0x0c010c00u)),
+                     sub16x2(perm(0u, p, 0x0c030c02u), perm(0u, r, 0x0c030c02u))};
+    } else {
+        return u32x2{sub16x2(p.x, r.x), sub16x2(p.y, r.y)};
+    }
+}
+
+// (row a, row b) pairs of the 4 columns of two difference rows
+__device__ __forceinline__ void diff_pairs(u32x2 da, u32x2 db, uint32_t p[4])
+{
+    p[0] = perm(db.x, da.x, 0x05040100u);
+    p[1] = perm(db.x, da.x, 0x07060302u);
+    p[2] = perm(db.y, da.y, 0x05040100u);
+    p[3] = perm(db.y, da.y, 0x07060302u);
+}
+
+// rounding term of the vertical pass, 2^(bpc - 1)
+template <int BPC>
+constexpr int32_t kV2Round = BPC == 8 ? 128 : 512;
+
+// Two columns' vertical sums (rounding term included) -> packed (Vh, Vh') and (Vl, Vl'). 8-bit:
+// V = s >> 8, so Vh is bits 16-31 of s and Vl bits 8-15; 10-bit: V = s >> 10 first.
+template <int BPC>
+__device__ __forceinline__ void split_pack(int32_t s0, int32_t s1, uint32_t &h, uint32_t &l)
+{
+    if constexpr (BPC == 8) {
+        h = perm((uint32_t)s1, (uint32_t)s0, 0x07060302u);
+        l = perm((uint32_t)s1, (uint32_t)s0, 0x0c050c01u);
+    } else {
+        const uint32_t v0 = (uint32_t)(s0 >> 10), v1 = (uint32_t)(s1 >> 10);
+        h = perm(v1, v0, 0x06050201u);
+        l = perm(v1, v0, 0x0c040c00u);
+    }
+}
+
+// Vertical pass of the transposed halo's differences (lane k: the two halo columns of tile row
+// k - 2 as a signed pair), split as above; lane i + 2 (left) and i + 34 (right) serve row i.
+template <int BPC>
+__device__ __forceinline__ void halo_vertical_v2(uint32_t dh, uint32_t &hvh, uint32_t &hvl)
+{
+    const uint32_t m1 = from_left(dh), m2 = from_left(m1);    // rows k-1, k-2
+    const uint32_t p1 = from_right(dh), p2 = from_right(p1);  // rows k+1, k+2
+    const int32_t sa = dot2s(p2 & 0xffffu, T0z,
+                             dot2s(perm(p1, dh, 0x05040100u), T21,
+                                   dot2s(perm(m1, m2, 0x05040100u), T01, kV2Round<BPC>)));
+    const int32_t sb = dot2s(p2 >> 16, T0z,
+                             dot2s(perm(p1, dh, 0x07060302u), T21,
+                                   dot2s(perm(m1, m2, 0x07060302u), T01, kV2Round<BPC>)));
+    split_pack<BPC>(sa, sb, hvh, hvl);
+}
+
+// |F| of one output from its biased high sum (A + 2^25) and its low sum (B + 2^15): the biased
+// result F + 2^17 is non-negative, so the shifts are logical, and |F| = |(F + 2^17) - 2^17|.
+constexpr int32_t kV2Bias = 1 << 25;
+constexpr uint32_t kV2Zero = 1u << 17;
+__device__ __forceinline__ uint32_t abs_f(int32_t a_biased, uint32_t b)
+{
+    const uint32_t fk = (uint32_t)(a_biased + (int32_t)(b >> 8)) >> 8;
+    return fk > kV2Zero ? fk - kV2Zero : kV2Zero - fk;
 }
 
 // One frame of one tile from its loaded samples: blur the reference luma (vertical pass once per
@@ -707,28 +948,12 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
     const uint32_t hv = halo_vertical<BPC>(F.HL, T.hsel, shift);
 
     // SSE of the chroma tiles first, which frees their registers before the blur
-    Sq<BPC> su = 0, sv = 0;
-    uint32_t su2 = 0, sv2 = 0;
-    if (accumulate) {
-#pragma unroll
-        for (int k = 0; k < FD::kChromaSteps; ++k) {
-            uint32_t ru = F.cu[k], rdu = F.du[k], rv = F.cv[k], rdv = F.dv[k];
-            if constexpr (GENERIC) {
-                const int row = T.crow0 + FD::kChromaStep * k + (T.c_upper ? 1 : 0);
-                const uint32_t m = row < a.Hc ? T.cm : 0u;
-                ru &= m;
-                rdu &= m;
-                rv &= m;
-                rdv &= m;
-            }
-            sse_chroma<BPC>(ru, rdu, su, su2);
-            sse_chroma<BPC>(rv, rdv, sv, sv2);
-        }
-    }
+    FrameStats<BPC> S;
+    if (accumulate)
+        chroma_sse<BPC, TH, GENERIC>(a, T, F, S.su, S.su2, S.sv, S.sv2);
 
     // blur, SAD against the previous blurred tile, and SSE of the luma rows as they go by
-    uint32_t acc_c = 0, acc_min = 0, sy2 = 0, m1r = 0, m1d = 0;
-    Sq<BPC> sy = 0, m2r = 0, m2d = 0;
+    uint32_t acc_c = 0, acc_min = 0;
 #pragma unroll
     for (int i = 0; i < TH; ++i) {
         uint32_t pa[4], pb[4], pc[4];
@@ -743,33 +968,11 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
             v[b] = dot2u(pc[b], T0z, dot2u(pb[b], T21, dot2u(pa[b], T01, kVRound)));
         uint32_t q0 = perm(v[1], v[0], kVSel);  // V of columns c, c+1
         uint32_t q1 = perm(v[3], v[2], kVSel);  // V of columns c+2, c+3
-        // V of columns c-2, c-1: the lane to the left, or the left halo for lane 0
+        // halo V of this row: columns s-2, s-1 (lane i + 2) and e, e+1 (lane i + 34)
         const uint32_t hl = (uint32_t)__builtin_amdgcn_readlane((int)hv, i + 2);
-        uint32_t ql = from_left_or(q1, hl);
-        // generic path: (V(c+2), V(c+1)), the mirror image of the lane's own columns, stands for
-        // columns W, W+1 at the right frame edge when W % 4 == 0
-        const uint32_t mirrored = GENERIC ? perm(q0, q1, 0x07060100u) : 0u;
-        if constexpr (GENERIC) {
-            if (T.right_rem == 1) {  // columns W, W+1 -> W-2, W-3
-                q0 = T.right_fix ? perm(ql, q0, 0x07060100u) : q0;
-                q1 = T.right_fix ? ql : q1;
-            } else if (T.right_rem == 2) {
-                q1 = T.right_fix ? perm(ql, q0, 0x07060100u) : q1;
-            } else if (T.right_rem == 3) {
-                q1 = T.right_fix ? perm(q0, q1, 0x07060100u) : q1;
-            }
-        }
-        // V of columns c+4, c+5: the lane to the right, or the right halo for lane 63
         const uint32_t hr = (uint32_t)__builtin_amdgcn_readlane((int)hv, i + kWave / 2 + 2);
-        uint32_t qr = from_right_or(q0, hr);
-        if constexpr (GENERIC && ROWSTAGE)
-            qr = T.halo_fix ? perm(q1, qr, 0x07060100u) : qr;  // (V(e), V(e-1))
-        if constexpr (GENERIC) {
-            if (T.right_rem == 0)
-                qr = T.right_fix ? mirrored : qr;
-            else if (T.right_rem == 3)
-                qr = T.right_fix ? q0 : qr;
-        }
+        uint32_t ql, qr;
+        neighbours<GENERIC, ROWSTAGE>(T, hl, hr, q0, q1, ql, qr);
         const uint32_t h0 = dot2u(q1, T0z, dot2u(q0, T21, dot2u(ql, T01, 32768u)));
         const uint32_t h1 = dot2u(q1, T10, dot2u(q0, T12, dot2u(ql, Tz0, 32768u)));
         const uint32_t h2 = dot2u(qr, T0z, dot2u(q1, T21, dot2u(q0, T01, 32768u)));
@@ -779,53 +982,102 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
         if (!GENERIC || i < T.rows_valid) {
             acc_c = dot2u(c1, T.w1, dot2u(c0, T.w0, acc_c));
             acc_min = dot2u(pkmin(c1, prev1[i]), T.w1, dot2u(pkmin(c0, prev0[i]), T.w0, acc_min));
-            if (accumulate) {
-                Luma r = F.R[i + 2], d = F.D[i];
-                if constexpr (GENERIC) {
-                    r = masked<BPC>(r, T.ym0, T.ym1);
-                    d = masked<BPC>(d, T.ym0, T.ym1);
-                }
-                if constexpr (MOM)
-                    moments_luma<BPC>(r, d, m1r, m1d, m2r, m2d, sy, sy2);
-                else
-                    sse_luma<BPC>(r, d, sy, sy2);
-            }
+            if (accumulate)
+                luma_row_stats<BPC, TH, GENERIC, MOM>(T, F, i, S);
         }
         next0[i] = c0;
         next1[i] = c1;
     }
 
-    if (accumulate) {
-        const uint32_t sad = have_prev ? acc_c + sum_prev - 2u * acc_min : 0u;
-        // squared errors: 8-bit sy (or, with moments, m2r + m2d) holds sum r^2 + d^2 and sy2
-        // sum r d; deeper samples keep the difference squares in sy (su, sv likewise)
-        Sq<BPC> ey = sy, eu = su, ev = sv;
-        if constexpr (BPC == 8) {
-            ey = (MOM ? m2r + m2d : sy) - 2u * sy2;
-            eu = su - 2u * su2;
-            ev = sv - 2u * sv2;
-        }
-        const Sq<BPC> zero = 0;
-        if constexpr (MOM) {
-            const unsigned long long sums[kMaxSums] = {
-                wave_sum(sad),
-                wave_sum_sq(T.out_lane ? ey : zero),
-                wave_sum_sq(T.c_on ? eu : zero),
-                wave_sum_sq(T.c_on ? ev : zero),
-                wave_sum(T.out_lane ? m1r : 0u),
-                wave_sum(T.out_lane ? m1d : 0u),
-                wave_sum_sq(T.out_lane ? m2r : zero),
-                wave_sum_sq(T.out_lane ? m2d : zero)};
-            push_sums(a, P, T.lane, sums);
-        } else {
-            const unsigned long long sums[kSums] = {wave_sum(sad),
-                                                    wave_sum_sq(T.out_lane ? ey : zero),
-                                                    wave_sum_sq(T.c_on ? eu : zero),
-                                                    wave_sum_sq(T.c_on ? ev : zero)};
-            push_sums(a, P, T.lane, sums);
-        }
-    }
+    if (accumulate)
+        push_frame_sums<BPC, MOM>(a, T, P, have_prev ? acc_c + sum_prev - 2u * acc_min : 0u, S);
     sum_prev = acc_c;
+    have_prev = true;
+}
+
+// One frame of one tile for motion v2: the filter of prev - cur and the sum of its absolute
+// values, plus the same squared errors (and moments) as compute_frame. pin holds the previous
+// frame's reference luma rows (mirrored like F.R) and pxin its halo pair; on return pout and
+// pxout hold this frame's, for the next.
+template <int BPC, int TH, bool GENERIC, bool ROWSTAGE, bool MOM>
+__device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile &T,
+                                                 bool accumulate, FrameData<BPC, TH> &F,
+                                                 const typename Px<BPC>::Luma (&pin)[TH + 4],
+                                                 uint32_t pxin,
+                                                 typename Px<BPC>::Luma (&pout)[TH + 4],
+                                                 uint32_t &pxout, bool &have_prev,
+                                                 Pending<MOM ? kMaxSums : kSums> &P)
+{
+    if constexpr (!GENERIC) {
+        if (T.edge_tile)
+            mirror_halo<BPC, TH, ROWSTAGE>(T, F);
+    }
+    const uint32_t x0 = perm(F.HL.y, F.HL.x, T.hsel);  // this frame's halo pair
+    if (accumulate) {
+        FrameStats<BPC> S;
+        chroma_sse<BPC, TH, GENERIC>(a, T, F, S.su, S.su2, S.sv, S.sv2);
+        uint32_t sad = 0;
+        if (have_prev) {
+            uint32_t hvh, hvl;
+            halo_vertical_v2<BPC>(sub16x2(pxin, x0), hvh, hvl);
+            const u32x2 zero{};
+#pragma unroll
+            for (int i = 0; i < TH; ++i) {
+                uint32_t pa[4], pb[4], pc[4];
+                diff_pairs(diff_row<BPC>(pin[i], F.R[i]), diff_row<BPC>(pin[i + 1], F.R[i + 1]),
+                           pa);  // rows i-2, i-1
+                diff_pairs(diff_row<BPC>(pin[i + 2], F.R[i + 2]),
+                           diff_row<BPC>(pin[i + 3], F.R[i + 3]), pb);  // rows i, i+1
+                diff_pairs(diff_row<BPC>(pin[i + 4], F.R[i + 4]),
+                           i + 5 < TH + 4 ? diff_row<BPC>(pin[i + 5], F.R[i + 5]) : zero,
+                           pc);  // rows i+2 (tap 0 on i+3)
+                int32_t v[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    v[b] = dot2s(pc[b], T0z, dot2s(pb[b], T21, dot2s(pa[b], T01, kV2Round<BPC>)));
+                uint32_t q0h, q0l, q1h, q1l;
+                split_pack<BPC>(v[0], v[1], q0h, q0l);  // columns c, c+1
+                split_pack<BPC>(v[2], v[3], q1h, q1l);  // columns c+2, c+3
+                const uint32_t hlh = (uint32_t)__builtin_amdgcn_readlane((int)hvh, i + 2);
+                const uint32_t hll = (uint32_t)__builtin_amdgcn_readlane((int)hvl, i + 2);
+                const uint32_t hrh = (uint32_t)__builtin_amdgcn_readlane((int)hvh, i + kWave / 2 + 2);
+                const uint32_t hrl = (uint32_t)__builtin_amdgcn_readlane((int)hvl, i + kWave / 2 + 2);
+                uint32_t qlh, qrh, qll, qrl;
+                neighbours<GENERIC, ROWSTAGE>(T, hlh, hrh, q0h, q1h, qlh, qrh);
+                neighbours<GENERIC, ROWSTAGE>(T, hll, hrl, q0l, q1l, qll, qrl);
+                uint32_t f[4];
+                f[0] = abs_f(dot2s(q1h, T0z, dot2s(q0h, T21, dot2s(qlh, T01, kV2Bias))),
+                             dot2u(q1l, T0z, dot2u(q0l, T21, dot2u(qll, T01, 32768u))));
+                f[1] = abs_f(dot2s(q1h, T10, dot2s(q0h, T12, dot2s(qlh, Tz0, kV2Bias))),
+                             dot2u(q1l, T10, dot2u(q0l, T12, dot2u(qll, Tz0, 32768u))));
+                f[2] = abs_f(dot2s(qrh, T0z, dot2s(q1h, T21, dot2s(q0h, T01, kV2Bias))),
+                             dot2u(qrl, T0z, dot2u(q1l, T21, dot2u(q0l, T01, 32768u))));
+                f[3] = abs_f(dot2s(qrh, T10, dot2s(q1h, T12, dot2s(q0h, Tz0, kV2Bias))),
+                             dot2u(qrl, T10, dot2u(q1l, T12, dot2u(q0l, Tz0, 32768u))));
+                if constexpr (GENERIC) {
+                    if (i < T.rows_valid)
+                        sad += ((T.w0 & 1u) ? f[0] : 0u) + ((T.w0 >> 16) ? f[1] : 0u) +
+                               ((T.w1 & 1u) ? f[2] : 0u) + ((T.w1 >> 16) ? f[3] : 0u);
+                } else {
+                    sad += (f[0] + f[1]) + (f[2] + f[3]);
+                }
+                if (!GENERIC || i < T.rows_valid)
+                    luma_row_stats<BPC, TH, GENERIC, MOM>(T, F, i, S);
+            }
+            if constexpr (!GENERIC)
+                sad = T.out_lane ? sad : 0u;
+        } else {
+#pragma unroll
+            for (int i = 0; i < TH; ++i)
+                if (!GENERIC || i < T.rows_valid)
+                    luma_row_stats<BPC, TH, GENERIC, MOM>(T, F, i, S);
+        }
+        push_frame_sums<BPC, MOM>(a, T, P, sad, S);
+    }
+#pragma unroll
+    for (int k = 0; k < TH + 4; ++k)
+        pout[k] = F.R[k];
+    pxout = x0;
     have_prev = true;
 }
 
@@ -890,6 +1142,113 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
     flush_sums(a, P, T.lane);
 }
 
+// The frames of this workgroup's time chunk for motion v2. The state carried from frame to frame
+// is the previous frame's reference luma rows and halo pair, in two register sets whose roles
+// swap every frame; chunks after the first load the frame before them as their first state.
+template <int BPC, int TH, bool GENERIC, bool STAGED, bool MOM>
+__device__ __forceinline__ void frame_loop_v2(const KernelArgs &a, const Tile &T,
+                                              const StageOffsets<TH> &O,
+                                              typename Px<BPC>::Luma (&prev)[TH + 4],
+                                              uint32_t &pxprev, bool have_prev,
+                                              uint32_t (*lds)[kWave])
+{
+    typedef typename Px<BPC>::Luma Luma;
+    const int f_begin = uni(T.chunk * a.chunk_len);
+    const int f_end = uni(min(f_begin + a.chunk_len, a.nframes));
+    const int t0 = T.chunk > 0 ? f_begin - 1 : f_begin;
+    constexpr int NS = MOM ? kMaxSums : kSums;
+    Pending<NS> P;
+#pragma unroll
+    for (int k = 0; k < 2 * NS; ++k)
+        P.v[k] = 0;
+    P.first = f_begin;
+    P.count = 0;
+    if constexpr (STAGED)
+        load_frame_staged<TH>(a, T, O, t0, t0 >= f_begin, lds);
+    auto step = [&](int t, const Luma(&pin)[TH + 4], uint32_t pxin, Luma(&pout)[TH + 4],
+                    uint32_t &pxout) {
+        FrameData<BPC, TH> F;
+        if constexpr (STAGED) {
+            __builtin_amdgcn_s_setprio(3);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): frame t is in LDS
+            read_stage<TH>(t >= f_begin, lds, T.lane, T.hlds, F);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 1 < f_end)
+                load_frame_staged<TH>(a, T, O, t + 1, true, lds);
+            __builtin_amdgcn_s_setprio(0);
+        } else {
+            load_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F);
+        }
+        compute_frame_v2<BPC, TH, GENERIC, STAGED, MOM>(a, T, t >= f_begin, F, pin, pxin, pout,
+                                                        pxout, have_prev, P);
+    };
+    Luma alt[TH + 4];
+    uint32_t pxalt = 0;
+    for (int t = t0; t < f_end; t += 2) {
+        step(t, prev, pxprev, alt, pxalt);
+        if (t + 1 < f_end) {
+            step(t + 1, alt, pxalt, prev, pxprev);
+        } else {
+#pragma unroll
+            for (int k = 0; k < TH + 4; ++k)
+                prev[k] = alt[k];
+            pxprev = pxalt;
+        }
+    }
+    flush_sums(a, P, T.lane);
+}
+
+// Motion v2 state across launches: the last frame's reference luma, saved as a plane of
+// strips * 256 samples per row (ring_out, read back through ring_in by the next launch).
+template <int BPC>
+__device__ __forceinline__ uint32_t saved_pitch(const KernelArgs &a)
+{
+    return (uint32_t)(a.strips * kStripCols * Px<BPC>::kBytes);
+}
+
+// The previous frame's rows and halo pair from the saved plane, as the frame loop would have
+// left them: rows mirrored at the top and bottom, the lane's columns as its loads take them
+// (staged: its own four; registers: T.luma_off), the halo pair through the register-path source.
+template <int BPC, int TH, bool GENERIC, bool STAGED>
+__device__ __forceinline__ void load_saved(const KernelArgs &a, const Tile &T, int s,
+                                           typename Px<BPC>::Luma (&prev)[TH + 4],
+                                           uint32_t &pxprev)
+{
+    constexpr int B = Px<BPC>::kBytes;
+    const uint32_t pitch = saved_pitch<BPC>(a);
+    const Rsrc rs = plane_rsrc(reinterpret_cast<const uint8_t *>(a.ring_in), pitch * (uint32_t)a.H);
+    const uint32_t col = STAGED ? (uint32_t)((s + kLumaCols * T.lane) * B) : T.luma_off;
+#pragma unroll
+    for (int k = 0; k < TH + 4; ++k)
+        prev[k] = ld_luma<BPC>(rs, col, (uint32_t)mirror_clamp(T.r0 - 2 + k, a.H) * pitch);
+    int hcol;
+    uint32_t hsel;
+    halo_source<BPC>(T.lane, T.strip, s, a.W, hcol, hsel);
+    const int hrow = mirror_clamp(T.r0 - 2 + min(T.lane & (kWave / 2 - 1), TH + 3), a.H);
+    const u32x2 h = ld_luma<10>(rs, (uint32_t)(hcol * B) + (uint32_t)hrow * pitch, 0u);
+    pxprev = perm(h.y, h.x, hsel);
+    if constexpr (!GENERIC) {
+        if (T.edge_tile)
+            mirror_rows<BPC, TH, STAGED>(T, prev);
+    }
+}
+
+// The tile's own rows of the launch's last frame into the saved plane.
+template <int BPC, int TH>
+__device__ __forceinline__ void store_saved(const KernelArgs &a, const Tile &T, int s,
+                                            const typename Px<BPC>::Luma (&prev)[TH + 4])
+{
+    constexpr int B = Px<BPC>::kBytes;
+    const uint32_t pitch = saved_pitch<BPC>(a);
+    uint8_t *base = reinterpret_cast<uint8_t *>(a.ring_out) + (size_t)(s + kLumaCols * T.lane) * B;
+#pragma unroll
+    for (int i = 0; i < TH; ++i)
+        if (i < T.rows_valid)
+            *reinterpret_cast<typename Px<BPC>::Luma *>(base + (size_t)(T.r0 + i) * pitch) =
+                prev[i + 2];
+}
+
 // The launch's last workgroup to finish (counted with one device-scope atomic per workgroup)
 // folds the kSumSlots partial sums of each of the NS sums of every frame, writes the totals straight to the
 // caller-visible pinned buffer and zeroes the partial sums and the counter for the next launch.
@@ -945,7 +1304,7 @@ __device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane)
     // the end of the kernel releases these stores to the host before its completion signal
 }
 
-template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE, bool MOM>
+template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE, bool MOM, bool V2>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void
 frames_kernel(const KernelArgs a)
 {
@@ -1002,27 +1361,7 @@ frames_kernel(const KernelArgs a)
         const int e = s + kStripCols;  // first column right of the tile
         int col;
         uint32_t sel;
-        if (lane < kWave / 2) {
-            if (T.strip == 0) {  // columns -2, -1 mirror 2, 1
-                col = 0;
-                sel = BPC == 8 ? 0x0c010c02u : 0x03020504u;
-            } else {  // columns s-2, s-1
-                col = s - 4;
-                sel = BPC == 8 ? 0x0c030c02u : 0x07060504u;
-            }
-        } else if (e < W - 1) {  // columns e, e+1
-            col = BPC == 8 ? e - 4 : e;
-            sel = BPC == 8 ? 0x0c050c04u : 0x03020100u;
-        } else if (e == W - 1) {  // column e, then e+1 = W mirrors W-2 = e-1
-            col = BPC == 8 ? e - 4 : e - 2;
-            sel = BPC == 8 ? 0x0c030c04u : 0x03020504u;
-        } else if (e == W) {  // columns W, W+1 mirror W-2, W-3
-            col = BPC == 8 ? W - 8 : W - 4;
-            sel = BPC == 8 ? 0x0c050c06u : 0x03020504u;
-        } else {  // the frame ends inside the tile: unused
-            col = 0;
-            sel = 0u;
-        }
+        halo_source<BPC>(lane, T.strip, s, W, col, sel);
         T.hvoff = (uint32_t)(col * B) + (uint32_t)hrow * (uint32_t)a.pitch[0];
         T.hsel = sel;
         T.hlds = 0u;
@@ -1081,28 +1420,6 @@ frames_kernel(const KernelArgs a)
             T.coff[k] = col + (T.c_upper ? (uint32_t)a.pitch[pk[k]] : 0u);
     }
 
-    // previous blurred tile: from the launch before, else none (chunk 0), or re-blurred by the
-    // chunk's prologue (later chunks)
-    uint32_t prev0[TH], prev1[TH];
-    uint32_t sum_prev = 0;
-    bool have_prev = false;
-    if (T.chunk == 0 && a.has_prev) {
-        const uint2 *rin = reinterpret_cast<const uint2 *>(a.ring_in);
-#pragma unroll
-        for (int i = 0; i < TH; ++i) {
-            const uint2 v = rin[(T.tile * TH + i) * kWave + lane];
-            prev0[i] = v.x;
-            prev1[i] = v.y;
-            if (i < T.rows_valid)
-                sum_prev = dot2u(v.y, T.w1, dot2u(v.x, T.w0, sum_prev));
-        }
-        have_prev = true;
-    } else {
-#pragma unroll
-        for (int i = 0; i < TH; ++i)
-            prev0[i] = prev1[i] = 0;
-    }
-
     // every tile of a launch takes the same path, so wavefronts cost the same and none trails
     // staged: per-lane offsets of the 16-byte loads (16 lanes per luma row, 8 per chroma row)
     StageOffsets<TH> O;
@@ -1120,16 +1437,59 @@ frames_kernel(const KernelArgs a)
                           (uint32_t)(lane >> 3) * (uint32_t)a.pitch[pk[p]];
     }
 
-    frame_loop<BPC, TH, GENERIC, STAGED, MOM>(a, T, O, prev0, prev1, sum_prev, have_prev, stage);
-
-    // counted before the state write, so the count waits only for this workgroup's sum atomics
-    publish_if_last<MOM ? kMaxSums : kSums>(a, lane);
-
-    if (T.chunk == a.chunks - 1) {
-        uint2 *rout = reinterpret_cast<uint2 *>(a.ring_out);
+    if constexpr (V2) {
+        // previous reference luma: from the launch before (saved plane), else none (chunk 0), or
+        // loaded by the chunk's prologue (later chunks)
+        typename Px<BPC>::Luma prev[TH + 4];
+        uint32_t pxprev = 0;
+        bool have_prev = false;
+        if (T.chunk == 0 && a.has_prev) {
+            load_saved<BPC, TH, GENERIC, STAGED>(a, T, s, prev, pxprev);
+            have_prev = true;
+        } else {
 #pragma unroll
-        for (int i = 0; i < TH; ++i)
-            rout[(T.tile * TH + i) * kWave + lane] = make_uint2(prev0[i], prev1[i]);
+            for (int k = 0; k < TH + 4; ++k)
+                prev[k] = typename Px<BPC>::Luma{};
+        }
+        frame_loop_v2<BPC, TH, GENERIC, STAGED, MOM>(a, T, O, prev, pxprev, have_prev, stage);
+        publish_if_last<MOM ? kMaxSums : kSums>(a, lane);
+        if (T.chunk == a.chunks - 1)
+            store_saved<BPC, TH>(a, T, s, prev);
+    } else {
+        // previous blurred tile: from the launch before, else none (chunk 0), or re-blurred by
+        // the chunk's prologue (later chunks)
+        uint32_t prev0[TH], prev1[TH];
+        uint32_t sum_prev = 0;
+        bool have_prev = false;
+        if (T.chunk == 0 && a.has_prev) {
+            const uint2 *rin = reinterpret_cast<const uint2 *>(a.ring_in);
+#pragma unroll
+            for (int i = 0; i < TH; ++i) {
+                const uint2 v = rin[(T.tile * TH + i) * kWave + lane];
+                prev0[i] = v.x;
+                prev1[i] = v.y;
+                if (i < T.rows_valid)
+                    sum_prev = dot2u(v.y, T.w1, dot2u(v.x, T.w0, sum_prev));
+            }
+            have_prev = true;
+        } else {
+#pragma unroll
+            for (int i = 0; i < TH; ++i)
+                prev0[i] = prev1[i] = 0;
+        }
+
+        frame_loop<BPC, TH, GENERIC, STAGED, MOM>(a, T, O, prev0, prev1, sum_prev, have_prev,
+                                                  stage);
+
+        // counted before the state write, so the count waits only for this workgroup's atomics
+        publish_if_last<MOM ? kMaxSums : kSums>(a, lane);
+
+        if (T.chunk == a.chunks - 1) {
+            uint2 *rout = reinterpret_cast<uint2 *>(a.ring_out);
+#pragma unroll
+            for (int i = 0; i < TH; ++i)
+                rout[(T.tile * TH + i) * kWave + lane] = make_uint2(prev0[i], prev1[i]);
+        }
     }
 }
 
@@ -1152,17 +1512,17 @@ frames_kernel(const KernelArgs a)
 
 // Every (bit depth, tile height, path) the host may pick. The fast path needs W % 8 == 0 and
 // H % TH == 0 (no ragged tile, no partial sample group); the generic path takes any size.
-template <int BPC, bool GENERIC, bool MOM>
+template <int BPC, bool GENERIC, bool MOM, bool V2 = false>
 FramesFn frames_fn(int th)
 {
     constexpr bool P = BPC == 8 ? IIR_STAGE8 : IIR_STAGE10;
     switch (th) {
     case 12:
-        return frames_kernel<BPC, 12, P, GENERIC, IIR_WPE12, MOM>;
+        return frames_kernel<BPC, 12, P, GENERIC, IIR_WPE12, MOM, V2>;
     case 16:
-        return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16, MOM>;
+        return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16, MOM, V2>;
     case 20:
-        return frames_kernel<BPC, 20, P, GENERIC, IIR_WPE20, MOM>;
+        return frames_kernel<BPC, 20, P, GENERIC, IIR_WPE20, MOM, V2>;
     default:
         return nullptr;
     }

@@ -86,9 +86,12 @@ struct iir_ctx {
     int min_chunk = 4;
     int max_chunks = 1;
     bool moments = false;  // IIR_FLAG_MOMENTS: the kernels also sum the luma moments
+    bool v2 = false;       // IIR_FLAG_MOTION_V2: motion of the filtered frame difference
     int nsums = kSums;     // 64-bit sums per frame: kSums, or kMaxSums with moments
     uint32_t *ring[2] = {nullptr, nullptr};
-    int ring_cur = 0;  // ring[ring_cur] holds the blurred state of the last submitted frame
+    // ring[ring_cur] holds the blurred state of the last submitted frame (motion v2: its
+    // reference luma, as a plane of strips * 256 samples per row, which fits the same bytes)
+    int ring_cur = 0;
     unsigned long long *sums = nullptr;       // device, [max_batch][nsums][kSumSlots], zero
                                               // between launches (each launch re-zeroes it)
     unsigned int *arrivals = nullptr;         // device, finished-workgroup counter, zero
@@ -145,8 +148,10 @@ int check_config(const iir_config *c)
         return fail(IIR_EINVAL, "frame size %dx%d outside 3..32768", c->width, c->height);
     if (c->max_batch < 1 || c->max_batch > 65536)
         return fail(IIR_EINVAL, "max_batch %d outside 1..65536", c->max_batch);
-    if (c->flags & ~(IIR_FLAG_TIMING | IIR_FLAG_MOMENTS))
+    if (c->flags & ~(IIR_FLAG_TIMING | IIR_FLAG_MOMENTS | IIR_FLAG_MOTION_V2))
         return fail(IIR_EINVAL, "unknown flags 0x%x", c->flags);
+    if ((c->flags & IIR_FLAG_MOTION_V2) && c->bpc != 8 && c->bpc != 10)
+        return fail(IIR_EINVAL, "motion v2 needs 8- or 10-bit samples, got %d", c->bpc);
     return IIR_OK;
 }
 
@@ -217,7 +222,8 @@ int choose_rows(iir_ctx *c, int cus, int forced)
             continue;
         int per_cu = 0;
         const bool generic = !fast_path_ok(c->cfg.width, c->cfg.height, th);
-        if (frames_occupancy(c->cfg.bpc, th, generic, c->moments, &per_cu) != hipSuccess ||
+        if (frames_occupancy(c->cfg.bpc, th, generic, c->moments, c->v2, &per_cu) !=
+                hipSuccess ||
             per_cu < 1)
             continue;
         const int64_t waves = (int64_t)c->strips * ((c->cfg.height + th - 1) / th);
@@ -368,7 +374,7 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
         HIP_TRY(hipEventRecord(sub.k0, c->stream));
     HIP_TRY(launch_frames(c->cfg.bpc, c->rows_per_tile,
                           !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile),
-                          c->moments, a, c->stream));
+                          c->moments, c->v2, a, c->stream));
     // the kernel itself writes the totals to host_sums; one event marks the end (with timing,
     // the event that closes the kernel's timed interval)
     HIP_TRY(hipEventRecord(timing ? sub.k1 : sub.done, c->stream));
@@ -420,6 +426,7 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     c->Wc = (cfg->width + 1) / 2;
     c->Hc = (cfg->height + 1) / 2;
     c->moments = (cfg->flags & IIR_FLAG_MOMENTS) != 0;
+    c->v2 = (cfg->flags & IIR_FLAG_MOTION_V2) != 0;
     c->nsums = c->moments ? kMaxSums : kSums;
     choose_columns(c);
     c->rows_per_tile = choose_rows(c, prop.multiProcessorCount, env_int("IIR_ROWS_PER_TILE", 0, 0, 64));
@@ -656,6 +663,8 @@ IIR_API int iir_export_blur(iir_ctx *ctx, void *dst, int64_t pitch)
         return fail(IIR_EINVAL, "pitch %lld: needs >= 2*W and 4-byte alignment", (long long)pitch);
     if (!ctx->any_frame)
         return fail(IIR_ESTATE, "no frame submitted since create or reset");
+    if (ctx->v2)
+        return fail(IIR_ESTATE, "motion v2 keeps no blurred frame");
     DeviceScope ds(ctx->device);
     if (ds.err != hipSuccess)
         return fail_hip(ds.err, "hipSetDevice");

@@ -51,20 +51,26 @@ struct KernelArgs {
     int32_t shift;  // 16-bit samples: 16 - bit depth, the left shift that scales them to 16 bits
 };
 
-// The frames kernel of one configuration, or nullptr: one function per sample type, each in its
-// own translation unit (iir_frames_8.hip, iir_frames_10.hip, iir_frames_16.hip).
+// The frames kernel of one configuration, or nullptr: one function per sample type and motion
+// variant, each in its own translation unit (iir_frames_8.hip, iir_frames_10.hip,
+// iir_frames_16.hip, and the motion v2 units iir_frames_8_v2.hip, iir_frames_10_v2.hip).
 typedef void (*FramesFn)(KernelArgs);
 FramesFn frames_pick_8(int th, bool generic, bool moments);
 FramesFn frames_pick_10(int th, bool generic, bool moments);
 FramesFn frames_pick_16(int th, bool generic, bool moments);
+FramesFn frames_pick_8_v2(int th, bool generic, bool moments);
+FramesFn frames_pick_10_v2(int th, bool generic, bool moments);
 
 // Host-side launchers (iir_kernels.hip). Each returns the launch's hipError_t.
 bool supported_rows_per_tile(int th);           // 12, 16 or 20
 bool fast_path_ok(int W, int H, int th);         // the uniform fast path applies
-// `moments`: the launch also sums the luma moments (S = kMaxSums)
-hipError_t frames_occupancy(int bpc, int th, bool generic, bool moments, int *waves_per_cu);
-hipError_t launch_frames(int bpc, int th, bool generic, bool moments, const KernelArgs &a,
-                         hipStream_t stream);
+// `moments`: the launch also sums the luma moments (S = kMaxSums); `v2`: the motion sum is the
+// motion v2 one (8- and 10-bit only), with ring_in / ring_out holding the last frame's reference
+// luma as a plane of strips * 256 samples per row instead of the tiled blurred state
+hipError_t frames_occupancy(int bpc, int th, bool generic, bool moments, bool v2,
+                            int *waves_per_cu);
+hipError_t launch_frames(int bpc, int th, bool generic, bool moments, bool v2,
+                         const KernelArgs &a, hipStream_t stream);
 hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
                          int strips, int th, hipStream_t stream);
 hipError_t launch_probe(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream);

@@ -66,8 +66,15 @@ __global__ __launch_bounds__(256) void probe_copy(const uint4 *src, uint4 *dst, 
 
 // 8-bit and 10-bit samples have kernels of their own; every other depth up to 16 bits takes the
 // 16-bit one with the launch's scale shift
-FramesFn pick(int bpc, int th, bool generic, bool moments)
+FramesFn pick(int bpc, int th, bool generic, bool moments, bool v2 = false)
 {
+    if (v2) {
+        if (bpc == 8)
+            return frames_pick_8_v2(th, generic, moments);
+        if (bpc == 10)
+            return frames_pick_10_v2(th, generic, moments);
+        return nullptr;
+    }
     if (bpc == 8)
         return frames_pick_8(th, generic, moments);
     if (bpc == 10)
@@ -88,9 +95,10 @@ bool fast_path_ok(int W, int H, int th)
     return W % 8 == 0 && H % th == 0;
 }
 
-hipError_t frames_occupancy(int bpc, int th, bool generic, bool moments, int *waves_per_cu)
+hipError_t frames_occupancy(int bpc, int th, bool generic, bool moments, bool v2,
+                            int *waves_per_cu)
 {
-    FramesFn f = pick(bpc, th, generic, moments);
+    FramesFn f = pick(bpc, th, generic, moments, v2);
     if (!f)
         return hipErrorInvalidValue;
     int blocks = 0;
@@ -100,10 +108,10 @@ hipError_t frames_occupancy(int bpc, int th, bool generic, bool moments, int *wa
     return e;
 }
 
-hipError_t launch_frames(int bpc, int th, bool generic, bool moments, const KernelArgs &a,
-                         hipStream_t stream)
+hipError_t launch_frames(int bpc, int th, bool generic, bool moments, bool v2,
+                         const KernelArgs &a, hipStream_t stream)
 {
-    FramesFn f = pick(bpc, th, generic, moments);
+    FramesFn f = pick(bpc, th, generic, moments, v2);
     if (!f)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(f, dim3((unsigned)(a.tiles * a.chunks)), dim3(kWave), 0, stream, a);

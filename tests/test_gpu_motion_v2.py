@@ -1,0 +1,135 @@
+"""GPU parity of motion v2 (IIR_FLAG_MOTION_V2), through the C ABI.
+
+Motion v2 filters the difference prev - cur of consecutive reference luma frames with the same
+separable taps (floor shifts) and sums the absolute values. Every sum equals the oracle's
+(oracle.clip_v2) exactly: small and ragged clips, every tile height and path, streamed frame by
+frame (the last frame's luma crossing launches), split clips, time chunks, with moments, and the
+five named workloads at full size.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import integer_image_reductions_amd as iir
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(clip):
+    return iir.upload_planes(clip.ref), iir.upload_planes(clip.dist)
+
+
+def _check(sums, hm, want, want_hm, what):
+    assert list(hm) == list(want_hm), what
+    bad = np.argwhere(sums != want)
+    assert bad.size == 0, f"{what}: first mismatch frame {bad[0][0]} sum {bad[0][1]}: " \
+                          f"{sums[bad[0][0]]} vs {want[bad[0][0]]}"
+
+
+SIZES = [(3, 3), (4, 7), (9, 5), (17, 23), (64, 5), (70, 3), (131, 17), (250, 40), (255, 33),
+         (256, 5), (257, 9), (258, 35), (259, 6), (260, 4), (513, 7), (1283, 723)]
+
+
+@pytest.mark.parametrize("bpc", [8, 10])
+@pytest.mark.parametrize("w,h", SIZES, ids=[f"{w}x{h}" for w, h in SIZES])
+def test_v2_small(w, h, bpc):
+    for i, kind in enumerate(["uniform", "extreme", "checker", "impulse"]):
+        frames = 3 if w * h < 200_000 else 2
+        clip = synth.random_clip(w, h, bpc, frames, seed=7000 + 3 * w + h + i, kind=kind)
+        _say("v2", w, h, bpc, kind)
+        ref, dist = _dev(clip)
+        with iir.Context(w, h, bpc, max_batch=4, motion_v2=True) as ctx:
+            sums, hm = ctx.run_clip(ref, dist)
+        want, want_hm = oracle.clip_v2(clip.ref, clip.dist, bpc)
+        _check(sums, hm, want, want_hm, f"{kind} {w}x{h} {bpc}")
+
+
+V2_PATHS = [(504, 36), (1000, 80), (248, 60), (8, 12), (64, 240), (512, 48), (768, 60),
+            (257, 40), (513, 24), (512, 50)]
+
+
+@pytest.mark.parametrize("bpc", [8, 10])
+@pytest.mark.parametrize("th", ["12", "16", "20"])
+@pytest.mark.parametrize("w,h", V2_PATHS, ids=[f"{w}x{h}" for w, h in V2_PATHS])
+def test_v2_each_tile_height_and_path(w, h, th, bpc, monkeypatch):
+    monkeypatch.setenv("IIR_ROWS_PER_TILE", th)
+    clip = synth.random_clip(w, h, bpc, 3, seed=11 * w + h + int(th), kind="uniform")
+    ref, dist = _dev(clip)
+    _say("v2 path", w, h, th, bpc)
+    with iir.Context(w, h, bpc, max_batch=4, motion_v2=True) as ctx:
+        assert ctx.geometry()["rows_per_tile"] == int(th)
+        sums, hm = ctx.run_clip(ref, dist)
+    want, want_hm = oracle.clip_v2(clip.ref, clip.dist, bpc)
+    _check(sums, hm, want, want_hm, f"{w}x{h} th={th} bpc={bpc}")
+
+
+@pytest.mark.parametrize("bpc", [8, 10])
+@pytest.mark.parametrize("w,h", [(300, 70), (512, 48), (257, 33)])
+def test_v2_streaming_split_and_chunks(w, h, bpc, monkeypatch):
+    """Frame by frame (every frame's previous luma comes from the saved plane of the launch
+    before), in two submissions, in one launch, and in time chunks all give the same sums."""
+    f = 9
+    clip = synth.random_clip(w, h, bpc, f, seed=w + h + bpc, kind="uniform")
+    ref, dist = _dev(clip)
+    want, want_hm = oracle.clip_v2(clip.ref, clip.dist, bpc)
+    _say("v2 streaming", w, h, bpc)
+    with iir.Context(w, h, bpc, max_batch=16, motion_v2=True) as ctx:
+        for t in range(f):
+            ctx.submit([p[t] for p in ref], [p[t] for p in dist])
+        sums, hm = ctx.collect()
+        _check(sums, hm, want, want_hm, "streaming")
+        ctx.reset()
+        ctx.submit_clip(tuple(p[:4] for p in ref), tuple(p[:4] for p in dist))
+        ctx.submit_clip(tuple(p[4:] for p in ref), tuple(p[4:] for p in dist))
+        sums, hm = ctx.collect()
+        _check(sums, hm, want, want_hm, "split")
+        with pytest.raises(iir.IIRError) as e:
+            ctx.export_blur()
+        assert e.value.code == -6
+    monkeypatch.setenv("IIR_TARGET_WAVES", "100000")
+    monkeypatch.setenv("IIR_MIN_CHUNK", "2")
+    _say("v2 chunks", w, h, bpc)
+    with iir.Context(w, h, bpc, max_batch=16, motion_v2=True) as ctx:
+        assert ctx.plan_chunks(f) > 1
+        ctx.run_clip(tuple(p[:1] for p in ref), tuple(p[:1] for p in dist))
+        sums, hm = ctx.run_clip(tuple(p[1:] for p in ref), tuple(p[1:] for p in dist))
+    _check(sums, hm, want[1:], want_hm[1:], "chunks")
+
+
+@pytest.mark.parametrize("bpc", [8, 10])
+@pytest.mark.parametrize("w,h", [(131, 17), (512, 48), (1283, 723)])
+def test_v2_with_moments(w, h, bpc):
+    clip = synth.random_clip(w, h, bpc, 3, seed=3 * w + h, kind="extreme")
+    ref, dist = _dev(clip)
+    _say("v2 moments", w, h, bpc)
+    with iir.Context(w, h, bpc, max_batch=4, motion_v2=True, moments=True) as ctx:
+        sums, hm = ctx.run_clip(ref, dist)
+    want, want_hm = oracle.clip_v2(clip.ref, clip.dist, bpc)
+    _check(sums[:, :4], hm, want, want_hm, f"v2 moments {w}x{h} {bpc}")
+    for t in range(3):
+        r1, r2 = oracle.moments(clip.ref[0][t], bpc)
+        d1, d2 = oracle.moments(clip.dist[0][t], bpc)
+        assert [int(v) for v in sums[t, 4:]] == [r1, d1, r2, d2]
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c5", "c3", "c4"])
+def test_v2_workload_full(name):
+    """Every frame of a named workload at full size with motion v2, in one launch."""
+    _say("v2 workload", name, "generate")
+    clip = synth.make_clip(name)
+    ref, dist = _dev(clip)
+    _say("v2 workload", name, "gpu")
+    with iir.Context(clip.width, clip.height, clip.bpc, max_batch=clip.frames,
+                     motion_v2=True) as ctx:
+        sums, hm = ctx.run_clip(ref, dist)
+    _say("v2 workload", name, "oracle")
+    want, want_hm = oracle.clip_v2(clip.ref, clip.dist, clip.bpc)
+    _check(sums, hm, want, want_hm, name)

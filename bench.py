@@ -1,7 +1,7 @@
 """Benchmark: frames/s of the integer motion + PSNR sums on 3840x2160 8-bit 4:2:0, one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--moments] [--no-cpu]
-                    [--probe]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--moments]
+                    [--motion-v2] [--no-cpu] [--probe]
     python bench.py --workload c3 --traffic-from FETCH.csv WRITE.csv   (host only, see below)
 
 A step is one pass of the whole path over one batch: one iir_submit_clip of the 50-frame clip
@@ -21,7 +21,10 @@ copy probe (probe_copy moves a known 1 GiB in and 1 GiB out per dispatch).
 cpu_baseline: the plain C oracle (single thread) over the same frames, on the host.
 --moments runs the same workload with the luma moments summed in the same pass (IIR_FLAG_MOMENTS):
 the bytes moved are the same, the arithmetic per sample grows; its traffic summary is kept under
-the workload name with a _moments suffix.
+the workload name with a _moments suffix. --motion-v2 replaces the blurred-frame SAD by motion v2
+(the filter of the frame difference; 8 and 10 bits), suffix _v2; its state across launches is the
+last reference luma frame (W H samples read and written once per launch) instead of the blurred
+plane (2 bytes per pixel each way).
 """
 from __future__ import annotations
 
@@ -52,6 +55,13 @@ WORKLOADS = {
 }
 
 
+def describe(workload: str, moments: bool, motion_v2: bool) -> str:
+    text = WORKLOADS[workload]
+    if motion_v2:
+        text = text.replace("motion SAD", "motion v2 SAD")
+    return text + (" + luma moments" if moments else "")
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -64,12 +74,14 @@ def kernel_sha() -> str:
     return h.hexdigest()
 
 
-def algorithmic_bytes(w: int, h: int, bpc: int, frames: int) -> int:
+def algorithmic_bytes(w: int, h: int, bpc: int, frames: int, motion_v2: bool = False) -> int:
     """Bytes one launch must move: each sample of the 6 planes of every frame pair read once, and
-    the blurred luma state (uint16 per luma pixel) read once and written once per launch."""
+    the state carried between launches read once and written once: the blurred luma (uint16 per
+    luma pixel), or with motion v2 the last reference luma frame (one sample per pixel)."""
     b = 1 if bpc == 8 else 2
     n, nc = w * h, ((w + 1) // 2) * ((h + 1) // 2)
-    return frames * 2 * b * (n + 2 * nc) + 4 * n
+    state = 2 * b * n if motion_v2 else 4 * n
+    return frames * 2 * b * (n + 2 * nc) + state
 
 
 def load_traffic(workload: str):
@@ -105,16 +117,17 @@ def _counter_means(path: str, counter: str):
     return sum(main) / len(main), len(main), sum(copy) / len(copy), len(copy)
 
 
-def write_traffic(workload: str, moments: bool, fetch_csv: str, write_csv: str) -> dict:
+def write_traffic(workload: str, moments: bool, motion_v2: bool, fetch_csv: str,
+                  write_csv: str) -> dict:
     fm, fn, fc, fcn = _counter_means(fetch_csv, "FETCH_SIZE")
     wm, wn, wc, wcn = _counter_means(write_csv, "WRITE_SIZE")
     f_scale = PROBE_BYTES / (fc * 1024.0)
     w_scale = PROBE_BYTES / (wc * 1024.0)
     fetch_b, write_b = fm * 1024.0 * f_scale, wm * 1024.0 * w_scale
-    wl = workload + ("_moments" if moments else "")
-    flag = " --moments" if moments else ""
+    wl = workload + ("_moments" if moments else "") + ("_v2" if motion_v2 else "")
+    flag = (" --moments" if moments else "") + (" --motion-v2" if motion_v2 else "")
     d = {
-        "workload": WORKLOADS[workload] + (" + luma moments" if moments else ""),
+        "workload": describe(workload, moments, motion_v2),
         "kernel_sha256": kernel_sha(),
         "fetch_kib_per_launch": fm, "fetch_dispatches": fn,
         "write_kib_per_launch": wm, "write_dispatches": wn,
@@ -134,7 +147,7 @@ def write_traffic(workload: str, moments: bool, fetch_csv: str, write_csv: str) 
     import synth
     c = synth.CONFIGS[workload]
     d["algorithmic_bytes_per_launch"] = algorithmic_bytes(c["width"], c["height"], c["bpc"],
-                                                          c["frames"])
+                                                          c["frames"], motion_v2)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     path = os.path.join(ROOT, "profiles", f"frames_kernel_{wl}_traffic.json")
     with open(path, "w") as f:
@@ -143,14 +156,18 @@ def write_traffic(workload: str, moments: bool, fetch_csv: str, write_csv: str) 
     return d
 
 
-def cpu_baseline(clip, max_seconds: float = 20.0, moments: bool = False):
+def cpu_baseline(clip, max_seconds: float = 20.0, moments: bool = False,
+                 motion_v2: bool = False):
     """The oracle over the leading frames of the same clip that fit `max_seconds` (the whole clip
     when it fits), single-threaded; frames/s. With moments, also the oracle's luma moments of
     every ref and dist frame."""
     import oracle
 
     def run(c):
-        oracle.clip(c.ref, c.dist, clip.bpc)
+        if motion_v2:
+            oracle.clip_v2(c.ref, c.dist, clip.bpc)
+        else:
+            oracle.clip(c.ref, c.dist, clip.bpc)
         if moments:
             for t in range(c.frames):
                 oracle.moments(c.ref[0][t], clip.bpc)
@@ -178,15 +195,18 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--moments", action="store_true",
                     help="also sum the luma moments in the same pass (IIR_FLAG_MOMENTS)")
+    ap.add_argument("--motion-v2", action="store_true",
+                    help="motion v2 (filter of the frame difference) instead of the blurred SAD")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--probe", action="store_true", help="also measure the memory ceilings")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic summary from two counter CSVs and exit")
     args = ap.parse_args()
 
-    wl = args.workload + ("_moments" if args.moments else "")
+    wl = args.workload + ("_moments" if args.moments else "") + ("_v2" if args.motion_v2 else "")
     if args.traffic_from:
-        print(json.dumps(write_traffic(args.workload, args.moments, *args.traffic_from)))
+        print(json.dumps(write_traffic(args.workload, args.moments, args.motion_v2,
+                                       *args.traffic_from)))
         return
 
     if args.gpus != 1:
@@ -215,7 +235,8 @@ def main():
     log("uploaded", F, "frame pairs")
 
     # two batches in flight: step k is submitted before step k-1 is collected
-    ctx = iir.Context(W, H, bpc, max_batch=2 * F, timing=True, moments=args.moments)
+    ctx = iir.Context(W, H, bpc, max_batch=2 * F, timing=True, moments=args.moments,
+                      motion_v2=args.motion_v2)
     geo = ctx.geometry()
     chunks = ctx.plan_chunks(F)
     clip_dev = ctx.prepare_clip(ref, dist)
@@ -237,7 +258,7 @@ def main():
     ms_step = 1000.0 * elapsed / args.steps
     frames_per_s = F * args.steps / elapsed
     kernel_ms = total_ms / launches
-    alg = algorithmic_bytes(W, H, bpc, F)
+    alg = algorithmic_bytes(W, H, bpc, F, args.motion_v2)
     achieved = alg / (kernel_ms * 1e-3) / 1e9
     log(f"kernel {kernel_ms * 1e3:.1f} us/launch (mean of {launches}), "
         f"step {ms_step * 1e3:.1f} us, {achieved:.0f} GB/s")
@@ -255,8 +276,7 @@ def main():
         "vs_baseline": None,
         "dtype": "u8" if bpc == 8 else "u16",
         "data": "synthetic (seeded value-noise clip of the workload's shape; see synth.py)",
-        "config": {"workload": WORKLOADS[args.workload] + (" + luma moments" if args.moments
-                                                           else ""),
+        "config": {"workload": describe(args.workload, args.moments, args.motion_v2),
                    "width": W, "height": H, "bpc": bpc,
                    "frames_per_step": F, "chroma": "4:2:0", "tiles": geo["tiles"],
                    "time_chunks": chunks, "parallelism": "single GPU"},
@@ -280,7 +300,7 @@ def main():
     ctx.close()
     if not args.no_cpu:
         log("cpu baseline")
-        out["cpu_baseline"] = cpu_baseline(clip, moments=args.moments)
+        out["cpu_baseline"] = cpu_baseline(clip, moments=args.moments, motion_v2=args.motion_v2)
     print(json.dumps(out), flush=True)
 
 

@@ -61,6 +61,7 @@ constexpr uint32_t T10 = G1 | (G0 << 16);
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t dot2u(uint32_t a, uint32_t b, uint32_t c)
 {
@@ -460,6 +461,9 @@ struct Tile {
     uint32_t ym0, ym1;           // luma sample masks for SSE (valid columns)
     uint32_t cm;                 // chroma sample mask for SSE (valid columns)
     bool c_upper;                // 8-bit: lane reads the second chroma row of each step
+    // staged: byte masks of the lane's 16-byte chroma groups (load q, dword j): the columns
+    // inside the plane, on rows of the tile inside the plane
+    uint32_t cmk[2][4];
 };
 
 // The loaded samples of one frame for one tile: reference luma rows r0-2 .. r0+TH+1, distorted
@@ -477,23 +481,31 @@ struct FrameData {
     u32x2 HL;  // the lane's 8 halo bytes (see Tile::hvoff)
 };
 
-// LDS staging of one 8-bit frame (one wavefront per workgroup, so the workgroup's LDS is the
-// wave's), in rows of 256 bytes (one dword per lane). Loads write LDS directly, 16 bytes per
-// lane, so one instruction moves 1 KB: four luma rows of the tile (16 lanes per row) or eight
-// chroma rows (8 lanes per row). A chroma LDS row holds two chroma rows, the second for the
-// upper half-wave, which is the order the chroma SSE steps read them in.
+// LDS staging of one 8-bit frame's luma (one wavefront per workgroup, so the workgroup's LDS is
+// the wave's), in rows of 256 bytes (one dword per lane). Loads write LDS directly, 16 bytes per
+// lane, so one instruction moves 1 KB: four luma rows of the tile (16 lanes per row). Two stages
+// alternate, so the luma of frames t+1 and t+2 is in flight while frame t is computed. Chroma,
+// which only feeds the squared error, skips LDS: 16-byte register loads, the same lane layout for
+// the reference and distorted planes (8 lanes per 128-byte chroma row, eight rows per load).
 template <int TH>
 struct Stage {
     static constexpr int kRefLoads = (TH + 4) / 4;    // 16-byte loads of reference luma
     static constexpr int kDistLoads = TH / 4;         // of distorted luma
     static constexpr int kChromaLoads = (TH + 15) / 16;  // per chroma plane (8 rows each)
-    static constexpr int kChromaRows = 4 * kChromaLoads;  // LDS rows per chroma plane
     static constexpr int kRef = 0;
     static constexpr int kDist = TH + 4;
-    static constexpr int kChroma = kDist + TH;      // planes ref U, dist U, ref V, dist V
-    static constexpr int kHalo = kChroma + 4 * kChromaRows;  // four rows: 16 bytes per lane
+    static constexpr int kHalo = kDist + TH;  // four rows: 16 bytes per lane
     static constexpr int kRows = kHalo + 4;
+    // staged loads of an accumulated frame, all counted by vmcnt in issue order
+    static constexpr int kDmaLoads = kRefLoads + 1 + kDistLoads;
     static_assert(TH % 4 == 0, "whole 16-byte luma loads");
+    static_assert(kDmaLoads < 16, "the frame wait encodes the count in vmcnt's low bits");
+};
+
+// A frame's chroma for the staged path: ref U, dist U, ref V, dist V, 16 bytes per lane per load.
+template <int TH>
+struct ChromaX4 {
+    u32x4 p[4][Stage<TH>::kChromaLoads];
 };
 
 // Per-lane byte offsets of a tile's staged loads, fixed for the whole launch: one per reference
@@ -598,24 +610,32 @@ __device__ __forceinline__ void load_frame_staged(const KernelArgs &a, const Til
 #pragma unroll
     for (int q = 0; q < ST::kDistLoads; ++q)
         dma16_stream(rd, ST::kDist + 4 * q, O.dist, (uint32_t)(T.r0 + 4 * q) * pd);
+}
+
+// Issue frame t's chroma loads into registers (staged path).
+template <int TH>
+__device__ __forceinline__ void load_chroma_x4(const KernelArgs &a, const Tile &T,
+                                               const StageOffsets<TH> &O, int t, ChromaX4<TH> &C)
+{
     constexpr int pk[4] = {1, 4, 2, 5};
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const Rsrc rc = plane_rsrc(frame_plane(a, t, pk[p]), a.span[pk[p]]);
         const uint32_t pc = opaque((uint32_t)a.pitch[pk[p]]);
 #pragma unroll
-        for (int q = 0; q < ST::kChromaLoads; ++q)
-            dma16_stream(rc, ST::kChroma + p * ST::kChromaRows + 4 * q, O.chroma[p],
-                         (uint32_t)(T.crow0 + 8 * q) * pc);
+        for (int q = 0; q < Stage<TH>::kChromaLoads; ++q) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+                rc, (int)O.chroma[p], (int)((uint32_t)(T.crow0 + 8 * q) * pc), kStream);
+            C.p[p][q] = u32x4{v[0], v[1], v[2], v[3]};
+        }
     }
 }
 
-// The staged 8-bit frame, from LDS into registers.
+// The staged 8-bit frame's luma, from LDS into registers.
 template <int TH>
 __device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWave], int lane,
                                            uint32_t hlds, FrameData<8, TH> &F)
 {
-    typedef FrameData<8, TH> FD;
     typedef Stage<TH> ST;
 #pragma unroll
     for (int k = 0; k < TH + 4; ++k)
@@ -626,13 +646,6 @@ __device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWav
 #pragma unroll
     for (int i = 0; i < TH; ++i)
         F.D[i] = lds[ST::kDist + i][lane];
-#pragma unroll
-    for (int k = 0; k < FD::kChromaSteps; ++k) {
-        F.cu[k] = lds[ST::kChroma + k][lane];
-        F.du[k] = lds[ST::kChroma + ST::kChromaRows + k][lane];
-        F.cv[k] = lds[ST::kChroma + 2 * ST::kChromaRows + k][lane];
-        F.dv[k] = lds[ST::kChroma + 3 * ST::kChromaRows + k][lane];
-    }
 }
 
 // Fast path, last strip with the frame's right edge inside it: the lane whose first column is W
@@ -747,6 +760,21 @@ struct FrameStats {
     Sq<BPC> sy = 0, su = 0, sv = 0, m2r = 0, m2d = 0;
     uint32_t sy2 = 0, su2 = 0, sv2 = 0, m1r = 0, m1d = 0;
 };
+
+// Squared error of the staged path's chroma (16 bytes per lane per load, masked to the tile).
+template <int TH>
+__device__ __forceinline__ void chroma_sse_x4(const Tile &T, const ChromaX4<TH> &C,
+                                              FrameStats<8> &S)
+{
+#pragma unroll
+    for (int q = 0; q < Stage<TH>::kChromaLoads; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t m = T.cmk[q][j];
+            sse_chroma<8>(C.p[0][q][j] & m, C.p[1][q][j] & m, S.su, S.su2);
+            sse_chroma<8>(C.p[2][q][j] & m, C.p[3][q][j] & m, S.sv, S.sv2);
+        }
+}
 
 // Squared error (and moments) of output row i's luma samples.
 template <int BPC, int TH, bool GENERIC, bool MOM>
@@ -929,6 +957,7 @@ __device__ __forceinline__ uint32_t abs_f(int32_t a_biased, uint32_t b)
 template <int BPC, int TH, bool GENERIC, bool ROWSTAGE, bool MOM>
 __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T, int t,
                                               bool accumulate, FrameData<BPC, TH> &F,
+                                              FrameStats<BPC> &S,
                                               const uint32_t (&prev0)[TH],
                                               const uint32_t (&prev1)[TH], uint32_t (&next0)[TH],
                                               uint32_t (&next1)[TH], uint32_t &sum_prev,
@@ -947,10 +976,12 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
     const uint32_t shift = (uint32_t)a.shift;
     const uint32_t hv = halo_vertical<BPC>(F.HL, T.hsel, shift);
 
-    // SSE of the chroma tiles first, which frees their registers before the blur
-    FrameStats<BPC> S;
-    if (accumulate)
-        chroma_sse<BPC, TH, GENERIC>(a, T, F, S.su, S.su2, S.sv, S.sv2);
+    // SSE of the chroma tiles first, which frees their registers before the blur (the staged
+    // path has already summed its chroma into S)
+    if constexpr (!ROWSTAGE) {
+        if (accumulate)
+            chroma_sse<BPC, TH, GENERIC>(a, T, F, S.su, S.su2, S.sv, S.sv2);
+    }
 
     // blur, SAD against the previous blurred tile, and SSE of the luma rows as they go by
     uint32_t acc_c = 0, acc_min = 0;
@@ -1002,6 +1033,7 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 template <int BPC, int TH, bool GENERIC, bool ROWSTAGE, bool MOM>
 __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile &T,
                                                  bool accumulate, FrameData<BPC, TH> &F,
+                                                 FrameStats<BPC> &S,
                                                  const typename Px<BPC>::Luma (&pin)[TH + 4],
                                                  uint32_t pxin,
                                                  typename Px<BPC>::Luma (&pout)[TH + 4],
@@ -1014,8 +1046,8 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
     }
     const uint32_t x0 = perm(F.HL.y, F.HL.x, T.hsel);  // this frame's halo pair
     if (accumulate) {
-        FrameStats<BPC> S;
-        chroma_sse<BPC, TH, GENERIC>(a, T, F, S.su, S.su2, S.sv, S.sv2);
+        if constexpr (!ROWSTAGE)
+            chroma_sse<BPC, TH, GENERIC>(a, T, F, S.su, S.su2, S.sv, S.sv2);
         uint32_t sad = 0;
         if (have_prev) {
             uint32_t hvh, hvl;
@@ -1081,6 +1113,50 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
     have_prev = true;
 }
 
+// Staged path, frame t of a chunk's loop: wait until its luma (in the stage `lds`) and its chroma
+// (in C) have landed, read the luma out and sum the chroma, then issue frame t+1's chroma into C
+// and frame t+2's luma into the stage just read, so two frames of loads stay in flight while
+// frame t is computed. Loads complete in issue order (vmcnt): ... luma t, chroma t, luma t+1,
+// chroma t+1, luma t+2 ..., so frame t has landed once only the kDmaLoads loads of the luma
+// group after its chroma may still be outstanding. Every chroma group is followed by exactly one
+// luma group on every path (the chunk's last one reloads its last frame into the free stage, an
+// L2 hit), so that one wait is always right and the compiler's own count for the chroma registers
+// agrees with it. The wavefront raises its priority from the wait to the last load issued, so a
+// wavefront whose data has landed refills the memory pipe ahead of its SIMD's computing waves.
+template <int TH>
+__device__ __forceinline__ void staged_frame(const KernelArgs &a, const Tile &T,
+                                             const StageOffsets<TH> &O, int t, int f_begin,
+                                             int f_end, uint32_t (*lds)[kWave], ChromaX4<TH> &C,
+                                             FrameData<8, TH> &F, FrameStats<8> &S)
+{
+    __builtin_amdgcn_s_setprio(3);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | Stage<TH>::kDmaLoads);  // vmcnt(one luma group)
+    read_stage<TH>(t >= f_begin, lds, T.lane, T.hlds, F);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
+    if (t >= f_begin)
+        chroma_sse_x4<TH>(T, C, S);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < f_end) {
+        load_chroma_x4<TH>(a, T, O, t + 1, C);
+        load_frame_staged<TH>(a, T, O, min(t + 2, f_end - 1), true, lds);
+    }
+    __builtin_amdgcn_s_setprio(0);
+}
+
+// The first loads of a chunk's loop: luma and chroma of its first frame, then the luma of the
+// second (of the first again for a one-frame chunk). The frame loop waits for all of its loads
+// before the chunk's sums are published (vmcnt(0)), so no load into LDS outlives the wavefront.
+template <int TH>
+__device__ __forceinline__ void staged_start(const KernelArgs &a, const Tile &T,
+                                             const StageOffsets<TH> &O, int t0, int f_begin,
+                                             int f_end, uint32_t (*lds)[kWave], ChromaX4<TH> &C)
+{
+    load_frame_staged<TH>(a, T, O, t0, t0 >= f_begin, lds);
+    if (t0 >= f_begin)
+        load_chroma_x4<TH>(a, T, O, t0, C);
+    load_frame_staged<TH>(a, T, O, min(t0 + 1, f_end - 1), true, lds + Stage<TH>::kRows);
+}
+
 // The frames of this workgroup's time chunk. Chunks after the first start by re-blurring the
 // frame before them. STAGED keeps the next frame's loads in flight while the current one is
 // computed: the loads of frame t+1 write the wave's LDS stage (no registers held), issued as soon
@@ -1102,35 +1178,27 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
         P.v[k] = 0;
     P.first = f_begin;
     P.count = 0;
+    ChromaX4<TH> C;
     if constexpr (STAGED)
-        load_frame_staged<TH>(a, T, O, t0, t0 >= f_begin, lds);
-    // one frame: blurred tile in (i0, i1), out to (o0, o1)
-    auto step = [&](int t, const uint32_t(&i0)[TH], const uint32_t(&i1)[TH], uint32_t(&o0)[TH],
-                    uint32_t(&o1)[TH]) {
+        staged_start<TH>(a, T, O, t0, f_begin, f_end, lds, C);
+    // one frame: blurred tile in (i0, i1), out to (o0, o1); staged, its luma in stage `sidx`
+    auto step = [&](int t, int sidx, const uint32_t(&i0)[TH], const uint32_t(&i1)[TH],
+                    uint32_t(&o0)[TH], uint32_t(&o1)[TH]) {
         // a fresh frame per step: no sample register is carried from one frame to the next
         FrameData<BPC, TH> F;
-        if constexpr (STAGED) {
-            // raised priority from the wait to the last load issued: a wavefront whose frame has
-            // landed reads it out and refills the memory pipe ahead of its SIMD's computing waves
-            __builtin_amdgcn_s_setprio(3);
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): frame t is in LDS
-            read_stage<TH>(t >= f_begin, lds, T.lane, T.hlds, F);
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
-            __builtin_amdgcn_sched_barrier(0);
-            if (t + 1 < f_end)
-                load_frame_staged<TH>(a, T, O, t + 1, true, lds);
-            __builtin_amdgcn_s_setprio(0);
-        } else {
+        FrameStats<BPC> S;
+        if constexpr (STAGED)
+            staged_frame<TH>(a, T, O, t, f_begin, f_end, lds + sidx * Stage<TH>::kRows, C, F, S);
+        else
             load_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F);
-        }
-        compute_frame<BPC, TH, GENERIC, STAGED, MOM>(a, T, t, t >= f_begin, F, i0, i1, o0, o1,
-                                                     sum_prev, have_prev, P);
+        compute_frame<BPC, TH, GENERIC, STAGED, MOM>(a, T, t, t >= f_begin, F, S, i0, i1, o0,
+                                                     o1, sum_prev, have_prev, P);
     };
     uint32_t alt0[TH], alt1[TH];
     for (int t = t0; t < f_end; t += 2) {
-        step(t, prev0, prev1, alt0, alt1);
+        step(t, 0, prev0, prev1, alt0, alt1);
         if (t + 1 < f_end) {
-            step(t + 1, alt0, alt1, prev0, prev1);
+            step(t + 1, 1, alt0, alt1, prev0, prev1);
         } else {
 #pragma unroll
             for (int i = 0; i < TH; ++i) {
@@ -1163,32 +1231,26 @@ __device__ __forceinline__ void frame_loop_v2(const KernelArgs &a, const Tile &T
         P.v[k] = 0;
     P.first = f_begin;
     P.count = 0;
+    ChromaX4<TH> C;
     if constexpr (STAGED)
-        load_frame_staged<TH>(a, T, O, t0, t0 >= f_begin, lds);
-    auto step = [&](int t, const Luma(&pin)[TH + 4], uint32_t pxin, Luma(&pout)[TH + 4],
-                    uint32_t &pxout) {
+        staged_start<TH>(a, T, O, t0, f_begin, f_end, lds, C);
+    auto step = [&](int t, int sidx, const Luma(&pin)[TH + 4], uint32_t pxin,
+                    Luma(&pout)[TH + 4], uint32_t &pxout) {
         FrameData<BPC, TH> F;
-        if constexpr (STAGED) {
-            __builtin_amdgcn_s_setprio(3);
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): frame t is in LDS
-            read_stage<TH>(t >= f_begin, lds, T.lane, T.hlds, F);
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
-            __builtin_amdgcn_sched_barrier(0);
-            if (t + 1 < f_end)
-                load_frame_staged<TH>(a, T, O, t + 1, true, lds);
-            __builtin_amdgcn_s_setprio(0);
-        } else {
+        FrameStats<BPC> S;
+        if constexpr (STAGED)
+            staged_frame<TH>(a, T, O, t, f_begin, f_end, lds + sidx * Stage<TH>::kRows, C, F, S);
+        else
             load_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F);
-        }
-        compute_frame_v2<BPC, TH, GENERIC, STAGED, MOM>(a, T, t >= f_begin, F, pin, pxin, pout,
-                                                        pxout, have_prev, P);
+        compute_frame_v2<BPC, TH, GENERIC, STAGED, MOM>(a, T, t >= f_begin, F, S, pin, pxin,
+                                                        pout, pxout, have_prev, P);
     };
     Luma alt[TH + 4];
     uint32_t pxalt = 0;
     for (int t = t0; t < f_end; t += 2) {
-        step(t, prev, pxprev, alt, pxalt);
+        step(t, 0, prev, pxprev, alt, pxalt);
         if (t + 1 < f_end) {
-            step(t + 1, alt, pxalt, prev, pxprev);
+            step(t + 1, 1, alt, pxalt, prev, pxprev);
         } else {
 #pragma unroll
             for (int k = 0; k < TH + 4; ++k)
@@ -1308,7 +1370,7 @@ template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE, bool MOM, bool V2
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void
 frames_kernel(const KernelArgs a)
 {
-    __shared__ uint32_t stage[STAGED ? Stage<TH>::kRows : 1][kWave];
+    __shared__ uint32_t stage[STAGED ? 2 * Stage<TH>::kRows : 1][kWave];  // two stages
     static_assert(TH % 4 == 0, "tile height must be a multiple of 4 (two chroma rows per step)");
     static_assert(!STAGED || BPC == 8, "LDS staging is laid out for 8-bit samples");
     constexpr int B = Px<BPC>::kBytes;
@@ -1412,6 +1474,26 @@ frames_kernel(const KernelArgs a)
         T.cm = (ccol < a.Wc ? 0xffffu : 0u) | (ccol + 1 < a.Wc ? 0xffff0000u : 0u);
     }
     T.crow0 = uni(T.r0 / 2);
+    if constexpr (STAGED) {
+        // staged chroma: lane l reads the 16 bytes at column cs + 16 (l mod 8) of tile chroma row
+        // 8q + l / 8; rows past the tile's TH / 2 or past the plane, and columns past Wc, are
+        // masked out
+        const int c16 = cs + 16 * (lane & 7);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int row = 8 * q + (lane >> 3);
+            const bool row_ok = row < TH / 2 && T.crow0 + row < a.Hc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    m |= c16 + 4 * j + b < a.Wc ? 0xffu << (8 * b) : 0u;
+                T.cmk[q][j] = row_ok ? m : 0u;
+            }
+        }
+        T.c_on = true;
+    }
     {
         const uint32_t col = T.c_on ? (uint32_t)(ccol * B) : 0u;
         const int pk[4] = {1, 4, 2, 5};

@@ -248,7 +248,8 @@ typedef struct iir_geometry {
     int32_t strips;            /* tiles across: ceil(W / 256) */
     int32_t row_tiles;         /* tiles down */
     int32_t tiles;             /* strips * row_tiles */
-    int32_t sum_slots;         /* partial accumulators per sum, folded on the host */
+    int32_t sum_slots;         /* partial accumulators per sum (64), folded on the device in 8
+                                  groups whose totals the host adds */
     int32_t max_chunks;        /* most time chunks one launch may split a clip into */
 } iir_geometry;
 IIR_API int iir_get_geometry(const iir_ctx *ctx, iir_geometry *out);

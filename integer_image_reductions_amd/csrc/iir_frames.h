@@ -34,7 +34,8 @@
 //   * A workgroup loops over the frames of its time chunk, keeping the previous blurred tile in
 //     registers; the blurred state crosses launches through a small tiled plane (ring).
 //   * Per frame, per workgroup: one 64-bit atomic per sum ("ADR-1392", Decision 1), into one of
-//     kSumSlots partial slots chosen by XCD; the host adds the slots.
+//     kSumSlots partial slots; the last workgroup of each of 8 slot groups folds its group's slots
+//     and the host adds the 8 group totals.
 //   * Workgroup ids are remapped so each XCD (and its L2) gets a contiguous run of vertically
 //     adjacent tiles, which share their halo rows.
 #pragma once
@@ -1311,24 +1312,31 @@ __device__ __forceinline__ void store_saved(const KernelArgs &a, const Tile &T, 
                 prev[i + 2];
 }
 
-// The launch's last workgroup to finish (counted with one device-scope atomic per workgroup)
-// folds the kSumSlots partial sums of each of the NS sums of every frame, writes the totals straight to the
-// caller-visible pinned buffer and zeroes the partial sums and the counter for the next launch.
-// No workgroup waits for another, and no separate readback copy follows the kernel. Ordering:
-// the sum atomics are device-scope read-modify-writes; each workgroup waits until its own have
-// completed (vmcnt(0)) before counting itself, and the last one reads them back with
+// Each workgroup adds its per-frame sums into slot blockIdx mod kSumSlots, so a slot takes the
+// atomics of 1/64 of the workgroups: with fewer slots the atomics of the whole grid, all issued
+// when the workgroups finish their last frames, queue on the same few addresses (8 slots cost
+// ~20 us more per 4K launch than 64). The slots form kSumGroups groups by blockIdx mod 8; the last
+// workgroup of a group to finish (one device-scope counter per group) folds its group's slots of
+// every sum of every frame, writes the group totals straight to the caller-visible pinned buffer
+// [frame][sum][group] and zeroes the slots and its counter for the next launch; the host adds
+// the group totals. No workgroup waits for another, and no readback copy follows the kernel.
+// Ordering: the sum atomics are device-scope read-modify-writes; each workgroup waits until its
+// own have completed (vmcnt(0)) before counting itself, and the last one reads them back with
 // device-scope atomic loads after an acquire fence. A release fence per workgroup would write
 // back every XCD's L2 once per workgroup, which costs far more than the copy it replaces.
 template <int NS>
 __device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane)
 {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this workgroup's sum atomics completed
+    constexpr int kPerGroup = kSumSlots / kSumGroups;  // slots g, g + 8, ..., g + 56
+    const unsigned int g = blockIdx.x % kSumGroups;
+    const unsigned int members = gridDim.x / kSumGroups + (g < gridDim.x % kSumGroups ? 1u : 0u);
     unsigned int arrived = 0;
     if (lane == 0)
-        arrived = __hip_atomic_fetch_add(a.arrivals, 1u, __ATOMIC_RELAXED,
+        arrived = __hip_atomic_fetch_add(a.arrivals + g, 1u, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
     arrived = (unsigned int)uni((int)arrived);
-    if (arrived != gridDim.x - 1u)
+    if (arrived != members - 1u)
         return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     // kPer totals per lane per pass, all of their slot loads issued before any is added, so a
@@ -1336,14 +1344,14 @@ __device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane)
     constexpr int kPer = 4;
     const int n = a.nframes * NS;
     for (int base = 0; base < n; base += kPer * kWave) {
-        unsigned long long v[kPer][kSumSlots];
+        unsigned long long v[kPer][kPerGroup];
 #pragma unroll
         for (int q = 0; q < kPer; ++q) {
             const int i = min(base + q * kWave + lane, n - 1);
 #pragma unroll
-            for (int j = 0; j < kSumSlots; ++j)
-                v[q][j] = __hip_atomic_load(a.sums + (size_t)i * kSumSlots + j, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
+            for (int j = 0; j < kPerGroup; ++j)
+                v[q][j] = __hip_atomic_load(a.sums + (size_t)i * kSumSlots + g + kSumGroups * j,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
         for (int q = 0; q < kPer; ++q) {
@@ -1351,18 +1359,18 @@ __device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane)
             if (i < n) {
                 unsigned long long total = 0;
 #pragma unroll
-                for (int j = 0; j < kSumSlots; ++j) {
+                for (int j = 0; j < kPerGroup; ++j) {
                     total += v[q][j];
-                    __hip_atomic_store(a.sums + (size_t)i * kSumSlots + j, 0ull,
+                    __hip_atomic_store(a.sums + (size_t)i * kSumSlots + g + kSumGroups * j, 0ull,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                __hip_atomic_store(a.publish + i, total, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_SYSTEM);
+                __hip_atomic_store(a.publish + (size_t)i * kSumGroups + g, total,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             }
         }
     }
     if (lane == 0)
-        __hip_atomic_store(a.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.arrivals + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // the end of the kernel releases these stores to the host before its completion signal
 }
 

@@ -94,9 +94,11 @@ struct iir_ctx {
     int ring_cur = 0;
     unsigned long long *sums = nullptr;       // device, [max_batch][nsums][kSumSlots], zero
                                               // between launches (each launch re-zeroes it)
-    unsigned int *arrivals = nullptr;         // device, finished-workgroup counter, zero
+    unsigned int *arrivals = nullptr;         // device, [kSumGroups] finished-workgroup counters, zero
     int64_t sums_n = 0;
-    unsigned long long *host_sums = nullptr;  // pinned coherent, [max_batch][nsums] totals
+    // pinned coherent, [max_batch][nsums][kSumGroups] group totals (the launch's last workgroup of
+    // each slot group writes its group's; the host adds the groups)
+    unsigned long long *host_sums = nullptr;
     unsigned long long *host_sums_dev = nullptr;  // the same memory as the device sees it
     FramePtrs *table_dev = nullptr;
     FramePtrs *table_host = nullptr;  // pinned, [max_batch]
@@ -108,6 +110,7 @@ struct iir_ctx {
         int n;           // frames
         int taken;       // frames already returned by iir_collect
         bool has_prev;   // frame 0 has a previous frame
+        int groups;      // slot groups with workgroups in the launch (their totals are valid)
         hipEvent_t done; // recorded after the submission's readback
         hipEvent_t k0, k1;  // bracket the main kernel (IIR_FLAG_TIMING)
     };
@@ -353,7 +356,7 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     a.ring_in = c->ring[c->ring_cur];
     a.ring_out = c->ring[c->ring_cur ^ 1];
     a.sums = c->sums;
-    a.publish = c->host_sums_dev + (size_t)first * c->nsums;
+    a.publish = c->host_sums_dev + (size_t)first * c->nsums * kSumGroups;
     a.arrivals = c->arrivals;
     a.W = c->cfg.width;
     a.H = c->cfg.height;
@@ -382,6 +385,7 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     sub.n = n;
     sub.taken = 0;
     sub.has_prev = c->has_prev;
+    sub.groups = std::min(a.tiles * a.chunks, kSumGroups);
     c->sub_count++;
     c->slot_head = first + n;
     c->pending += n;
@@ -450,11 +454,12 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     if (e == hipSuccess)
         e = hipMalloc(&c->sums, sizeof(unsigned long long) * c->sums_n);
     if (e == hipSuccess)
-        e = hipMalloc(&c->arrivals, sizeof(unsigned int));
+        e = hipMalloc(&c->arrivals, sizeof(unsigned int) * kSumGroups);
     if (e == hipSuccess)
         e = hipMalloc(&c->table_dev, sizeof(FramePtrs) * cfg->max_batch);
     if (e == hipSuccess)
-        e = hipHostMalloc(&c->host_sums, sizeof(unsigned long long) * cfg->max_batch * c->nsums,
+        e = hipHostMalloc(&c->host_sums,
+                          sizeof(unsigned long long) * cfg->max_batch * c->nsums * kSumGroups,
                           hipHostMallocCoherent | hipHostMallocMapped);
     if (e == hipSuccess)
         e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->host_sums_dev), c->host_sums, 0);
@@ -475,7 +480,7 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     if (e == hipSuccess)
         e = hipMemsetAsync(c->sums, 0, sizeof(unsigned long long) * c->sums_n, c->stream);
     if (e == hipSuccess)
-        e = hipMemsetAsync(c->arrivals, 0, sizeof(unsigned int), c->stream);
+        e = hipMemsetAsync(c->arrivals, 0, sizeof(unsigned int) * kSumGroups, c->stream);
     for (int i = 0; i < 2 && e == hipSuccess; ++i)
         e = hipMemsetAsync(c->ring[i], 0, ring_bytes, c->stream);
     if (e == hipSuccess)
@@ -527,8 +532,12 @@ IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_o
         const int take = std::min(n - got, sub.n - sub.taken);
         for (int i = 0; i < take; ++i) {
             const int f = sub.taken + i;
-            const volatile unsigned long long *v =
-                ctx->host_sums + (size_t)(sub.first + f) * ctx->nsums;
+            const volatile unsigned long long *g =
+                ctx->host_sums + (size_t)(sub.first + f) * ctx->nsums * kSumGroups;
+            uint64_t v[kMaxSums] = {};
+            for (int k = 0; k < ctx->nsums; ++k)
+                for (int j = 0; j < sub.groups; ++j)
+                    v[k] += g[k * kSumGroups + j];
             iir_result &r = out[got + i];
             r.has_motion = (f > 0 || sub.has_prev) ? 1 : 0;
             r.sad = r.has_motion ? v[0] : 0;

@@ -11,7 +11,8 @@
 namespace iir {
 
 constexpr int kWave = 64;          // CDNA wavefront; one wavefront is one workgroup
-constexpr int kSumSlots = 8;       // partial slots per sum (one per XCD), added up on the host
+constexpr int kSumSlots = 64;      // partial slots per sum: the slot of workgroup b is b mod 64
+constexpr int kSumGroups = 8;      // slot groups (slot mod 8), each folded by its last workgroup
 constexpr int kSums = 4;           // SAD, SSE_Y, SSE_U, SSE_V
 constexpr int kMoments = 4;        // optional: sum ref Y, sum dist Y, sum ref Y^2, sum dist Y^2
 constexpr int kMaxSums = kSums + kMoments;
@@ -37,12 +38,13 @@ struct KernelArgs {
     const uint32_t *ring_in;
     uint32_t *ring_out;
     // per-frame partial sums [nframes][S][kSumSlots], S = kSums, or kMaxSums when the launch
-    // also sums the luma moments; zero at launch; the launch's last workgroup folds the slots,
-    // writes the totals to `publish` and zeroes them again
+    // also sums the luma moments; zero at launch; the last workgroup of each slot group folds
+    // the group's slots, writes its totals to `publish` and zeroes them again
     unsigned long long *sums;
-    // host-visible [nframes][S] totals of this launch (pinned host memory)
+    // host-visible [nframes][S][kSumGroups] group totals of this launch (pinned host memory)
     unsigned long long *publish;
-    // workgroups of this launch that have finished, zero at launch (the last one resets it)
+    // [kSumGroups] finished workgroups of each slot group, zero at launch (each group's last
+    // workgroup resets its counter)
     unsigned int *arrivals;
     int32_t W, H, Wc, Hc;
     int32_t strips, row_tiles, tiles;

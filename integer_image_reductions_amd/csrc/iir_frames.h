@@ -1297,7 +1297,9 @@ __device__ __forceinline__ void load_saved(const KernelArgs &a, const Tile &T, i
     }
 }
 
-// The tile's own rows of the launch's last frame into the saved plane.
+// The tile's rows of the launch's last frame into the saved plane: exactly TH store
+// instructions (rows of a ragged last tile past the frame land in the plane's padding rows,
+// which nothing reads).
 template <int BPC, int TH>
 __device__ __forceinline__ void store_saved(const KernelArgs &a, const Tile &T, int s,
                                             const typename Px<BPC>::Luma (&prev)[TH + 4])
@@ -1307,9 +1309,8 @@ __device__ __forceinline__ void store_saved(const KernelArgs &a, const Tile &T, 
     uint8_t *base = reinterpret_cast<uint8_t *>(a.ring_out) + (size_t)(s + kLumaCols * T.lane) * B;
 #pragma unroll
     for (int i = 0; i < TH; ++i)
-        if (i < T.rows_valid)
-            *reinterpret_cast<typename Px<BPC>::Luma *>(base + (size_t)(T.r0 + i) * pitch) =
-                prev[i + 2];
+        *reinterpret_cast<typename Px<BPC>::Luma *>(base + (size_t)(T.r0 + i) * pitch) =
+            prev[i + 2];
 }
 
 // Each workgroup adds its per-frame sums into slot blockIdx mod kSumSlots, so a slot takes the
@@ -1317,25 +1318,52 @@ __device__ __forceinline__ void store_saved(const KernelArgs &a, const Tile &T, 
 // when the workgroups finish their last frames, queue on the same few addresses (8 slots cost
 // ~20 us more per 4K launch than 64). The slots form kSumGroups groups by blockIdx mod 8; the last
 // workgroup of a group to finish (one device-scope counter per group) folds its group's slots of
-// every sum of every frame, writes the group totals straight to the caller-visible pinned buffer
-// [frame][sum][group] and zeroes the slots and its counter for the next launch; the host adds
-// the group totals. No workgroup waits for another, and no readback copy follows the kernel.
-// Ordering: the sum atomics are device-scope read-modify-writes; each workgroup waits until its
-// own have completed (vmcnt(0)) before counting itself, and the last one reads them back with
-// device-scope atomic loads after an acquire fence. A release fence per workgroup would write
-// back every XCD's L2 once per workgroup, which costs far more than the copy it replaces.
-template <int NS>
-__device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane)
+// every sum of every frame and writes the group totals straight to the caller-visible pinned
+// buffer [frame][sum][group]; the host adds the group totals. No workgroup waits for another,
+// and no readback copy follows the kernel. Launches alternate between two slot buffers; each
+// launch's workgroups clear the other one (the previous launch's) with plain stores as they
+// start, so the fold does not zero anything. Ordering: the sum atomics are device-scope
+// read-modify-writes; each workgroup waits until its own have completed (vmcnt(0)) before
+// counting itself, and the last one reads them back with device-scope atomic loads after an
+// acquire fence. A release fence per workgroup would write back every XCD's L2 once per
+// workgroup, which costs far more than the copy it replaces.
+
+// Clear this workgroup's share of the previous launch's slot buffer.
+__device__ __forceinline__ void clear_idle_slots(const KernelArgs &a, int lane)
 {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this workgroup's sum atomics completed
+    const int64_t step = (int64_t)gridDim.x * kWave;
+    for (int64_t i = (int64_t)blockIdx.x * kWave + lane; i < a.zero_n; i += step)
+        a.zero[i] = 0ull;
+}
+
+// s_waitcnt immediate for vmcnt(n), 0 <= n < 64 (low four bits, then bits 15:14)
+constexpr int vmcnt_imm(int n)
+{
+    return 0x0F70 | (n & 15) | ((n >> 4) << 14);
+}
+
+// Count this workgroup as finished in its slot group, once its sum atomics have completed: they
+// precede the YOUNGER vector memory instructions the caller issued last (its state stores),
+// which may still be in flight, so the stores drain while the count makes its round trip.
+template <int YOUNGER>
+__device__ __forceinline__ unsigned int count_arrival(const KernelArgs &a, int lane)
+{
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(YOUNGER));  // the sum atomics have completed
+    unsigned int arrived = 0;
+    if (lane == 0)
+        arrived = __hip_atomic_fetch_add(a.arrivals + blockIdx.x % kSumGroups, 1u,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return arrived;
+}
+
+template <int NS>
+__device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane,
+                                                unsigned int arrived_lane0)
+{
     constexpr int kPerGroup = kSumSlots / kSumGroups;  // slots g, g + 8, ..., g + 56
     const unsigned int g = blockIdx.x % kSumGroups;
     const unsigned int members = gridDim.x / kSumGroups + (g < gridDim.x % kSumGroups ? 1u : 0u);
-    unsigned int arrived = 0;
-    if (lane == 0)
-        arrived = __hip_atomic_fetch_add(a.arrivals + g, 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    arrived = (unsigned int)uni((int)arrived);
+    const unsigned int arrived = (unsigned int)uni((int)arrived_lane0);
     if (arrived != members - 1u)
         return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -1359,11 +1387,8 @@ __device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane)
             if (i < n) {
                 unsigned long long total = 0;
 #pragma unroll
-                for (int j = 0; j < kPerGroup; ++j) {
+                for (int j = 0; j < kPerGroup; ++j)
                     total += v[q][j];
-                    __hip_atomic_store(a.sums + (size_t)i * kSumSlots + g + kSumGroups * j, 0ull,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
                 __hip_atomic_store(a.publish + (size_t)i * kSumGroups + g, total,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             }
@@ -1383,6 +1408,8 @@ frames_kernel(const KernelArgs a)
     static_assert(!STAGED || BPC == 8, "LDS staging is laid out for 8-bit samples");
     constexpr int B = Px<BPC>::kBytes;
     const int lane = threadIdx.x;
+
+    clear_idle_slots(a, lane);
 
     Tile T;
     const int L = uni(xcd_linear(blockIdx.x, gridDim.x));
@@ -1542,9 +1569,15 @@ frames_kernel(const KernelArgs a)
                 prev[k] = typename Px<BPC>::Luma{};
         }
         frame_loop_v2<BPC, TH, GENERIC, STAGED, MOM>(a, T, O, prev, pxprev, have_prev, stage);
-        publish_if_last<MOM ? kMaxSums : kSums>(a, lane);
-        if (T.chunk == a.chunks - 1)
+        // the state stores drain while the group count is in flight
+        unsigned int arrived;
+        if (T.chunk == a.chunks - 1) {
             store_saved<BPC, TH>(a, T, s, prev);
+            arrived = count_arrival<TH>(a, lane);
+        } else {
+            arrived = count_arrival<0>(a, lane);
+        }
+        publish_if_last<MOM ? kMaxSums : kSums>(a, lane, arrived);
     } else {
         // previous blurred tile: from the launch before, else none (chunk 0), or re-blurred by
         // the chunk's prologue (later chunks)
@@ -1571,15 +1604,18 @@ frames_kernel(const KernelArgs a)
         frame_loop<BPC, TH, GENERIC, STAGED, MOM>(a, T, O, prev0, prev1, sum_prev, have_prev,
                                                   stage);
 
-        // counted before the state write, so the count waits only for this workgroup's atomics
-        publish_if_last<MOM ? kMaxSums : kSums>(a, lane);
-
+        // the state stores (TH instructions) drain while the group count is in flight
+        unsigned int arrived;
         if (T.chunk == a.chunks - 1) {
             uint2 *rout = reinterpret_cast<uint2 *>(a.ring_out);
 #pragma unroll
             for (int i = 0; i < TH; ++i)
                 rout[(T.tile * TH + i) * kWave + lane] = make_uint2(prev0[i], prev1[i]);
+            arrived = count_arrival<TH>(a, lane);
+        } else {
+            arrived = count_arrival<0>(a, lane);
         }
+        publish_if_last<MOM ? kMaxSums : kSums>(a, lane, arrived);
     }
 }
 

@@ -92,7 +92,11 @@ struct iir_ctx {
     // ring[ring_cur] holds the blurred state of the last submitted frame (motion v2: its
     // reference luma, as a plane of strips * 256 samples per row, which fits the same bytes)
     int ring_cur = 0;
-    unsigned long long *sums = nullptr;       // device, [max_batch][nsums][kSumSlots], zero
+    // device, two slot buffers of [max_batch][nsums][kSumSlots] u64 that launches alternate
+    // between; the one a launch uses is zero (the launch before cleared it)
+    unsigned long long *sums = nullptr;
+    int sums_cur = 0;         // the buffer the next launch uses
+    int64_t sums_dirty = 0;   // words of the other buffer the last launch left non-zero
                                               // between launches (each launch re-zeroes it)
     unsigned int *arrivals = nullptr;         // device, [kSumGroups] finished-workgroup counters, zero
     int64_t sums_n = 0;
@@ -355,7 +359,9 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     }
     a.ring_in = c->ring[c->ring_cur];
     a.ring_out = c->ring[c->ring_cur ^ 1];
-    a.sums = c->sums;
+    a.sums = c->sums + (size_t)c->sums_cur * c->sums_n;
+    a.zero = c->sums + (size_t)(c->sums_cur ^ 1) * c->sums_n;
+    a.zero_n = c->sums_dirty;
     a.publish = c->host_sums_dev + (size_t)first * c->nsums * kSumGroups;
     a.arrivals = c->arrivals;
     a.W = c->cfg.width;
@@ -387,6 +393,8 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     sub.has_prev = c->has_prev;
     sub.groups = std::min(a.tiles * a.chunks, kSumGroups);
     c->sub_count++;
+    c->sums_dirty = (int64_t)n * c->nsums * kSumSlots;  // left in a.sums for the next launch
+    c->sums_cur ^= 1;
     c->slot_head = first + n;
     c->pending += n;
     c->ring_cur ^= 1;
@@ -452,7 +460,7 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     for (int i = 0; i < 2 && e == hipSuccess; ++i)
         e = hipMalloc(&c->ring[i], ring_bytes);
     if (e == hipSuccess)
-        e = hipMalloc(&c->sums, sizeof(unsigned long long) * c->sums_n);
+        e = hipMalloc(&c->sums, sizeof(unsigned long long) * 2 * c->sums_n);
     if (e == hipSuccess)
         e = hipMalloc(&c->arrivals, sizeof(unsigned int) * kSumGroups);
     if (e == hipSuccess)
@@ -478,7 +486,7 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
             e = hipEventCreate(&sub.k1);
     }
     if (e == hipSuccess)
-        e = hipMemsetAsync(c->sums, 0, sizeof(unsigned long long) * c->sums_n, c->stream);
+        e = hipMemsetAsync(c->sums, 0, sizeof(unsigned long long) * 2 * c->sums_n, c->stream);
     if (e == hipSuccess)
         e = hipMemsetAsync(c->arrivals, 0, sizeof(unsigned int) * kSumGroups, c->stream);
     for (int i = 0; i < 2 && e == hipSuccess; ++i)

@@ -39,8 +39,11 @@ struct KernelArgs {
     uint32_t *ring_out;
     // per-frame partial sums [nframes][S][kSumSlots], S = kSums, or kMaxSums when the launch
     // also sums the luma moments; zero at launch; the last workgroup of each slot group folds
-    // the group's slots, writes its totals to `publish` and zeroes them again
+    // the group's slots and writes its totals to `publish`
     unsigned long long *sums;
+    // the other slot buffer (the previous launch's), whose first zero_n words the launch clears
+    unsigned long long *zero;
+    int64_t zero_n;
     // host-visible [nframes][S][kSumGroups] group totals of this launch (pinned host memory)
     unsigned long long *publish;
     // [kSumGroups] finished workgroups of each slot group, zero at launch (each group's last

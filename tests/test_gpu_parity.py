@@ -258,3 +258,24 @@ def test_bit_depth_invariance_4k():
     if not (os.path.exists(p8) and os.path.exists(p10)):
         pytest.skip("needs test_workload_full[c3] and [c4] in the same run")
     assert np.array_equal(np.load(p8), np.load(p10))
+
+
+@pytest.mark.parametrize("moments", [False, True])
+def test_varying_batches_reuse_slots(moments):
+    """Consecutive submissions of different lengths on one context: each launch accumulates into
+    the slot buffer the launch before cleared, so a clearing that missed rows would leak partial
+    sums into later results. Every frame still equals the oracle."""
+    w, h = 520, 70
+    clip = synth.random_clip(w, h, 8, 40, seed=515, kind="uniform")
+    ref, dist = _dev(clip)
+    want, want_hm = _oracle(clip)
+    _say("varying batches", moments)
+    got, got_hm = [], []
+    with iir.Context(w, h, 8, max_batch=40, moments=moments) as ctx:
+        t = 0
+        for n in (7, 2, 13, 1, 9, 3, 5):
+            sums, hm = ctx.run_clip(tuple(p[t:t + n] for p in ref), tuple(p[t:t + n] for p in dist))
+            got.append(sums[:, :4])
+            got_hm.append(hm)
+            t += n
+    _check(clip, np.concatenate(got), np.concatenate(got_hm), want, want_hm, "varying batches")

@@ -56,7 +56,9 @@ enum {
 #define IIR_CHROMA_420 420
 
 /* iir_config.flags */
-#define IIR_FLAG_TIMING 1u /* record HIP events around each main kernel launch (iir_kernel_time) */
+/* time each main kernel with HIP events attached to its dispatch (its own start and end; see
+   iir_kernel_time) */
+#define IIR_FLAG_TIMING 1u
 /*
  * Also sum the luma moments of every frame pair in the same pass (iir_result.moment): the sums
  * and sums of squares of the reference and distorted luma, the four accumulators of the moment
@@ -228,9 +230,9 @@ IIR_API int iir_reset(iir_ctx *ctx);
 IIR_API int iir_export_blur(iir_ctx *ctx, void *dst, int64_t pitch);
 
 /*
- * Duration in milliseconds of the main kernel of the most recently collected submission, from HIP
- * events recorded around the launch on the context's stream. Needs IIR_FLAG_TIMING; IIR_ESTATE
- * until a timed submission has been collected.
+ * Duration in milliseconds of the main kernel of the most recently collected submission, from the
+ * HIP start and stop events attached to its dispatch (hipExtLaunchKernelGGL) on the context's
+ * stream. Needs IIR_FLAG_TIMING; IIR_ESTATE until a timed submission has been collected.
  */
 IIR_API int iir_kernel_time(iir_ctx *ctx, float *ms);
 

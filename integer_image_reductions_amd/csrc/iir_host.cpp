@@ -379,14 +379,14 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
 
     const bool timing = (c->cfg.flags & IIR_FLAG_TIMING) != 0;
     iir_ctx::Sub &sub = c->subs[(c->sub_head + c->sub_count) % iir_ctx::kMaxPending];
-    if (timing)
-        HIP_TRY(hipEventRecord(sub.k0, c->stream));
+    // the kernel itself writes the totals to host_sums; one event marks the end: with timing,
+    // the launch's own start and end events (no separate marker packets), else one marker
     HIP_TRY(launch_frames(c->cfg.bpc, c->rows_per_tile,
                           !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile),
-                          c->moments, c->v2, a, c->stream));
-    // the kernel itself writes the totals to host_sums; one event marks the end (with timing,
-    // the event that closes the kernel's timed interval)
-    HIP_TRY(hipEventRecord(timing ? sub.k1 : sub.done, c->stream));
+                          c->moments, c->v2, a, c->stream, timing ? sub.k0 : nullptr,
+                          timing ? sub.k1 : nullptr));
+    if (!timing)
+        HIP_TRY(hipEventRecord(sub.done, c->stream));
     sub.first = first;
     sub.n = n;
     sub.taken = 0;

@@ -74,8 +74,10 @@ bool fast_path_ok(int W, int H, int th);         // the uniform fast path applie
 // luma as a plane of strips * 256 samples per row instead of the tiled blurred state
 hipError_t frames_occupancy(int bpc, int th, bool generic, bool moments, bool v2,
                             int *waves_per_cu);
+// start / stop (both or neither): events the launch records as the kernel's own start and end
 hipError_t launch_frames(int bpc, int th, bool generic, bool moments, bool v2,
-                         const KernelArgs &a, hipStream_t stream);
+                         const KernelArgs &a, hipStream_t stream, hipEvent_t start = nullptr,
+                         hipEvent_t stop = nullptr);
 hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
                          int strips, int th, hipStream_t stream);
 hipError_t launch_probe(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream);

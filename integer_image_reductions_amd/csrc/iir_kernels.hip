@@ -1,6 +1,8 @@
 // iir_kernels.hip -- launchers of the gfx950 kernels (the frames kernel itself is in
 // iir_frames.h, instantiated by the iir_frames_*.hip units), the blurred-plane export and the
 // memory-ceiling probes.
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 #include "iir_internal.h"
@@ -109,12 +111,17 @@ hipError_t frames_occupancy(int bpc, int th, bool generic, bool moments, bool v2
 }
 
 hipError_t launch_frames(int bpc, int th, bool generic, bool moments, bool v2,
-                         const KernelArgs &a, hipStream_t stream)
+                         const KernelArgs &a, hipStream_t stream, hipEvent_t start,
+                         hipEvent_t stop)
 {
     FramesFn f = pick(bpc, th, generic, moments, v2);
     if (!f)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(f, dim3((unsigned)(a.tiles * a.chunks)), dim3(kWave), 0, stream, a);
+    const dim3 grid((unsigned)(a.tiles * a.chunks)), block(kWave);
+    if (start && stop)  // the events are the dispatch's own start and end timestamps
+        hipExtLaunchKernelGGL(f, grid, block, 0, stream, start, stop, 0, a);
+    else
+        hipLaunchKernelGGL(f, grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

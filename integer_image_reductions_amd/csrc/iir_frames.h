@@ -865,36 +865,32 @@ __device__ __forceinline__ void neighbours(const Tile &T, uint32_t hl, uint32_t 
 // Motion v2: the separable filter applied to the difference prev - cur of consecutive reference
 // luma frames ("ADR-1392", Decision 4: the kernel stages prev - cur, runs the vertical pass once,
 // rounded by the bit depth, then the five horizontal taps shifted by 16). Shifts of negative
-// sums floor. The vertical value V of a difference needs 17 bits, so it travels split into its
-// high part Vh = floor(V / 256) (a signed 16-bit lane) and its low byte Vl = V mod 256; the
-// horizontal sum, 33 bits wide ("ADR-1392", the alternative of 32-bit horizontal sums), is then
-// the exact combination of two 32-bit sums A = sum g Vh and B = sum g Vl:
+// sums floor. The kernel works on the biased difference d' = d + 2^bpc, which is positive, so
+// every product is an unsigned 16-bit dot product: the taps sum to 2^16, so the vertical value
+// of d' is exactly V' = V + 2^16 (the bias is a multiple of the shift). V' needs 17 bits, so it
+// travels split into its high part Vh' = floor(V' / 256) = floor(V / 256) + 256 and its low byte
+// Vl = V mod 256; the horizontal sum, 33 bits wide ("ADR-1392", the alternative of 32-bit
+// horizontal sums), is then the exact combination of two 32-bit sums A' = sum g Vh' = A + 2^24
+// (A = sum g floor(V / 256)) and B = sum g Vl:
 //   floor((256 A + B + 2^15) / 2^16) = floor((A + floor((B + 2^15) / 2^8)) / 2^8).
 
-// signed 16-bit pair dot product, accumulated in 32 bits
-__device__ __forceinline__ int32_t dot2s(uint32_t a, uint32_t b, int32_t c)
-{
-    return __builtin_amdgcn_sdot2(__builtin_bit_cast(i16x2, a), __builtin_bit_cast(i16x2, b), c,
-                                  false);
-}
-
-// a - b of both 16-bit halves (each difference fits a signed 16-bit lane)
-__device__ __forceinline__ uint32_t sub16x2(uint32_t a, uint32_t b)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, a) - __builtin_bit_cast(i16x2, b));
-}
-
-// prev - cur of one row's 4 samples as two signed 16-bit pairs: columns (c, c+1), (c+2, c+3)
+// prev - cur + 2^bpc of one row's 4 samples as two 16-bit pairs: columns (c, c+1), (c+2, c+3).
+// Each half lies in [1, 2^(bpc+1) - 1], so whole-dword arithmetic never carries between halves.
 template <int BPC>
 __device__ __forceinline__ u32x2 diff_row(typename Px<BPC>::Luma p, typename Px<BPC>::Luma r)
 {
     if constexpr (BPC == 8) {
-        return u32x2{sub16x2(perm(0u, p, 0x0c010c00u), perm(0u, r, 0x0c010c00u)),
-                     sub16x2(perm(0u, p, 0x0c030c02u), perm(0u, r, 0x0c030c02u))};
+        // bytes of prev widened to 16 bits with 0x01 as the high byte: prev + 256
+        return u32x2{perm(0x01010101u, p, 0x04010400u) - perm(0u, r, 0x0c010c00u),
+                     perm(0x01010101u, p, 0x04030402u) - perm(0u, r, 0x0c030c02u)};
     } else {
-        return u32x2{sub16x2(p.x, r.x), sub16x2(p.y, r.y)};
+        return u32x2{(p.x | 0x04000400u) - r.x, (p.y | 0x04000400u) - r.y};
     }
 }
+
+// the bias of diff_row in both halves
+template <int BPC>
+constexpr uint32_t kV2DiffBias = BPC == 8 ? 0x01000100u : 0x04000400u;
 
 // (row a, row b) pairs of the 4 columns of two difference rows
 __device__ __forceinline__ void diff_pairs(u32x2 da, u32x2 db, uint32_t p[4])
@@ -907,47 +903,56 @@ __device__ __forceinline__ void diff_pairs(u32x2 da, u32x2 db, uint32_t p[4])
 
 // rounding term of the vertical pass, 2^(bpc - 1)
 template <int BPC>
-constexpr int32_t kV2Round = BPC == 8 ? 128 : 512;
+constexpr uint32_t kV2Round = BPC == 8 ? 128u : 512u;
 
-// Two columns' vertical sums (rounding term included) -> packed (Vh, Vh') and (Vl, Vl'). 8-bit:
-// V = s >> 8, so Vh is bits 16-31 of s and Vl bits 8-15; 10-bit: V = s >> 10 first.
+// Two columns' vertical sums of biased differences (rounding term included) -> packed
+// (Vh', Vh'') and (Vl, Vl'). 8-bit: V' = s >> 8, so Vh' is bits 16-31 of s and Vl bits 8-15;
+// 10-bit: V' = s >> 10 first.
 template <int BPC>
-__device__ __forceinline__ void split_pack(int32_t s0, int32_t s1, uint32_t &h, uint32_t &l)
+__device__ __forceinline__ void split_pack(uint32_t s0, uint32_t s1, uint32_t &h, uint32_t &l)
 {
     if constexpr (BPC == 8) {
-        h = perm((uint32_t)s1, (uint32_t)s0, 0x07060302u);
-        l = perm((uint32_t)s1, (uint32_t)s0, 0x0c050c01u);
+        h = perm(s1, s0, 0x07060302u);
+        l = perm(s1, s0, 0x0c050c01u);
     } else {
-        const uint32_t v0 = (uint32_t)(s0 >> 10), v1 = (uint32_t)(s1 >> 10);
+        const uint32_t v0 = s0 >> 10, v1 = s1 >> 10;
         h = perm(v1, v0, 0x06050201u);
         l = perm(v1, v0, 0x0c040c00u);
     }
 }
 
-// Vertical pass of the transposed halo's differences (lane k: the two halo columns of tile row
-// k - 2 as a signed pair), split as above; lane i + 2 (left) and i + 34 (right) serve row i.
+// Vertical pass of the transposed halo's biased differences (lane k: the two halo columns of
+// tile row k - 2 as a pair), split as above; lane i + 2 (left) and i + 34 (right) serve row i.
 template <int BPC>
 __device__ __forceinline__ void halo_vertical_v2(uint32_t dh, uint32_t &hvh, uint32_t &hvl)
 {
     const uint32_t m1 = from_left(dh), m2 = from_left(m1);    // rows k-1, k-2
     const uint32_t p1 = from_right(dh), p2 = from_right(p1);  // rows k+1, k+2
-    const int32_t sa = dot2s(p2 & 0xffffu, T0z,
-                             dot2s(perm(p1, dh, 0x05040100u), T21,
-                                   dot2s(perm(m1, m2, 0x05040100u), T01, kV2Round<BPC>)));
-    const int32_t sb = dot2s(p2 >> 16, T0z,
-                             dot2s(perm(p1, dh, 0x07060302u), T21,
-                                   dot2s(perm(m1, m2, 0x07060302u), T01, kV2Round<BPC>)));
+    const uint32_t sa = dot2u(p2, T0z,
+                              dot2u(perm(p1, dh, 0x05040100u), T21,
+                                    dot2u(perm(m1, m2, 0x05040100u), T01, kV2Round<BPC>)));
+    const uint32_t sb = dot2u(p2 >> 16, T0z,
+                              dot2u(perm(p1, dh, 0x07060302u), T21,
+                                    dot2u(perm(m1, m2, 0x07060302u), T01, kV2Round<BPC>)));
     split_pack<BPC>(sa, sb, hvh, hvl);
 }
 
-// |F| of one output from its biased high sum (A + 2^25) and its low sum (B + 2^15): the biased
-// result F + 2^17 is non-negative, so the shifts are logical, and |F| = |(F + 2^17) - 2^17|.
-constexpr int32_t kV2Bias = 1 << 25;
+// F + 2^17 of one output from its high sum A' (started at 2^24, so it holds A + 2^25) and its
+// low sum B + 2^15: the biased result is non-negative, so the shifts are logical, and
+// |F| = |(F + 2^17) - 2^17|.
+constexpr uint32_t kV2Bias = 1u << 24;
 constexpr uint32_t kV2Zero = 1u << 17;
-__device__ __forceinline__ uint32_t abs_f(int32_t a_biased, uint32_t b)
+__device__ __forceinline__ uint32_t biased_f(uint32_t a_biased, uint32_t b)
 {
-    const uint32_t fk = (uint32_t)(a_biased + (int32_t)(b >> 8)) >> 8;
-    return fk > kV2Zero ? fk - kV2Zero : kV2Zero - fk;
+    return (a_biased + (b >> 8)) >> 8;
+}
+
+// acc + |x - y| in one instruction (v_sad_u32)
+__device__ __forceinline__ uint32_t add_absdiff(uint32_t x, uint32_t y, uint32_t acc)
+{
+    uint32_t d;
+    asm("v_sad_u32 %0, %1, %2, %3" : "=v"(d) : "v"(x), "v"(y), "v"(acc));
+    return d;
 }
 
 // One frame of one tile from its loaded samples: blur the reference luma (vertical pass once per
@@ -1052,7 +1057,7 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
         uint32_t sad = 0;
         if (have_prev) {
             uint32_t hvh, hvl;
-            halo_vertical_v2<BPC>(sub16x2(pxin, x0), hvh, hvl);
+            halo_vertical_v2<BPC>((pxin + kV2DiffBias<BPC>) - x0, hvh, hvl);
             const u32x2 zero{};
 #pragma unroll
             for (int i = 0; i < TH; ++i) {
@@ -1064,10 +1069,10 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
                 diff_pairs(diff_row<BPC>(pin[i + 4], F.R[i + 4]),
                            i + 5 < TH + 4 ? diff_row<BPC>(pin[i + 5], F.R[i + 5]) : zero,
                            pc);  // rows i+2 (tap 0 on i+3)
-                int32_t v[4];
+                uint32_t v[4];
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    v[b] = dot2s(pc[b], T0z, dot2s(pb[b], T21, dot2s(pa[b], T01, kV2Round<BPC>)));
+                    v[b] = dot2u(pc[b], T0z, dot2u(pb[b], T21, dot2u(pa[b], T01, kV2Round<BPC>)));
                 uint32_t q0h, q0l, q1h, q1l;
                 split_pack<BPC>(v[0], v[1], q0h, q0l);  // columns c, c+1
                 split_pack<BPC>(v[2], v[3], q1h, q1l);  // columns c+2, c+3
@@ -1078,21 +1083,27 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
                 uint32_t qlh, qrh, qll, qrl;
                 neighbours<GENERIC, ROWSTAGE>(T, hlh, hrh, q0h, q1h, qlh, qrh);
                 neighbours<GENERIC, ROWSTAGE>(T, hll, hrl, q0l, q1l, qll, qrl);
-                uint32_t f[4];
-                f[0] = abs_f(dot2s(q1h, T0z, dot2s(q0h, T21, dot2s(qlh, T01, kV2Bias))),
+                uint32_t f[4];  // F + 2^17 of columns c .. c+3
+                f[0] = biased_f(dot2u(q1h, T0z, dot2u(q0h, T21, dot2u(qlh, T01, kV2Bias))),
                              dot2u(q1l, T0z, dot2u(q0l, T21, dot2u(qll, T01, 32768u))));
-                f[1] = abs_f(dot2s(q1h, T10, dot2s(q0h, T12, dot2s(qlh, Tz0, kV2Bias))),
+                f[1] = biased_f(dot2u(q1h, T10, dot2u(q0h, T12, dot2u(qlh, Tz0, kV2Bias))),
                              dot2u(q1l, T10, dot2u(q0l, T12, dot2u(qll, Tz0, 32768u))));
-                f[2] = abs_f(dot2s(qrh, T0z, dot2s(q1h, T21, dot2s(q0h, T01, kV2Bias))),
+                f[2] = biased_f(dot2u(qrh, T0z, dot2u(q1h, T21, dot2u(q0h, T01, kV2Bias))),
                              dot2u(qrl, T0z, dot2u(q1l, T21, dot2u(q0l, T01, 32768u))));
-                f[3] = abs_f(dot2s(qrh, T10, dot2s(q1h, T12, dot2s(q0h, Tz0, kV2Bias))),
+                f[3] = biased_f(dot2u(qrh, T10, dot2u(q1h, T12, dot2u(q0h, Tz0, kV2Bias))),
                              dot2u(qrl, T10, dot2u(q1l, T12, dot2u(q0l, Tz0, 32768u))));
                 if constexpr (GENERIC) {
-                    if (i < T.rows_valid)
-                        sad += ((T.w0 & 1u) ? f[0] : 0u) + ((T.w0 >> 16) ? f[1] : 0u) +
-                               ((T.w1 & 1u) ? f[2] : 0u) + ((T.w1 >> 16) ? f[3] : 0u);
+                    // a column outside the frame counts as F = 0
+                    if (i < T.rows_valid) {
+                        sad = add_absdiff((T.w0 & 1u) ? f[0] : kV2Zero, kV2Zero, sad);
+                        sad = add_absdiff((T.w0 >> 16) ? f[1] : kV2Zero, kV2Zero, sad);
+                        sad = add_absdiff((T.w1 & 1u) ? f[2] : kV2Zero, kV2Zero, sad);
+                        sad = add_absdiff((T.w1 >> 16) ? f[3] : kV2Zero, kV2Zero, sad);
+                    }
                 } else {
-                    sad += (f[0] + f[1]) + (f[2] + f[3]);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        sad = add_absdiff(f[b], kV2Zero, sad);
                 }
                 if (!GENERIC || i < T.rows_valid)
                     luma_row_stats<BPC, TH, GENERIC, MOM>(T, F, i, S);

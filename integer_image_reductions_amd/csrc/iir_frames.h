@@ -867,12 +867,11 @@ __device__ __forceinline__ void neighbours(const Tile &T, uint32_t hl, uint32_t 
 // rounded by the bit depth, then the five horizontal taps shifted by 16). Shifts of negative
 // sums floor. The kernel works on the biased difference d' = d + 2^bpc, which is positive, so
 // every product is an unsigned 16-bit dot product: the taps sum to 2^16, so the vertical value
-// of d' is exactly V' = V + 2^16 (the bias is a multiple of the shift). V' needs 17 bits, so it
-// travels split into its high part Vh' = floor(V' / 256) = floor(V / 256) + 256 and its low byte
-// Vl = V mod 256; the horizontal sum, 33 bits wide ("ADR-1392", the alternative of 32-bit
-// horizontal sums), is then the exact combination of two 32-bit sums A' = sum g Vh' = A + 2^24
-// (A = sum g floor(V / 256)) and B = sum g Vl:
-//   floor((256 A + B + 2^15) / 2^16) = floor((A + floor((B + 2^15) / 2^8)) / 2^8).
+// of d' is exactly V' = V + 2^16 (the bias is a multiple of the shift), in [0, 2^17). V' travels
+// split into its top bit Vb = floor(V' / 2^16) and its low half Vlo = V' mod 2^16. The horizontal
+// sum S' = sum g V' = S + 2^32 is 33 bits wide ("ADR-1392", the alternative of 32-bit horizontal
+// sums), so it is taken as two 32-bit sums Q = sum g Vb and L = sum g Vlo + 2^15 (below 2^32):
+//   F + 2^16 = floor((S' + 2^15) / 2^16) = Q + floor(L / 2^16).
 
 // prev - cur + 2^bpc of one row's 4 samples as two 16-bit pairs: columns (c, c+1), (c+2, c+3).
 // Each half lies in [1, 2^(bpc+1) - 1], so whole-dword arithmetic never carries between halves.
@@ -905,19 +904,19 @@ __device__ __forceinline__ void diff_pairs(u32x2 da, u32x2 db, uint32_t p[4])
 template <int BPC>
 constexpr uint32_t kV2Round = BPC == 8 ? 128u : 512u;
 
-// Two columns' vertical sums of biased differences (rounding term included) -> packed
-// (Vh', Vh'') and (Vl, Vl'). 8-bit: V' = s >> 8, so Vh' is bits 16-31 of s and Vl bits 8-15;
-// 10-bit: V' = s >> 10 first.
+// Two columns' vertical sums of biased differences (rounding term included) -> packed top bits
+// (Vb, Vb') and low halves (Vlo, Vlo'). 8-bit: V' = s >> 8 < 2^17, so Vlo is bits 8-23 of s and
+// Vb its byte 3; 10-bit: V' = s >> 10 first.
 template <int BPC>
 __device__ __forceinline__ void split_pack(uint32_t s0, uint32_t s1, uint32_t &h, uint32_t &l)
 {
     if constexpr (BPC == 8) {
-        h = perm(s1, s0, 0x07060302u);
-        l = perm(s1, s0, 0x0c050c01u);
+        h = perm(s1, s0, 0x0c070c03u);
+        l = perm(s1, s0, 0x06050201u);
     } else {
         const uint32_t v0 = s0 >> 10, v1 = s1 >> 10;
-        h = perm(v1, v0, 0x06050201u);
-        l = perm(v1, v0, 0x0c040c00u);
+        h = perm(v1, v0, 0x0c060c02u);
+        l = perm(v1, v0, 0x05040100u);
     }
 }
 
@@ -937,14 +936,14 @@ __device__ __forceinline__ void halo_vertical_v2(uint32_t dh, uint32_t &hvh, uin
     split_pack<BPC>(sa, sb, hvh, hvl);
 }
 
-// F + 2^17 of one output from its high sum A' (started at 2^24, so it holds A + 2^25) and its
-// low sum B + 2^15: the biased result is non-negative, so the shifts are logical, and
-// |F| = |(F + 2^17) - 2^17|.
-constexpr uint32_t kV2Bias = 1u << 24;
-constexpr uint32_t kV2Zero = 1u << 17;
-__device__ __forceinline__ uint32_t biased_f(uint32_t a_biased, uint32_t b)
+// F + 2^16 = Q + floor(L / 2^16) of one output in one instruction: v_mad_u32_u16 multiplies the
+// high half of L (op_sel) by 1 and adds Q. |F| = |(F + 2^16) - 2^16|.
+constexpr uint32_t kV2Zero = 1u << 16;
+__device__ __forceinline__ uint32_t biased_f(uint32_t q, uint32_t l)
 {
-    return (a_biased + (b >> 8)) >> 8;
+    uint32_t d;
+    asm("v_mad_u32_u16 %0, %1, 1, %2 op_sel:[1,0,0,0]" : "=v"(d) : "v"(l), "v"(q));
+    return d;
 }
 
 // acc + |x - y| in one instruction (v_sad_u32)
@@ -1083,15 +1082,15 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
                 uint32_t qlh, qrh, qll, qrl;
                 neighbours<GENERIC, ROWSTAGE>(T, hlh, hrh, q0h, q1h, qlh, qrh);
                 neighbours<GENERIC, ROWSTAGE>(T, hll, hrl, q0l, q1l, qll, qrl);
-                uint32_t f[4];  // F + 2^17 of columns c .. c+3
-                f[0] = biased_f(dot2u(q1h, T0z, dot2u(q0h, T21, dot2u(qlh, T01, kV2Bias))),
-                             dot2u(q1l, T0z, dot2u(q0l, T21, dot2u(qll, T01, 32768u))));
-                f[1] = biased_f(dot2u(q1h, T10, dot2u(q0h, T12, dot2u(qlh, Tz0, kV2Bias))),
-                             dot2u(q1l, T10, dot2u(q0l, T12, dot2u(qll, Tz0, 32768u))));
-                f[2] = biased_f(dot2u(qrh, T0z, dot2u(q1h, T21, dot2u(q0h, T01, kV2Bias))),
-                             dot2u(qrl, T0z, dot2u(q1l, T21, dot2u(q0l, T01, 32768u))));
-                f[3] = biased_f(dot2u(qrh, T10, dot2u(q1h, T12, dot2u(q0h, Tz0, kV2Bias))),
-                             dot2u(qrl, T10, dot2u(q1l, T12, dot2u(q0l, Tz0, 32768u))));
+                uint32_t f[4];  // F + 2^16 of columns c .. c+3
+                f[0] = biased_f(dot2u(q1h, T0z, dot2u(q0h, T21, dot2u(qlh, T01, 0u))),
+                                dot2u(q1l, T0z, dot2u(q0l, T21, dot2u(qll, T01, 32768u))));
+                f[1] = biased_f(dot2u(q1h, T10, dot2u(q0h, T12, dot2u(qlh, Tz0, 0u))),
+                                dot2u(q1l, T10, dot2u(q0l, T12, dot2u(qll, Tz0, 32768u))));
+                f[2] = biased_f(dot2u(qrh, T0z, dot2u(q1h, T21, dot2u(q0h, T01, 0u))),
+                                dot2u(qrl, T0z, dot2u(q1l, T21, dot2u(q0l, T01, 32768u))));
+                f[3] = biased_f(dot2u(qrh, T10, dot2u(q1h, T12, dot2u(q0h, Tz0, 0u))),
+                                dot2u(qrl, T10, dot2u(q1l, T12, dot2u(q0l, Tz0, 32768u))));
                 if constexpr (GENERIC) {
                     // a column outside the frame counts as F = 0
                     if (i < T.rows_valid) {

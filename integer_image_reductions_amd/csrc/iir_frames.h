@@ -634,7 +634,7 @@ __device__ __forceinline__ void load_chroma_x4(const KernelArgs &a, const Tile &
 
 // The staged 8-bit frame's luma, from LDS into registers.
 template <int TH>
-__device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWave], int lane,
+__device__ __forceinline__ void read_stage(bool with_dist, uint32_t (*lds)[kWave], int lane,
                                            uint32_t hlds, FrameData<8, TH> &F)
 {
     typedef Stage<TH> ST;
@@ -642,7 +642,7 @@ __device__ __forceinline__ void read_stage(bool accumulate, uint32_t (*lds)[kWav
     for (int k = 0; k < TH + 4; ++k)
         F.R[k] = lds[ST::kRef + k][lane];
     F.HL = u32x2{(&lds[0][0])[hlds], 0u};
-    if (!accumulate)
+    if (!with_dist)
         return;
 #pragma unroll
     for (int i = 0; i < TH; ++i)
@@ -1018,7 +1018,8 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
         if (!GENERIC || i < T.rows_valid) {
             acc_c = dot2u(c1, T.w1, dot2u(c0, T.w0, acc_c));
             acc_min = dot2u(pkmin(c1, prev1[i]), T.w1, dot2u(pkmin(c0, prev0[i]), T.w0, acc_min));
-            if (accumulate)
+            // with moments, staged frames always hold distorted rows (staged_frame's ALL_DIST)
+            if ((ROWSTAGE && MOM) || accumulate)
                 luma_row_stats<BPC, TH, GENERIC, MOM>(T, F, i, S);
         }
         next0[i] = c0;
@@ -1134,7 +1135,9 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
 // L2 hit), so that one wait is always right and the compiler's own count for the chroma registers
 // agrees with it. The wavefront raises its priority from the wait to the last load issued, so a
 // wavefront whose data has landed refills the memory pipe ahead of its SIMD's computing waves.
-template <int TH>
+// ALL_DIST reads the distorted rows out of a frame that is not accumulated too (its stage then
+// holds stale rows), so that the luma sums can run for every frame without a branch per row.
+template <int TH, bool ALL_DIST>
 __device__ __forceinline__ void staged_frame(const KernelArgs &a, const Tile &T,
                                              const StageOffsets<TH> &O, int t, int f_begin,
                                              int f_end, uint32_t (*lds)[kWave], ChromaX4<TH> &C,
@@ -1142,7 +1145,7 @@ __device__ __forceinline__ void staged_frame(const KernelArgs &a, const Tile &T,
 {
     __builtin_amdgcn_s_setprio(3);
     __builtin_amdgcn_s_waitcnt(0x0F70 | Stage<TH>::kDmaLoads);  // vmcnt(one luma group)
-    read_stage<TH>(t >= f_begin, lds, T.lane, T.hlds, F);
+    read_stage<TH>(ALL_DIST || t >= f_begin, lds, T.lane, T.hlds, F);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
     if (t >= f_begin)
         chroma_sse_x4<TH>(T, C, S);
@@ -1199,7 +1202,8 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
         FrameData<BPC, TH> F;
         FrameStats<BPC> S;
         if constexpr (STAGED)
-            staged_frame<TH>(a, T, O, t, f_begin, f_end, lds + sidx * Stage<TH>::kRows, C, F, S);
+            staged_frame<TH, MOM>(a, T, O, t, f_begin, f_end, lds + sidx * Stage<TH>::kRows, C,
+                                  F, S);
         else
             load_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F);
         compute_frame<BPC, TH, GENERIC, STAGED, MOM>(a, T, t, t >= f_begin, F, S, i0, i1, o0,
@@ -1250,7 +1254,8 @@ __device__ __forceinline__ void frame_loop_v2(const KernelArgs &a, const Tile &T
         FrameData<BPC, TH> F;
         FrameStats<BPC> S;
         if constexpr (STAGED)
-            staged_frame<TH>(a, T, O, t, f_begin, f_end, lds + sidx * Stage<TH>::kRows, C, F, S);
+            staged_frame<TH, false>(a, T, O, t, f_begin, f_end, lds + sidx * Stage<TH>::kRows, C,
+                                    F, S);
         else
             load_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F);
         compute_frame_v2<BPC, TH, GENERIC, STAGED, MOM>(a, T, t >= f_begin, F, S, pin, pxin,

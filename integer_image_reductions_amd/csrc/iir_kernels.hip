@@ -34,33 +34,55 @@ __global__ void export_kernel(const uint32_t *ring, uint16_t *dst, int64_t pitch
 }
 
 // Memory-ceiling probes: read-only (xor-reduced, written only if a runtime flag asks), write-only,
-// copy. 16-byte accesses, grid-stride.
-__global__ __launch_bounds__(256) void probe_read(const uint4 *src, int64_t n, uint4 *sink, int keep)
+// copy. 16-byte non-temporal accesses; each thread keeps kProbeUnroll independent accesses in
+// flight per pass (grid-stride), then finishes the tail one at a time.
+constexpr int kProbeUnroll = 8;
+typedef unsigned int probe_v4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void probe_read(const probe_v4 *src, int64_t n, probe_v4 *sink,
+                                                  int keep)
 {
-    uint4 acc = make_uint4(0, 0, 0, 0);
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const uint4 v = src[i];
-        acc.x ^= v.x;
-        acc.y ^= v.y;
-        acc.z ^= v.z;
-        acc.w ^= v.w;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    probe_v4 acc = {0, 0, 0, 0};
+    for (; i + (kProbeUnroll - 1) * stride < n; i += kProbeUnroll * stride) {
+        probe_v4 v[kProbeUnroll];
+#pragma unroll
+        for (int k = 0; k < kProbeUnroll; ++k)
+            v[k] = __builtin_nontemporal_load(src + i + k * stride);
+#pragma unroll
+        for (int k = 0; k < kProbeUnroll; ++k)
+            acc ^= v[k];
     }
+    for (; i < n; i += stride)
+        acc ^= src[i];
     if (keep)
         sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
-__global__ __launch_bounds__(256) void probe_write(uint4 *dst, int64_t n)
+__global__ __launch_bounds__(256) void probe_write(probe_v4 *dst, int64_t n)
 {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
-        dst[i] = make_uint4((uint32_t)i, (uint32_t)(i >> 32), 0x9e3779b9u, 0u);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const probe_v4 v = {(uint32_t)i, (uint32_t)(i >> 32), 0x9e3779b9u, 0u};
+        __builtin_nontemporal_store(v, dst + i);
+    }
 }
 
-__global__ __launch_bounds__(256) void probe_copy(const uint4 *src, uint4 *dst, int64_t n)
+__global__ __launch_bounds__(256) void probe_copy(const probe_v4 *src, probe_v4 *dst, int64_t n)
 {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + (kProbeUnroll - 1) * stride < n; i += kProbeUnroll * stride) {
+        probe_v4 v[kProbeUnroll];
+#pragma unroll
+        for (int k = 0; k < kProbeUnroll; ++k)
+            v[k] = __builtin_nontemporal_load(src + i + k * stride);
+#pragma unroll
+        for (int k = 0; k < kProbeUnroll; ++k)
+            __builtin_nontemporal_store(v[k], dst + i + k * stride);
+    }
+    for (; i < n; i += stride)
         dst[i] = src[i];
 }
 
@@ -139,16 +161,18 @@ hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int
 hipError_t launch_probe(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream)
 {
     const int64_t n = bytes / 16;
-    const unsigned blocks = (unsigned)std::min<int64_t>(std::max<int64_t>(n / (256 * 4), 1), 256 * 16);
+    // enough threads to fill every CU several times over, each with a few full passes of work
+    const unsigned blocks =
+        (unsigned)std::min<int64_t>(std::max<int64_t>(n / (256 * kProbeUnroll * 4), 1), 256 * 16);
     if (mode == 0)
         hipLaunchKernelGGL(probe_read, dim3(blocks), dim3(256), 0, stream,
-                           static_cast<const uint4 *>(src), n, static_cast<uint4 *>(dst), 0);
+                           static_cast<const probe_v4 *>(src), n, static_cast<probe_v4 *>(dst), 0);
     else if (mode == 1)
         hipLaunchKernelGGL(probe_write, dim3(blocks), dim3(256), 0, stream,
-                           static_cast<uint4 *>(dst), n);
+                           static_cast<probe_v4 *>(dst), n);
     else
         hipLaunchKernelGGL(probe_copy, dim3(blocks), dim3(256), 0, stream,
-                           static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), n);
+                           static_cast<const probe_v4 *>(src), static_cast<probe_v4 *>(dst), n);
     return hipGetLastError();
 }
 

@@ -34,24 +34,27 @@ __global__ void export_kernel(const uint32_t *ring, uint16_t *dst, int64_t pitch
 }
 
 // Memory-ceiling probes: read-only (xor-reduced, written only if a runtime flag asks), write-only,
-// copy. 16-byte non-temporal accesses; each thread keeps kProbeUnroll independent accesses in
-// flight per pass (grid-stride), then finishes the tail one at a time.
-constexpr int kProbeUnroll = 8;
+// copy. 16-byte non-temporal accesses; each thread keeps U independent accesses in flight per
+// pass (grid-stride), then finishes the tail one at a time. The shapes (8 reads or 4 copies in
+// flight, 16384 workgroups of 256) measured fastest on MI355X among 4-16 in flight and
+// 1024-16384 workgroups.
+constexpr int kReadUnroll = 8, kCopyUnroll = 4, kProbeBlocks = 16384;
 typedef unsigned int probe_v4 __attribute__((ext_vector_type(4)));
 
+template <int U>
 __global__ __launch_bounds__(256) void probe_read(const probe_v4 *src, int64_t n, probe_v4 *sink,
                                                   int keep)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     probe_v4 acc = {0, 0, 0, 0};
-    for (; i + (kProbeUnroll - 1) * stride < n; i += kProbeUnroll * stride) {
-        probe_v4 v[kProbeUnroll];
+    for (; i + (U - 1) * stride < n; i += U * stride) {
+        probe_v4 v[U];
 #pragma unroll
-        for (int k = 0; k < kProbeUnroll; ++k)
+        for (int k = 0; k < U; ++k)
             v[k] = __builtin_nontemporal_load(src + i + k * stride);
 #pragma unroll
-        for (int k = 0; k < kProbeUnroll; ++k)
+        for (int k = 0; k < U; ++k)
             acc ^= v[k];
     }
     for (; i < n; i += stride)
@@ -69,17 +72,18 @@ __global__ __launch_bounds__(256) void probe_write(probe_v4 *dst, int64_t n)
     }
 }
 
+template <int U>
 __global__ __launch_bounds__(256) void probe_copy(const probe_v4 *src, probe_v4 *dst, int64_t n)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + (kProbeUnroll - 1) * stride < n; i += kProbeUnroll * stride) {
-        probe_v4 v[kProbeUnroll];
+    for (; i + (U - 1) * stride < n; i += U * stride) {
+        probe_v4 v[U];
 #pragma unroll
-        for (int k = 0; k < kProbeUnroll; ++k)
+        for (int k = 0; k < U; ++k)
             v[k] = __builtin_nontemporal_load(src + i + k * stride);
 #pragma unroll
-        for (int k = 0; k < kProbeUnroll; ++k)
+        for (int k = 0; k < U; ++k)
             __builtin_nontemporal_store(v[k], dst + i + k * stride);
     }
     for (; i < n; i += stride)
@@ -161,17 +165,17 @@ hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int
 hipError_t launch_probe(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream)
 {
     const int64_t n = bytes / 16;
-    // enough threads to fill every CU several times over, each with a few full passes of work
+    // up to kProbeBlocks workgroups of 256, fewer for a small buffer
     const unsigned blocks =
-        (unsigned)std::min<int64_t>(std::max<int64_t>(n / (256 * kProbeUnroll * 4), 1), 256 * 16);
+        (unsigned)std::min<int64_t>(std::max<int64_t>(n / (256 * 8), 1), kProbeBlocks);
     if (mode == 0)
-        hipLaunchKernelGGL(probe_read, dim3(blocks), dim3(256), 0, stream,
+        hipLaunchKernelGGL(probe_read<kReadUnroll>, dim3(blocks), dim3(256), 0, stream,
                            static_cast<const probe_v4 *>(src), n, static_cast<probe_v4 *>(dst), 0);
     else if (mode == 1)
         hipLaunchKernelGGL(probe_write, dim3(blocks), dim3(256), 0, stream,
                            static_cast<probe_v4 *>(dst), n);
     else
-        hipLaunchKernelGGL(probe_copy, dim3(blocks), dim3(256), 0, stream,
+        hipLaunchKernelGGL(probe_copy<kCopyUnroll>, dim3(blocks), dim3(256), 0, stream,
                            static_cast<const probe_v4 *>(src), static_cast<probe_v4 *>(dst), n);
     return hipGetLastError();
 }

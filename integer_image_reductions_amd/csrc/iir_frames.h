@@ -21,7 +21,8 @@
 //   * The two columns left and right of the tile (horizontal halo) arrive transposed: one load
 //     per frame gives lane k the halo samples of tile row k-2 (lanes 0-31 the left side, lanes
 //     32-63 the right side), their vertical pass runs once per frame across lanes, and each row
-//     hands the result to lane 0 and lane 63 with two readlanes.
+//     hands the result to lane 0 and lane 63 with two readlanes (motion v2, with twice the halo
+//     values, gathers them with ds_bpermute instead).
 //   * The separable filter runs on packed 16-bit pairs: v_perm_b32 builds (row r, row r+1) pairs
 //     per column, v_dot2_u32_u16 applies two taps per instruction with the rounding constant as
 //     the accumulator, and v_perm_b32 extracts the 16-bit result of a byte-aligned shift. 10-bit
@@ -450,6 +451,9 @@ struct Tile {
     uint32_t hvoff;              // byte offset of the lane's halo load in the plane
     uint32_t hsel;               // byte permutation: (column -2, column -1) or (+256, +257)
     uint32_t hlds;               // staged: LDS dword index of the lane's halo dword
+    // motion v2: ds_bpermute byte addresses of row 0's halo values: lane 0 reads lane 2 (left
+    // halo), lane 63 reads lane 34 (right halo); row i adds 4 i. Other lanes' gathers are unused.
+    int hl_addr, hr_addr;
     bool halo_fix;               // staged, generic: lane 63 when column e+1 = W mirrors e-1
     // right frame edge inside the last strip (W % 256 != 0), fast path: the lane whose first
     // column is W loads the group before it and permutes it into the mirror image
@@ -828,6 +832,23 @@ __device__ __forceinline__ void push_frame_sums(const KernelArgs &a, const Tile 
     }
 }
 
+// Row i's halo value for lane 0 (addr = T.hl_addr: hv of lane i + 2) or lane 63 (T.hr_addr: hv of
+// lane i + 34), gathered across lanes by ds_bpermute; it only feeds the DPP edge operand below.
+__device__ __forceinline__ uint32_t halo_gather(uint32_t hv, int addr, int i)
+{
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(addr + 4 * i, (int)hv);
+}
+
+// The gather addresses for one frame. The empty asm makes them a value of this frame, so the
+// compiler does not hoist the per-row sums addr + 4 i out of the frame loop (32 registers held);
+// each sum then folds into the gather's immediate offset.
+__device__ __forceinline__ void halo_addrs(const Tile &T, int &hl, int &hr)
+{
+    hl = T.hl_addr;
+    hr = T.hr_addr;
+    asm volatile("" : "+v"(hl), "+v"(hr));
+}
+
 // The horizontal neighbours of one row's packed vertical values. q0, q1 hold the lane's columns
 // (c, c+1) and (c+2, c+3) as 16-bit pairs; ql receives (c-2, c-1) from the lane to the left or,
 // for lane 0, the left halo hl; qr receives (c+4, c+5) from the lane to the right or, for lane
@@ -1005,6 +1026,8 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
         uint32_t q0 = perm(v[1], v[0], kVSel);  // V of columns c, c+1
         uint32_t q1 = perm(v[3], v[2], kVSel);  // V of columns c+2, c+3
         // halo V of this row: columns s-2, s-1 (lane i + 2) and e, e+1 (lane i + 34)
+        // (readlane + a broadcast move measured faster here than the ds_bpermute gather of
+        // motion v2: the staged frame's LDS is busy with its own reads)
         const uint32_t hl = (uint32_t)__builtin_amdgcn_readlane((int)hv, i + 2);
         const uint32_t hr = (uint32_t)__builtin_amdgcn_readlane((int)hv, i + kWave / 2 + 2);
         uint32_t ql, qr;
@@ -1058,6 +1081,8 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
         if (have_prev) {
             uint32_t hvh, hvl;
             halo_vertical_v2<BPC>((pxin + kV2DiffBias<BPC>) - x0, hvh, hvl);
+            int hla, hra;
+            halo_addrs(T, hla, hra);
             const u32x2 zero{};
 #pragma unroll
             for (int i = 0; i < TH; ++i) {
@@ -1076,10 +1101,10 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
                 uint32_t q0h, q0l, q1h, q1l;
                 split_pack<BPC>(v[0], v[1], q0h, q0l);  // columns c, c+1
                 split_pack<BPC>(v[2], v[3], q1h, q1l);  // columns c+2, c+3
-                const uint32_t hlh = (uint32_t)__builtin_amdgcn_readlane((int)hvh, i + 2);
-                const uint32_t hll = (uint32_t)__builtin_amdgcn_readlane((int)hvl, i + 2);
-                const uint32_t hrh = (uint32_t)__builtin_amdgcn_readlane((int)hvh, i + kWave / 2 + 2);
-                const uint32_t hrl = (uint32_t)__builtin_amdgcn_readlane((int)hvl, i + kWave / 2 + 2);
+                const uint32_t hlh = halo_gather(hvh, hla, i);
+                const uint32_t hll = halo_gather(hvl, hla, i);
+                const uint32_t hrh = halo_gather(hvh, hra, i);
+                const uint32_t hrl = halo_gather(hvl, hra, i);
                 uint32_t qlh, qrh, qll, qrl;
                 neighbours<GENERIC, ROWSTAGE>(T, hlh, hrh, q0h, q1h, qlh, qrh);
                 neighbours<GENERIC, ROWSTAGE>(T, hll, hrl, q0l, q1l, qll, qrl);
@@ -1445,6 +1470,10 @@ frames_kernel(const KernelArgs a)
                  : (!GENERIC && c == W) ? (uint32_t)((W - kLumaCols) * B)
                                         : 0u;
     T.out_lane = c < W;
+    if constexpr (V2) {
+        T.hl_addr = lane == 0 ? 4 * 2 : 4 * lane;
+        T.hr_addr = lane == kWave - 1 ? 4 * (kWave / 2 + 2) : 4 * lane;
+    }
     T.w0 = (c < W ? 1u : 0u) | (c + 1 < W ? 0x10000u : 0u);
     T.w1 = (c + 2 < W ? 1u : 0u) | (c + 3 < W ? 0x10000u : 0u);
     T.edge_tile = T.strip == a.strips - 1 && W % kStripCols != 0;

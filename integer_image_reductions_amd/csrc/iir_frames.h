@@ -454,6 +454,8 @@ struct Tile {
     // motion v2: ds_bpermute byte addresses of row 0's halo values: lane 0 reads lane 2 (left
     // halo), lane 63 reads lane 34 (right halo); row i adds 4 i. Other lanes' gathers are unused.
     int hl_addr, hr_addr;
+    // parity of the wavefront's slot on its SIMD (hardware wave id, HW_ID bits 3:0)
+    uint32_t slot;
     bool halo_fix;               // staged, generic: lane 63 when column e+1 = W mirrors e-1
     // right frame edge inside the last strip (W % 256 != 0), fast path: the lane whose first
     // column is W loads the group before it and permutes it into the mirror image
@@ -1150,6 +1152,19 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
     have_prev = true;
 }
 
+// s_setprio takes an immediate
+__device__ __forceinline__ void set_prio(uint32_t p)
+{
+    if (p == 3u)
+        __builtin_amdgcn_s_setprio(3);
+    else if (p == 2u)
+        __builtin_amdgcn_s_setprio(2);
+    else if (p == 1u)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
+}
+
 // Staged path, frame t of a chunk's loop: wait until its luma (in the stage `lds`) and its chroma
 // (in C) have landed, read the luma out and sum the chroma, then issue frame t+1's chroma into C
 // and frame t+2's luma into the stage just read, so two frames of loads stay in flight while
@@ -1160,6 +1175,10 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
 // L2 hit), so that one wait is always right and the compiler's own count for the chroma registers
 // agrees with it. The wavefront raises its priority from the wait to the last load issued, so a
 // wavefront whose data has landed refills the memory pipe ahead of its SIMD's computing waves.
+// At equal priority a SIMD's arbiter favours its older wavefront: with two per SIMD, per-wave
+// timestamps showed the younger finishing a 50-frame launch about 40% after the older, the SIMD
+// then running one wavefront alone. So the two slots take turns, frame by frame, at the higher
+// of two priority levels, in the load window (3 or 2) and in the compute that follows (1 or 0).
 // ALL_DIST reads the distorted rows out of a frame that is not accumulated too (its stage then
 // holds stale rows), so that the luma sums can run for every frame without a branch per row.
 template <int TH, bool ALL_DIST>
@@ -1168,7 +1187,8 @@ __device__ __forceinline__ void staged_frame(const KernelArgs &a, const Tile &T,
                                              int f_end, uint32_t (*lds)[kWave], ChromaX4<TH> &C,
                                              FrameData<8, TH> &F, FrameStats<8> &S)
 {
-    __builtin_amdgcn_s_setprio(3);
+    const uint32_t favoured = ((uint32_t)t + T.slot) & 1u;
+    set_prio(2u + favoured);
     __builtin_amdgcn_s_waitcnt(0x0F70 | Stage<TH>::kDmaLoads);  // vmcnt(one luma group)
     read_stage<TH>(ALL_DIST || t >= f_begin, lds, T.lane, T.hlds, F);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
@@ -1179,7 +1199,7 @@ __device__ __forceinline__ void staged_frame(const KernelArgs &a, const Tile &T,
         load_chroma_x4<TH>(a, T, O, t + 1, C);
         load_frame_staged<TH>(a, T, O, min(t + 2, f_end - 1), true, lds);
     }
-    __builtin_amdgcn_s_setprio(0);
+    set_prio(favoured);
 }
 
 // The first loads of a chunk's loop: luma and chroma of its first frame, then the luma of the
@@ -1470,6 +1490,8 @@ frames_kernel(const KernelArgs a)
                  : (!GENERIC && c == W) ? (uint32_t)((W - kLumaCols) * B)
                                         : 0u;
     T.out_lane = c < W;
+    if constexpr (STAGED)
+        T.slot = (uint32_t)__builtin_amdgcn_s_getreg(0xF804) & 1u;  // hwreg(HW_REG_HW_ID)
     if constexpr (V2) {
         T.hl_addr = lane == 0 ? 4 * 2 : 4 * lane;
         T.hr_addr = lane == kWave - 1 ? 4 * (kWave / 2 + 2) : 4 * lane;

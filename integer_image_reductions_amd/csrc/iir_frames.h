@@ -896,23 +896,42 @@ __device__ __forceinline__ void neighbours(const Tile &T, uint32_t hl, uint32_t 
 // sums), so it is taken as two 32-bit sums Q = sum g Vb and L = sum g Vlo + 2^15 (below 2^32):
 //   F + 2^16 = floor((S' + 2^15) / 2^16) = Q + floor(L / 2^16).
 
-// prev - cur + 2^bpc of one row's 4 samples as two 16-bit pairs: columns (c, c+1), (c+2, c+3).
-// Each half lies in [1, 2^(bpc+1) - 1], so whole-dword arithmetic never carries between halves.
+// The constants of motion v2 at bit depth bpc: the difference bias 2^bpc in both 16-bit halves,
+// the vertical rounding term 2^(bpc - 1) and the vertical shift bpc. 8 and 10 bits are
+// compile-time; 16-bit storage takes its depth, 9 to 15, from the launch's scale shift
+// (16 - depth); the biased difference of 16-bit samples would need 17 bits.
+struct V2Depth {
+    uint32_t bias, round, vshift;
+};
+
 template <int BPC>
-__device__ __forceinline__ u32x2 diff_row(typename Px<BPC>::Luma p, typename Px<BPC>::Luma r)
+__device__ __forceinline__ V2Depth v2_depth(const KernelArgs &a)
+{
+    if constexpr (BPC == 8) {
+        return V2Depth{0x01000100u, 128u, 8u};
+    } else if constexpr (BPC == 10) {
+        return V2Depth{0x04000400u, 512u, 10u};
+    } else {
+        const uint32_t b = 16u - (uint32_t)a.shift;
+        return V2Depth{(1u << b) * 0x10001u, 1u << (b - 1u), b};
+    }
+}
+
+// prev - cur + 2^bpc of one row's 4 samples as two 16-bit pairs: columns (c, c+1), (c+2, c+3).
+// Each half lies in [1, 2^(bpc+1) - 1], so whole-dword arithmetic never carries between halves
+// (prev < 2^bpc, so OR-ing the bias in adds it).
+template <int BPC>
+__device__ __forceinline__ u32x2 diff_row(typename Px<BPC>::Luma p, typename Px<BPC>::Luma r,
+                                          const V2Depth &D)
 {
     if constexpr (BPC == 8) {
         // bytes of prev widened to 16 bits with 0x01 as the high byte: prev + 256
         return u32x2{perm(0x01010101u, p, 0x04010400u) - perm(0u, r, 0x0c010c00u),
                      perm(0x01010101u, p, 0x04030402u) - perm(0u, r, 0x0c030c02u)};
     } else {
-        return u32x2{(p.x | 0x04000400u) - r.x, (p.y | 0x04000400u) - r.y};
+        return u32x2{(p.x | D.bias) - r.x, (p.y | D.bias) - r.y};
     }
 }
-
-// the bias of diff_row in both halves
-template <int BPC>
-constexpr uint32_t kV2DiffBias = BPC == 8 ? 0x01000100u : 0x04000400u;
 
 // (row a, row b) pairs of the 4 columns of two difference rows
 __device__ __forceinline__ void diff_pairs(u32x2 da, u32x2 db, uint32_t p[4])
@@ -923,21 +942,18 @@ __device__ __forceinline__ void diff_pairs(u32x2 da, u32x2 db, uint32_t p[4])
     p[3] = perm(db.y, da.y, 0x07060302u);
 }
 
-// rounding term of the vertical pass, 2^(bpc - 1)
-template <int BPC>
-constexpr uint32_t kV2Round = BPC == 8 ? 128u : 512u;
-
 // Two columns' vertical sums of biased differences (rounding term included) -> packed top bits
 // (Vb, Vb') and low halves (Vlo, Vlo'). 8-bit: V' = s >> 8 < 2^17, so Vlo is bits 8-23 of s and
-// Vb its byte 3; 10-bit: V' = s >> 10 first.
+// Vb its byte 3; deeper: V' = s >> bpc first (s < 2^32 up to 15 bits).
 template <int BPC>
-__device__ __forceinline__ void split_pack(uint32_t s0, uint32_t s1, uint32_t &h, uint32_t &l)
+__device__ __forceinline__ void split_pack(uint32_t s0, uint32_t s1, uint32_t &h, uint32_t &l,
+                                           const V2Depth &D)
 {
     if constexpr (BPC == 8) {
         h = perm(s1, s0, 0x0c070c03u);
         l = perm(s1, s0, 0x06050201u);
     } else {
-        const uint32_t v0 = s0 >> 10, v1 = s1 >> 10;
+        const uint32_t v0 = s0 >> D.vshift, v1 = s1 >> D.vshift;
         h = perm(v1, v0, 0x0c060c02u);
         l = perm(v1, v0, 0x05040100u);
     }
@@ -946,17 +962,18 @@ __device__ __forceinline__ void split_pack(uint32_t s0, uint32_t s1, uint32_t &h
 // Vertical pass of the transposed halo's biased differences (lane k: the two halo columns of
 // tile row k - 2 as a pair), split as above; lane i + 2 (left) and i + 34 (right) serve row i.
 template <int BPC>
-__device__ __forceinline__ void halo_vertical_v2(uint32_t dh, uint32_t &hvh, uint32_t &hvl)
+__device__ __forceinline__ void halo_vertical_v2(uint32_t dh, uint32_t &hvh, uint32_t &hvl,
+                                                 const V2Depth &D)
 {
     const uint32_t m1 = from_left(dh), m2 = from_left(m1);    // rows k-1, k-2
     const uint32_t p1 = from_right(dh), p2 = from_right(p1);  // rows k+1, k+2
     const uint32_t sa = dot2u(p2, T0z,
                               dot2u(perm(p1, dh, 0x05040100u), T21,
-                                    dot2u(perm(m1, m2, 0x05040100u), T01, kV2Round<BPC>)));
+                                    dot2u(perm(m1, m2, 0x05040100u), T01, D.round)));
     const uint32_t sb = dot2u(p2 >> 16, T0z,
                               dot2u(perm(p1, dh, 0x07060302u), T21,
-                                    dot2u(perm(m1, m2, 0x07060302u), T01, kV2Round<BPC>)));
-    split_pack<BPC>(sa, sb, hvh, hvl);
+                                    dot2u(perm(m1, m2, 0x07060302u), T01, D.round)));
+    split_pack<BPC>(sa, sb, hvh, hvl, D);
 }
 
 // F + 2^16 = Q + floor(L / 2^16) of one output in one instruction: v_mad_u32_u16 multiplies the
@@ -1082,27 +1099,28 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
         uint32_t sad = 0;
         if (have_prev) {
             uint32_t hvh, hvl;
-            halo_vertical_v2<BPC>((pxin + kV2DiffBias<BPC>) - x0, hvh, hvl);
+            const V2Depth D = v2_depth<BPC>(a);
+            halo_vertical_v2<BPC>((pxin + D.bias) - x0, hvh, hvl, D);
             int hla, hra;
             halo_addrs(T, hla, hra);
             const u32x2 zero{};
 #pragma unroll
             for (int i = 0; i < TH; ++i) {
                 uint32_t pa[4], pb[4], pc[4];
-                diff_pairs(diff_row<BPC>(pin[i], F.R[i]), diff_row<BPC>(pin[i + 1], F.R[i + 1]),
-                           pa);  // rows i-2, i-1
-                diff_pairs(diff_row<BPC>(pin[i + 2], F.R[i + 2]),
-                           diff_row<BPC>(pin[i + 3], F.R[i + 3]), pb);  // rows i, i+1
-                diff_pairs(diff_row<BPC>(pin[i + 4], F.R[i + 4]),
-                           i + 5 < TH + 4 ? diff_row<BPC>(pin[i + 5], F.R[i + 5]) : zero,
+                diff_pairs(diff_row<BPC>(pin[i], F.R[i], D),
+                           diff_row<BPC>(pin[i + 1], F.R[i + 1], D), pa);  // rows i-2, i-1
+                diff_pairs(diff_row<BPC>(pin[i + 2], F.R[i + 2], D),
+                           diff_row<BPC>(pin[i + 3], F.R[i + 3], D), pb);  // rows i, i+1
+                diff_pairs(diff_row<BPC>(pin[i + 4], F.R[i + 4], D),
+                           i + 5 < TH + 4 ? diff_row<BPC>(pin[i + 5], F.R[i + 5], D) : zero,
                            pc);  // rows i+2 (tap 0 on i+3)
                 uint32_t v[4];
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    v[b] = dot2u(pc[b], T0z, dot2u(pb[b], T21, dot2u(pa[b], T01, kV2Round<BPC>)));
+                    v[b] = dot2u(pc[b], T0z, dot2u(pb[b], T21, dot2u(pa[b], T01, D.round)));
                 uint32_t q0h, q0l, q1h, q1l;
-                split_pack<BPC>(v[0], v[1], q0h, q0l);  // columns c, c+1
-                split_pack<BPC>(v[2], v[3], q1h, q1l);  // columns c+2, c+3
+                split_pack<BPC>(v[0], v[1], q0h, q0l, D);  // columns c, c+1
+                split_pack<BPC>(v[2], v[3], q1h, q1l, D);  // columns c+2, c+3
                 const uint32_t hlh = halo_gather(hvh, hla, i);
                 const uint32_t hll = halo_gather(hvl, hla, i);
                 const uint32_t hrh = halo_gather(hvh, hra, i);
@@ -1704,19 +1722,25 @@ frames_kernel(const KernelArgs a)
 
 // Every (bit depth, tile height, path) the host may pick. The fast path needs W % 8 == 0 and
 // H % TH == 0 (no ragged tile, no partial sample group); the generic path takes any size.
+// Motion v2 of 16-bit storage carries the previous frame's 16-bit rows beside the 64-bit squared
+// error sums: it only has the 12-row tile, at two wavefronts per SIMD (taller tiles spill).
 template <int BPC, bool GENERIC, bool MOM, bool V2 = false>
 FramesFn frames_fn(int th)
 {
     constexpr bool P = BPC == 8 ? IIR_STAGE8 : IIR_STAGE10;
-    switch (th) {
-    case 12:
-        return frames_kernel<BPC, 12, P, GENERIC, IIR_WPE12, MOM, V2>;
-    case 16:
-        return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16, MOM, V2>;
-    case 20:
-        return frames_kernel<BPC, 20, P, GENERIC, IIR_WPE20, MOM, V2>;
-    default:
-        return nullptr;
+    if constexpr (BPC == 16 && V2) {
+        return th == 12 ? frames_kernel<BPC, 12, P, GENERIC, 2, MOM, V2> : nullptr;
+    } else {
+        switch (th) {
+        case 12:
+            return frames_kernel<BPC, 12, P, GENERIC, IIR_WPE12, MOM, V2>;
+        case 16:
+            return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16, MOM, V2>;
+        case 20:
+            return frames_kernel<BPC, 20, P, GENERIC, IIR_WPE20, MOM, V2>;
+        default:
+            return nullptr;
+        }
     }
 }
 

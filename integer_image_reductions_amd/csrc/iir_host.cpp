@@ -157,8 +157,8 @@ int check_config(const iir_config *c)
         return fail(IIR_EINVAL, "max_batch %d outside 1..65536", c->max_batch);
     if (c->flags & ~(IIR_FLAG_TIMING | IIR_FLAG_MOMENTS | IIR_FLAG_MOTION_V2))
         return fail(IIR_EINVAL, "unknown flags 0x%x", c->flags);
-    if ((c->flags & IIR_FLAG_MOTION_V2) && c->bpc != 8 && c->bpc != 10)
-        return fail(IIR_EINVAL, "motion v2 needs 8- or 10-bit samples, got %d", c->bpc);
+    if ((c->flags & IIR_FLAG_MOTION_V2) && c->bpc > 15)
+        return fail(IIR_EINVAL, "motion v2 needs 8- to 15-bit samples, got %d", c->bpc);
     return IIR_OK;
 }
 
@@ -222,7 +222,7 @@ void choose_columns(iir_ctx *c)
 int choose_rows(iir_ctx *c, int cus, int forced)
 {
     static const int kCandidates[] = {12, 16, 20};
-    int best = 16;
+    int best = 0;  // none: no kernel for this configuration
     double best_cost = 1e300;
     for (int th : kCandidates) {
         if (forced && th != forced)
@@ -441,7 +441,13 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     c->v2 = (cfg->flags & IIR_FLAG_MOTION_V2) != 0;
     c->nsums = c->moments ? kMaxSums : kSums;
     choose_columns(c);
-    c->rows_per_tile = choose_rows(c, prop.multiProcessorCount, env_int("IIR_ROWS_PER_TILE", 0, 0, 64));
+    const int forced_rows = env_int("IIR_ROWS_PER_TILE", 0, 0, 64);
+    c->rows_per_tile = choose_rows(c, prop.multiProcessorCount, forced_rows);
+    if (c->rows_per_tile == 0) {
+        delete c;
+        return fail(IIR_EINVAL, "no frames kernel for this configuration (rows per tile %d)",
+                    forced_rows);
+    }
     c->row_tiles = (cfg->height + c->rows_per_tile - 1) / c->rows_per_tile;
     c->tiles = c->strips * c->row_tiles;
     c->target_waves = env_int("IIR_TARGET_WAVES", 4 * prop.multiProcessorCount, 1, 1 << 20);

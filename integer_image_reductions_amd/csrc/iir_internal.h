@@ -58,13 +58,15 @@ struct KernelArgs {
 
 // The frames kernel of one configuration, or nullptr: one function per sample type and motion
 // variant, each in its own translation unit (iir_frames_8.hip, iir_frames_10.hip,
-// iir_frames_16.hip, and the motion v2 units iir_frames_8_v2.hip, iir_frames_10_v2.hip).
+// iir_frames_16.hip, and the motion v2 units iir_frames_8_v2.hip, iir_frames_10_v2.hip,
+// iir_frames_16_v2.hip).
 typedef void (*FramesFn)(KernelArgs);
 FramesFn frames_pick_8(int th, bool generic, bool moments);
 FramesFn frames_pick_10(int th, bool generic, bool moments);
 FramesFn frames_pick_16(int th, bool generic, bool moments);
 FramesFn frames_pick_8_v2(int th, bool generic, bool moments);
 FramesFn frames_pick_10_v2(int th, bool generic, bool moments);
+FramesFn frames_pick_16_v2(int th, bool generic, bool moments);
 
 // Host-side launchers (iir_kernels.hip). Each returns the launch's hipError_t.
 bool supported_rows_per_tile(int th);           // 12, 16 or 20

@@ -469,7 +469,7 @@ def _pairs(bpc, seed):
 
 
 def pin_diff_blur_brute_force(o):
-    for bpc in (8, 10, 12):
+    for bpc in (8, 10, 12, 15, 16):
         for i, (p, c) in enumerate(_pairs(bpc, 71 + bpc)):
             assert np.array_equal(o.diff_blur(p, c, bpc), brute_force_diff_blur(p, c, bpc)), \
                 (bpc, i, p.shape)
@@ -483,11 +483,10 @@ def pin_diff_blur_scipy(o):
 
 def pin_diff_blur_constant(o):
     """Flat frames c + d then c: every output is d 2^(16 - bpc), of either sign."""
-    for bpc in (8, 10):
+    for bpc in (8, 10, 12, 15):
         dt = np.uint8 if bpc == 8 else np.uint16
         for c0, d in ((100, 3), (100, -7), (0, 255), (255, -255)):
-            if bpc == 10:
-                c0, d = c0 * 4, d * 4
+            c0, d = c0 << (bpc - 8), d * (1 << (bpc - 8))
             p = np.full((6, 9), c0 + d, dt)
             c = np.full((6, 9), c0, dt)
             assert np.all(o.diff_blur(p, c, bpc) == d * (1 << (16 - bpc))), (bpc, c0, d)
@@ -499,7 +498,7 @@ def pin_diff_blur_bounds(o):
     """Within 1 of the exact real filter of prev - cur scaled to 16 bits; within 3 of the
     difference of the two blurred frames; swapping the frames negates the result up to 1."""
     g = np.array(TAPS, dtype=np.float64) / 65536.0
-    for bpc in (8, 10):
+    for bpc in (8, 10, 12, 15):
         for p, c in _pairs(bpc, 97 + bpc):
             h, w = p.shape
             f = o.diff_blur(p, c, bpc).astype(np.int64)
@@ -514,11 +513,22 @@ def pin_diff_blur_bounds(o):
             assert np.abs(f + o.diff_blur(c, p, bpc).astype(np.int64)).max() <= 1
 
 
+def pin_diff_blur_depth(o):
+    """The filter of 8-bit frames scaled to depth b (x 2^(b - 8)) is the 8-bit filter, exactly: the
+    vertical rounding term and shift scale with the samples."""
+    for b in (9, 10, 12, 15, 16):
+        for i, (p, c) in enumerate(_pairs(8, 113)):
+            s = 1 << (b - 8)
+            ps, cs = (p.astype(np.uint16) * s), (c.astype(np.uint16) * s)
+            assert np.array_equal(o.diff_blur(ps, cs, b), o.diff_blur(p, c, 8)), (b, i)
+
+
 def pin_clip_v2_composition(o):
     """Per frame: SSE by brute force, SAD2 = sum |F| of the brute-force filter of the previous and
     the current reference luma; a clip split in two with the first part's last luma as prev_luma
     equals the whole clip."""
-    for bpc, (f, h, w) in ((8, (4, 7, 9)), (10, (3, 5, 6)), (8, (3, 3, 3))):
+    for bpc, (f, h, w) in ((8, (4, 7, 9)), (10, (3, 5, 6)), (8, (3, 3, 3)), (12, (3, 6, 5)),
+                           (15, (3, 5, 7))):
         ref, dist = _tiny_clip(bpc, f, h, w, 300 + h)
         sums, hm = o.clip_v2(ref, dist, bpc)
         assert list(hm) == [0] + [1] * (f - 1)

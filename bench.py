@@ -119,7 +119,7 @@ def _counter_means(path: str, counter: str):
 
 
 def write_traffic(workload: str, moments: bool, motion_v2: bool, fetch_csv: str,
-                  write_csv: str) -> dict:
+                  write_csv: str, out_dir: str = None) -> dict:
     fm, fn, fc, fcn = _counter_means(fetch_csv, "FETCH_SIZE")
     wm, wn, wc, wcn = _counter_means(write_csv, "WRITE_SIZE")
     f_scale = PROBE_BYTES / (fc * 1024.0)
@@ -149,8 +149,9 @@ def write_traffic(workload: str, moments: bool, motion_v2: bool, fetch_csv: str,
     c = synth.CONFIGS[workload]
     d["algorithmic_bytes_per_launch"] = algorithmic_bytes(c["width"], c["height"], c["bpc"],
                                                           c["frames"], motion_v2)
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    path = os.path.join(ROOT, "profiles", f"frames_kernel_{wl}_traffic.json")
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    path = os.path.join(out_dir, f"frames_kernel_{wl}_traffic.json")
     with open(path, "w") as f:
         json.dump(d, f, indent=1)
         f.write("\n")

@@ -66,8 +66,7 @@ enum {
  */
 #define IIR_FLAG_MOMENTS 2u
 /*
- * Motion v2 instead of the blurred-frame SAD (8 to 15 bits; IIR_EINVAL at 16, whose frame
- * difference needs 17 bits): iir_result.sad becomes
+ * Motion v2 instead of the blurred-frame SAD (every depth, 8 to 16 bits): iir_result.sad becomes
  * SAD2 = sum over the luma plane of |F|, F the same separable filter applied to the difference
  * prev - cur of consecutive reference luma frames, with both rounded shifts taken as floor
  * ("ADR-1392", Decision 4: the kernel stages prev - cur and filters it separably). The context

@@ -976,6 +976,51 @@ __device__ __forceinline__ void halo_vertical_v2(uint32_t dh, uint32_t &hvh, uin
     split_pack<BPC>(sa, sb, hvh, hvl, D);
 }
 
+// 16 bits ("wide"): the biased difference d' = d + 2^16 needs 17 bits, so it travels halved:
+// dh = floor(d / 2) + 2^15 (16 bits) and dl = d mod 2, d' = 2 dh + dl. With y1 = sum g dh and
+// y2 = sum g dl + 2^15, the vertical value is V' = (2 y1 + y2) >> 16 = (y1 + (y2 >> 1)) >> 15 =
+// V + 2^16, every sum below 2^32 (y1 + (y2 >> 1) <= 4,294,950,912); the horizontal pass is then
+// the one above.
+struct WideDiff {
+    uint32_t h, l;  // dh and dl of two columns, as 16-bit pairs
+};
+
+// dh and dl of one dword of prev and cur samples (two 16-bit columns): floor((p - r) / 2) =
+// (p >> 1) - (r >> 1) - (~p & r & 1) per half, plus 2^15, never below 0 or above 65535, so the
+// whole-dword arithmetic does not borrow between halves; d mod 2 = (p ^ r) & 1.
+__device__ __forceinline__ WideDiff wide_diff(uint32_t p, uint32_t r)
+{
+    const uint32_t half_p = ((p >> 1) & 0x7fff7fffu) | 0x80008000u;
+    const uint32_t half_r = (r >> 1) & 0x7fff7fffu;
+    return WideDiff{half_p - half_r - (~p & r & 0x00010001u), (p ^ r) & 0x00010001u};
+}
+
+// One dword of V' for the halved representation: the two sums of a column's chain
+__device__ __forceinline__ uint32_t wide_vertical(uint32_t y1, uint32_t y2)
+{
+    return y1 + (y2 >> 1);
+}
+
+// halo_vertical_v2 for the halved differences (dh, dl of the halo pair, one lane per tile row)
+__device__ __forceinline__ void halo_vertical_v2_wide(WideDiff d, uint32_t &hvh, uint32_t &hvl)
+{
+    uint32_t s[2][2];  // [dh, dl][column s-2, s-1]
+    const uint32_t src[2] = {d.h, d.l};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t x = src[k];
+        const uint32_t m1 = from_left(x), m2 = from_left(m1);
+        const uint32_t p1 = from_right(x), p2 = from_right(p1);
+        const uint32_t start = k == 0 ? 0u : 32768u;
+        s[k][0] = dot2u(p2, T0z, dot2u(perm(p1, x, 0x05040100u), T21,
+                                       dot2u(perm(m1, m2, 0x05040100u), T01, start)));
+        s[k][1] = dot2u(p2 >> 16, T0z, dot2u(perm(p1, x, 0x07060302u), T21,
+                                             dot2u(perm(m1, m2, 0x07060302u), T01, start)));
+    }
+    const V2Depth D{0u, 0u, 15u};
+    split_pack<16>(wide_vertical(s[0][0], s[1][0]), wide_vertical(s[0][1], s[1][1]), hvh, hvl, D);
+}
+
 // F + 2^16 = Q + floor(L / 2^16) of one output in one instruction: v_mad_u32_u16 multiplies the
 // high half of L (op_sel) by 1 and adds Q. |F| = |(F + 2^16) - 2^16|.
 constexpr uint32_t kV2Zero = 1u << 16;
@@ -1077,8 +1122,8 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
 // One frame of one tile for motion v2: the filter of prev - cur and the sum of its absolute
 // values, plus the same squared errors (and moments) as compute_frame. pin holds the previous
 // frame's reference luma rows (mirrored like F.R) and pxin its halo pair; on return pout and
-// pxout hold this frame's, for the next.
-template <int BPC, int TH, bool GENERIC, bool ROWSTAGE, bool MOM>
+// pxout hold this frame's, for the next. WIDE: 16-bit samples, halved differences (above).
+template <int BPC, int TH, bool GENERIC, bool ROWSTAGE, bool MOM, bool WIDE>
 __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile &T,
                                                  bool accumulate, FrameData<BPC, TH> &F,
                                                  FrameStats<BPC> &S,
@@ -1099,25 +1144,59 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
         uint32_t sad = 0;
         if (have_prev) {
             uint32_t hvh, hvl;
-            const V2Depth D = v2_depth<BPC>(a);
-            halo_vertical_v2<BPC>((pxin + D.bias) - x0, hvh, hvl, D);
+            const V2Depth D = WIDE ? V2Depth{0u, 0u, 15u} : v2_depth<BPC>(a);
+            if constexpr (WIDE)
+                halo_vertical_v2_wide(wide_diff(pxin, x0), hvh, hvl);
+            else
+                halo_vertical_v2<BPC>((pxin + D.bias) - x0, hvh, hvl, D);
             int hla, hra;
             halo_addrs(T, hla, hra);
             const u32x2 zero{};
 #pragma unroll
             for (int i = 0; i < TH; ++i) {
-                uint32_t pa[4], pb[4], pc[4];
-                diff_pairs(diff_row<BPC>(pin[i], F.R[i], D),
-                           diff_row<BPC>(pin[i + 1], F.R[i + 1], D), pa);  // rows i-2, i-1
-                diff_pairs(diff_row<BPC>(pin[i + 2], F.R[i + 2], D),
-                           diff_row<BPC>(pin[i + 3], F.R[i + 3], D), pb);  // rows i, i+1
-                diff_pairs(diff_row<BPC>(pin[i + 4], F.R[i + 4], D),
-                           i + 5 < TH + 4 ? diff_row<BPC>(pin[i + 5], F.R[i + 5], D) : zero,
-                           pc);  // rows i+2 (tap 0 on i+3)
                 uint32_t v[4];
+                if constexpr (WIDE) {
+                    // rows k of the halved differences: (dh, dl) of columns (c, c+1), (c+2, c+3)
+                    auto wd = [&](int k, u32x2 &h, u32x2 &l) {
+                        if (k >= TH + 4) {
+                            h = zero;
+                            l = zero;
+                        } else {
+                            const WideDiff d0 = wide_diff(pin[k].x, F.R[k].x);
+                            const WideDiff d1 = wide_diff(pin[k].y, F.R[k].y);
+                            h = u32x2{d0.h, d1.h};
+                            l = u32x2{d0.l, d1.l};
+                        }
+                    };
+                    u32x2 h[6], l[6];
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    v[b] = dot2u(pc[b], T0z, dot2u(pb[b], T21, dot2u(pa[b], T01, D.round)));
+                    for (int k = 0; k < 6; ++k)
+                        wd(i + k, h[k], l[k]);
+                    uint32_t ph[3][4], pl[3][4];
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) {
+                        diff_pairs(h[2 * k], h[2 * k + 1], ph[k]);
+                        diff_pairs(l[2 * k], l[2 * k + 1], pl[k]);
+                    }
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        v[b] = wide_vertical(
+                            dot2u(ph[2][b], T0z, dot2u(ph[1][b], T21, dot2u(ph[0][b], T01, 0u))),
+                            dot2u(pl[2][b], T0z,
+                                  dot2u(pl[1][b], T21, dot2u(pl[0][b], T01, 32768u))));
+                } else {
+                    uint32_t pa[4], pb[4], pc[4];
+                    diff_pairs(diff_row<BPC>(pin[i], F.R[i], D),
+                               diff_row<BPC>(pin[i + 1], F.R[i + 1], D), pa);  // rows i-2, i-1
+                    diff_pairs(diff_row<BPC>(pin[i + 2], F.R[i + 2], D),
+                               diff_row<BPC>(pin[i + 3], F.R[i + 3], D), pb);  // rows i, i+1
+                    diff_pairs(diff_row<BPC>(pin[i + 4], F.R[i + 4], D),
+                               i + 5 < TH + 4 ? diff_row<BPC>(pin[i + 5], F.R[i + 5], D) : zero,
+                               pc);  // rows i+2 (tap 0 on i+3)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        v[b] = dot2u(pc[b], T0z, dot2u(pb[b], T21, dot2u(pa[b], T01, D.round)));
+                }
                 uint32_t q0h, q0l, q1h, q1l;
                 split_pack<BPC>(v[0], v[1], q0h, q0l, D);  // columns c, c+1
                 split_pack<BPC>(v[2], v[3], q1h, q1l, D);  // columns c+2, c+3
@@ -1291,7 +1370,7 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
 // The frames of this workgroup's time chunk for motion v2. The state carried from frame to frame
 // is the previous frame's reference luma rows and halo pair, in two register sets whose roles
 // swap every frame; chunks after the first load the frame before them as their first state.
-template <int BPC, int TH, bool GENERIC, bool STAGED, bool MOM>
+template <int BPC, int TH, bool GENERIC, bool STAGED, bool MOM, bool WIDE>
 __device__ __forceinline__ void frame_loop_v2(const KernelArgs &a, const Tile &T,
                                               const StageOffsets<TH> &O,
                                               typename Px<BPC>::Luma (&prev)[TH + 4],
@@ -1321,8 +1400,8 @@ __device__ __forceinline__ void frame_loop_v2(const KernelArgs &a, const Tile &T
                                     F, S);
         else
             load_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F);
-        compute_frame_v2<BPC, TH, GENERIC, STAGED, MOM>(a, T, t >= f_begin, F, S, pin, pxin,
-                                                        pout, pxout, have_prev, P);
+        compute_frame_v2<BPC, TH, GENERIC, STAGED, MOM, WIDE>(a, T, t >= f_begin, F, S, pin,
+                                                              pxin, pout, pxout, have_prev, P);
     };
     Luma alt[TH + 4];
     uint32_t pxalt = 0;
@@ -1477,7 +1556,8 @@ __device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane,
     // the end of the kernel releases these stores to the host before its completion signal
 }
 
-template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE, bool MOM, bool V2>
+// V2: 0 the blurred-frame SAD, 1 motion v2, 2 motion v2 of 16-bit samples (halved differences)
+template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE, bool MOM, int V2>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void
 frames_kernel(const KernelArgs a)
 {
@@ -1652,7 +1732,8 @@ frames_kernel(const KernelArgs a)
             for (int k = 0; k < TH + 4; ++k)
                 prev[k] = typename Px<BPC>::Luma{};
         }
-        frame_loop_v2<BPC, TH, GENERIC, STAGED, MOM>(a, T, O, prev, pxprev, have_prev, stage);
+        frame_loop_v2<BPC, TH, GENERIC, STAGED, MOM, V2 == 2>(a, T, O, prev, pxprev, have_prev,
+                                                             stage);
         // the state stores drain while the group count is in flight
         unsigned int arrived;
         if (T.chunk == a.chunks - 1) {
@@ -1724,7 +1805,7 @@ frames_kernel(const KernelArgs a)
 // H % TH == 0 (no ragged tile, no partial sample group); the generic path takes any size.
 // Motion v2 of 16-bit storage carries the previous frame's 16-bit rows beside the 64-bit squared
 // error sums: it only has the 12-row tile, at two wavefronts per SIMD (taller tiles spill).
-template <int BPC, bool GENERIC, bool MOM, bool V2 = false>
+template <int BPC, bool GENERIC, bool MOM, int V2 = 0>
 FramesFn frames_fn(int th)
 {
     constexpr bool P = BPC == 8 ? IIR_STAGE8 : IIR_STAGE10;

@@ -157,8 +157,6 @@ int check_config(const iir_config *c)
         return fail(IIR_EINVAL, "max_batch %d outside 1..65536", c->max_batch);
     if (c->flags & ~(IIR_FLAG_TIMING | IIR_FLAG_MOMENTS | IIR_FLAG_MOTION_V2))
         return fail(IIR_EINVAL, "unknown flags 0x%x", c->flags);
-    if ((c->flags & IIR_FLAG_MOTION_V2) && c->bpc > 15)
-        return fail(IIR_EINVAL, "motion v2 needs 8- to 15-bit samples, got %d", c->bpc);
     return IIR_OK;
 }
 

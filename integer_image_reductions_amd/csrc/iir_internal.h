@@ -66,13 +66,13 @@ FramesFn frames_pick_10(int th, bool generic, bool moments);
 FramesFn frames_pick_16(int th, bool generic, bool moments);
 FramesFn frames_pick_8_v2(int th, bool generic, bool moments);
 FramesFn frames_pick_10_v2(int th, bool generic, bool moments);
-FramesFn frames_pick_16_v2(int th, bool generic, bool moments);
+FramesFn frames_pick_16_v2(int th, bool generic, bool moments, bool wide);
 
 // Host-side launchers (iir_kernels.hip). Each returns the launch's hipError_t.
 bool supported_rows_per_tile(int th);           // 12, 16 or 20
 bool fast_path_ok(int W, int H, int th);         // the uniform fast path applies
 // `moments`: the launch also sums the luma moments (S = kMaxSums); `v2`: the motion sum is the
-// motion v2 one (8 to 15 bits), with ring_in / ring_out holding the last frame's reference
+// motion v2 one (8 to 16 bits), with ring_in / ring_out holding the last frame's reference
 // luma as a plane of strips * 256 samples per row instead of the tiled blurred state
 hipError_t frames_occupancy(int bpc, int th, bool generic, bool moments, bool v2,
                             int *waves_per_cu);

@@ -101,8 +101,8 @@ FramesFn pick(int bpc, int th, bool generic, bool moments, bool v2 = false)
             return frames_pick_8_v2(th, generic, moments);
         if (bpc == 10)
             return frames_pick_10_v2(th, generic, moments);
-        if (bpc >= 9 && bpc <= 15)
-            return frames_pick_16_v2(th, generic, moments);
+        if (bpc >= 9 && bpc <= 16)
+            return frames_pick_16_v2(th, generic, moments, bpc == 16);
         return nullptr;
     }
     if (bpc == 8)

@@ -47,7 +47,7 @@ def _create(lib, **kw):
 
 @pytest.mark.parametrize("kw", [dict(bpc=7), dict(bpc=17), dict(chroma=444), dict(w=2),
                                 dict(h=2), dict(w=40000), dict(max_batch=0),
-                                dict(max_batch=70000), dict(flags=8), dict(flags=4, bpc=16)])
+                                dict(max_batch=70000), dict(flags=8)])
 def test_create_rejects_bad_config(lib, kw):
     assert _create(lib, **kw) == B.IIR_EINVAL
     assert lib.iir_last_error().decode()

@@ -2,9 +2,9 @@
 
 Motion v2 filters the difference prev - cur of consecutive reference luma frames with the same
 separable taps (floor shifts) and sums the absolute values. Every sum equals the oracle's
-(oracle.clip_v2) exactly: small and ragged clips at 8 to 15 bits, every tile height and path,
+(oracle.clip_v2) exactly: small and ragged clips at 8 to 16 bits, every tile height and path,
 streamed frame by frame (the last frame's luma crossing launches), split clips, time chunks, with
-moments, the five named workloads at full size, and a full-size 4K clip at 15 bits.
+moments, the five named workloads at full size, and full-size 4K clips at 15 and 16 bits.
 """
 import sys
 
@@ -38,7 +38,7 @@ SIZES = [(3, 3), (4, 7), (9, 5), (17, 23), (64, 5), (70, 3), (131, 17), (250, 40
          (256, 5), (257, 9), (258, 35), (259, 6), (260, 4), (513, 7), (1283, 723)]
 
 
-@pytest.mark.parametrize("bpc", [8, 10, 12, 15])
+@pytest.mark.parametrize("bpc", [8, 10, 12, 15, 16])
 @pytest.mark.parametrize("w,h", SIZES, ids=[f"{w}x{h}" for w, h in SIZES])
 def test_v2_small(w, h, bpc):
     for i, kind in enumerate(["uniform", "extreme", "checker", "impulse"]):
@@ -71,7 +71,7 @@ def test_v2_each_tile_height_and_path(w, h, th, bpc, monkeypatch):
     _check(sums, hm, want, want_hm, f"{w}x{h} th={th} bpc={bpc}")
 
 
-@pytest.mark.parametrize("bpc", [8, 10, 12])
+@pytest.mark.parametrize("bpc", [8, 10, 12, 16])
 @pytest.mark.parametrize("w,h", [(300, 70), (512, 48), (257, 33)])
 def test_v2_streaming_split_and_chunks(w, h, bpc, monkeypatch):
     """Frame by frame (every frame's previous luma comes from the saved plane of the launch
@@ -104,7 +104,7 @@ def test_v2_streaming_split_and_chunks(w, h, bpc, monkeypatch):
     _check(sums, hm, want[1:], want_hm[1:], "chunks")
 
 
-@pytest.mark.parametrize("bpc", [8, 10, 12, 15])
+@pytest.mark.parametrize("bpc", [8, 10, 12, 15, 16])
 @pytest.mark.parametrize("w,h", [(131, 17), (512, 48), (1283, 723)])
 def test_v2_with_moments(w, h, bpc):
     clip = synth.random_clip(w, h, bpc, 3, seed=3 * w + h, kind="extreme")
@@ -135,10 +135,10 @@ def test_v2_workload_full(name):
     _check(sums, hm, want, want_hm, name)
 
 
-@pytest.mark.parametrize("bpc", [9, 12, 15])
+@pytest.mark.parametrize("bpc", [9, 12, 15, 16])
 @pytest.mark.parametrize("w,h", V2_PATHS, ids=[f"{w}x{h}" for w, h in V2_PATHS])
 def test_v2_deep_tiles(w, h, bpc, monkeypatch):
-    """16-bit storage (9 to 15 bits): one kernel, the 12-row tile on every shape; a forced other
+    """16-bit storage (9 to 16 bits): one kernel, the 12-row tile on every shape; a forced other
     tile height is refused at create."""
     clip = synth.random_clip(w, h, bpc, 3, seed=13 * w + h + bpc, kind="uniform")
     ref, dist = _dev(clip)
@@ -167,3 +167,37 @@ def test_v2_full_4k_15bit():
     _say("v2 4k 15-bit oracle")
     want, want_hm = oracle.clip_v2(ref_np, dist_np, 15)
     _check(sums, hm, want, want_hm, "c6 >> 1")
+
+
+def test_v2_full_4k_16bit():
+    """The 4K 16-bit clip, every frame, in one launch, with motion v2 (halved differences)."""
+    _say("v2 4k 16-bit generate")
+    clip = synth.make_clip("c6")
+    ref, dist = _dev(clip)
+    _say("v2 4k 16-bit gpu")
+    with iir.Context(clip.width, clip.height, 16, max_batch=clip.frames, motion_v2=True) as ctx:
+        sums, hm = ctx.run_clip(ref, dist)
+    _say("v2 4k 16-bit oracle")
+    want, want_hm = oracle.clip_v2(clip.ref, clip.dist, 16)
+    _check(sums, hm, want, want_hm, "c6")
+
+
+def test_v2_16bit_extremes():
+    """Differences of +-65535 everywhere and in checkerboards: every halved sum at its bound."""
+    w, h = 264, 40
+    peak = 65535
+    yy, xx = np.mgrid[0:h, 0:w]
+    chk = (((yy + xx) % 2) * peak).astype(np.uint16)
+    frames_y = np.stack([np.full((h, w), peak, np.uint16), np.zeros((h, w), np.uint16), chk,
+                         peak - chk, np.full((h, w), peak, np.uint16)])
+    hc, wc = (h + 1) // 2, (w + 1) // 2
+    cz = np.zeros((5, hc, wc), np.uint16)
+    ref_np = (frames_y, cz, cz)
+    dist_np = (frames_y[::-1].copy(), cz, cz)
+    ref, dist = iir.upload_planes(ref_np), iir.upload_planes(dist_np)
+    with iir.Context(w, h, 16, max_batch=5, motion_v2=True) as ctx:
+        sums, hm = ctx.run_clip(ref, dist)
+    want, want_hm = oracle.clip_v2(ref_np, dist_np, 16)
+    _check(sums, hm, want, want_hm, "16-bit extremes")
+    # flat frames 65535 then 0: every output is 65535 (d 2^(16 - bpc) at 16 bits)
+    assert int(sums[1, 0]) == w * h * peak

@@ -899,7 +899,8 @@ __device__ __forceinline__ void neighbours(const Tile &T, uint32_t hl, uint32_t 
 // The constants of motion v2 at bit depth bpc: the difference bias 2^bpc in both 16-bit halves,
 // the vertical rounding term 2^(bpc - 1) and the vertical shift bpc. 8 and 10 bits are
 // compile-time; 16-bit storage takes its depth, 9 to 15, from the launch's scale shift
-// (16 - depth); the biased difference of 16-bit samples would need 17 bits.
+// (16 - depth). At 16 bits the biased difference needs 17 bits: that depth has its own kernel
+// variant on halved differences (WideDiff below), which does not use these constants.
 struct V2Depth {
     uint32_t bias, round, vshift;
 };

@@ -178,3 +178,11 @@ def test_scores_moments():
     s = iir.scores(w, h, 8, row, 1)
     assert s["moment"] == [4.0, 7.0, 16.0, 49.0]
     assert iir.scores(w, h, 8, row[:4], 1)["moment"] == [0.0, 0.0, 0.0, 0.0]
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No fallback: without the built library the binding raises, naming how to build it."""
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(ImportError) as e:
+        B.load_library(str(tmp_path / "libiir.so"))
+    assert "build" in str(e.value)

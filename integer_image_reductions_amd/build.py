@@ -4,7 +4,7 @@
     python -m integer_image_reductions_amd.build --asm    # also write the gfx950 assembly
 
 The library lands next to this file so that tests, the smoke check and the benchmark load exactly
-this build.
+the library built here.
 """
 from __future__ import annotations
 

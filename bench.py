@@ -1,7 +1,7 @@
 """Benchmark: frames/s of the integer motion + PSNR sums on 3840x2160 8-bit 4:2:0, one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--moments]
-                    [--motion-v2] [--no-cpu] [--probe]
+                    [--motion-v2] [--no-cpu] [--no-probe]
     python bench.py --workload c3 --traffic-from FETCH.csv WRITE.csv   (host only, see below)
 
 A step is one pass of the whole path over one batch: one iir_submit_clip of the 50-frame clip
@@ -14,6 +14,9 @@ plus the blurred-luma state read and written once per launch) divided by its mea
 measured with HIP events on the context's stream, against the 8 TB/s HBM peak. traffic: HBM bytes
 per launch from the committed rocprofv3 counter summary for this workload, reported only while
 the kernel source still matches the one the counters were taken on.
+ceilings_GBps: the memory ceilings measured by the library's probes (16-byte non-temporal reads,
+writes and copies of a 1 GiB buffer), and roofline.frac_of_read_ceiling the kernel's achieved
+bandwidth against the read ceiling (skip with --no-probe).
 --traffic-from turns two rocprofv3 counter-collection CSVs of `bench.py --probe` runs (one with
 --pmc FETCH_SIZE, one with --pmc WRITE_SIZE) into profiles/frames_kernel_<workload>_traffic.json:
 each counter's mean KiB per main-kernel dispatch, scaled by what the same counter reads for the
@@ -22,7 +25,7 @@ cpu_baseline: the plain C oracle (single thread) over the same frames, on the ho
 --moments runs the same workload with the luma moments summed in the same pass (IIR_FLAG_MOMENTS):
 the bytes moved are the same, the arithmetic per sample grows; its traffic summary is kept under
 the workload name with a _moments suffix. --motion-v2 replaces the blurred-frame SAD by motion v2
-(the filter of the frame difference; 8 and 10 bits), suffix _v2; its state across launches is the
+(the filter of the frame difference; 8 to 16 bits), suffix _v2; its state across launches is the
 last reference luma frame (W H samples read and written once per launch) instead of the blurred
 plane (2 bytes per pixel each way).
 """
@@ -206,7 +209,9 @@ def main():
     ap.add_argument("--motion-v2", action="store_true",
                     help="motion v2 (filter of the frame difference) instead of the blurred SAD")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--probe", action="store_true", help="also measure the memory ceilings")
+    ap.add_argument("--probe", action="store_true",
+                    help="measure the memory ceilings (the default; kept for older commands)")
+    ap.add_argument("--no-probe", action="store_true", help="skip the memory-ceiling probes")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic summary from two counter CSVs and exit")
     args = ap.parse_args()
@@ -293,7 +298,7 @@ def main():
                      "kernel": "frames_kernel", "kernel_us": kernel_ms * 1e3,
                      "algorithmic_bytes_per_launch": alg},
     }
-    if args.probe:
+    if not args.no_probe:
         nbytes = PROBE_BYTES
         a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         b = torch.empty(nbytes, dtype=torch.uint8, device=dev)

@@ -122,3 +122,20 @@ def test_depth_full_4k():
     want, want_hm, last = oracle.clip(clip.ref, clip.dist, clip.bpc, want_last_blur=True)
     _check(sums, hm, want, want_hm, "c6")
     assert np.array_equal(blur, last)
+
+
+def test_depth_full_4k_moments():
+    """The 4K 16-bit clip with the luma moments, every frame, in one launch."""
+    _say("depth 4k moments generate")
+    clip = synth.make_clip("c6")
+    ref, dist = _dev(clip)
+    _say("depth 4k moments gpu")
+    with iir.Context(clip.width, clip.height, clip.bpc, max_batch=clip.frames, moments=True) as ctx:
+        sums, hm = ctx.run_clip(ref, dist)
+    _say("depth 4k moments oracle")
+    want, want_hm = oracle.clip(clip.ref, clip.dist, clip.bpc)
+    _check(sums[:, :4], hm, want, want_hm, "c6 moments")
+    for t in range(0, clip.frames, 7):
+        r1, r2 = oracle.moments(clip.ref[0][t], clip.bpc)
+        d1, d2 = oracle.moments(clip.dist[0][t], clip.bpc)
+        assert [int(v) for v in sums[t, 4:]] == [r1, d1, r2, d2], t

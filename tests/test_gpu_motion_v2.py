@@ -201,3 +201,21 @@ def test_v2_16bit_extremes():
     _check(sums, hm, want, want_hm, "16-bit extremes")
     # flat frames 65535 then 0: every output is 65535 (d 2^(16 - bpc) at 16 bits)
     assert int(sums[1, 0]) == w * h * peak
+
+
+def test_v2_full_4k_16bit_moments():
+    """The 4K 16-bit clip with motion v2 and the luma moments (the generic 16-bit v2 kernel)."""
+    _say("v2 4k 16-bit moments generate")
+    clip = synth.make_clip("c6")
+    ref, dist = _dev(clip)
+    _say("v2 4k 16-bit moments gpu")
+    with iir.Context(clip.width, clip.height, 16, max_batch=clip.frames, motion_v2=True,
+                     moments=True) as ctx:
+        sums, hm = ctx.run_clip(ref, dist)
+    _say("v2 4k 16-bit moments oracle")
+    want, want_hm = oracle.clip_v2(clip.ref, clip.dist, 16)
+    _check(sums[:, :4], hm, want, want_hm, "c6 v2 moments")
+    for t in range(0, clip.frames, 7):
+        r1, r2 = oracle.moments(clip.ref[0][t], 16)
+        d1, d2 = oracle.moments(clip.dist[0][t], 16)
+        assert [int(v) for v in sums[t, 4:]] == [r1, d1, r2, d2], t

@@ -22,6 +22,15 @@ CASES = [
     ("impulse", 64, 20, 8, 4, 5),
 ]
 
+# motion v2 (the filter of the frame difference) at 8, 10, 12 and 16 bits
+V2_CASES = [
+    ("uniform", 9, 7, 8, 3, 11),
+    ("extreme", 17, 9, 10, 3, 12),
+    ("checker", 12, 10, 12, 3, 13),
+    ("uniform", 21, 11, 16, 3, 14),
+    ("extreme", 8, 6, 16, 3, 15),
+]
+
 
 def main():
     out = {"cases": []}
@@ -31,6 +40,13 @@ def main():
         out["cases"].append({"kind": kind, "width": w, "height": h, "bpc": bpc, "frames": f,
                              "seed": seed, "sums": [[int(v) for v in r] for r in sums],
                              "has_motion": [int(v) for v in hm]})
+    out["v2_cases"] = []
+    for kind, w, h, bpc, f, seed in V2_CASES:
+        c = synth.random_clip(w, h, bpc, f, seed, kind)
+        sums, hm = oracle.clip_v2(c.ref, c.dist, bpc)
+        out["v2_cases"].append({"kind": kind, "width": w, "height": h, "bpc": bpc, "frames": f,
+                                "seed": seed, "sums": [[int(v) for v in r] for r in sums],
+                                "has_motion": [int(v) for v in hm]})
     c = synth.make_clip("c1", 3)
     sums, hm = oracle.clip(c.ref, c.dist, 8)
     out["c1_first3"] = {"sums": [[int(v) for v in r] for r in sums],

@@ -17,6 +17,9 @@ the kernel source still matches the one the counters were taken on.
 ceilings_GBps: the memory ceilings measured by the library's probes (16-byte non-temporal reads,
 writes and copies of a 1 GiB buffer), and roofline.frac_of_read_ceiling the kernel's achieved
 bandwidth against the read ceiling (skip with --no-probe).
+streaming: the same frames submitted one pair per call (one launch per frame, the motion state
+crossing launches through the device ring): frames/s and the kernel per launch (skip with
+--no-streaming). Not the headline value, which is the batch of 50.
 --traffic-from turns two rocprofv3 counter-collection CSVs of `bench.py --probe` runs (one with
 --pmc FETCH_SIZE, one with --pmc WRITE_SIZE) into profiles/frames_kernel_<workload>_traffic.json:
 each counter's mean KiB per main-kernel dispatch, scaled by what the same counter reads for the
@@ -198,6 +201,41 @@ def cpu_baseline(clip, max_seconds: float = 20.0, moments: bool = False,
                       f"({dt:.1f} s)"}
 
 
+def streaming(ref, dist, clip, moments: bool, motion_v2: bool, rounds: int = 4) -> dict:
+    """Every frame pair its own submission (one launch per frame; the motion state crosses the
+    launches through the device ring): frames/s over `rounds` passes of the clip, each pass
+    collected once, and the mean kernel time per launch against that launch's algorithmic bytes
+    (one frame pair plus the state read and written)."""
+    import torch
+    import integer_image_reductions_amd as iir
+    F = clip.frames
+    ctx = iir.Context(clip.width, clip.height, clip.bpc, max_batch=F, timing=True,
+                      moments=moments, motion_v2=motion_v2)
+    frames = [ctx.prepare_clip(tuple(p[t:t + 1] for p in ref), tuple(p[t:t + 1] for p in dist))
+              for t in range(F)]
+    for fr in frames:
+        ctx.submit_prepared(fr)
+    ctx.collect()
+    torch.cuda.synchronize()
+    ctx.kernel_stats(reset=True)
+    t0 = time.perf_counter()
+    for _ in range(rounds):
+        for fr in frames:
+            ctx.submit_prepared(fr)
+        ctx.collect()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    launches, total_ms = ctx.kernel_stats()
+    ctx.close()
+    kernel_us = 1e3 * total_ms / max(launches, 1)
+    alg = algorithmic_bytes(clip.width, clip.height, clip.bpc, 1, motion_v2)
+    return {"frames_per_s": rounds * F / dt, "kernel_us_per_launch": kernel_us,
+            "launches": launches, "algorithmic_bytes_per_launch": alg,
+            "achieved_GBps": alg / (kernel_us * 1e-6) / 1e9,
+            "mode": f"one frame pair per submission, {F} submissions then one collect, "
+                    f"{rounds} passes"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +250,8 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="measure the memory ceilings (the default; kept for older commands)")
     ap.add_argument("--no-probe", action="store_true", help="skip the memory-ceiling probes")
+    ap.add_argument("--no-streaming", action="store_true",
+                    help="skip the one-frame-per-submission measurement")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic summary from two counter CSVs and exit")
     args = ap.parse_args()
@@ -311,6 +351,9 @@ def main():
         out["roofline"]["frac_of_read_ceiling"] = achieved / ceil["read"]
         del a, b
     ctx.close()
+    if not args.no_streaming:
+        log("streaming submissions")
+        out["streaming"] = streaming(ref, dist, clip, args.moments, args.motion_v2)
     if not args.no_cpu:
         log("cpu baseline")
         out["cpu_baseline"] = cpu_baseline(clip, moments=args.moments, motion_v2=args.motion_v2)

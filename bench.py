@@ -1,7 +1,7 @@
 """Benchmark: frames/s of the integer motion + PSNR sums on 3840x2160 8-bit 4:2:0, one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--moments]
-                    [--motion-v2] [--no-cpu] [--no-probe]
+                    [--motion-v2] [--no-cpu] [--no-probe] [--streaming]
     python bench.py --workload c3 --traffic-from FETCH.csv WRITE.csv   (host only, see below)
 
 A step is one pass of the whole path over one batch: one iir_submit_clip of the 50-frame clip
@@ -18,8 +18,8 @@ ceilings_GBps: the memory ceilings measured by the library's probes (16-byte non
 writes and copies of a 1 GiB buffer), and roofline.frac_of_read_ceiling the kernel's achieved
 bandwidth against the read ceiling (skip with --no-probe).
 streaming: the same frames submitted one pair per call (one launch per frame, the motion state
-crossing launches through the device ring): frames/s and the kernel per launch (skip with
---no-streaming). Not the headline value, which is the batch of 50.
+crossing launches through the device ring): frames/s and the kernel per launch, with
+--streaming. Not the headline value, which is the batch of 50.
 --traffic-from turns two rocprofv3 counter-collection CSVs of `bench.py --probe` runs (one with
 --pmc FETCH_SIZE, one with --pmc WRITE_SIZE) into profiles/frames_kernel_<workload>_traffic.json:
 each counter's mean KiB per main-kernel dispatch, scaled by what the same counter reads for the
@@ -250,8 +250,8 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="measure the memory ceilings (the default; kept for older commands)")
     ap.add_argument("--no-probe", action="store_true", help="skip the memory-ceiling probes")
-    ap.add_argument("--no-streaming", action="store_true",
-                    help="skip the one-frame-per-submission measurement")
+    ap.add_argument("--streaming", action="store_true",
+                    help="also time one frame pair per submission (one launch per frame)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic summary from two counter CSVs and exit")
     args = ap.parse_args()
@@ -351,7 +351,7 @@ def main():
         out["roofline"]["frac_of_read_ceiling"] = achieved / ceil["read"]
         del a, b
     ctx.close()
-    if not args.no_streaming:
+    if args.streaming:
         log("streaming submissions")
         out["streaming"] = streaming(ref, dist, clip, args.moments, args.motion_v2)
     if not args.no_cpu:

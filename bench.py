@@ -164,6 +164,77 @@ def write_traffic(workload: str, moments: bool, motion_v2: bool, fetch_csv: str,
     return d
 
 
+def launch_distribution(series, warm) -> dict:
+    """Per-launch kernel microseconds of the timed launches: min, median, max, the means of the
+    first and second halves, and the whole series (and the untimed warm-up launches before it),
+    so a transient at the start of a run shows beside the mean."""
+    us = [1e3 * v for v in series]
+    s = sorted(us)
+    n = len(s)
+    med = s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+    h = max(n // 2, 1)
+    return {"min": s[0], "median": med, "max": s[-1],
+            "mean_first_half": sum(us[:h]) / h,
+            "mean_second_half": sum(us[h:]) / max(n - h, 1) if n > 1 else us[0],
+            "series": [round(v, 1) for v in us],
+            "warmup_series": [round(1e3 * v, 1) for v in warm]}
+
+
+def timed_upload(clip, ref, dist) -> dict:
+    """Host-to-device copy of the whole clip (6 planes of every frame pair) from pinned host
+    memory into the device planes the benchmark reads, timed with events on the current stream.
+    It rewrites the same values; it is reported beside the kernel, never in `value`."""
+    import numpy as np
+    import torch
+    src = []
+    for host, devs in ((clip.ref, ref), (clip.dist, dist)):
+        for a, d in zip(host, devs):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            p = torch.from_numpy(a).pin_memory()
+            src.append((p, d))
+    nbytes = sum(p.numel() * p.element_size() for p, _ in src)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for p, d in src:
+        d.copy_(p, non_blocking=True)
+    e1.record(s)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1)
+    return {"bytes": nbytes, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
+            "us_per_frame_pair": 1e3 * ms / clip.frames,
+            "source": "pinned host memory, one copy per plane of the whole clip"}
+
+
+def measure_ceilings(dev) -> dict:
+    """Read, write and copy ceilings (GB/s) of the library's probes over a 1 GiB buffer."""
+    import torch
+    import integer_image_reductions_amd as iir
+    nbytes = PROBE_BYTES
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    ceil = {}
+    for mode, name, mult in ((0, "read", 1), (1, "write", 1), (2, "copy", 2)):
+        ms = iir.probe_bandwidth(mode, a, b, iters=20)
+        ceil[name] = mult * nbytes / (ms * 1e-3) / 1e9
+    del a, b
+    return ceil
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(clip, max_seconds: float = 20.0, moments: bool = False,
                  motion_v2: bool = False, min_seconds: float = 10.0):
     """The oracle over the leading frames of the same clip that fit `max_seconds` (the whole clip
@@ -181,6 +252,17 @@ def cpu_baseline(clip, max_seconds: float = 20.0, moments: bool = False,
                 oracle.moments(c.ref[0][t], clip.bpc)
                 oracle.moments(c.dist[0][t], clip.bpc)
 
+    # one thread on one core: pin this process to a single CPU for the leg, then restore
+    saved = os.sched_getaffinity(0)
+    core = min(saved)
+    os.sched_setaffinity(0, {core})
+    try:
+        return _cpu_leg(clip, run, max_seconds, min_seconds, core, len(saved))
+    finally:
+        os.sched_setaffinity(0, saved)
+
+
+def _cpu_leg(clip, run, max_seconds, min_seconds, core, allowed):
     one = clip.slice(0, 1)
     t0 = time.perf_counter()
     run(one)
@@ -196,6 +278,8 @@ def cpu_baseline(clip, max_seconds: float = 20.0, moments: bool = False,
         run(sub)
     dt = time.perf_counter() - t0
     return {"value": n * passes / dt, "unit": "frames/s", "cores": 1, "kind": "oracle",
+            "pinned_cpu": core, "nproc": os.cpu_count(), "affinity_cpus": allowed,
+            "cpu_model": cpu_model(),
             "sample": f"first {n} of {clip.frames} frame pairs of the same workload, "
                       f"{passes} pass{'es' if passes > 1 else ''}, single-threaded C oracle "
                       f"({dt:.1f} s)"}
@@ -239,8 +323,8 @@ def streaming(ref, dist, clip, moments: bool, motion_v2: bool, rounds: int = 4) 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--moments", action="store_true",
                     help="also sum the luma moments in the same pass (IIR_FLAG_MOMENTS)")
@@ -250,8 +334,10 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="measure the memory ceilings (the default; kept for older commands)")
     ap.add_argument("--no-probe", action="store_true", help="skip the memory-ceiling probes")
-    ap.add_argument("--streaming", action="store_true",
-                    help="also time one frame pair per submission (one launch per frame)")
+    ap.add_argument("--probe-first", action="store_true",
+                    help="measure the memory ceilings before the frames launches, not after")
+    ap.add_argument("--no-streaming", action="store_true",
+                    help="skip timing one frame pair per submission (one launch per frame)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic summary from two counter CSVs and exit")
     args = ap.parse_args()
@@ -286,6 +372,13 @@ def main():
     torch.cuda.synchronize()
     F, W, H, bpc = clip.frames, clip.width, clip.height, clip.bpc
     log("uploaded", F, "frame pairs")
+    upload = timed_upload(clip, ref, dist)
+    log(f"upload {upload['GBps']:.1f} GB/s from pinned host memory")
+
+    ceilings = None
+    if args.probe_first and not args.no_probe:
+        ceilings = measure_ceilings(dev)
+        log("ceilings measured before the frames launches")
 
     # two batches in flight: step k is submitted before step k-1 is collected
     ctx = iir.Context(W, H, bpc, max_batch=2 * F, timing=True, moments=args.moments,
@@ -293,27 +386,34 @@ def main():
     geo = ctx.geometry()
     chunks = ctx.plan_chunks(F)
     clip_dev = ctx.prepare_clip(ref, dist)
-    for _ in range(max(args.warmup, 1)):
+    warm = []
+    for _ in range(args.warmup):
         ctx.submit_prepared(clip_dev)
         ctx.collect(F)
+        warm.append(ctx.kernel_time_ms())
     torch.cuda.synchronize()
     ctx.kernel_stats(reset=True)
+    series = []
     t0 = time.perf_counter()
     ctx.submit_prepared(clip_dev)
     for _ in range(args.steps - 1):
         ctx.submit_prepared(clip_dev)
         ctx.collect(F)
+        series.append(ctx.kernel_time_ms())
     ctx.collect(F)
+    series.append(ctx.kernel_time_ms())
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     launches, total_ms = ctx.kernel_stats()
-    assert launches == args.steps, (launches, args.steps)
+    assert launches == args.steps == len(series), (launches, args.steps, len(series))
     ms_step = 1000.0 * elapsed / args.steps
     frames_per_s = F * args.steps / elapsed
     kernel_ms = total_ms / launches
     alg = algorithmic_bytes(W, H, bpc, F, args.motion_v2)
     achieved = alg / (kernel_ms * 1e-3) / 1e9
-    log(f"kernel {kernel_ms * 1e3:.1f} us/launch (mean of {launches}), "
+    dist_us = launch_distribution(series, warm)
+    log(f"kernel {kernel_ms * 1e3:.1f} us/launch (mean of {launches}; median "
+        f"{dist_us['median']:.1f}, min {dist_us['min']:.1f}, max {dist_us['max']:.1f}), "
         f"step {ms_step * 1e3:.1f} us, {achieved:.0f} GB/s")
 
     out = {
@@ -336,22 +436,18 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(wl),
                      "kernel": "frames_kernel", "kernel_us": kernel_ms * 1e3,
-                     "algorithmic_bytes_per_launch": alg},
+                     "algorithmic_bytes_per_launch": alg,
+                     "frac_of_median_launch": alg / (dist_us["median"] * 1e-6) / 1e9
+                     / HBM_PEAK_GBS},
+        "launch_us": dist_us,
+        "upload": upload,
     }
     if not args.no_probe:
-        nbytes = PROBE_BYTES
-        a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        a.fill_(1)
-        ceil = {}
-        for mode, name, mult in ((0, "read", 1), (1, "write", 1), (2, "copy", 2)):
-            ms = iir.probe_bandwidth(mode, a, b, iters=20)
-            ceil[name] = mult * nbytes / (ms * 1e-3) / 1e9
+        ceil = ceilings if ceilings is not None else measure_ceilings(dev)
         out["ceilings_GBps"] = ceil
         out["roofline"]["frac_of_read_ceiling"] = achieved / ceil["read"]
-        del a, b
     ctx.close()
-    if args.streaming:
+    if not args.no_streaming:
         log("streaming submissions")
         out["streaming"] = streaming(ref, dist, clip, args.moments, args.motion_v2)
     if not args.no_cpu:

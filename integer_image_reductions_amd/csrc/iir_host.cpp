@@ -124,6 +124,7 @@ struct iir_ctx {
     int sub_count = 0;   // pending submissions
     int slot_head = 0;   // next free frame slot
     int pending = 0;     // frames submitted and not yet returned
+    bool broken = false;              // a submission's completion event could not be recorded
     bool has_prev = false;            // the next frame has a previous blurred frame
     bool any_frame = false;           // ring[ring_cur] is valid
     // kernel timing of collected submissions (IIR_FLAG_TIMING)
@@ -315,6 +316,8 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
 {
     if (!c)
         return fail(IIR_EINVAL, "context is NULL");
+    if (c->broken)
+        return fail(IIR_ESTATE, "an earlier submission's event failed; destroy the context");
     if (n < 1 || n > c->cfg.max_batch)
         return fail(IIR_EINVAL, "nframes %d outside 1..max_batch (%d)", n, c->cfg.max_batch);
     int rc = check_frames(c, ref, dist, n);
@@ -383,8 +386,8 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
                           !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile),
                           c->moments, c->v2, a, c->stream, timing ? sub.k0 : nullptr,
                           timing ? sub.k1 : nullptr));
-    if (!timing)
-        HIP_TRY(hipEventRecord(sub.done, c->stream));
+    // the launch is enqueued: the device state it leaves behind (the other slot buffer to clear,
+    // the ring to read next) is committed before anything else can fail
     sub.first = first;
     sub.n = n;
     sub.taken = 0;
@@ -398,6 +401,14 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     c->ring_cur ^= 1;
     c->has_prev = true;
     c->any_frame = true;
+    if (!timing) {
+        const hipError_t e = hipEventRecord(sub.done, c->stream);
+        if (e != hipSuccess) {
+            // the submission is queued but cannot be waited for: nothing more can be collected
+            c->broken = true;
+            return fail_hip(e, "hipEventRecord");
+        }
+    }
     return IIR_OK;
 }
 
@@ -521,6 +532,8 @@ IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_o
     if (!ctx || !out || !n_out || max < 0)
         return fail(IIR_EINVAL, "bad collect arguments");
     *n_out = 0;
+    if (ctx->broken)
+        return fail(IIR_ESTATE, "an earlier submission's event failed; destroy the context");
     const int n = std::min(max, ctx->pending);
     if (n == 0)
         return IIR_OK;

@@ -269,6 +269,28 @@ IIR_API int iir_plan_chunks(const iir_ctx *ctx, int32_t nframes, int32_t *chunks
 IIR_API int iir_probe_bandwidth(int32_t device, void *hip_stream, int32_t mode, const void *src,
                                 void *dst, int64_t bytes, int32_t iters, float *ms);
 
+/*
+ * For callers that cannot allocate device memory (code running under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): iir_run_clip without a context. Computes the
+ * sums of nframes consecutive frame pairs of a standalone clip -- frame 0 has no previous frame
+ * (has_motion 0), exactly as the first iir_run_clip after iir_create -- and writes them to `out`
+ * (nframes entries, host or device memory), then waits for the stream. cfg as for iir_create
+ * (max_batch is not used; IIR_FLAG_TIMING is ignored); ref/dist as for iir_submit_clip. Enqueues
+ * on hip_stream (NULL: the null stream) of HIP device `device`: a clearing kernel, the frames
+ * kernel, a folding kernel and one copy into `out`.
+ *
+ * Calls no hipMalloc, hipFree or other allocating routine: its working memory is a fixed array of
+ * about 1.2 MB in the library's device data, one copy per GPU, kept until the process ends, which
+ * bounds a call to IIR_STATIC_MAX_FRAMES frames (IIR_EINVAL beyond). The frame size is not
+ * bounded by it. Every call on one GPU uses that GPU's array: calls that overlap on one GPU (two
+ * host threads, or two streams in flight) race and give wrong sums; serialise them. Errors:
+ * IIR_EINVAL, IIR_ENODEV, IIR_EDEVICE.
+ */
+#define IIR_STATIC_MAX_FRAMES 256
+IIR_API int iir_run_clip_static(const iir_config *cfg, int32_t device, void *hip_stream,
+                                const iir_frame *ref, const iir_frame *dist, int32_t nframes,
+                                iir_result *out);
+
 /* Release everything the context owns. Waits for its pending work first. NULL is a no-op. */
 IIR_API void iir_destroy(iir_ctx *ctx);
 

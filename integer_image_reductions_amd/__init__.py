@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     PLANE_ALIGN,
     SIGNATURES,
+    STATIC_MAX_FRAMES,
     aggregate,
     motion2,
     Context,
@@ -18,6 +19,7 @@ from .binding import (  # noqa: F401
     frame_of,
     load_library,
     probe_bandwidth,
+    run_clip_static,
     sample_dtype,
     scores,
     upload_planes,

@@ -91,6 +91,8 @@ SIGNATURES = [
     ("iir_plan_chunks", [c_vp, c_i32, ctypes.POINTER(c_i32)], ctypes.c_int),
     ("iir_probe_bandwidth", [c_i32, c_vp, c_i32, c_vp, c_vp, c_i64, c_i32,
                              ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
+    ("iir_run_clip_static", [ctypes.POINTER(Config), c_i32, c_vp, ctypes.POINTER(Frame),
+                             ctypes.POINTER(Frame), c_i32, ctypes.POINTER(Result)], ctypes.c_int),
     ("iir_destroy", [c_vp], None),
     ("iir_strerror", [ctypes.c_int], ctypes.c_char_p),
     ("iir_last_error", [], ctypes.c_char_p),
@@ -337,6 +339,48 @@ class Context:
         ms = ctypes.c_float()
         _check(self._lib.iir_kernel_time(self._h, ctypes.byref(ms)), "iir_kernel_time")
         return ms.value
+
+
+STATIC_MAX_FRAMES = 256  # IIR_STATIC_MAX_FRAMES
+
+
+def run_clip_static(width: int, height: int, bpc: int, ref, dist, moments: bool = False,
+                    motion_v2: bool = False, device=None, stream=None):
+    """iir_run_clip_static: the sums of a standalone clip with no context (the library allocates
+    nothing). ref and dist are (Y, U, V) device tensors of shape (F, h, w), or lists of per-frame
+    (Y, U, V) 2-D tensors (any addresses); same return as Context.collect()."""
+    torch = _torch()
+    lib = load_library()
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    cfg = Config(width, height, bpc, IIR_CHROMA_420, 1,
+                 (IIR_FLAG_MOMENTS if moments else 0) | (IIR_FLAG_MOTION_V2 if motion_v2 else 0))
+    if isinstance(ref, (list, tuple)) and isinstance(ref[0], (list, tuple)):
+        n = len(ref)
+        fr, fd = (Frame * n)(), (Frame * n)()
+        for t in range(n):
+            fr[t] = frame_of(ref[t], width, height)
+            fd[t] = frame_of(dist[t], width, height)
+    else:
+        n = ref[0].shape[0]
+        fr, fd = (Frame * n)(), (Frame * n)()
+        for t in range(n):
+            fr[t] = frame_of([p[t] for p in ref], width, height)
+            fd[t] = frame_of([p[t] for p in dist], width, height)
+    out = (Result * n)()
+    _check(lib.iir_run_clip_static(ctypes.byref(cfg), dev.index, c_vp(s.cuda_stream), fr, fd, n,
+                                   out), "iir_run_clip_static")
+    cols = 8 if moments else 4
+    sums = np.zeros((n, cols), dtype=np.uint64)
+    hm = np.zeros(n, dtype=np.int32)
+    for i in range(n):
+        r = out[i]
+        row = [r.sad, r.sse[0], r.sse[1], r.sse[2]]
+        if moments:
+            row += list(r.moment)
+        sums[i] = row
+        hm[i] = r.has_motion
+    return sums, hm
 
 
 def _result(row, has_motion) -> Result:

@@ -1738,7 +1738,7 @@ frames_kernel(const KernelArgs a)
                                                              stage);
         // the state stores drain while the group count is in flight
         unsigned int arrived;
-        if (T.chunk == a.chunks - 1) {
+        if (T.chunk == a.chunks - 1 && a.ring_out) {
             store_saved<BPC, TH>(a, T, s, prev);
             arrived = count_arrival<TH>(a, lane);
         } else {
@@ -1775,7 +1775,7 @@ frames_kernel(const KernelArgs a)
         // non-temporal, so the launch's end does not find 16 MB (at 4K) of them dirty in L2
         // (measured 2.6 us per 4K 8-bit launch)
         unsigned int arrived;
-        if (T.chunk == a.chunks - 1) {
+        if (T.chunk == a.chunks - 1 && a.ring_out) {
             unsigned long long *rout = reinterpret_cast<unsigned long long *>(a.ring_out);
 #pragma unroll
             for (int i = 0; i < TH; ++i)

@@ -258,6 +258,36 @@ int plan_chunks(const iir_ctx *c, int nframes)
     return (nframes + len - 1) / len;
 }
 
+// The launch geometry of a configuration on a device with `cus` compute units: sample size,
+// chroma size, tile columns and rows, the time-chunk policy. Touches no device memory.
+int setup_geometry(iir_ctx *c, const iir_config *cfg, int device, int cus)
+{
+    c->cfg = *cfg;
+    c->device = device;
+    c->bps = cfg->bpc == 8 ? 1 : 2;
+    c->Wc = (cfg->width + 1) / 2;
+    c->Hc = (cfg->height + 1) / 2;
+    c->moments = (cfg->flags & IIR_FLAG_MOMENTS) != 0;
+    c->v2 = (cfg->flags & IIR_FLAG_MOTION_V2) != 0;
+    c->nsums = c->moments ? kMaxSums : kSums;
+    choose_columns(c);
+    const int forced_rows = env_int("IIR_ROWS_PER_TILE", 0, 0, 64);
+    c->rows_per_tile = choose_rows(c, cus, forced_rows);
+    if (c->rows_per_tile == 0)
+        return fail(IIR_EINVAL, "no frames kernel for this configuration (rows per tile %d)",
+                    forced_rows);
+    c->row_tiles = (cfg->height + c->rows_per_tile - 1) / c->rows_per_tile;
+    c->tiles = c->strips * c->row_tiles;
+    c->target_waves = env_int("IIR_TARGET_WAVES", 4 * cus, 1, 1 << 20);
+    c->min_chunk = env_int("IIR_MIN_CHUNK", 4, 1, 65536);
+    c->max_chunks = plan_chunks(c, cfg->max_batch);
+    // launch geometry must fit a 1-D grid ("ADR-1380", Consequences: an oversized launch failed
+    // with an invalid-value error at 1080p and 4K; here every shape is checked once, up front)
+    if ((int64_t)c->tiles * c->max_chunks > INT32_MAX / kWave)
+        return fail(IIR_EINVAL, "frame too large for one grid");
+    return IIR_OK;
+}
+
 void release(iir_ctx *c)
 {
     if (!c)
@@ -312,6 +342,52 @@ int reserve_slots(const iir_ctx *c, int n)
     return head + n <= tail ? head : -1;
 }
 
+// The frame part of one launch's arguments: plane pointers of n frame pairs (a base and a
+// per-frame stride when every plane advances uniformly, else a descriptor table written at
+// table_host and copied to table_dev on the context's stream), pitches, readable spans, the
+// geometry and the time chunks. The state, sum and publish pointers are the caller's to set.
+int frame_args(const iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n,
+               FramePtrs *table_host, FramePtrs *table_dev, KernelArgs &a)
+{
+    // uniform frame stride: pointers travel in the kernel arguments
+    bool uniform = true;
+    for (int k = 0; k < 6 && uniform; ++k) {
+        const uint8_t *p0 = plane_ptr(ref, dist, 0, k);
+        const int64_t step = n > 1 ? plane_ptr(ref, dist, 1, k) - p0 : 0;
+        for (int t = 2; t < n && uniform; ++t)
+            uniform = plane_ptr(ref, dist, t, k) == p0 + (int64_t)t * step;
+        a.base[k] = p0;
+        a.fstride[k] = step;
+    }
+    if (!uniform) {
+        for (int t = 0; t < n; ++t)
+            for (int k = 0; k < 6; ++k)
+                table_host[t].p[k] = plane_ptr(ref, dist, t, k);
+        HIP_TRY(hipMemcpyAsync(table_dev, table_host, sizeof(FramePtrs) * n,
+                               hipMemcpyHostToDevice, c->stream));
+        a.table = table_dev;
+    }
+    for (int k = 0; k < 3; ++k) {
+        const int64_t rows = k == 0 ? c->cfg.height : c->Hc;
+        a.pitch[k] = (int32_t)ref[0].plane[k].pitch;
+        a.pitch[k + 3] = (int32_t)dist[0].plane[k].pitch;
+        a.span[k] = (uint32_t)(rows * ref[0].plane[k].pitch);
+        a.span[k + 3] = (uint32_t)(rows * dist[0].plane[k].pitch);
+    }
+    a.W = c->cfg.width;
+    a.H = c->cfg.height;
+    a.Wc = c->Wc;
+    a.Hc = c->Hc;
+    a.strips = c->strips;
+    a.row_tiles = c->row_tiles;
+    a.tiles = c->tiles;
+    a.nframes = n;
+    a.chunks = plan_chunks(c, n);
+    a.chunk_len = (n + a.chunks - 1) / a.chunks;
+    a.shift = c->cfg.bpc == 8 ? 0 : 16 - c->cfg.bpc;
+    return IIR_OK;
+}
+
 int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
 {
     if (!c)
@@ -332,32 +408,9 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
         return fail_hip(ds.err, "hipSetDevice");
 
     KernelArgs a{};
-    // uniform frame stride: pointers travel in the kernel arguments
-    bool uniform = true;
-    for (int k = 0; k < 6 && uniform; ++k) {
-        const uint8_t *p0 = plane_ptr(ref, dist, 0, k);
-        const int64_t step = n > 1 ? plane_ptr(ref, dist, 1, k) - p0 : 0;
-        for (int t = 2; t < n && uniform; ++t)
-            uniform = plane_ptr(ref, dist, t, k) == p0 + (int64_t)t * step;
-        a.base[k] = p0;
-        a.fstride[k] = step;
-    }
-    if (!uniform) {
-        FramePtrs *th = c->table_host + first;
-        for (int t = 0; t < n; ++t)
-            for (int k = 0; k < 6; ++k)
-                th[t].p[k] = plane_ptr(ref, dist, t, k);
-        HIP_TRY(hipMemcpyAsync(c->table_dev + first, th, sizeof(FramePtrs) * n,
-                               hipMemcpyHostToDevice, c->stream));
-        a.table = c->table_dev + first;
-    }
-    for (int k = 0; k < 3; ++k) {
-        const int64_t rows = k == 0 ? c->cfg.height : c->Hc;
-        a.pitch[k] = (int32_t)ref[0].plane[k].pitch;
-        a.pitch[k + 3] = (int32_t)dist[0].plane[k].pitch;
-        a.span[k] = (uint32_t)(rows * ref[0].plane[k].pitch);
-        a.span[k + 3] = (uint32_t)(rows * dist[0].plane[k].pitch);
-    }
+    rc = frame_args(c, ref, dist, n, c->table_host + first, c->table_dev + first, a);
+    if (rc != IIR_OK)
+        return rc;
     a.ring_in = c->ring[c->ring_cur];
     a.ring_out = c->ring[c->ring_cur ^ 1];
     a.sums = c->sums + (size_t)c->sums_cur * c->sums_n;
@@ -365,18 +418,7 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     a.zero_n = c->sums_dirty;
     a.publish = c->host_sums_dev + (size_t)first * c->nsums * kSumGroups;
     a.arrivals = c->arrivals;
-    a.W = c->cfg.width;
-    a.H = c->cfg.height;
-    a.Wc = c->Wc;
-    a.Hc = c->Hc;
-    a.strips = c->strips;
-    a.row_tiles = c->row_tiles;
-    a.tiles = c->tiles;
-    a.nframes = n;
-    a.chunks = plan_chunks(c, n);
-    a.chunk_len = (n + a.chunks - 1) / a.chunks;
     a.has_prev = c->has_prev ? 1 : 0;
-    a.shift = c->cfg.bpc == 8 ? 0 : 16 - c->cfg.bpc;
 
     const bool timing = (c->cfg.flags & IIR_FLAG_TIMING) != 0;
     iir_ctx::Sub &sub = c->subs[(c->sub_head + c->sub_count) % iir_ctx::kMaxPending];
@@ -440,34 +482,12 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     iir_ctx *c = new (std::nothrow) iir_ctx;
     if (!c)
         return fail(IIR_ENOMEM, "host allocation failed");
-    c->cfg = *cfg;
-    c->device = device;
-    c->stream = static_cast<hipStream_t>(hip_stream);
-    c->bps = cfg->bpc == 8 ? 1 : 2;
-    c->Wc = (cfg->width + 1) / 2;
-    c->Hc = (cfg->height + 1) / 2;
-    c->moments = (cfg->flags & IIR_FLAG_MOMENTS) != 0;
-    c->v2 = (cfg->flags & IIR_FLAG_MOTION_V2) != 0;
-    c->nsums = c->moments ? kMaxSums : kSums;
-    choose_columns(c);
-    const int forced_rows = env_int("IIR_ROWS_PER_TILE", 0, 0, 64);
-    c->rows_per_tile = choose_rows(c, prop.multiProcessorCount, forced_rows);
-    if (c->rows_per_tile == 0) {
+    rc = setup_geometry(c, cfg, device, prop.multiProcessorCount);
+    if (rc != IIR_OK) {
         delete c;
-        return fail(IIR_EINVAL, "no frames kernel for this configuration (rows per tile %d)",
-                    forced_rows);
+        return rc;
     }
-    c->row_tiles = (cfg->height + c->rows_per_tile - 1) / c->rows_per_tile;
-    c->tiles = c->strips * c->row_tiles;
-    c->target_waves = env_int("IIR_TARGET_WAVES", 4 * prop.multiProcessorCount, 1, 1 << 20);
-    c->min_chunk = env_int("IIR_MIN_CHUNK", 4, 1, 65536);
-    c->max_chunks = plan_chunks(c, cfg->max_batch);
-    // launch geometry must fit a 1-D grid ("ADR-1380", Consequences: an oversized launch failed
-    // with an invalid-value error at 1080p and 4K; here every shape is checked once, up front)
-    if ((int64_t)c->tiles * c->max_chunks > INT32_MAX / kWave) {
-        release(c);
-        return fail(IIR_EINVAL, "frame too large for one grid");
-    }
+    c->stream = static_cast<hipStream_t>(hip_stream);
     c->sums_n = (int64_t)cfg->max_batch * c->nsums * kSumSlots;
 
     const size_t ring_bytes = (size_t)c->tiles * c->rows_per_tile * kWave * sizeof(uint2);
@@ -610,6 +630,74 @@ IIR_API int iir_run_clip(iir_ctx *ctx, const iir_frame *ref, const iir_frame *di
     if (rc == IIR_OK && got != nframes)
         return fail(IIR_EDEVICE, "collected %d of %d results", got, nframes);
     return rc;
+}
+
+IIR_API int iir_run_clip_static(const iir_config *cfg, int32_t device, void *hip_stream,
+                                const iir_frame *ref, const iir_frame *dist, int32_t nframes,
+                                iir_result *out)
+{
+    if (!out)
+        return fail(IIR_EINVAL, "out is NULL");
+    int rc = check_config(cfg);
+    if (rc != IIR_OK)
+        return rc;
+    if (nframes < 1 || nframes > kStaticMaxFrames)
+        return fail(IIR_EINVAL, "nframes %d outside 1..%d (the static working memory's bound)",
+                    nframes, kStaticMaxFrames);
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0)
+        return fail(IIR_ENODEV, "no HIP device visible");
+    if (device < 0 || device >= count)
+        return fail(IIR_ENODEV, "device %d not in [0, %d)", device, count);
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, device));
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(IIR_ENODEV, "device %d is %s; this library is built for gfx950", device,
+                    prop.gcnArchName);
+    DeviceScope ds(device);
+    if (ds.err != hipSuccess)
+        return fail_hip(ds.err, "hipSetDevice");
+
+    // geometry only: this context lives on the stack and owns no device or host memory
+    iir_ctx c;
+    iir_config one = *cfg;
+    one.max_batch = nframes;
+    rc = setup_geometry(&c, &one, device, prop.multiProcessorCount);
+    if (rc != IIR_OK)
+        return rc;
+    c.stream = static_cast<hipStream_t>(hip_stream);
+    rc = check_frames(&c, ref, dist, nframes);
+    if (rc != IIR_OK)
+        return rc;
+
+    StaticScratch s;
+    HIP_TRY(static_scratch(device, &s));
+    // a non-uniformly strided clip's plane pointers go through this stack table (the stream is
+    // synchronised before it goes out of scope)
+    FramePtrs table[kStaticMaxFrames];
+    KernelArgs a{};
+    rc = frame_args(&c, ref, dist, nframes, table, s.table, a);
+    if (rc != IIR_OK)
+        return rc;
+    a.ring_in = nullptr;
+    a.ring_out = nullptr;
+    a.has_prev = 0;
+    a.sums = s.sums;
+    a.zero = nullptr;
+    a.zero_n = 0;
+    a.publish = s.publish;
+    a.arrivals = s.arrivals;
+    // the partial slots and arrival counters start at zero; the array keeps the last call's values
+    HIP_TRY(launch_clear(s.sums, (int64_t)nframes * c.nsums * kSumSlots, s.arrivals, c.stream));
+    HIP_TRY(launch_frames(one.bpc, c.rows_per_tile,
+                          !fast_path_ok(one.width, one.height, c.rows_per_tile), c.moments, c.v2,
+                          a, c.stream));
+    HIP_TRY(launch_fold(s.publish, nframes, c.nsums, std::min(a.tiles * a.chunks, kSumGroups),
+                        s.results, c.stream));
+    HIP_TRY(hipMemcpyAsync(out, s.results, sizeof(iir_result) * nframes, hipMemcpyDefault,
+                           c.stream));
+    HIP_TRY(hipStreamSynchronize(c.stream));
+    return IIR_OK;
 }
 
 IIR_API int iir_scores_of(const iir_config *cfg, const iir_result *r, iir_scores *s)

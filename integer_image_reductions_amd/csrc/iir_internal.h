@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "iir.h"
+
 namespace iir {
 
 constexpr int kWave = 64;          // CDNA wavefront; one wavefront is one workgroup
@@ -36,7 +38,7 @@ struct KernelArgs {
     // launch's last frame (written); tiled: uint2 at [(tile * TH + row) * kWave + lane], TH the
     // launch's rows per tile
     const uint32_t *ring_in;
-    uint32_t *ring_out;
+    uint32_t *ring_out;  // null: the launch keeps no state (its last frame is not stored)
     // per-frame partial sums [nframes][S][kSumSlots], S = kSums, or kMaxSums when the launch
     // also sums the luma moments; zero at launch; the last workgroup of each slot group folds
     // the group's slots and writes its totals to `publish`
@@ -83,5 +85,27 @@ hipError_t launch_frames(int bpc, int th, bool generic, bool moments, bool v2,
 hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
                          int strips, int th, hipStream_t stream);
 hipError_t launch_probe(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream);
+
+// Working memory of the entry point that allocates nothing (iir_run_clip_static): one
+// file-scope device array per GPU, holding the regions below at 256-byte boundaries. The clip
+// runs standalone (no previous frame, no state kept), so no region depends on the frame size.
+constexpr int kStaticMaxFrames = IIR_STATIC_MAX_FRAMES;
+struct StaticScratch {
+    unsigned long long *sums;     // [frames][kMaxSums][kSumSlots] partial slots
+    unsigned long long *publish;  // [frames][kMaxSums][kSumGroups] group totals
+    iir_result *results;          // [frames] folded results
+    FramePtrs *table;             // [frames] plane pointers of a non-uniformly strided clip
+    unsigned int *arrivals;       // [kSumGroups] finished-workgroup counters
+};
+// The scratch regions as addressed on the current device (looked up once per device).
+hipError_t static_scratch(int device, StaticScratch *out);
+// Zero words [0, n) of `sums` and the kSumGroups arrival counters (a fill kernel, not a memset,
+// so the clearing is an ordinary kernel node for callers that capture the stream).
+hipError_t launch_clear(unsigned long long *sums, int64_t n, unsigned int *arrivals,
+                        hipStream_t stream);
+// Fold each frame's `groups` group totals of `nsums` sums into iir_result rows (has_motion = 1
+// for every frame after the first; frame 0 has none).
+hipError_t launch_fold(const unsigned long long *publish, int nframes, int nsums, int groups,
+                       iir_result *out, hipStream_t stream);
 
 }  // namespace iir

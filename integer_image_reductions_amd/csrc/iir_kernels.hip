@@ -4,6 +4,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "iir_internal.h"
 
@@ -90,7 +91,115 @@ __global__ __launch_bounds__(256) void probe_copy(const probe_v4 *src, probe_v4 
         dst[i] = src[i];
 }
 
+
+// Zero n 64-bit words and the group arrival counters.
+__global__ __launch_bounds__(256) void clear_kernel(unsigned long long *p, int64_t n,
+                                                     unsigned int *arrivals)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t i = i0; i < n; i += stride)
+        p[i] = 0ull;
+    if (i0 < kSumGroups)
+        arrivals[i0] = 0u;
+}
+
+// One thread per frame: the sum of its `groups` group totals of every sum, as an iir_result.
+__global__ __launch_bounds__(256) void fold_kernel(const unsigned long long *publish, int nframes,
+                                                    int nsums, int groups, iir_result *out)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nframes)
+        return;
+    const unsigned long long *g = publish + (size_t)t * nsums * kSumGroups;
+    unsigned long long v[kMaxSums] = {};
+    for (int k = 0; k < nsums; ++k)
+        for (int j = 0; j < groups; ++j)
+            v[k] += g[k * kSumGroups + j];
+    iir_result r;
+    r.has_motion = t > 0 ? 1 : 0;
+    r.sad = t > 0 ? v[0] : 0ull;
+    for (int c = 0; c < 3; ++c)
+        r.sse[c] = v[1 + c];
+    for (int k = 0; k < kMoments; ++k)
+        r.moment[k] = nsums > kSums ? v[kSums + k] : 0ull;
+    r.reserved = 0;
+    out[t] = r;
+}
+
+// The working memory of iir_run_clip_static, in the library's own device data: each GPU the
+// library runs on holds one copy until the process ends. Region sizes for kStaticMaxFrames frames,
+// each rounded up to 256 bytes.
+constexpr size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+constexpr size_t kScrSums = round256(sizeof(unsigned long long) * kStaticMaxFrames * kMaxSums *
+                                     kSumSlots);
+constexpr size_t kScrPublish = round256(sizeof(unsigned long long) * kStaticMaxFrames * kMaxSums *
+                                        kSumGroups);
+constexpr size_t kScrResults = round256(sizeof(iir_result) * kStaticMaxFrames);
+constexpr size_t kScrTable = round256(sizeof(FramePtrs) * kStaticMaxFrames);
+constexpr size_t kScrArrivals = round256(sizeof(unsigned int) * kSumGroups);
+constexpr size_t kScratchBytes = kScrSums + kScrPublish + kScrResults + kScrTable + kScrArrivals;
+static_assert(kScratchBytes < (size_t)2 << 20, "the static working memory stays modest");
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 }  // namespace
+
+// The array's address on the current device. In host code `scratch` names a host-side stand-in,
+// not device memory, so the device address is looked up once per device (with that device
+// current) and only that address is handed to kernels and copies.
+hipError_t static_scratch(int device, StaticScratch *out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex lock;
+    static void *addr[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    void *p = nullptr;
+    {
+        std::lock_guard<std::mutex> g(lock);
+        if (!addr[device]) {
+            void *q = nullptr;
+            const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return e;
+            if (!q)
+                return hipErrorInvalidSymbol;
+            addr[device] = q;
+        }
+        p = addr[device];
+    }
+    unsigned char *b = static_cast<unsigned char *>(p);
+    out->sums = reinterpret_cast<unsigned long long *>(b);
+    b += kScrSums;
+    out->publish = reinterpret_cast<unsigned long long *>(b);
+    b += kScrPublish;
+    out->results = reinterpret_cast<iir_result *>(b);
+    b += kScrResults;
+    out->table = reinterpret_cast<FramePtrs *>(b);
+    b += kScrTable;
+    out->arrivals = reinterpret_cast<unsigned int *>(b);
+    return hipSuccess;
+}
+
+hipError_t launch_clear(unsigned long long *sums, int64_t n, unsigned int *arrivals,
+                        hipStream_t stream)
+{
+    const unsigned blocks =
+        (unsigned)std::min<int64_t>(std::max<int64_t>((n + 255) / 256, 1), 1024);
+    hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(256), 0, stream, sums, n, arrivals);
+    return hipGetLastError();
+}
+
+hipError_t launch_fold(const unsigned long long *publish, int nframes, int nsums, int groups,
+                       iir_result *out, hipStream_t stream)
+{
+    const unsigned blocks = (unsigned)((nframes + 255) / 256);
+    hipLaunchKernelGGL(fold_kernel, dim3(blocks), dim3(256), 0, stream, publish, nframes, nsums,
+                       groups, out);
+    return hipGetLastError();
+}
+
 
 // 8-bit and 10-bit samples have kernels of their own; every other depth up to 16 bits takes the
 // 16-bit one with the launch's scale shift

@@ -186,3 +186,17 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     with pytest.raises(ImportError) as e:
         B.load_library(str(tmp_path / "libiir.so"))
     assert "build" in str(e.value)
+
+
+def test_static_rejects_before_device_work(lib):
+    # argument errors are found on the host before any device is touched
+    cfg = B.Config(64, 32, 8, B.IIR_CHROMA_420, 1, 0)
+    f = (B.Frame * 1)()
+    out = (B.Result * 1)()
+    assert lib.iir_run_clip_static(ctypes.byref(cfg), 0, None, f, f, 1, None) == B.IIR_EINVAL
+    assert lib.iir_run_clip_static(None, 0, None, f, f, 1, out) == B.IIR_EINVAL
+    for n in (0, -1, B.STATIC_MAX_FRAMES + 1):
+        assert lib.iir_run_clip_static(ctypes.byref(cfg), 0, None, f, f, n, out) == B.IIR_EINVAL
+        assert str(B.STATIC_MAX_FRAMES) in lib.iir_last_error().decode()
+    bad = B.Config(64, 32, 7, B.IIR_CHROMA_420, 1, 0)
+    assert lib.iir_run_clip_static(ctypes.byref(bad), 0, None, f, f, 1, out) == B.IIR_EINVAL

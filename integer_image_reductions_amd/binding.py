@@ -282,17 +282,7 @@ class Context:
         return n
 
     def _unpack(self, out, n):
-        cols = 8 if self.moments else 4
-        sums = np.zeros((n, cols), dtype=np.uint64)
-        hm = np.zeros(n, dtype=np.int32)
-        for i in range(n):
-            r = out[i]
-            row = [r.sad, r.sse[0], r.sse[1], r.sse[2]]
-            if self.moments:
-                row += list(r.moment)
-            sums[i] = row
-            hm[i] = r.has_motion
-        return sums, hm
+        return _unpack_results(out, n, self.moments)
 
     def collect(self, max_results: int = 1 << 20):
         """Wait for pending work; returns (sums (n, 4) uint64 [SAD, SSE_Y, SSE_U, SSE_V] -- (n, 8)
@@ -341,6 +331,19 @@ class Context:
         return ms.value
 
 
+# iir_result as a numpy record (the C layout: eight u64, then two i32)
+RESULT_DTYPE = np.dtype([("sad", "<u8"), ("sse", "<u8", (3,)), ("moment", "<u8", (4,)),
+                         ("has_motion", "<i4"), ("reserved", "<i4")])
+
+
+def _unpack_results(out, n: int, moments: bool):
+    """(sums (n, 4 or 8) uint64, has_motion (n,) int32) from the first n iir_result of `out`."""
+    assert ctypes.sizeof(Result) == RESULT_DTYPE.itemsize
+    rec = np.frombuffer(out, dtype=RESULT_DTYPE, count=n)
+    cols = [rec["sad"][:, None], rec["sse"]] + ([rec["moment"]] if moments else [])
+    return np.concatenate(cols, axis=1).astype(np.uint64), rec["has_motion"].astype(np.int32)
+
+
 STATIC_MAX_FRAMES = 256  # IIR_STATIC_MAX_FRAMES
 
 
@@ -370,17 +373,7 @@ def run_clip_static(width: int, height: int, bpc: int, ref, dist, moments: bool 
     out = (Result * n)()
     _check(lib.iir_run_clip_static(ctypes.byref(cfg), dev.index, c_vp(s.cuda_stream), fr, fd, n,
                                    out), "iir_run_clip_static")
-    cols = 8 if moments else 4
-    sums = np.zeros((n, cols), dtype=np.uint64)
-    hm = np.zeros(n, dtype=np.int32)
-    for i in range(n):
-        r = out[i]
-        row = [r.sad, r.sse[0], r.sse[1], r.sse[2]]
-        if moments:
-            row += list(r.moment)
-        sums[i] = row
-        hm[i] = r.has_motion
-    return sums, hm
+    return _unpack_results(out, n, moments)
 
 
 def _result(row, has_motion) -> Result:

@@ -82,8 +82,9 @@ struct iir_ctx {
     int Wc = 0, Hc = 0;
     int lanes_out = 0, strips = 0, row_tiles = 0, tiles = 0;
     int rows_per_tile = 16;
-    int target_waves = 1024;
-    int min_chunk = 4;
+    int target_waves = 0;   // cap on the wavefronts chunks may fill (0: none)
+    int fill = 1;           // wavefronts a launch's time chunks may fill
+    int min_chunk = 2;
     int max_chunks = 1;
     bool moments = false;  // IIR_FLAG_MOMENTS: the kernels also sum the luma moments
     bool v2 = false;       // IIR_FLAG_MOTION_V2: motion of the filtered frame difference
@@ -214,11 +215,29 @@ void choose_columns(iir_ctx *c)
     c->lanes_out = kWave;
 }
 
+// Time chunks for a launch of n frames over `tiles` tiles, filling at most `fill` wavefronts at
+// once: as many chunks as fit, each of at least min_chunk frames (every chunk after the first
+// re-blurs the frame before it, so a one-frame chunk doubles its blur work). With few tiles (small
+// frames) the chunks give each SIMD a second wavefront to overlap its loads with; more than two
+// per SIMD measured slower (1080p: 2 chunks 87 us, 3 or 4 chunks 92 us), since more fronts of
+// frames in flight push the halo rows a tile shares with its neighbours out of each XCD's L2.
+int chunks_for(int64_t tiles, int64_t fill, int n, int min_chunk)
+{
+    if (n < 2 * min_chunk || tiles >= fill)
+        return 1;
+    int chunks = (int)std::max<int64_t>(1, std::min<int64_t>(fill / tiles, n / min_chunk));
+    // no empty chunks
+    const int len = (n + chunks - 1) / chunks;
+    return (n + len - 1) / len;
+}
+
 // Rows per tile: each candidate's kernel has its own register footprint and hence its own number
-// of resident wavefronts per CU. A launch whose tiles all fit at once finishes when its busiest
-// SIMD does, so the estimated cost is (wavefronts per SIMD, rounded up) x (rows + the 4 halo
-// rows each tile re-reads), times the number of rounds when they do not all fit.
-int choose_rows(iir_ctx *c, int cus, int forced)
+// of resident wavefronts per CU (its slots). A launch whose tiles all fit at once finishes when
+// its busiest SIMD does, so the estimated cost is (wavefronts per SIMD, rounded up) x (rows + the
+// 4 halo rows each tile re-reads), times the number of rounds when they do not all fit. The
+// generic path (ragged sizes) costs half as much again per row: at 960x544 the 12-row generic
+// kernel lost to the 16-row fast one.
+int choose_rows(iir_ctx *c, int cus, int forced, int *slots_out)
 {
     static const int kCandidates[] = {12, 16, 20};
     int best = 0;  // none: no kernel for this configuration
@@ -237,11 +256,11 @@ int choose_rows(iir_ctx *c, int cus, int forced)
         const int64_t simds = 4LL * cus;
         const int64_t rounds = (waves + slots - 1) / slots;
         const int64_t per_simd = (std::min(waves, slots) + simds - 1) / simds;
-        // the generic path's edge handling costs about a fifth more per row
-        const double cost = (double)rounds * (double)per_simd * (th + 4) * (generic ? 1.2 : 1.0);
+        const double cost = (double)rounds * (double)per_simd * (th + 4) * (generic ? 1.5 : 1.0);
         if (cost < best_cost - 1e-9 || (cost <= best_cost + 1e-9 && th > best)) {
             best_cost = cost;
             best = th;
+            *slots_out = (int)std::min<int64_t>(slots, INT32_MAX);
         }
     }
     return best;
@@ -249,13 +268,7 @@ int choose_rows(iir_ctx *c, int cus, int forced)
 
 int plan_chunks(const iir_ctx *c, int nframes)
 {
-    if (c->tiles >= c->target_waves || nframes < 2 * c->min_chunk)
-        return 1;
-    const int want = (c->target_waves + c->tiles - 1) / c->tiles;
-    int chunks = std::max(1, std::min(want, nframes / c->min_chunk));
-    // no empty chunks
-    const int len = (nframes + chunks - 1) / chunks;
-    return (nframes + len - 1) / len;
+    return chunks_for(c->tiles, c->fill, nframes, c->min_chunk);
 }
 
 // The launch geometry of a configuration on a device with `cus` compute units: sample size,
@@ -271,15 +284,22 @@ int setup_geometry(iir_ctx *c, const iir_config *cfg, int device, int cus)
     c->v2 = (cfg->flags & IIR_FLAG_MOTION_V2) != 0;
     c->nsums = c->moments ? kMaxSums : kSums;
     choose_columns(c);
+    // IIR_TARGET_WAVES caps the wavefronts a launch's time chunks may fill (0: no cap beyond
+    // two per SIMD)
+    c->target_waves = env_int("IIR_TARGET_WAVES", 0, 0, 1 << 20);
+    c->min_chunk = env_int("IIR_MIN_CHUNK", 2, 1, 65536);
     const int forced_rows = env_int("IIR_ROWS_PER_TILE", 0, 0, 64);
-    c->rows_per_tile = choose_rows(c, cus, forced_rows);
+    int slots = 0;
+    c->rows_per_tile = choose_rows(c, cus, forced_rows, &slots);
     if (c->rows_per_tile == 0)
         return fail(IIR_EINVAL, "no frames kernel for this configuration (rows per tile %d)",
                     forced_rows);
     c->row_tiles = (cfg->height + c->rows_per_tile - 1) / c->rows_per_tile;
     c->tiles = c->strips * c->row_tiles;
-    c->target_waves = env_int("IIR_TARGET_WAVES", 4 * cus, 1, 1 << 20);
-    c->min_chunk = env_int("IIR_MIN_CHUNK", 4, 1, 65536);
+    // time chunks fill at most two wavefronts per SIMD (and the kernel's slots)
+    c->fill = std::min(slots, 8 * cus);
+    if (c->target_waves > 0)
+        c->fill = std::min(c->fill, c->target_waves);
     c->max_chunks = plan_chunks(c, cfg->max_batch);
     // launch geometry must fit a 1-D grid ("ADR-1380", Consequences: an oversized launch failed
     // with an invalid-value error at 1080p and 4K; here every shape is checked once, up front)

@@ -200,3 +200,21 @@ def test_static_rejects_before_device_work(lib):
         assert str(B.STATIC_MAX_FRAMES) in lib.iir_last_error().decode()
     bad = B.Config(64, 32, 7, B.IIR_CHROMA_420, 1, 0)
     assert lib.iir_run_clip_static(ctypes.byref(bad), 0, None, f, f, 1, out) == B.IIR_EINVAL
+
+
+def test_unpack_results_matches_struct():
+    # the numpy view of iir_result rows reads the same fields as ctypes
+    out = (B.Result * 4)()
+    for i in range(4):
+        out[i].sad = 3 * i + 1
+        out[i].sse[0], out[i].sse[1], out[i].sse[2] = 2 ** 64 - 1 - i, 7 * i, 2 ** 40 + i
+        for k in range(4):
+            out[i].moment[k] = 100 * i + k
+        out[i].has_motion = i % 2
+    for moments in (False, True):
+        sums, hm = B._unpack_results(out, 3, moments)
+        assert sums.shape == (3, 8 if moments else 4) and sums.dtype == np.uint64
+        for i in range(3):
+            row = [out[i].sad] + list(out[i].sse) + (list(out[i].moment) if moments else [])
+            assert [int(v) for v in sums[i]] == row
+            assert hm[i] == out[i].has_motion

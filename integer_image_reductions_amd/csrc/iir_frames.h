@@ -1501,29 +1501,48 @@ constexpr int vmcnt_imm(int n)
     return 0x0F70 | (n & 15) | ((n >> 4) << 14);
 }
 
-// Count this workgroup as finished in its slot group, once its sum atomics have completed: they
-// precede the YOUNGER vector memory instructions the caller issued last (its state stores),
-// which may still be in flight, so the stores drain while the count makes its round trip.
+// Count this workgroup as finished, once its sum atomics have completed: they precede the
+// YOUNGER vector memory instructions the caller issued last (its state stores), which may still be
+// in flight, so the stores drain while the count makes its round trip. Counting takes two levels,
+// so that no counter takes more than about 32 arrivals: device-scope atomics on one address are
+// performed one after another at memory, and one counter per slot group (253 arrivals each at 4K)
+// made the last workgroups of a launch wait up to 18 us for their turn. A workgroup counts into
+// its slot's counter (blockIdx mod kSumSlots); the last member of a slot resets it and counts the
+// slot into its group's counter (slot mod kSumGroups); the last slot of a group publishes the
+// group. Returns (wave-uniform) whether this workgroup publishes.
 template <int YOUNGER>
-__device__ __forceinline__ unsigned int count_arrival(const KernelArgs &a, int lane)
+__device__ __forceinline__ bool count_arrival(const KernelArgs &a, int lane)
 {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(YOUNGER));  // the sum atomics have completed
-    unsigned int arrived = 0;
-    if (lane == 0)
-        arrived = __hip_atomic_fetch_add(a.arrivals + blockIdx.x % kSumGroups, 1u,
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return arrived;
+    const unsigned int n = gridDim.x;
+    const unsigned int slot = blockIdx.x % kSumSlots;
+    const unsigned int g = blockIdx.x % kSumGroups;
+    const unsigned int slot_members = n / kSumSlots + (slot < n % kSumSlots ? 1u : 0u);
+    // slots of group g with members: g, g + 8, ..., below min(n, kSumSlots)
+    const unsigned int used = min(n, (unsigned int)kSumSlots);
+    const unsigned int group_slots = used / kSumGroups + (g < used % kSumGroups ? 1u : 0u);
+    unsigned int last = 0;
+    if (lane == 0) {
+        const unsigned int s = __hip_atomic_fetch_add(a.arrivals + slot, 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+        if (s == slot_members - 1u) {
+            // every member of the slot has counted (each after its own sums completed)
+            __hip_atomic_store(a.arrivals + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned int q = __hip_atomic_fetch_add(a.arrivals + kSumSlots + g, 1u,
+                                                          __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+            last = q == group_slots - 1u ? 1u : 0u;
+        }
+    }
+    return uni((int)last) != 0;
 }
 
 template <int NS>
-__device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane,
-                                                unsigned int arrived_lane0)
+__device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane, bool last)
 {
     constexpr int kPerGroup = kSumSlots / kSumGroups;  // slots g, g + 8, ..., g + 56
     const unsigned int g = blockIdx.x % kSumGroups;
-    const unsigned int members = gridDim.x / kSumGroups + (g < gridDim.x % kSumGroups ? 1u : 0u);
-    const unsigned int arrived = (unsigned int)uni((int)arrived_lane0);
-    if (arrived != members - 1u)
+    if (!last)
         return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     // kPer totals per lane per pass, all of their slot loads issued before any is added, so a
@@ -1554,7 +1573,8 @@ __device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane,
         }
     }
     if (lane == 0)
-        __hip_atomic_store(a.arrivals + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.arrivals + kSumSlots + g, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     // the end of the kernel releases these stores to the host before its completion signal
 }
 
@@ -1737,7 +1757,7 @@ frames_kernel(const KernelArgs a)
         frame_loop_v2<BPC, TH, GENERIC, STAGED, MOM, V2 == 2>(a, T, O, prev, pxprev, have_prev,
                                                              stage);
         // the state stores drain while the group count is in flight
-        unsigned int arrived;
+        bool arrived;
         if (T.chunk == a.chunks - 1 && a.ring_out) {
             store_saved<BPC, TH>(a, T, s, prev);
             arrived = count_arrival<TH>(a, lane);
@@ -1774,7 +1794,7 @@ frames_kernel(const KernelArgs a)
         // the state stores (TH instructions) drain while the group count is in flight; they are
         // non-temporal, so the launch's end does not find 16 MB (at 4K) of them dirty in L2
         // (measured 2.6 us per 4K 8-bit launch)
-        unsigned int arrived;
+        bool arrived;
         if (T.chunk == a.chunks - 1 && a.ring_out) {
             unsigned long long *rout = reinterpret_cast<unsigned long long *>(a.ring_out);
 #pragma unroll

@@ -99,7 +99,7 @@ struct iir_ctx {
     int sums_cur = 0;         // the buffer the next launch uses
     int64_t sums_dirty = 0;   // words of the other buffer the last launch left non-zero
                                               // between launches (each launch re-zeroes it)
-    unsigned int *arrivals = nullptr;         // device, [kSumGroups] finished-workgroup counters, zero
+    unsigned int *arrivals = nullptr;         // device, [kArrivals] finished-workgroup counters, zero
     int64_t sums_n = 0;
     // pinned coherent, [max_batch][nsums][kSumGroups] group totals (the launch's last workgroup of
     // each slot group writes its group's; the host adds the groups)
@@ -517,7 +517,7 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     if (e == hipSuccess)
         e = hipMalloc(&c->sums, sizeof(unsigned long long) * 2 * c->sums_n);
     if (e == hipSuccess)
-        e = hipMalloc(&c->arrivals, sizeof(unsigned int) * kSumGroups);
+        e = hipMalloc(&c->arrivals, sizeof(unsigned int) * kArrivals);
     if (e == hipSuccess)
         e = hipMalloc(&c->table_dev, sizeof(FramePtrs) * cfg->max_batch);
     if (e == hipSuccess)
@@ -543,7 +543,7 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
     if (e == hipSuccess)
         e = hipMemsetAsync(c->sums, 0, sizeof(unsigned long long) * 2 * c->sums_n, c->stream);
     if (e == hipSuccess)
-        e = hipMemsetAsync(c->arrivals, 0, sizeof(unsigned int) * kSumGroups, c->stream);
+        e = hipMemsetAsync(c->arrivals, 0, sizeof(unsigned int) * kArrivals, c->stream);
     for (int i = 0; i < 2 && e == hipSuccess; ++i)
         e = hipMemsetAsync(c->ring[i], 0, ring_bytes, c->stream);
     if (e == hipSuccess)

@@ -15,6 +15,8 @@ namespace iir {
 constexpr int kWave = 64;          // CDNA wavefront; one wavefront is one workgroup
 constexpr int kSumSlots = 64;      // partial slots per sum: the slot of workgroup b is b mod 64
 constexpr int kSumGroups = 8;      // slot groups (slot mod 8), each folded by its last workgroup
+// finished-workgroup counters: one per slot, then one per slot group
+constexpr int kArrivals = kSumSlots + kSumGroups;
 constexpr int kSums = 4;           // SAD, SSE_Y, SSE_U, SSE_V
 constexpr int kMoments = 4;        // optional: sum ref Y, sum dist Y, sum ref Y^2, sum dist Y^2
 constexpr int kMaxSums = kSums + kMoments;
@@ -48,8 +50,8 @@ struct KernelArgs {
     int64_t zero_n;
     // host-visible [nframes][S][kSumGroups] group totals of this launch (pinned host memory)
     unsigned long long *publish;
-    // [kSumGroups] finished workgroups of each slot group, zero at launch (each group's last
-    // workgroup resets its counter)
+    // [kArrivals] zero at launch: finished workgroups of each slot (kSumSlots), then finished
+    // slots of each slot group (kSumGroups); the last arrival at a counter resets it
     unsigned int *arrivals;
     int32_t W, H, Wc, Hc;
     int32_t strips, row_tiles, tiles;
@@ -95,11 +97,11 @@ struct StaticScratch {
     unsigned long long *publish;  // [frames][kMaxSums][kSumGroups] group totals
     iir_result *results;          // [frames] folded results
     FramePtrs *table;             // [frames] plane pointers of a non-uniformly strided clip
-    unsigned int *arrivals;       // [kSumGroups] finished-workgroup counters
+    unsigned int *arrivals;       // [kArrivals] finished-workgroup counters
 };
 // The scratch regions as addressed on the current device (looked up once per device).
 hipError_t static_scratch(int device, StaticScratch *out);
-// Zero words [0, n) of `sums` and the kSumGroups arrival counters (a fill kernel, not a memset,
+// Zero words [0, n) of `sums` and the kArrivals arrival counters (a fill kernel, not a memset,
 // so the clearing is an ordinary kernel node for callers that capture the stream).
 hipError_t launch_clear(unsigned long long *sums, int64_t n, unsigned int *arrivals,
                         hipStream_t stream);

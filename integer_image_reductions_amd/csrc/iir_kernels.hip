@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void clear_kernel(unsigned long long *p, int64
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (int64_t i = i0; i < n; i += stride)
         p[i] = 0ull;
-    if (i0 < kSumGroups)
+    if (i0 < kArrivals)
         arrivals[i0] = 0u;
 }
 
@@ -137,7 +137,7 @@ constexpr size_t kScrPublish = round256(sizeof(unsigned long long) * kStaticMaxF
                                         kSumGroups);
 constexpr size_t kScrResults = round256(sizeof(iir_result) * kStaticMaxFrames);
 constexpr size_t kScrTable = round256(sizeof(FramePtrs) * kStaticMaxFrames);
-constexpr size_t kScrArrivals = round256(sizeof(unsigned int) * kSumGroups);
+constexpr size_t kScrArrivals = round256(sizeof(unsigned int) * kArrivals);
 constexpr size_t kScratchBytes = kScrSums + kScrPublish + kScrResults + kScrTable + kScrArrivals;
 static_assert(kScratchBytes < (size_t)2 << 20, "the static working memory stays modest");
 

@@ -161,15 +161,22 @@ typedef struct iir_ctx iir_ctx;
  * `hip_stream` (a hipStream_t; NULL means the device's null stream). Allocates everything the
  * context will ever use: the blurred-luma state (two planes of uint16 in a tiled layout), the
  * device sum slots, pinned readback and descriptor staging, and events. Nothing is allocated
- * afterwards. Errors: IIR_EINVAL (config), IIR_ENODEV (no such device or not gfx950),
- * IIR_ENOMEM, IIR_EDEVICE. *out is set only on success.
+ * afterwards ("Making it fast: three rounds on one pipeline", Round 2: allocation and freeing on
+ * the hot path were the largest single cost, removed by keeping and reusing the buffers). The
+ * launch geometry is sized from the device's compute units and checked here, once ("ADR-1226:
+ * Size the CUDA AIM CM launch by SM count ...", Decision; "ADR-1380: The CUDA SpEED twins are
+ * device-resident ...", Consequences: an oversized launch failed only at run time).
+ * Errors: IIR_EINVAL (config), IIR_ENODEV (no such device or not gfx950), IIR_ENOMEM,
+ * IIR_EDEVICE. *out is set only on success.
  */
 IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, iir_ctx **out);
 
 /*
  * Enqueue one frame pair (asynchronous: returns before the GPU runs it). ref and dist are host
  * structs describing device planes; the planes must stay valid and unmodified until the result
- * has been collected. One kernel launch and one small readback of its sums; no host wait.
+ * has been collected. One kernel launch and one small readback of its sums; no host wait
+ * ("ADR-1380", Decision, second item: the chain is enqueued on the picture's stream and its small
+ * result read back behind an event).
  * Errors: IIR_EINVAL, IIR_EBUSY (the pending results would exceed max_batch frames or 64
  * submissions), IIR_EDEVICE.
  */
@@ -190,7 +197,8 @@ IIR_API int iir_submit_clip(iir_ctx *ctx, const iir_frame *ref, const iir_frame 
 /*
  * Copy up to `max` pending results, oldest first, into the HOST array `out`; *n_out receives the
  * number copied. Waits once, for the submission holding the last result returned (later
- * submissions keep running). Results beyond `max` stay queued for the next call. With nothing
+ * submissions keep running; "ADR-1380", Consequences (Positive): one small readback and one wait
+ * per frame, no host work inside it). Results beyond `max` stay queued for the next call. With nothing
  * pending it returns IIR_OK with *n_out = 0. Errors: IIR_EINVAL (null out or n_out, max < 0),
  * IIR_EDEVICE.
  */
@@ -199,6 +207,8 @@ IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_o
 /*
  * iir_submit_clip followed by iir_collect of exactly those nframes results into the host array
  * `out` (which must hold nframes entries). Requires nothing else pending (IIR_ESTATE otherwise).
+ * One launch for the whole clip, one wait ("ADR-1380", Consequences (Positive); the clip stays
+ * resident on the device, "ADR-1392", Consequences (Negative): copying frames in dominates).
  */
 IIR_API int iir_run_clip(iir_ctx *ctx, const iir_frame *ref, const iir_frame *dist,
                          int32_t nframes, iir_result *out);
@@ -218,7 +228,12 @@ IIR_API int iir_motion2(const double *motion, int32_t n, double *motion2);
 IIR_API int iir_aggregate_of(const iir_config *cfg, const iir_result *r, int32_t n,
                              iir_aggregate *out);
 
-/* Forget the previous frame: the next submitted frame gets has_motion = 0. Enqueues nothing. */
+/*
+ * Forget the previous frame: the next submitted frame gets has_motion = 0, as the first frame of a
+ * clip does. Enqueues nothing. (The context keeps the previous frame's state on the device between
+ * submissions, as the temporal extractor keeps the previous luma in a slot: "ADR-1380",
+ * Decision, second item.)
+ */
 IIR_API int iir_reset(iir_ctx *ctx);
 
 /*
@@ -232,7 +247,9 @@ IIR_API int iir_export_blur(iir_ctx *ctx, void *dst, int64_t pitch);
 /*
  * Duration in milliseconds of the main kernel of the most recently collected submission, from the
  * HIP start and stop events attached to its dispatch (hipExtLaunchKernelGGL) on the context's
- * stream. Needs IIR_FLAG_TIMING; IIR_ESTATE until a timed submission has been collected.
+ * stream: the kernel's own time, as the pages' kernel traces report it ("ADR-1392",
+ * Consequences (Positive)). Needs IIR_FLAG_TIMING; IIR_ESTATE until a timed submission has been
+ * collected.
  */
 IIR_API int iir_kernel_time(iir_ctx *ctx, float *ms);
 
@@ -243,7 +260,8 @@ IIR_API int iir_kernel_time(iir_ctx *ctx, float *ms);
  */
 IIR_API int iir_kernel_stats(iir_ctx *ctx, int32_t reset, int64_t *launches, double *total_ms);
 
-/* Launch geometry chosen at create, for reports and tests. */
+/* Launch geometry chosen at create from the device's compute units, for reports and tests
+   ("ADR-1226", Decision: the launch is sized by the processor count). */
 typedef struct iir_geometry {
     int32_t rows_per_tile;     /* output luma rows per wavefront tile */
     int32_t lanes_out;         /* output lanes per wavefront (4 luma columns each): 64 */
@@ -256,7 +274,8 @@ typedef struct iir_geometry {
 } iir_geometry;
 IIR_API int iir_get_geometry(const iir_ctx *ctx, iir_geometry *out);
 
-/* Time chunks the next iir_submit_clip of nframes frames will use (1 = no split). */
+/* Time chunks the next iir_submit_clip of nframes frames will use (1 = no split); small frames
+   are split so the launch fills the GPU ("ADR-1226", Decision). */
 IIR_API int iir_plan_chunks(const iir_ctx *ctx, int32_t nframes, int32_t *chunks);
 
 /*
@@ -291,7 +310,8 @@ IIR_API int iir_run_clip_static(const iir_config *cfg, int32_t device, void *hip
                                 const iir_frame *ref, const iir_frame *dist, int32_t nframes,
                                 iir_result *out);
 
-/* Release everything the context owns. Waits for its pending work first. NULL is a no-op. */
+/* Release everything the context owns, once, off the hot path ("Making it fast", Round 2). Waits
+   for its pending work first. NULL is a no-op. */
 IIR_API void iir_destroy(iir_ctx *ctx);
 
 /* Static text for an IIR_* code. */

@@ -1836,6 +1836,18 @@ FramesFn frames_fn(int th)
     constexpr bool P = BPC == 8 ? IIR_STAGE8 : IIR_STAGE10;
     if constexpr (BPC == 16 && V2) {
         return th == 12 ? frames_kernel<BPC, 12, P, GENERIC, 2, MOM, V2> : nullptr;
+    } else if constexpr (BPC == 10 && V2 && MOM) {
+        // 10-bit motion v2 with moments holds two frames' rows beside the moment sums: the 12-row
+        // tile spills at three wavefronts per SIMD and the 20-row tile at two, so it has the 12-
+        // and 16-row tiles at two wavefronts per SIMD, without scratch
+        switch (th) {
+        case 12:
+            return frames_kernel<BPC, 12, P, GENERIC, 2, MOM, V2>;
+        case 16:
+            return frames_kernel<BPC, 16, P, GENERIC, IIR_WPE16, MOM, V2>;
+        default:
+            return nullptr;
+        }
     } else {
         switch (th) {
         case 12:

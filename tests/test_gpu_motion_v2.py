@@ -219,3 +219,30 @@ def test_v2_full_4k_16bit_moments():
         r1, r2 = oracle.moments(clip.ref[0][t], 16)
         d1, d2 = oracle.moments(clip.dist[0][t], 16)
         assert [int(v) for v in sums[t, 4:]] == [r1, d1, r2, d2], t
+
+
+@pytest.mark.parametrize("th", ["12", "16"])
+@pytest.mark.parametrize("w,h", [(512, 48), (257, 40), (768, 60)])
+def test_v2_moments_10bit_tiles(w, h, th, monkeypatch):
+    """10-bit motion v2 with moments has its 12- and 16-row tiles at two wavefronts per SIMD
+    (no scratch); each matches the oracle on the fast and the generic path."""
+    monkeypatch.setenv("IIR_ROWS_PER_TILE", th)
+    clip = synth.random_clip(w, h, 10, 3, seed=5 * w + h + int(th), kind="extreme")
+    ref, dist = _dev(clip)
+    _say("v2 moments 10-bit", w, h, th)
+    with iir.Context(w, h, 10, max_batch=4, motion_v2=True, moments=True) as ctx:
+        assert ctx.geometry()["rows_per_tile"] == int(th)
+        sums, hm = ctx.run_clip(ref, dist)
+    want, want_hm = oracle.clip_v2(clip.ref, clip.dist, 10)
+    _check(sums[:, :4], hm, want, want_hm, f"v2 moments 10-bit {w}x{h} th={th}")
+    for t in range(3):
+        r1, r2 = oracle.moments(clip.ref[0][t], 10)
+        d1, d2 = oracle.moments(clip.dist[0][t], 10)
+        assert [int(v) for v in sums[t, 4:]] == [r1, d1, r2, d2]
+
+
+def test_v2_moments_10bit_has_no_20_row_tile(monkeypatch):
+    monkeypatch.setenv("IIR_ROWS_PER_TILE", "20")
+    with pytest.raises(iir.IIRError) as e:
+        iir.Context(512, 40, 10, max_batch=2, motion_v2=True, moments=True)
+    assert e.value.code == -1

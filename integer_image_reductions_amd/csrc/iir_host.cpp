@@ -3,16 +3,19 @@
 // iir_kernels.hip).
 //
 // Per submission the context enqueues, on the caller's stream: (only for a non-uniformly strided
-// clip) one host-to-device copy of the frame table, one kernel launch, whose last workgroup writes
-// the per-frame totals into pinned host memory, and one event; iir_collect waits on that event
-// once ("ADR-1380: The CUDA SpEED twins are device-resident ...", Decision: submit on the
-// picture's stream, read the small result back behind an event, collect waits once). Everything is allocated
+// clip) one host-to-device copy of the frame table and one kernel launch, whose last workgroups
+// write the per-frame totals into pinned host memory; iir_collect waits once, until they are all
+// there ("ADR-1380: The CUDA SpEED twins are device-resident ...", Decision: submit on the
+// picture's stream, read the small result back, collect waits once). The totals are their own
+// completion signal: an event packet per submission cost about 3 us of GPU time between
+// one-frame launches. Everything is allocated
 // in iir_create ("Making it fast: three rounds on one pipeline", Round 2: no allocation or free on
 // the hot path).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
+#include <thread>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -116,7 +119,6 @@ struct iir_ctx {
         int taken;       // frames already returned by iir_collect
         bool has_prev;   // frame 0 has a previous frame
         int groups;      // slot groups with workgroups in the launch (their totals are valid)
-        hipEvent_t done; // recorded after the submission's readback
         hipEvent_t k0, k1;  // bracket the main kernel (IIR_FLAG_TIMING)
     };
     static constexpr int kMaxPending = 64;
@@ -125,7 +127,6 @@ struct iir_ctx {
     int sub_count = 0;   // pending submissions
     int slot_head = 0;   // next free frame slot
     int pending = 0;     // frames submitted and not yet returned
-    bool broken = false;              // a submission's completion event could not be recorded
     bool has_prev = false;            // the next frame has a previous blurred frame
     bool any_frame = false;           // ring[ring_cur] is valid
     // kernel timing of collected submissions (IIR_FLAG_TIMING)
@@ -330,8 +331,6 @@ void release(iir_ctx *c)
     if (c->table_host)
         (void)hipHostFree(c->table_host);
     for (auto &sub : c->subs) {
-        if (sub.done)
-            (void)hipEventDestroy(sub.done);
         if (sub.k0)
             (void)hipEventDestroy(sub.k0);
         if (sub.k1)
@@ -360,6 +359,17 @@ int reserve_slots(const iir_ctx *c, int n)
         return n <= tail ? 0 : -1;  // wrap to the front
     }
     return head + n <= tail ? head : -1;
+}
+
+// No total reaches 2^63 (the largest, a sum of 2^30 squares of 16-bit differences, is below
+// 2^62), so an all-ones word in host_sums means "not written yet".
+constexpr unsigned long long kUnwritten = ~0ull;
+
+// Mark the group totals of frames [first, first + n) as not yet written.
+void fill_pending(iir_ctx *c, int first, int n)
+{
+    unsigned long long *p = c->host_sums + (size_t)first * c->nsums * kSumGroups;
+    std::fill(p, p + (size_t)n * c->nsums * kSumGroups, kUnwritten);
 }
 
 // The frame part of one launch's arguments: plane pointers of n frame pairs (a base and a
@@ -412,8 +422,6 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
 {
     if (!c)
         return fail(IIR_EINVAL, "context is NULL");
-    if (c->broken)
-        return fail(IIR_ESTATE, "an earlier submission's event failed; destroy the context");
     if (n < 1 || n > c->cfg.max_batch)
         return fail(IIR_EINVAL, "nframes %d outside 1..max_batch (%d)", n, c->cfg.max_batch);
     int rc = check_frames(c, ref, dist, n);
@@ -442,14 +450,20 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
 
     const bool timing = (c->cfg.flags & IIR_FLAG_TIMING) != 0;
     iir_ctx::Sub &sub = c->subs[(c->sub_head + c->sub_count) % iir_ctx::kMaxPending];
-    // the kernel itself writes the totals to host_sums; one event marks the end: with timing,
-    // the launch's own start and end events (no separate marker packets), else one marker
+    // untimed: the launch's totals are their own completion signal. Its rows of host_sums are
+    // filled with a value no total can take before it is enqueued; iir_collect waits until every
+    // one of them has been overwritten (no event packet in the stream between launches). Timed:
+    // the dispatch's own end event marks it.
+    if (!timing)
+        fill_pending(c, first, n);
+    // the kernel itself writes the totals to host_sums and then the completion flag; with
+    // timing, the dispatch's own start and end events bracket it instead
     HIP_TRY(launch_frames(c->cfg.bpc, c->rows_per_tile,
                           !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile),
                           c->moments, c->v2, a, c->stream, timing ? sub.k0 : nullptr,
                           timing ? sub.k1 : nullptr));
     // the launch is enqueued: the device state it leaves behind (the other slot buffer to clear,
-    // the ring to read next) is committed before anything else can fail
+    // the ring to read next) is committed
     sub.first = first;
     sub.n = n;
     sub.taken = 0;
@@ -463,15 +477,41 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     c->ring_cur ^= 1;
     c->has_prev = true;
     c->any_frame = true;
-    if (!timing) {
-        const hipError_t e = hipEventRecord(sub.done, c->stream);
-        if (e != hipSuccess) {
-            // the submission is queued but cannot be waited for: nothing more can be collected
-            c->broken = true;
-            return fail_hip(e, "hipEventRecord");
-        }
-    }
     return IIR_OK;
+}
+
+// Wait until the kernel of an untimed submission has written every group total of its frames
+// (each one 64-bit store, so a word is either the unwritten mark or its total). The scan resumes
+// where it last found a mark. The stream is queried now and then, so a launch that failed, or one
+// that finished without writing a total, ends the wait with an error instead of spinning forever.
+int wait_published(iir_ctx *c, const iir_ctx::Sub &sub)
+{
+    const volatile unsigned long long *p = c->host_sums + (size_t)sub.first * c->nsums * kSumGroups;
+    const int rows = sub.n * c->nsums;
+    int row = 0, g = 0;
+    for (uint64_t spin = 0;; ++spin) {
+        while (row < rows && p[(size_t)row * kSumGroups + g] != kUnwritten) {
+            if (++g == sub.groups) {
+                g = 0;
+                ++row;
+            }
+        }
+        if (row == rows)
+            return IIR_OK;
+        if ((spin & 1023) == 1023) {
+            const hipError_t e = hipStreamQuery(c->stream);
+            if (e == hipSuccess) {
+                if (p[(size_t)row * kSumGroups + g] != kUnwritten)
+                    continue;
+                return fail(IIR_EDEVICE, "the launch finished without writing its totals");
+            }
+            if (e != hipErrorNotReady)
+                return fail_hip(e, "hipStreamQuery");
+            if (spin > (1u << 20))
+                std::this_thread::yield();
+        }
+        __builtin_ia32_pause();
+    }
 }
 
 }  // namespace
@@ -528,13 +568,12 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
         e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->host_sums_dev), c->host_sums, 0);
     if (e == hipSuccess)
         e = hipHostMalloc(&c->table_host, sizeof(FramePtrs) * cfg->max_batch, hipHostMallocDefault);
+
     if (e != hipSuccess) {
         release(c);
         return fail(IIR_ENOMEM, "allocation failed: %s", hipGetErrorString(e));
     }
     for (auto &sub : c->subs) {
-        if (e == hipSuccess)
-            e = hipEventCreateWithFlags(&sub.done, hipEventDisableTiming);
         if (e == hipSuccess && (cfg->flags & IIR_FLAG_TIMING))
             e = hipEventCreate(&sub.k0);
         if (e == hipSuccess && (cfg->flags & IIR_FLAG_TIMING))
@@ -572,8 +611,6 @@ IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_o
     if (!ctx || !out || !n_out || max < 0)
         return fail(IIR_EINVAL, "bad collect arguments");
     *n_out = 0;
-    if (ctx->broken)
-        return fail(IIR_ESTATE, "an earlier submission's event failed; destroy the context");
     const int n = std::min(max, ctx->pending);
     if (n == 0)
         return IIR_OK;
@@ -589,7 +626,13 @@ IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_o
         DeviceScope ds(ctx->device);
         if (ds.err != hipSuccess)
             return fail_hip(ds.err, "hipSetDevice");
-        HIP_TRY(hipEventSynchronize((ctx->cfg.flags & IIR_FLAG_TIMING) ? last->k1 : last->done));
+        if (ctx->cfg.flags & IIR_FLAG_TIMING)
+            HIP_TRY(hipEventSynchronize(last->k1));
+        else {
+            const int rc = wait_published(ctx, *last);
+            if (rc != IIR_OK)
+                return rc;
+        }
     }
     int got = 0;
     while (got < n) {

@@ -48,8 +48,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 # the frames kernel's sources: its templates and the units that instantiate them
 KERNEL_SRCS = [os.path.join(ROOT, "integer_image_reductions_amd", "csrc", n) for n in
-               ("iir_frames.h", "iir_frames_8.hip", "iir_frames_10.hip", "iir_frames_16.hip",
-                "iir_frames_8_v2.hip", "iir_frames_10_v2.hip", "iir_frames_16_v2.hip")]
+               ("iir_frames.h", "iir_frames_8.hip", "iir_frames_8_one.hip", "iir_frames_10.hip",
+                "iir_frames_16.hip", "iir_frames_8_v2.hip", "iir_frames_10_v2.hip",
+                "iir_frames_16_v2.hip")]
 
 WORKLOADS = {
     "c3": "3840x2160 8-bit 4:2:0, 50 frame pairs, motion SAD + Y/U/V SSE",

@@ -21,8 +21,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libiir.so")
 # one translation unit per sample type of the frames kernel, so they compile in parallel
 SOURCES = [os.path.join(CSRC, n) for n in
-           ("iir_frames_8.hip", "iir_frames_10.hip", "iir_frames_16.hip", "iir_frames_8_v2.hip",
-            "iir_frames_10_v2.hip", "iir_frames_16_v2.hip", "iir_kernels.hip", "iir_host.cpp")]
+           ("iir_frames_8.hip", "iir_frames_8_one.hip", "iir_frames_10.hip", "iir_frames_16.hip",
+            "iir_frames_8_v2.hip", "iir_frames_10_v2.hip", "iir_frames_16_v2.hip",
+            "iir_kernels.hip", "iir_host.cpp")]
 HEADERS = [os.path.join(CSRC, n) for n in ("iir_frames.h", "iir_internal.h")]
 ARCH = "gfx950"
 

@@ -1279,7 +1279,7 @@ __device__ __forceinline__ void set_prio(uint32_t p)
 // of two priority levels, in the load window (3 or 2) and in the compute that follows (1 or 0).
 // ALL_DIST reads the distorted rows out of a frame that is not accumulated too (its stage then
 // holds stale rows), so that the luma sums can run for every frame without a branch per row.
-template <int TH, bool ALL_DIST>
+template <int TH, bool ALL_DIST, bool ONE = false>
 __device__ __forceinline__ void staged_frame(const KernelArgs &a, const Tile &T,
                                              const StageOffsets<TH> &O, int t, int f_begin,
                                              int f_end, uint32_t (*lds)[kWave], ChromaX4<TH> &C,
@@ -1287,7 +1287,10 @@ __device__ __forceinline__ void staged_frame(const KernelArgs &a, const Tile &T,
 {
     const uint32_t favoured = ((uint32_t)t + T.slot) & 1u;
     set_prio(2u + favoured);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | Stage<TH>::kDmaLoads);  // vmcnt(one luma group)
+    if constexpr (ONE)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): a one-frame launch has no second group
+    else
+        __builtin_amdgcn_s_waitcnt(0x0F70 | Stage<TH>::kDmaLoads);  // vmcnt(one luma group)
     read_stage<TH>(ALL_DIST || t >= f_begin, lds, T.lane, T.hlds, F);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
     if (t >= f_begin)
@@ -1303,15 +1306,53 @@ __device__ __forceinline__ void staged_frame(const KernelArgs &a, const Tile &T,
 // The first loads of a chunk's loop: luma and chroma of its first frame, then the luma of the
 // second (of the first again for a one-frame chunk). The frame loop waits for all of its loads
 // before the chunk's sums are published (vmcnt(0)), so no load into LDS outlives the wavefront.
-template <int TH>
+// ONE: a launch of one frame (one chunk). Its only luma group and chroma are followed by `mid`,
+// the previous state's loads, so those are in flight with the frame's instead of one memory
+// round trip ahead of them, and no second luma group is loaded.
+struct NoLoads {
+    __device__ void operator()() const {}
+};
+
+template <int TH, bool ONE = false, typename Mid = NoLoads>
 __device__ __forceinline__ void staged_start(const KernelArgs &a, const Tile &T,
                                              const StageOffsets<TH> &O, int t0, int f_begin,
-                                             int f_end, uint32_t (*lds)[kWave], ChromaX4<TH> &C)
+                                             int f_end, uint32_t (*lds)[kWave], ChromaX4<TH> &C,
+                                             Mid mid = {})
 {
     load_frame_staged<TH>(a, T, O, t0, t0 >= f_begin, lds);
     if (t0 >= f_begin)
         load_chroma_x4<TH>(a, T, O, t0, C);
-    load_frame_staged<TH>(a, T, O, min(t0 + 1, f_end - 1), true, lds + Stage<TH>::kRows);
+    if constexpr (ONE)
+        mid();
+    else
+        load_frame_staged<TH>(a, T, O, min(t0 + 1, f_end - 1), true, lds + Stage<TH>::kRows);
+}
+
+// The previous launch's blurred tile of this wavefront (its rows in the tiled state plane), and
+// its sum over the valid columns and rows (the SAD's "sum of the previous frame").
+template <int TH>
+__device__ __forceinline__ void load_prev_tile(const KernelArgs &a, const Tile &T,
+                                               uint32_t (&prev0)[TH], uint32_t (&prev1)[TH])
+{
+    const uint2 *rin = reinterpret_cast<const uint2 *>(a.ring_in);
+#pragma unroll
+    for (int i = 0; i < TH; ++i) {
+        const uint2 v = rin[(T.tile * TH + i) * kWave + T.lane];
+        prev0[i] = v.x;
+        prev1[i] = v.y;
+    }
+}
+
+template <int TH>
+__device__ __forceinline__ uint32_t prev_tile_sum(const Tile &T, const uint32_t (&prev0)[TH],
+                                                  const uint32_t (&prev1)[TH])
+{
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < TH; ++i)
+        if (i < T.rows_valid)
+            s = dot2u(prev1[i], T.w1, dot2u(prev0[i], T.w0, s));
+    return s;
 }
 
 // The frames of this workgroup's time chunk. Chunks after the first start by re-blurring the
@@ -1319,7 +1360,7 @@ __device__ __forceinline__ void staged_start(const KernelArgs &a, const Tile &T,
 // computed: the loads of frame t+1 write the wave's LDS stage (no registers held), issued as soon
 // as frame t has been read out of it. Frames go in pairs that swap the roles of two blurred-tile
 // register sets (prev -> alt -> prev), so no frame ends by copying its blurred tile back.
-template <int BPC, int TH, bool GENERIC, bool STAGED, bool MOM>
+template <int BPC, int TH, bool GENERIC, bool STAGED, bool MOM, bool ONE = false>
 __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
                                            const StageOffsets<TH> &O, uint32_t (&prev0)[TH],
                                            uint32_t (&prev1)[TH], uint32_t sum_prev,
@@ -1336,8 +1377,20 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
     P.first = f_begin;
     P.count = 0;
     ChromaX4<TH> C;
-    if constexpr (STAGED)
+    if constexpr (STAGED && ONE) {
+        // the previous blurred tile's loads go out behind the frame's own
+        const bool load_prev = T.chunk == 0 && a.has_prev != 0;
+        staged_start<TH, true>(a, T, O, t0, f_begin, f_end, lds, C, [&]() {
+            if (load_prev)
+                load_prev_tile<TH>(a, T, prev0, prev1);
+        });
+        if (load_prev) {
+            sum_prev = prev_tile_sum<TH>(T, prev0, prev1);
+            have_prev = true;
+        }
+    } else if constexpr (STAGED) {
         staged_start<TH>(a, T, O, t0, f_begin, f_end, lds, C);
+    }
     // one frame: blurred tile in (i0, i1), out to (o0, o1); staged, its luma in stage `sidx`
     auto step = [&](int t, int sidx, const uint32_t(&i0)[TH], const uint32_t(&i1)[TH],
                     uint32_t(&o0)[TH], uint32_t(&o1)[TH]) {
@@ -1345,8 +1398,8 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
         FrameData<BPC, TH> F;
         FrameStats<BPC> S;
         if constexpr (STAGED)
-            staged_frame<TH, MOM>(a, T, O, t, f_begin, f_end, lds + sidx * Stage<TH>::kRows, C,
-                                  F, S);
+            staged_frame<TH, MOM, ONE>(a, T, O, t, f_begin, f_end,
+                                       lds + sidx * Stage<TH>::kRows, C, F, S);
         else
             load_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F);
         compute_frame<BPC, TH, GENERIC, STAGED, MOM>(a, T, t, t >= f_begin, F, S, i0, i1, o0,
@@ -1578,8 +1631,10 @@ __device__ __forceinline__ void publish_if_last(const KernelArgs &a, int lane, b
     // the end of the kernel releases these stores to the host before its completion signal
 }
 
-// V2: 0 the blurred-frame SAD, 1 motion v2, 2 motion v2 of 16-bit samples (halved differences)
-template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE, bool MOM, int V2>
+// V2: 0 the blurred-frame SAD, 1 motion v2, 2 motion v2 of 16-bit samples (halved differences).
+// ONE: the kernel of a one-frame launch (8-bit staged, blurred-frame SAD): the previous state's
+// loads go out behind the frame's own.
+template <int BPC, int TH, bool STAGED, bool GENERIC, int WPE, bool MOM, int V2, bool ONE = false>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void
 frames_kernel(const KernelArgs a)
 {
@@ -1771,7 +1826,8 @@ frames_kernel(const KernelArgs a)
         uint32_t prev0[TH], prev1[TH];
         uint32_t sum_prev = 0;
         bool have_prev = false;
-        if (T.chunk == 0 && a.has_prev) {
+        if (!ONE && T.chunk == 0 && a.has_prev) {
+            // (loads and sums interleaved; the one-frame kernel's helpers schedule differently)
             const uint2 *rin = reinterpret_cast<const uint2 *>(a.ring_in);
 #pragma unroll
             for (int i = 0; i < TH; ++i) {
@@ -1788,8 +1844,8 @@ frames_kernel(const KernelArgs a)
                 prev0[i] = prev1[i] = 0;
         }
 
-        frame_loop<BPC, TH, GENERIC, STAGED, MOM>(a, T, O, prev0, prev1, sum_prev, have_prev,
-                                                  stage);
+        frame_loop<BPC, TH, GENERIC, STAGED, MOM, ONE>(a, T, O, prev0, prev1, sum_prev,
+                                                       have_prev, stage);
 
         // the state stores (TH instructions) drain while the group count is in flight; they are
         // non-temporal, so the launch's end does not find 16 MB (at 4K) of them dirty in L2
@@ -1830,6 +1886,22 @@ frames_kernel(const KernelArgs a)
 // H % TH == 0 (no ragged tile, no partial sample group); the generic path takes any size.
 // Motion v2 of 16-bit storage carries the previous frame's 16-bit rows beside the 64-bit squared
 // error sums: it only has the 12-row tile, at two wavefronts per SIMD (taller tiles spill).
+// The one-frame kernels (8-bit staged, blurred-frame SAD), or nullptr.
+template <bool GENERIC, bool MOM>
+FramesFn frames_fn_one(int th)
+{
+    switch (th) {
+    case 12:
+        return frames_kernel<8, 12, true, GENERIC, IIR_WPE12, MOM, 0, true>;
+    case 16:
+        return frames_kernel<8, 16, true, GENERIC, IIR_WPE16, MOM, 0, true>;
+    case 20:
+        return frames_kernel<8, 20, true, GENERIC, IIR_WPE20, MOM, 0, true>;
+    default:
+        return nullptr;
+    }
+}
+
 template <int BPC, bool GENERIC, bool MOM, int V2 = 0>
 FramesFn frames_fn(int th)
 {

@@ -66,6 +66,7 @@ struct KernelArgs {
 // iir_frames_16_v2.hip).
 typedef void (*FramesFn)(KernelArgs);
 FramesFn frames_pick_8(int th, bool generic, bool moments);
+FramesFn frames_pick_8_one(int th, bool generic, bool moments);  // launches of one frame
 FramesFn frames_pick_10(int th, bool generic, bool moments);
 FramesFn frames_pick_16(int th, bool generic, bool moments);
 FramesFn frames_pick_8_v2(int th, bool generic, bool moments);

@@ -254,6 +254,11 @@ hipError_t launch_frames(int bpc, int th, bool generic, bool moments, bool v2,
     FramesFn f = pick(bpc, th, generic, moments, v2);
     if (!f)
         return hipErrorInvalidValue;
+    // a one-frame launch of 8-bit samples (a frame pair per submission) has its own kernel
+    if (a.nframes == 1 && a.chunks == 1 && bpc == 8 && !v2) {
+        if (FramesFn one = frames_pick_8_one(th, generic, moments))
+            f = one;
+    }
     const dim3 grid((unsigned)(a.tiles * a.chunks)), block(kWave);
     if (start && stop)  // the events are the dispatch's own start and end timestamps
         hipExtLaunchKernelGGL(f, grid, block, 0, stream, start, stop, 0, a);

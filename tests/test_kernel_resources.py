@@ -22,8 +22,8 @@ from integer_image_reductions_amd import build as B
 
 ALLOWED_SCRATCH = {
     # frames_kernel<16, 12, STAGED=false, GENERIC=false, WPE=2, MOM=false, V2=1 / 2>
-    "_ZN3iir12_GLOBAL__N_113frames_kernelILi16ELi12ELb0ELb0ELi2ELb0ELi1EEEvNS_10KernelArgsE": 12,
-    "_ZN3iir12_GLOBAL__N_113frames_kernelILi16ELi12ELb0ELb0ELi2ELb0ELi2EEEvNS_10KernelArgsE": 12,
+    "_ZN3iir12_GLOBAL__N_113frames_kernelILi16ELi12ELb0ELb0ELi2ELb0ELi1ELb0EEEvNS_10KernelArgsE": 12,
+    "_ZN3iir12_GLOBAL__N_113frames_kernelILi16ELi12ELb0ELb0ELi2ELb0ELi2ELb0EEEvNS_10KernelArgsE": 12,
 }
 
 

@@ -50,7 +50,8 @@ enum {
     IIR_ENOMEM = -3,  /* device or pinned host allocation failed (iir_create only) */
     IIR_EDEVICE = -4, /* a HIP call failed; see iir_last_error() */
     IIR_EBUSY = -5,   /* the submission would exceed max_batch uncollected frames */
-    IIR_ESTATE = -6   /* call not valid in the context's current state */
+    IIR_ESTATE = -6,  /* call not valid in the context's current state */
+    IIR_ERANGE = -7   /* IIR_FLAG_CHECK_RANGE found a sample >= 2^bpc (iir_collect) */
 };
 
 #define IIR_CHROMA_420 420
@@ -74,6 +75,18 @@ enum {
  * available (IIR_ESTATE).
  */
 #define IIR_FLAG_MOTION_V2 4u
+/*
+ * Debug mode: check that every input sample lies in the bit depth's range, a precondition the
+ * kernels do not verify. The pages fix the depths (8, 10 and 16-bit inputs, "ADR-1392",
+ * Consequences) but no check of the samples; this one is the library's own. At 9 to 15 bits each
+ * submission first runs a check kernel over its frames (every plane, every sample inside the
+ * plane's width; pitch padding is ignored), which costs one more read of the frames. At 8 and 16
+ * bits every stored value is a valid sample and nothing runs. iir_collect then returns IIR_ERANGE
+ * when a frame it returns held a sample >= 2^bpc, after writing all of its results as usual
+ * (those frames' sums are unspecified, and so is the motion state after them: call iir_reset);
+ * iir_last_error names the frame and plane. Not available in iir_run_clip_static (IIR_EINVAL).
+ */
+#define IIR_FLAG_CHECK_RANGE 8u
 
 /*
  * One plane of one frame. data is a DEVICE pointer, pitch is the distance between rows in bytes.
@@ -200,7 +213,8 @@ IIR_API int iir_submit_clip(iir_ctx *ctx, const iir_frame *ref, const iir_frame 
  * submissions keep running; "ADR-1380", Consequences (Positive): one small readback and one wait
  * per frame, no host work inside it). Results beyond `max` stay queued for the next call. With nothing
  * pending it returns IIR_OK with *n_out = 0. Errors: IIR_EINVAL (null out or n_out, max < 0),
- * IIR_EDEVICE.
+ * IIR_EDEVICE, IIR_ERANGE (IIR_FLAG_CHECK_RANGE: a returned frame held an out-of-range sample;
+ * out and *n_out are filled all the same).
  */
 IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_out);
 

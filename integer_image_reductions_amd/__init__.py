@@ -5,6 +5,8 @@ this package is its Python binding. Import is cheap: the library loads on first 
 """
 from .binding import (  # noqa: F401
     IIR_CHROMA_420,
+    IIR_ERANGE,
+    IIR_FLAG_CHECK_RANGE,
     IIR_FLAG_MOMENTS,
     IIR_FLAG_MOTION_V2,
     IIR_FLAG_TIMING,

@@ -15,10 +15,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libiir.so")
 
 IIR_OK, IIR_EINVAL, IIR_ENODEV, IIR_ENOMEM, IIR_EDEVICE, IIR_EBUSY, IIR_ESTATE = 0, -1, -2, -3, -4, -5, -6
+IIR_ERANGE = -7
 IIR_CHROMA_420 = 420
 IIR_FLAG_TIMING = 1
 IIR_FLAG_MOMENTS = 2
 IIR_FLAG_MOTION_V2 = 4
+IIR_FLAG_CHECK_RANGE = 8
 PLANE_ALIGN = 16  # bytes: plane data and pitch must be multiples of this
 
 c_i32, c_i64, c_u32, c_u64, c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
@@ -61,8 +63,12 @@ class Geometry(ctypes.Structure):
 
 
 class IIRError(RuntimeError):
+    """A library call's error code and iir_last_error(). `results` is set where the call still
+    returned results (iir_collect's IIR_ERANGE: the (sums, has_motion) of every frame)."""
+
     def __init__(self, code: int, func: str, detail: str):
         self.code = code
+        self.results = None
         super().__init__(f"{func} failed: {detail} (code {code})")
 
 
@@ -178,7 +184,7 @@ class Context:
 
     def __init__(self, width: int, height: int, bpc: int, max_batch: int = 64, device=None,
                  stream=None, timing: bool = False, moments: bool = False,
-                 motion_v2: bool = False):
+                 motion_v2: bool = False, check_range: bool = False):
         torch = _torch()
         lib = load_library()
         self._lib = lib
@@ -188,7 +194,8 @@ class Context:
         self.config = Config(width, height, bpc, IIR_CHROMA_420, max_batch,
                              (IIR_FLAG_TIMING if timing else 0) |
                              (IIR_FLAG_MOMENTS if moments else 0) |
-                             (IIR_FLAG_MOTION_V2 if motion_v2 else 0))
+                             (IIR_FLAG_MOTION_V2 if motion_v2 else 0) |
+                             (IIR_FLAG_CHECK_RANGE if check_range else 0))
         self.moments = bool(moments)
         h = c_vp()
         _check(lib.iir_create(ctypes.byref(self.config), dev.index, c_vp(self.stream.cuda_stream),
@@ -291,9 +298,16 @@ class Context:
         n_cap = min(max_results, self.config.max_batch)
         out = (Result * n_cap)()
         got = c_i32()
-        _check(self._lib.iir_collect(self._h, out, n_cap, ctypes.byref(got)), "iir_collect")
+        rc = self._lib.iir_collect(self._h, out, n_cap, ctypes.byref(got))
         if len(self._keep) > 64:
             self._keep = self._keep[-64:]
+        if rc == IIR_ERANGE:  # the results were returned all the same
+            try:
+                _check(rc, "iir_collect")
+            except IIRError as e:
+                e.results = self._unpack(out, got.value)
+                raise
+        _check(rc, "iir_collect")
         return self._unpack(out, got.value)
 
     def run_clip(self, ref, dist):
@@ -303,7 +317,14 @@ class Context:
         if n != m:
             raise ValueError("ref and dist have different frame counts")
         out = (Result * n)()
-        _check(self._lib.iir_run_clip(self._h, fr, fd, n, out), "iir_run_clip")
+        rc = self._lib.iir_run_clip(self._h, fr, fd, n, out)
+        if rc == IIR_ERANGE:
+            try:
+                _check(rc, "iir_run_clip")
+            except IIRError as e:
+                e.results = self._unpack(out, n)
+                raise
+        _check(rc, "iir_run_clip")
         return self._unpack(out, n)
 
     def reset(self):

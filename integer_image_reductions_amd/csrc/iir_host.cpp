@@ -89,6 +89,7 @@ struct iir_ctx {
     int fill = 1;           // wavefronts a launch's time chunks may fill
     int min_chunk = 2;
     int max_chunks = 1;
+    bool check_range = false;  // IIR_FLAG_CHECK_RANGE at 9 to 15 bits: a check kernel runs first
     bool moments = false;  // IIR_FLAG_MOMENTS: the kernels also sum the luma moments
     bool v2 = false;       // IIR_FLAG_MOTION_V2: motion of the filtered frame difference
     int nsums = kSums;     // 64-bit sums per frame: kSums, or kMaxSums with moments
@@ -110,6 +111,10 @@ struct iir_ctx {
     unsigned long long *host_sums_dev = nullptr;  // the same memory as the device sees it
     FramePtrs *table_dev = nullptr;
     FramePtrs *table_host = nullptr;  // pinned, [max_batch]
+    // pinned coherent, [kMaxPending]: per pending submission, 0 or the input-range check's code
+    // (t * 6 + k) + 1 of an out-of-range sample (IIR_FLAG_CHECK_RANGE)
+    uint32_t *range_host = nullptr;
+    uint32_t *range_dev = nullptr;
     // Pending submissions, oldest first, in a ring of kMaxPending records. Their results sit in
     // a circular region of max_batch frame slots of host_sums (and table slots), each submission
     // contiguous, so up to max_batch frames can be in flight across several submissions.
@@ -158,7 +163,8 @@ int check_config(const iir_config *c)
         return fail(IIR_EINVAL, "frame size %dx%d outside 3..32768", c->width, c->height);
     if (c->max_batch < 1 || c->max_batch > 65536)
         return fail(IIR_EINVAL, "max_batch %d outside 1..65536", c->max_batch);
-    if (c->flags & ~(IIR_FLAG_TIMING | IIR_FLAG_MOMENTS | IIR_FLAG_MOTION_V2))
+    if (c->flags &
+        ~(IIR_FLAG_TIMING | IIR_FLAG_MOMENTS | IIR_FLAG_MOTION_V2 | IIR_FLAG_CHECK_RANGE))
         return fail(IIR_EINVAL, "unknown flags 0x%x", c->flags);
     return IIR_OK;
 }
@@ -283,6 +289,7 @@ int setup_geometry(iir_ctx *c, const iir_config *cfg, int device, int cus)
     c->Hc = (cfg->height + 1) / 2;
     c->moments = (cfg->flags & IIR_FLAG_MOMENTS) != 0;
     c->v2 = (cfg->flags & IIR_FLAG_MOTION_V2) != 0;
+    c->check_range = (cfg->flags & IIR_FLAG_CHECK_RANGE) != 0 && cfg->bpc > 8 && cfg->bpc < 16;
     c->nsums = c->moments ? kMaxSums : kSums;
     choose_columns(c);
     // IIR_TARGET_WAVES caps the wavefronts a launch's time chunks may fill (0: no cap beyond
@@ -330,6 +337,8 @@ void release(iir_ctx *c)
         (void)hipHostFree(c->host_sums);
     if (c->table_host)
         (void)hipHostFree(c->table_host);
+    if (c->range_host)
+        (void)hipHostFree(c->range_host);
     for (auto &sub : c->subs) {
         if (sub.k0)
             (void)hipEventDestroy(sub.k0);
@@ -449,15 +458,21 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     a.has_prev = c->has_prev ? 1 : 0;
 
     const bool timing = (c->cfg.flags & IIR_FLAG_TIMING) != 0;
-    iir_ctx::Sub &sub = c->subs[(c->sub_head + c->sub_count) % iir_ctx::kMaxPending];
     // untimed: the launch's totals are their own completion signal. Its rows of host_sums are
     // filled with a value no total can take before it is enqueued; iir_collect waits until every
     // one of them has been overwritten (no event packet in the stream between launches). Timed:
     // the dispatch's own end event marks it.
     if (!timing)
         fill_pending(c, first, n);
-    // the kernel itself writes the totals to host_sums and then the completion flag; with
-    // timing, the dispatch's own start and end events bracket it instead
+    const int sub_idx = (c->sub_head + c->sub_count) % iir_ctx::kMaxPending;
+    iir_ctx::Sub &sub = c->subs[sub_idx];
+    if (c->check_range) {
+        // the slot's last submission has been collected, so its check kernel has finished
+        c->range_host[sub_idx] = 0;
+        HIP_TRY(launch_check_range(a, c->cfg.bpc, c->range_dev + sub_idx, c->stream));
+    }
+    // the kernel writes the totals to host_sums itself; with timing, the dispatch's own start
+    // and end events also bracket it
     HIP_TRY(launch_frames(c->cfg.bpc, c->rows_per_tile,
                           !fast_path_ok(c->cfg.width, c->cfg.height, c->rows_per_tile),
                           c->moments, c->v2, a, c->stream, timing ? sub.k0 : nullptr,
@@ -568,6 +583,11 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
         e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->host_sums_dev), c->host_sums, 0);
     if (e == hipSuccess)
         e = hipHostMalloc(&c->table_host, sizeof(FramePtrs) * cfg->max_batch, hipHostMallocDefault);
+    if (e == hipSuccess && c->check_range)
+        e = hipHostMalloc(&c->range_host, sizeof(uint32_t) * iir_ctx::kMaxPending,
+                          hipHostMallocCoherent | hipHostMallocMapped);
+    if (e == hipSuccess && c->check_range)
+        e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->range_dev), c->range_host, 0);
 
     if (e != hipSuccess) {
         release(c);
@@ -635,9 +655,22 @@ IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_o
         }
     }
     int got = 0;
+    int range_rc = IIR_OK;
     while (got < n) {
         iir_ctx::Sub &sub = ctx->subs[ctx->sub_head];
         const int take = std::min(n - got, sub.n - sub.taken);
+        if (ctx->check_range && range_rc == IIR_OK) {
+            // written by the check kernel, which finished before the frames kernel began
+            const uint32_t code = __atomic_load_n(ctx->range_host + ctx->sub_head, __ATOMIC_ACQUIRE);
+            const int t = code ? (int)(code - 1) / 6 : -1;
+            if (code && t >= sub.taken && t < sub.taken + take) {
+                static const char *const kPlanes[6] = {"ref Y", "ref U", "ref V",
+                                                       "dist Y", "dist U", "dist V"};
+                range_rc = fail(IIR_ERANGE, "result %d (frame %d of its submission): %s holds a "
+                                "sample >= 2^%d", got + t - sub.taken, t,
+                                kPlanes[(code - 1) % 6], ctx->cfg.bpc);
+            }
+        }
         for (int i = 0; i < take; ++i) {
             const int f = sub.taken + i;
             const volatile unsigned long long *g =
@@ -674,7 +707,7 @@ IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_o
     if (ctx->sub_count == 0)
         ctx->slot_head = 0;
     *n_out = n;
-    return IIR_OK;
+    return range_rc;
 }
 
 IIR_API int iir_run_clip(iir_ctx *ctx, const iir_frame *ref, const iir_frame *dist,
@@ -707,6 +740,8 @@ IIR_API int iir_run_clip_static(const iir_config *cfg, int32_t device, void *hip
     if (nframes < 1 || nframes > kStaticMaxFrames)
         return fail(IIR_EINVAL, "nframes %d outside 1..%d (the static working memory's bound)",
                     nframes, kStaticMaxFrames);
+    if (cfg->flags & IIR_FLAG_CHECK_RANGE)
+        return fail(IIR_EINVAL, "IIR_FLAG_CHECK_RANGE is not available in iir_run_clip_static");
     int count = 0;
     if (hipGetDeviceCount(&count) != hipSuccess || count <= 0)
         return fail(IIR_ENODEV, "no HIP device visible");
@@ -965,6 +1000,8 @@ IIR_API const char *iir_strerror(int code)
         return "too many frames pending";
     case IIR_ESTATE:
         return "invalid in the current state";
+    case IIR_ERANGE:
+        return "input sample out of range";
     default:
         return "unknown error";
     }

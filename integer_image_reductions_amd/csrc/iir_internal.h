@@ -88,6 +88,10 @@ hipError_t launch_frames(int bpc, int th, bool generic, bool moments, bool v2,
 hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int W, int H,
                          int strips, int th, hipStream_t stream);
 hipError_t launch_probe(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream);
+// Input-range check of a launch's frames (16-bit storage, bpc 9 to 15): a sample >= 2^bpc
+// inside a plane's width stores (t * 6 + k) + 1 to *flag, frame t and plane k (ref Y, U, V,
+// dist Y, U, V) of one offending sample; *flag is left alone when every sample is in range.
+hipError_t launch_check_range(const KernelArgs &a, int bpc, uint32_t *flag, hipStream_t stream);
 
 // Working memory of the entry point that allocates nothing (iir_run_clip_static): one
 // file-scope device array per GPU, holding the regions below at 256-byte boundaries. The clip

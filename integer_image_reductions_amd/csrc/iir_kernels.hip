@@ -1,6 +1,6 @@
 // iir_kernels.hip -- launchers of the gfx950 kernels (the frames kernel itself is in
-// iir_frames.h, instantiated by the iir_frames_*.hip units), the blurred-plane export and the
-// memory-ceiling probes.
+// iir_frames.h, instantiated by the iir_frames_*.hip units), the blurred-plane export, the
+// input-range check and the memory-ceiling probes.
 #include <hip/hip_ext.h>
 
 #include <algorithm>
@@ -31,6 +31,39 @@ __global__ void export_kernel(const uint32_t *ring, uint16_t *dst, int64_t pitch
         d[j] = (uint16_t)(w & 0xffffu);
         if (j + 1 < W)
             d[j + 1] = (uint16_t)(w >> 16);
+    }
+}
+
+// Blocks take (frame, plane, row) triples, grid-stride, and their 256 threads the row's 16-byte
+// groups of 8 samples (data and pitch are multiples of 16 bytes and pitch >= 2 * width, so every
+// group that starts inside the width ends inside the row's pitch). Samples past the width (the
+// pitch padding) are not checked.
+__global__ __launch_bounds__(256) void check_range_kernel(const KernelArgs a, uint32_t limit,
+                                                          uint32_t *flag)
+{
+    const int H = a.H;
+    const int64_t n = (int64_t)a.nframes * 6 * H;
+    for (int64_t id = blockIdx.x; id < n; id += gridDim.x) {
+        const int z = (int)(id / H), row = (int)(id - (int64_t)z * H);  // z = t * 6 + k
+        const int t = z / 6, k = z - 6 * t;
+        const bool luma = k % 3 == 0;
+        const int w = luma ? a.W : a.Wc;
+        if (row >= (luma ? H : a.Hc))
+            continue;
+        const uint8_t *plane = a.table ? a.table[t].p[k] : a.base[k] + (int64_t)t * a.fstride[k];
+        const uint4 *r = reinterpret_cast<const uint4 *>(plane + (int64_t)row * a.pitch[k]);
+        bool row_bad = false;
+        for (int g = threadIdx.x; 8 * g < w; g += blockDim.x) {
+            const uint4 v = r[g];
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t sample = (d[j / 2] >> (16 * (j % 2))) & 0xffffu;
+                row_bad |= 8 * g + j < w && sample >= limit;
+            }
+        }
+        if (row_bad)
+            *flag = (uint32_t)z + 1u;  // any offending thread's code will do
     }
 }
 
@@ -278,6 +311,19 @@ hipError_t launch_export(const uint32_t *ring, uint16_t *dst, int64_t pitch, int
 }
 
 // The probe's sink (mode 0) is dst; it must hold blocks * 256 * 16 bytes, which bytes covers.
+hipError_t launch_check_range(const KernelArgs &a, int bpc, uint32_t *flag, hipStream_t stream)
+{
+    if (bpc <= 8 || bpc >= 16)
+        return hipErrorInvalidValue;  // every stored value is a valid sample
+    const int64_t rows = (int64_t)a.nframes * 6 * a.H;
+    if (rows <= 0)
+        return hipErrorInvalidValue;
+    const unsigned blocks = (unsigned)std::min<int64_t>(rows, 1 << 20);
+    hipLaunchKernelGGL(check_range_kernel, dim3(blocks), dim3(256), 0, stream, a, 1u << bpc,
+                       flag);
+    return hipGetLastError();
+}
+
 hipError_t launch_probe(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream)
 {
     const int64_t n = bytes / 16;

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_strerror_all_codes(lib):
-    for code in range(0, -7, -1):
+    for code in range(0, -8, -1):
         assert lib.iir_strerror(code).decode() not in ("", "unknown error")
     assert lib.iir_strerror(-99).decode() == "unknown error"
 
@@ -47,7 +47,7 @@ def _create(lib, **kw):
 
 @pytest.mark.parametrize("kw", [dict(bpc=7), dict(bpc=17), dict(chroma=444), dict(w=2),
                                 dict(h=2), dict(w=40000), dict(max_batch=0),
-                                dict(max_batch=70000), dict(flags=8)])
+                                dict(max_batch=70000), dict(flags=16)])
 def test_create_rejects_bad_config(lib, kw):
     assert _create(lib, **kw) == B.IIR_EINVAL
     assert lib.iir_last_error().decode()
@@ -200,6 +200,10 @@ def test_static_rejects_before_device_work(lib):
         assert str(B.STATIC_MAX_FRAMES) in lib.iir_last_error().decode()
     bad = B.Config(64, 32, 7, B.IIR_CHROMA_420, 1, 0)
     assert lib.iir_run_clip_static(ctypes.byref(bad), 0, None, f, f, 1, out) == B.IIR_EINVAL
+    # the debug input-range check needs per-submission state the static entry does not keep
+    checked = B.Config(64, 32, 10, B.IIR_CHROMA_420, 1, B.IIR_FLAG_CHECK_RANGE)
+    assert lib.iir_run_clip_static(ctypes.byref(checked), 0, None, f, f, 1, out) == B.IIR_EINVAL
+    assert "IIR_FLAG_CHECK_RANGE" in lib.iir_last_error().decode()
 
 
 def test_unpack_results_matches_struct():

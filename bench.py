@@ -1,7 +1,7 @@
 """Benchmark: frames/s of the integer motion + PSNR sums on 3840x2160 8-bit 4:2:0, one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--moments]
-                    [--motion-v2] [--no-cpu] [--no-probe] [--streaming]
+                    [--motion-v2] [--no-cpu] [--no-probe] [--no-streaming]
     python bench.py --workload c3 --traffic-from FETCH.csv WRITE.csv   (host only, see below)
 
 A step is one pass of the whole path over one batch: one iir_submit_clip of the 50-frame clip
@@ -18,8 +18,9 @@ ceilings_GBps: the memory ceilings measured by the library's probes (16-byte non
 writes and copies of a 1 GiB buffer), and roofline.frac_of_read_ceiling the kernel's achieved
 bandwidth against the read ceiling (skip with --no-probe).
 streaming: the same frames submitted one pair per call (one launch per frame, the motion state
-crossing launches through the device ring): frames/s and the kernel per launch, with
---streaming. Not the headline value, which is the batch of 50.
+crossing launches through the device ring): frames/s of a context without events, and the
+kernel time per launch from a second context with an event pair per launch (skip with
+--no-streaming). Not the headline value, which is the batch of 50.
 --traffic-from turns two rocprofv3 counter-collection CSVs of `bench.py --probe` runs (one with
 --pmc FETCH_SIZE, one with --pmc WRITE_SIZE) into profiles/frames_kernel_<workload>_traffic.json:
 each counter's mean KiB per main-kernel dispatch, scaled by what the same counter reads for the
@@ -286,39 +287,55 @@ def _cpu_leg(clip, run, max_seconds, min_seconds, core, allowed):
                       f"({dt:.1f} s)"}
 
 
-def streaming(ref, dist, clip, moments: bool, motion_v2: bool, rounds: int = 4) -> dict:
+def streaming(ref, dist, clip, moments: bool, motion_v2: bool, rounds: int = 6) -> dict:
     """Every frame pair its own submission (one launch per frame; the motion state crosses the
-    launches through the device ring): frames/s over `rounds` passes of the clip, each pass
-    collected once, and the mean kernel time per launch against that launch's algorithmic bytes
-    (one frame pair plus the state read and written)."""
+    launches through the device ring), in two contexts. The first records no events: frames/s
+    over `rounds` passes of the clip, each pass submitted whole and collected once. The second
+    brackets every launch with HIP events: the mean kernel time per launch against that launch's
+    algorithmic bytes (one frame pair plus the state read and written), and its own frames/s,
+    which the events slow down."""
     import torch
     import integer_image_reductions_amd as iir
     F = clip.frames
-    ctx = iir.Context(clip.width, clip.height, clip.bpc, max_batch=F, timing=True,
-                      moments=moments, motion_v2=motion_v2)
-    frames = [ctx.prepare_clip(tuple(p[t:t + 1] for p in ref), tuple(p[t:t + 1] for p in dist))
-              for t in range(F)]
-    for fr in frames:
-        ctx.submit_prepared(fr)
-    ctx.collect()
-    torch.cuda.synchronize()
-    ctx.kernel_stats(reset=True)
-    t0 = time.perf_counter()
-    for _ in range(rounds):
-        for fr in frames:
-            ctx.submit_prepared(fr)
-        ctx.collect()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    launches, total_ms = ctx.kernel_stats()
-    ctx.close()
+    group = min(F, 64)  # a context holds at most 64 pending submissions
+
+    def passes(timing: bool):
+        ctx = iir.Context(clip.width, clip.height, clip.bpc, max_batch=group, timing=timing,
+                          moments=moments, motion_v2=motion_v2)
+        frames = [ctx.prepare_clip(tuple(p[t:t + 1] for p in ref),
+                                   tuple(p[t:t + 1] for p in dist)) for t in range(F)]
+
+        def one_pass():
+            for g in range(0, F, group):
+                for fr in frames[g:g + group]:
+                    ctx.submit_prepared(fr)
+                ctx.collect()
+
+        one_pass()
+        torch.cuda.synchronize()
+        if timing:
+            ctx.kernel_stats(reset=True)
+        t0 = time.perf_counter()
+        for _ in range(rounds):
+            one_pass()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        stats = ctx.kernel_stats() if timing else None
+        ctx.close()
+        return rounds * F / dt, stats
+
+    fps, _ = passes(False)
+    fps_timed, (launches, total_ms) = passes(True)
     kernel_us = 1e3 * total_ms / max(launches, 1)
     alg = algorithmic_bytes(clip.width, clip.height, clip.bpc, 1, motion_v2)
-    return {"frames_per_s": rounds * F / dt, "kernel_us_per_launch": kernel_us,
-            "launches": launches, "algorithmic_bytes_per_launch": alg,
+    return {"frames_per_s": fps, "us_per_frame": 1e6 / fps,
+            "kernel_us_per_launch": kernel_us, "launches": launches,
+            "frames_per_s_with_events": fps_timed,
+            "algorithmic_bytes_per_launch": alg,
             "achieved_GBps": alg / (kernel_us * 1e-6) / 1e9,
-            "mode": f"one frame pair per submission, {F} submissions then one collect, "
-                    f"{rounds} passes"}
+            "mode": f"one frame pair per submission, {group} submissions then one collect, "
+                    f"{rounds} passes over {F} frames; frames/s without events, kernel time from "
+                    f"a second context with an event pair per launch"}
 
 
 def main():

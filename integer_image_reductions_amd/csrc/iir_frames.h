@@ -1886,22 +1886,6 @@ frames_kernel(const KernelArgs a)
 // H % TH == 0 (no ragged tile, no partial sample group); the generic path takes any size.
 // Motion v2 of 16-bit storage carries the previous frame's 16-bit rows beside the 64-bit squared
 // error sums: it only has the 12-row tile, at two wavefronts per SIMD (taller tiles spill).
-// The one-frame kernels (8-bit staged, blurred-frame SAD), or nullptr.
-template <bool GENERIC, bool MOM>
-FramesFn frames_fn_one(int th)
-{
-    switch (th) {
-    case 12:
-        return frames_kernel<8, 12, true, GENERIC, IIR_WPE12, MOM, 0, true>;
-    case 16:
-        return frames_kernel<8, 16, true, GENERIC, IIR_WPE16, MOM, 0, true>;
-    case 20:
-        return frames_kernel<8, 20, true, GENERIC, IIR_WPE20, MOM, 0, true>;
-    default:
-        return nullptr;
-    }
-}
-
 template <int BPC, bool GENERIC, bool MOM, int V2 = 0>
 FramesFn frames_fn(int th)
 {
@@ -1931,6 +1915,22 @@ FramesFn frames_fn(int th)
         default:
             return nullptr;
         }
+    }
+}
+
+// The one-frame kernels (8-bit staged, blurred-frame SAD), or nullptr.
+template <bool GENERIC, bool MOM>
+FramesFn frames_fn_one(int th)
+{
+    switch (th) {
+    case 12:
+        return frames_kernel<8, 12, true, GENERIC, IIR_WPE12, MOM, 0, true>;
+    case 16:
+        return frames_kernel<8, 16, true, GENERIC, IIR_WPE16, MOM, 0, true>;
+    case 20:
+        return frames_kernel<8, 20, true, GENERIC, IIR_WPE20, MOM, 0, true>;
+    default:
+        return nullptr;
     }
 }
 

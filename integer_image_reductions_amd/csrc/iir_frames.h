@@ -175,6 +175,57 @@ __device__ __forceinline__ unsigned long long wave_sum_sq(uint32_t v)
     return wave_sum(v);
 }
 
+// Wavefront totals of NS (4 or 8) per-lane u32 sums at once, for sums whose every wavefront total
+// stays below 2^32 (8-bit samples). Each butterfly step takes two registers and one lane bit: the
+// lanes where the bit is clear keep the first register's sum, the others the second's, each plus
+// the same sum from a partner lane (lane bits 0 and 1 through quad permutations; bit 2 through a
+// rotation by 4 within each row of 16, which pairs every lane with one of the other half of its
+// group of 8, so each value is still counted once). Every step halves the registers. A rotation
+// by 8 then completes each row, and the two permlane swaps of gfx950 add the four rows, after
+// which every lane holds the total of sum (lane mod NS). 8 sums: 36 VALU instead of 64.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, true);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t pair_step(uint32_t a, uint32_t b, bool bit_set)
+{
+    return (bit_set ? b : a) + dpp_mov<CTRL>(bit_set ? a : b);
+}
+
+template <int NS>
+__device__ __forceinline__ void wave_sums_u32(const uint32_t (&x)[NS], int lane,
+                                              unsigned long long (&out)[NS])
+{
+    static_assert(NS == 4 || NS == 8, "four or eight sums");
+    constexpr int kSwap1 = 0xB1, kSwap2 = 0x4E;   // quad_perm [1,0,3,2] and [2,3,0,1]
+    constexpr int kRor4 = 0x124, kRor8 = 0x128;   // row_ror:4 and row_ror:8
+    const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+    uint32_t r;
+    if constexpr (NS == 8) {
+        const uint32_t p0 = pair_step<kSwap1>(x[0], x[1], b0);
+        const uint32_t p1 = pair_step<kSwap1>(x[2], x[3], b0);
+        const uint32_t p2 = pair_step<kSwap1>(x[4], x[5], b0);
+        const uint32_t p3 = pair_step<kSwap1>(x[6], x[7], b0);
+        r = pair_step<kRor4>(pair_step<kSwap2>(p0, p1, b1), pair_step<kSwap2>(p2, p3, b1),
+                             (lane & 4) != 0);
+    } else {
+        r = pair_step<kSwap2>(pair_step<kSwap1>(x[0], x[1], b0),
+                              pair_step<kSwap1>(x[2], x[3], b0), b1);
+        r += dpp_mov<kRor4>(r);
+    }
+    r += dpp_mov<kRor8>(r);
+    const auto h = __builtin_amdgcn_permlane32_swap(r, r, false, false);  // halves of the wave
+    r = h[0] + h[1];
+    const auto q = __builtin_amdgcn_permlane16_swap(r, r, false, false);  // rows 0-1 and 2-3
+    r = q[0] + q[1];
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+        out[k] = (uint32_t)__builtin_amdgcn_readlane((int)r, k);
+}
+
 __device__ __forceinline__ void add_sum(unsigned long long *p, unsigned long long v)
 {
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -814,7 +865,20 @@ __device__ __forceinline__ void push_frame_sums(const KernelArgs &a, const Tile 
         ev = S.sv - 2u * S.sv2;
     }
     const Sq<BPC> zero = 0;
-    if constexpr (MOM) {
+    if constexpr (MOM && BPC == 8) {
+        // every 8-bit total fits 32 bits: at most 20 rows x 4 samples x 255^2 per lane, x 64 lanes
+        const uint32_t x[kMaxSums] = {sad,
+                                      T.out_lane ? ey : 0u,
+                                      T.c_on ? eu : 0u,
+                                      T.c_on ? ev : 0u,
+                                      T.out_lane ? S.m1r : 0u,
+                                      T.out_lane ? S.m1d : 0u,
+                                      T.out_lane ? S.m2r : 0u,
+                                      T.out_lane ? S.m2d : 0u};
+        unsigned long long sums[kMaxSums];
+        wave_sums_u32<kMaxSums>(x, T.lane, sums);
+        push_sums(a, P, T.lane, sums);
+    } else if constexpr (MOM) {
         const unsigned long long sums[kMaxSums] = {
             wave_sum(sad),
             wave_sum_sq(T.out_lane ? ey : zero),

@@ -21,10 +21,11 @@
  * computed on the host.
  *
  * Frames stay on the device: the caller owns all frame memory (device pointers, e.g. torch
- * tensors); nothing returns to the host inside a frame, and each submission ends with one small
- * readback of its sums behind an event ("ADR-1380: The CUDA SpEED twins are device-resident ...",
- * Decision, second item: submit on the picture's stream, read a small result back behind an event,
- * collect waits once).
+ * tensors); nothing returns to the host inside a frame, and each submission's kernel writes its
+ * small per-frame totals straight into pinned host memory, where iir_collect finds them ("ADR-1380:
+ * The CUDA SpEED twins are device-resident ...", Decision: the work is enqueued on the picture's
+ * stream, a small result per frame comes back, and collect waits once; the pages wait on an event,
+ * this library on the totals themselves).
  *
  * Conventions for every call:
  *   - the return value is IIR_OK (0) or a negative IIR_E* code; no call throws or aborts;
@@ -173,7 +174,8 @@ typedef struct iir_ctx iir_ctx;
  * Create a context for one frame geometry on HIP device `device`, enqueuing all of its work on
  * `hip_stream` (a hipStream_t; NULL means the device's null stream). Allocates everything the
  * context will ever use: the blurred-luma state (two planes of uint16 in a tiled layout), the
- * device sum slots, pinned readback and descriptor staging, and events. Nothing is allocated
+ * device sum slots, pinned readback and descriptor staging, and (IIR_FLAG_TIMING) events; with
+ * IIR_FLAG_CHECK_RANGE, a pinned word per pending submission. Nothing is allocated
  * afterwards ("Making it fast: three rounds on one pipeline", Round 2: allocation and freeing on
  * the hot path were the largest single cost, removed by keeping and reusing the buffers). The
  * launch geometry is sized from the device's compute units and checked here, once ("ADR-1226:
@@ -187,9 +189,9 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
 /*
  * Enqueue one frame pair (asynchronous: returns before the GPU runs it). ref and dist are host
  * structs describing device planes; the planes must stay valid and unmodified until the result
- * has been collected. One kernel launch and one small readback of its sums; no host wait
- * ("ADR-1380", Decision, second item: the chain is enqueued on the picture's stream and its small
- * result read back behind an event).
+ * has been collected. One kernel launch, which writes the frame's totals into pinned host memory
+ * itself; no copy and no host wait ("ADR-1380", Decision: the work is enqueued on the picture's
+ * stream with a small result per frame).
  * Errors: IIR_EINVAL, IIR_EBUSY (the pending results would exceed max_batch frames or 64
  * submissions), IIR_EDEVICE.
  */

@@ -3,25 +3,25 @@
 // iir_kernels.hip).
 //
 // Per submission the context enqueues, on the caller's stream: (only for a non-uniformly strided
-// clip) one host-to-device copy of the frame table and one kernel launch, whose last workgroups
-// write the per-frame totals into pinned host memory; iir_collect waits once, until they are all
-// there ("ADR-1380: The CUDA SpEED twins are device-resident ...", Decision: submit on the
-// picture's stream, read the small result back, collect waits once). The totals are their own
-// completion signal: an event packet per submission cost about 3 us of GPU time between
-// one-frame launches. Everything is allocated
-// in iir_create ("Making it fast: three rounds on one pipeline", Round 2: no allocation or free on
-// the hot path).
+// clip) one host-to-device copy of the frame table, (only with IIR_FLAG_CHECK_RANGE at 9 to 15
+// bits) the input-range check, and one frames kernel launch, whose last workgroups write the
+// per-frame totals into pinned host memory; iir_collect waits once, until they are all there
+// ("ADR-1380: The CUDA SpEED twins are device-resident ...", Decision: submit on the picture's
+// stream, read the small result back, collect waits once). The totals are their own completion
+// signal: an event packet per submission cost about 3 us of GPU time between one-frame launches.
+// Everything is allocated in iir_create ("Making it fast: three rounds on one pipeline", Round 2:
+// no allocation or free on the hot path).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
-#include <thread>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "iir.h"

@@ -59,6 +59,9 @@ CASES = [
     (("rand", 300, 70, 10, 5), ("rand", 37, 19, 10, 2), False, True, False),
     (("rand", 513, 7, 8, 4), ("rand", 17, 23, 8, 3), False, False, True),
     (("c2", 12), ("c1", 5), False, False, False),
+    # one 8-bit frame pair per call: the one-frame kernels, without a previous state
+    (("rand", 300, 70, 8, 1), ("rand", 257, 40, 8, 1), False, False, False),
+    (("rand", 256, 48, 8, 1), ("rand", 64, 12, 8, 1), True, False, False),
 ]
 
 

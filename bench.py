@@ -40,6 +40,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -75,11 +76,21 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and with whitespace runs collapsed: a comment edit does not
+    change the compiled kernel, so it must not void the counters taken on it."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_sha() -> str:
+    """Hash of the frames kernel's code (its sources with the comments stripped)."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()
 
 

@@ -1593,7 +1593,7 @@ __device__ __forceinline__ void store_saved(const KernelArgs &a, const Tile &T, 
 // atomics of 1/64 of the workgroups: with fewer slots the atomics of the whole grid, all issued
 // when the workgroups finish their last frames, queue on the same few addresses (8 slots cost
 // ~20 us more per 4K launch than 64). The slots form kSumGroups groups by blockIdx mod 8; the last
-// workgroup of a group to finish (one device-scope counter per group) folds its group's slots of
+// workgroup of a group to finish (found by the two-level count below) folds its group's slots of
 // every sum of every frame and writes the group totals straight to the caller-visible pinned
 // buffer [frame][sum][group]; the host adds the group totals. No workgroup waits for another,
 // and no readback copy follows the kernel. Launches alternate between two slot buffers; each

@@ -77,3 +77,12 @@ def test_traffic_needs_both_kernels(tmp_path):
     _counter_csv(p, "FETCH_SIZE", [1.0], [])
     with pytest.raises(SystemExit):
         bench.write_traffic("c3", False, False, str(p), str(p), out_dir=str(tmp_path))
+
+
+def test_kernel_hash_ignores_comments_only():
+    """The traffic counters stay valid across comment edits, and not across code edits."""
+    base = "int f(int a) {\n    return a + 1;  // one more\n}\n/* block\n comment */\n"
+    assert bench._code_only(base) == bench._code_only(base.replace("one more", "the next"))
+    assert bench._code_only(base) == bench._code_only(base.replace("/* block", "/* other"))
+    assert bench._code_only(base) == bench._code_only(base.replace("    return", "  return"))
+    assert bench._code_only(base) != bench._code_only(base.replace("a + 1", "a + 2"))

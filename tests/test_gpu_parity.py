@@ -66,6 +66,23 @@ def test_tiny_sweep(w, h, bpc):
             assert np.array_equal(_blur_np(ctx), last), f"blurred plane {kind} {w}x{h} {bpc}"
 
 
+@pytest.mark.parametrize("w,h", TINY, ids=[f"{w}x{h}" for w, h in TINY])
+def test_tiny_sweep_streamed(w, h):
+    """The same tiny shapes submitted one 8-bit frame pair at a time (the one-frame kernels, whose
+    state crosses launches), with and without moments."""
+    for i, (kind, moments) in enumerate([("uniform", False), ("extreme", True)]):
+        clip = synth.random_clip(w, h, 8, 3, seed=2000 + 7 * w + h + i, kind=kind)
+        _say("tiny streamed", w, h, kind, moments)
+        ref, dist = _dev(clip)
+        want, want_hm, last = _oracle(clip, last=True)
+        with iir.Context(w, h, 8, max_batch=4, moments=moments) as ctx:
+            for t in range(3):
+                ctx.submit([p[t] for p in ref], [p[t] for p in dist])
+            sums, hm = ctx.collect()
+            _check(clip, sums[:, :4], hm, want, want_hm, f"{kind} {w}x{h} streamed")
+            assert np.array_equal(_blur_np(ctx), last), f"blurred plane {kind} {w}x{h}"
+
+
 # 256-column strips: right frame edge at a strip boundary (512, 768), inside the last strip
 # (504, 1000, 248, 8, 64), one column past a boundary (257, 513), ragged rows (512x50)
 PATH_SIZES = [(504, 36), (1000, 80), (248, 60), (8, 12), (64, 240), (512, 48), (768, 60),

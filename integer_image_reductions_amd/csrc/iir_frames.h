@@ -1524,8 +1524,13 @@ __device__ __forceinline__ void frame_loop_v2(const KernelArgs &a, const Tile &T
         if constexpr (STAGED)
             staged_frame<TH, false>(a, T, O, t, f_begin, f_end, lds + sidx * Stage<TH>::kRows, C,
                                     F, S);
-        else
+        else {
+            if constexpr (BPC == 10)  // as in frame_loop: the two wavefronts advance alike
+                set_prio(3u);
             load_frame<BPC, TH, GENERIC>(a, T, t, t >= f_begin, F);
+            if constexpr (BPC == 10)
+                set_prio(0u);
+        }
         compute_frame_v2<BPC, TH, GENERIC, STAGED, MOM, WIDE>(a, T, t >= f_begin, F, S, pin,
                                                               pxin, pout, pxout, have_prev, P);
     };

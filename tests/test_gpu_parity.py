@@ -108,26 +108,28 @@ def test_each_tile_height_and_path(w, h, th, bpc, monkeypatch):
     assert np.array_equal(blur, last)
 
 
+@pytest.mark.parametrize("bpc", [8, 10, 12])
 @pytest.mark.parametrize("moments", [False, True])
 @pytest.mark.parametrize("th", ["12", "16", "20"])
 @pytest.mark.parametrize("w,h", PATH_SIZES, ids=[f"{w}x{h}" for w, h in PATH_SIZES])
-def test_one_frame_launches_each_tile_height_and_path(w, h, th, moments, monkeypatch):
-    """8-bit frames submitted one at a time run the one-frame kernels, which load the previous
-    launch's blurred tile behind the frame's own: every tile height, the fast and the generic
-    path, with and without moments, ragged row tiles, and frames after a batch and a reset."""
+def test_one_frame_launches_each_tile_height_and_path(w, h, th, moments, bpc, monkeypatch):
+    """Frames submitted one at a time: at 8 bits the one-frame kernels, which load the previous
+    launch's blurred tile behind the frame's own; at 10 and 12 bits the batch kernels with one
+    frame. Every tile height, the fast and the generic path, with and without moments, ragged row
+    tiles, and frames after a batch and a reset."""
     monkeypatch.setenv("IIR_ROWS_PER_TILE", th)
     f = 4
-    clip = synth.random_clip(w, h, 8, f, seed=3 * w + h + int(th), kind="uniform")
+    clip = synth.random_clip(w, h, bpc, f, seed=3 * w + h + int(th) + bpc, kind="uniform")
     ref, dist = _dev(clip)
     want, want_hm, last = _oracle(clip, last=True)
     if moments:  # the sums, then the sums of squares, of the reference and distorted luma
         mom = np.zeros((f, 4), np.uint64)
         for t in range(f):
-            (r1, r2), (d1, d2) = (oracle.moments(c[0][t], 8) for c in (clip.ref, clip.dist))
+            (r1, r2), (d1, d2) = (oracle.moments(c[0][t], bpc) for c in (clip.ref, clip.dist))
             mom[t] = (r1, d1, r2, d2)
         want = np.concatenate([np.asarray(want, np.uint64), mom], axis=1)
-    _say("one-frame", w, h, th, moments)
-    with iir.Context(w, h, 8, max_batch=f, moments=moments) as ctx:
+    _say("one-frame", w, h, th, moments, bpc)
+    with iir.Context(w, h, bpc, max_batch=f, moments=moments) as ctx:
         assert ctx.geometry()["rows_per_tile"] == int(th)
         for t in range(f):
             ctx.submit([p[t] for p in ref], [p[t] for p in dist])

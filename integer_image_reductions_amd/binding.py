@@ -301,14 +301,7 @@ class Context:
         rc = self._lib.iir_collect(self._h, out, n_cap, ctypes.byref(got))
         if len(self._keep) > 64:
             self._keep = self._keep[-64:]
-        if rc == IIR_ERANGE:  # the results were returned all the same
-            try:
-                _check(rc, "iir_collect")
-            except IIRError as e:
-                e.results = self._unpack(out, got.value)
-                raise
-        _check(rc, "iir_collect")
-        return self._unpack(out, got.value)
+        return self._results_or_raise(rc, "iir_collect", out, got.value)
 
     def run_clip(self, ref, dist):
         """Submit a clip and wait for its sums; same return as collect()."""
@@ -318,13 +311,18 @@ class Context:
             raise ValueError("ref and dist have different frame counts")
         out = (Result * n)()
         rc = self._lib.iir_run_clip(self._h, fr, fd, n, out)
+        return self._results_or_raise(rc, "iir_run_clip", out, n)
+
+    def _results_or_raise(self, rc: int, func: str, out, n: int):
+        """The n results in `out`, or IIRError; IIR_ERANGE still returned them, so that error
+        carries them as `results`."""
         if rc == IIR_ERANGE:
             try:
-                _check(rc, "iir_run_clip")
+                _check(rc, func)
             except IIRError as e:
                 e.results = self._unpack(out, n)
                 raise
-        _check(rc, "iir_run_clip")
+        _check(rc, func)
         return self._unpack(out, n)
 
     def reset(self):

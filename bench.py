@@ -20,7 +20,8 @@ bandwidth against the read ceiling (skip with --no-probe).
 streaming: the same frames submitted one pair per call (one launch per frame, the motion state
 crossing launches through the device ring): frames/s of a context without events, and the
 kernel time per launch from a second context with an event pair per launch (skip with
---no-streaming). Not the headline value, which is the batch of 50.
+--no-streaming); `coalesced` is the same with iir_set_coalesce recording 8 pairs per launch. Not
+the headline value, which is the batch of 50.
 --traffic-from turns two rocprofv3 counter-collection CSVs of `bench.py --probe` runs (one with
 --pmc FETCH_SIZE, one with --pmc WRITE_SIZE) into profiles/frames_kernel_<workload>_traffic.json:
 each counter's mean KiB per main-kernel dispatch, scaled by what the same counter reads for the
@@ -310,9 +311,9 @@ def streaming(ref, dist, clip, moments: bool, motion_v2: bool, rounds: int = 6) 
     F = clip.frames
     group = min(F, 64)  # a context holds at most 64 pending submissions
 
-    def passes(timing: bool):
+    def passes(timing: bool, coalesce: int = 1):
         ctx = iir.Context(clip.width, clip.height, clip.bpc, max_batch=group, timing=timing,
-                          moments=moments, motion_v2=motion_v2)
+                          moments=moments, motion_v2=motion_v2, coalesce=coalesce)
         frames = [ctx.prepare_clip(tuple(p[t:t + 1] for p in ref),
                                    tuple(p[t:t + 1] for p in dist)) for t in range(F)]
 
@@ -337,11 +338,17 @@ def streaming(ref, dist, clip, moments: bool, motion_v2: bool, rounds: int = 6) 
 
     fps, _ = passes(False)
     fps_timed, (launches, total_ms) = passes(True)
+    coalesce = min(8, group)
+    fps_coalesced, _ = passes(False, coalesce)
     kernel_us = 1e3 * total_ms / max(launches, 1)
     alg = algorithmic_bytes(clip.width, clip.height, clip.bpc, 1, motion_v2)
     return {"frames_per_s": fps, "us_per_frame": 1e6 / fps,
             "kernel_us_per_launch": kernel_us, "launches": launches,
             "frames_per_s_with_events": fps_timed,
+            "coalesced": {"frames_per_launch": coalesce, "frames_per_s": fps_coalesced,
+                          "us_per_frame": 1e6 / fps_coalesced,
+                          "mode": "the same one-pair submissions with iir_set_coalesce: "
+                                  f"{coalesce} recorded pairs per launch"},
             "algorithmic_bytes_per_launch": alg,
             "achieved_GBps": alg / (kernel_us * 1e-6) / 1e9,
             "mode": f"one frame pair per submission, {group} submissions then one collect, "

@@ -198,6 +198,21 @@ IIR_API int iir_create(const iir_config *cfg, int32_t device, void *hip_stream, 
 IIR_API int iir_submit(iir_ctx *ctx, const iir_frame *ref, const iir_frame *dist);
 
 /*
+ * Opt-in coalescing of one-frame submissions, for callers that can wait for a result until a few
+ * more frames have been submitted. With frames = K > 1, iir_submit records the frame pair's
+ * descriptors on the host and enqueues nothing until K pairs are recorded; those then go out as
+ * one launch of K frames, with the sums of K separate submissions. iir_submit_clip, iir_collect,
+ * iir_reset, iir_export_blur and iir_set_coalesce itself first enqueue whatever is recorded; a
+ * recorded frame counts as pending (iir_run_clip returns IIR_ESTATE, iir_submit IIR_EBUSY when it
+ * would not fit). The frames must stay valid until collected, as always. Default 1 (every
+ * iir_submit is its own launch, as "ADR-1380", Decision, enqueues every frame's chain on its
+ * picture's stream); K = 1 switches it off again. A launch has a fixed cost beside its per-frame
+ * cost, and K frames share it. Errors: IIR_EINVAL (K outside 1..min(64, max_batch)), and those of
+ * the launch that enqueues the recorded frames.
+ */
+IIR_API int iir_set_coalesce(iir_ctx *ctx, int32_t frames);
+
+/*
  * Enqueue nframes consecutive frame pairs in one launch (asynchronous). ref[t] and dist[t]
  * describe frame t; every frame of a clip must use frame 0's pitches. When every plane advances
  * by a constant byte stride from frame to frame (e.g. one (F, H, W) tensor per plane), the

@@ -89,6 +89,7 @@ SIGNATURES = [
     ("iir_aggregate_of", [ctypes.POINTER(Config), ctypes.POINTER(Result), c_i32,
                           ctypes.POINTER(Aggregate)], ctypes.c_int),
     ("iir_reset", [c_vp], ctypes.c_int),
+    ("iir_set_coalesce", [c_vp, c_i32], ctypes.c_int),
     ("iir_export_blur", [c_vp, c_vp, c_i64], ctypes.c_int),
     ("iir_kernel_time", [c_vp, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
     ("iir_kernel_stats", [c_vp, c_i32, ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double)],
@@ -184,7 +185,7 @@ class Context:
 
     def __init__(self, width: int, height: int, bpc: int, max_batch: int = 64, device=None,
                  stream=None, timing: bool = False, moments: bool = False,
-                 motion_v2: bool = False, check_range: bool = False):
+                 motion_v2: bool = False, check_range: bool = False, coalesce: int = 1):
         torch = _torch()
         lib = load_library()
         self._lib = lib
@@ -202,6 +203,9 @@ class Context:
                               ctypes.byref(h)), "iir_create")
         self._h = h
         self._keep = []  # tensors referenced by pending submissions
+        self._coalesce = 1
+        if coalesce != 1:
+            self.set_coalesce(coalesce)
 
     @property
     def width(self):
@@ -299,8 +303,10 @@ class Context:
         out = (Result * n_cap)()
         got = c_i32()
         rc = self._lib.iir_collect(self._h, out, n_cap, ctypes.byref(got))
-        if len(self._keep) > 64:
-            self._keep = self._keep[-64:]
+        # at most 64 launches stay pending, each of up to `coalesce` submissions
+        keep = 64 * max(self._coalesce, 1)
+        if len(self._keep) > keep:
+            self._keep = self._keep[-keep:]
         return self._results_or_raise(rc, "iir_collect", out, got.value)
 
     def run_clip(self, ref, dist):
@@ -327,6 +333,11 @@ class Context:
 
     def reset(self):
         _check(self._lib.iir_reset(self._h), "iir_reset")
+
+    def set_coalesce(self, frames: int):
+        """Enqueue one-frame submissions `frames` at a time as one launch (1: each on its own)."""
+        _check(self._lib.iir_set_coalesce(self._h, frames), "iir_set_coalesce")
+        self._coalesce = frames
 
     def export_blur(self):
         """The blurred reference luma of the last submitted frame, as an (H, W) uint16 tensor

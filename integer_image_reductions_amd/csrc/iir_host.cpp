@@ -132,6 +132,13 @@ struct iir_ctx {
     int sub_count = 0;   // pending submissions
     int slot_head = 0;   // next free frame slot
     int pending = 0;     // frames submitted and not yet returned
+    // iir_set_coalesce: one-frame submissions are recorded here and enqueued `coalesce` at a time
+    // as one launch (1: every submission is its own launch)
+    static constexpr int kMaxCoalesce = 64;
+    int coalesce = 1;
+    int deferred = 0;
+    iir_frame def_ref[kMaxCoalesce] = {};
+    iir_frame def_dist[kMaxCoalesce] = {};
     bool has_prev = false;            // the next frame has a previous blurred frame
     bool any_frame = false;           // ring[ring_cur] is valid
     // kernel timing of collected submissions (IIR_FLAG_TIMING)
@@ -427,7 +434,7 @@ int frame_args(const iir_ctx *c, const iir_frame *ref, const iir_frame *dist, in
     return IIR_OK;
 }
 
-int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
+int submit_now(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
 {
     if (!c)
         return fail(IIR_EINVAL, "context is NULL");
@@ -492,6 +499,58 @@ int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
     c->ring_cur ^= 1;
     c->has_prev = true;
     c->any_frame = true;
+    return IIR_OK;
+}
+
+// Enqueue the recorded one-frame submissions as one launch (their descriptors go through the
+// frame table when their planes do not advance by a constant stride). They are forgotten even if
+// the launch fails: the error is the caller's.
+int flush_deferred(iir_ctx *c)
+{
+    if (c->deferred == 0)
+        return IIR_OK;
+    const int n = c->deferred;
+    c->deferred = 0;
+    return submit_now(c, c->def_ref, c->def_dist, n);
+}
+
+bool same_pitches(const iir_frame &a, const iir_frame &b)
+{
+    for (int k = 0; k < 3; ++k)
+        if (a.plane[k].pitch != b.plane[k].pitch)
+            return false;
+    return true;
+}
+
+// One submission: a clip goes out at once (after any recorded frames); with coalescing, a single
+// frame pair is recorded, and the record goes out when it holds `coalesce` frames. A frame whose
+// pitches differ from the recorded ones (one launch takes one set of pitches), or that would not
+// fit beside them in the result slots, sends the record out first.
+int submit(iir_ctx *c, const iir_frame *ref, const iir_frame *dist, int n)
+{
+    if (!c)
+        return fail(IIR_EINVAL, "context is NULL");
+    if (n != 1 || c->coalesce <= 1) {
+        const int rc = flush_deferred(c);
+        return rc != IIR_OK ? rc : submit_now(c, ref, dist, n);
+    }
+    int rc = check_frames(c, ref, dist, 1);
+    if (rc != IIR_OK)
+        return rc;
+    if (c->deferred > 0 && (!same_pitches(c->def_ref[0], ref[0]) ||
+                            !same_pitches(c->def_dist[0], dist[0]) ||
+                            reserve_slots(c, c->deferred + 1) < 0)) {
+        rc = flush_deferred(c);
+        if (rc != IIR_OK)
+            return rc;
+    }
+    if (reserve_slots(c, c->deferred + 1) < 0)
+        return fail(IIR_EBUSY, "%d frames in %d submissions pending; one more does not fit "
+                    "(max_batch %d)", c->pending, c->sub_count, c->cfg.max_batch);
+    c->def_ref[c->deferred] = ref[0];
+    c->def_dist[c->deferred] = dist[0];
+    if (++c->deferred == c->coalesce)
+        return flush_deferred(c);
     return IIR_OK;
 }
 
@@ -631,6 +690,9 @@ IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_o
     if (!ctx || !out || !n_out || max < 0)
         return fail(IIR_EINVAL, "bad collect arguments");
     *n_out = 0;
+    const int frc = flush_deferred(ctx);
+    if (frc != IIR_OK)
+        return frc;
     const int n = std::min(max, ctx->pending);
     if (n == 0)
         return IIR_OK;
@@ -715,9 +777,9 @@ IIR_API int iir_run_clip(iir_ctx *ctx, const iir_frame *ref, const iir_frame *di
 {
     if (!ctx || !out)
         return fail(IIR_EINVAL, "context or out is NULL");
-    if (ctx->pending != 0)
+    if (ctx->pending != 0 || ctx->deferred != 0)
         return fail(IIR_ESTATE, "iir_run_clip needs an empty queue (%d results pending)",
-                    ctx->pending);
+                    ctx->pending + ctx->deferred);
     int rc = submit(ctx, ref, dist, nframes);
     if (rc != IIR_OK)
         return rc;
@@ -870,8 +932,25 @@ IIR_API int iir_reset(iir_ctx *ctx)
 {
     if (!ctx)
         return fail(IIR_EINVAL, "context is NULL");
+    const int rc = flush_deferred(ctx);  // recorded frames still follow the frames before them
+    if (rc != IIR_OK)
+        return rc;
     ctx->has_prev = false;
     ctx->any_frame = false;
+    return IIR_OK;
+}
+
+IIR_API int iir_set_coalesce(iir_ctx *ctx, int32_t frames)
+{
+    if (!ctx)
+        return fail(IIR_EINVAL, "context is NULL");
+    const int most = std::min(iir_ctx::kMaxCoalesce, ctx->cfg.max_batch);
+    if (frames < 1 || frames > most)
+        return fail(IIR_EINVAL, "coalesce %d outside 1..%d", frames, most);
+    const int rc = flush_deferred(ctx);
+    if (rc != IIR_OK)
+        return rc;
+    ctx->coalesce = frames;
     return IIR_OK;
 }
 
@@ -881,6 +960,9 @@ IIR_API int iir_export_blur(iir_ctx *ctx, void *dst, int64_t pitch)
         return fail(IIR_EINVAL, "context or dst is NULL");
     if (pitch < 2 * (int64_t)ctx->cfg.width || (pitch % 4) || ((uintptr_t)dst % 4))
         return fail(IIR_EINVAL, "pitch %lld: needs >= 2*W and 4-byte alignment", (long long)pitch);
+    const int rc = flush_deferred(ctx);
+    if (rc != IIR_OK)
+        return rc;
     if (!ctx->any_frame)
         return fail(IIR_ESTATE, "no frame submitted since create or reset");
     if (ctx->v2)

@@ -75,6 +75,7 @@ def test_null_context_calls(lib):
     assert lib.iir_collect(None, out, 1, ctypes.byref(n)) == B.IIR_EINVAL
     assert lib.iir_run_clip(None, ctypes.byref(f), ctypes.byref(f), 1, out) == B.IIR_EINVAL
     assert lib.iir_reset(None) == B.IIR_EINVAL
+    assert lib.iir_set_coalesce(None, 2) == B.IIR_EINVAL
     assert lib.iir_export_blur(None, None, 0) == B.IIR_EINVAL
     assert lib.iir_kernel_time(None, ctypes.byref(ctypes.c_float())) == B.IIR_EINVAL
     assert lib.iir_kernel_stats(None, 0, ctypes.byref(ctypes.c_int64()),

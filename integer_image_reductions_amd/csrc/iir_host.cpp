@@ -728,7 +728,7 @@ IIR_API int iir_collect(iir_ctx *ctx, iir_result *out, int32_t max, int32_t *n_o
             if (code && t >= sub.taken && t < sub.taken + take) {
                 static const char *const kPlanes[6] = {"ref Y", "ref U", "ref V",
                                                        "dist Y", "dist U", "dist V"};
-                range_rc = fail(IIR_ERANGE, "result %d (frame %d of its submission): %s holds a "
+                range_rc = fail(IIR_ERANGE, "result %d (frame %d of its launch): %s holds a "
                                 "sample >= 2^%d", got + t - sub.taken, t,
                                 kPlanes[(code - 1) % 6], ctx->cfg.bpc);
             }

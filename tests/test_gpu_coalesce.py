@@ -136,3 +136,24 @@ def test_dispatches_per_coalesced_launch():
     assert sum("frames_kernel" in n for n in names) == 3, names
     want, want_hm = _want(synth.Clip("c1", clip.width, clip.height, 8, clip.ref, clip.dist))
     assert np.array_equal(sums, want) and list(hm) == want_hm
+
+
+def test_range_check_names_the_result_across_coalesced_launches():
+    """IIR_FLAG_CHECK_RANGE with coalescing: the error names the collected result that held the
+    sample, whichever launch carried it."""
+    w, h, f = 96, 20, 7
+    clip = synth.random_clip(w, h, 10, f, seed=13)
+    arrs = [np.array(a) for a in clip.ref + clip.dist]
+    arrs[3][5, 2, 7] = 1024  # dist Y of frame 5, carried by the second launch of 4
+    ref, dist = iir.upload_planes(arrs[:3]), iir.upload_planes(arrs[3:])
+    _say("coalesce range")
+    with iir.Context(w, h, 10, max_batch=8, coalesce=4, check_range=True) as ctx:
+        for t in range(f):
+            ctx.submit([p[t] for p in ref], [p[t] for p in dist])
+        with pytest.raises(iir.IIRError) as ei:
+            ctx.collect()
+    assert ei.value.code == iir.IIR_ERANGE
+    assert "result 5 (frame 1 of its launch): dist Y" in str(ei.value)
+    sums, hm = ei.value.results
+    want, _ = _want(clip)
+    assert len(sums) == f and np.array_equal(sums[:5], want[:5])

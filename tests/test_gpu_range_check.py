@@ -75,7 +75,7 @@ def test_one_bad_sample_is_named(plane, bpc):
             ctx.run_clip(ref, dist)
         e = ei.value
         assert e.code == iir.IIR_ERANGE
-        assert f"frame {bad_t} of its submission" in str(e) and PLANES[plane] in str(e)
+        assert f"frame {bad_t} of its launch" in str(e) and PLANES[plane] in str(e)
         sums, hm = e.results
         assert sums.shape[0] == f
         # frames before the bad one are untouched by it
@@ -121,7 +121,7 @@ def test_streaming_names_the_right_result_and_later_frames_pass():
         with pytest.raises(iir.IIRError) as ei:
             ctx.collect()
         assert ei.value.code == iir.IIR_ERANGE
-        assert "result 1 (frame 0 of its submission): dist U" in str(ei.value)
+        assert "result 1 (frame 0 of its launch): dist U" in str(ei.value)
         sums, hm = ei.value.results
         assert sums.shape[0] == f - 2 and np.array_equal(sums[0], want[2])
 
@@ -142,7 +142,7 @@ def test_frame_table_path_is_checked():
         ctx.submit_frames(rf, df)
         with pytest.raises(iir.IIRError) as ei:
             ctx.collect()
-    assert ei.value.code == iir.IIR_ERANGE and "frame 1 of its submission): dist V" in str(ei.value)
+    assert ei.value.code == iir.IIR_ERANGE and "frame 1 of its launch): dist V" in str(ei.value)
 
 
 @pytest.mark.parametrize("bpc", [8, 10, 16])

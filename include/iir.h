@@ -85,7 +85,8 @@ enum {
  * bits every stored value is a valid sample and nothing runs. iir_collect then returns IIR_ERANGE
  * when a frame it returns held a sample >= 2^bpc, after writing all of its results as usual
  * (those frames' sums are unspecified, and so is the motion state after them: call iir_reset);
- * iir_last_error names the result, the frame within its launch, and the plane. Not available in iir_run_clip_static (IIR_EINVAL).
+ * iir_last_error names the result, the frame within its launch, and the plane. Not available
+ * in iir_run_clip_static (IIR_EINVAL).
  */
 #define IIR_FLAG_CHECK_RANGE 8u
 

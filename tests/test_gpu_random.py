@@ -1,8 +1,9 @@
 """GPU parity on seeded random configurations, through the C ABI.
 
 Each case draws a frame size (3 to 1400 columns, 3 to 300 rows), a bit depth (8, 9, 10, 12, 15 or
-16), a clip length, the moments and motion v2 flags, a sample pattern and a submission pattern (one
-launch, one frame pair per submission, or two launches), and compares every sum with the oracle's.
+16), a clip length, the moments, motion v2 and input-range-check flags, a sample pattern, a
+submission pattern (one launch, one frame pair per submission, or two launches) and a coalescing
+factor, and compares every sum with the oracle's.
 The draws are fixed by the seed, so a failure names a reproducible case.
 """
 import random
@@ -28,7 +29,8 @@ def _cases(seed: int, n: int):
                         moments=rng.random() < 0.4, v2=rng.random() < 0.3,
                         mode=rng.choice(["batch", "stream", "split"]),
                         kind=rng.choice(["uniform", "extreme", "impulse", "checker"]),
-                        seed=rng.randint(0, 10**6)))
+                        seed=rng.randint(0, 10**6), coalesce=rng.choice([1, 1, 2, 3, 5]),
+                        check=rng.random() < 0.3))
     return out
 
 
@@ -42,7 +44,8 @@ def test_random_configuration(c):
     w, h, bpc, f = c["w"], c["h"], c["bpc"], c["f"]
     clip = synth.random_clip(w, h, bpc, f, seed=c["seed"], kind=c["kind"])
     ref, dist = iir.upload_planes(clip.ref), iir.upload_planes(clip.dist)
-    with iir.Context(w, h, bpc, max_batch=8, moments=c["moments"], motion_v2=c["v2"]) as ctx:
+    with iir.Context(w, h, bpc, max_batch=8, moments=c["moments"], motion_v2=c["v2"],
+                     coalesce=c["coalesce"], check_range=c["check"]) as ctx:
         if c["mode"] == "batch":
             sums, hm = ctx.run_clip(ref, dist)
         elif c["mode"] == "stream":

@@ -293,7 +293,10 @@ IIR_API int iir_kernel_time(iir_ctx *ctx, float *ms);
 IIR_API int iir_kernel_stats(iir_ctx *ctx, int32_t reset, int64_t *launches, double *total_ms);
 
 /* Launch geometry chosen at create from the device's compute units, for reports and tests
-   ("ADR-1226", Decision: the launch is sized by the processor count). */
+   ("ADR-1226", Decision: the launch is sized by the processor count). Three environment variables,
+   read at create, override the choice for tuning and tests: IIR_ROWS_PER_TILE (12, 16 or 20),
+   IIR_TARGET_WAVES (a cap on the wavefronts a launch's time chunks may fill) and IIR_MIN_CHUNK
+   (the fewest frames per time chunk, default 2). */
 typedef struct iir_geometry {
     int32_t rows_per_tile;     /* output luma rows per wavefront tile */
     int32_t lanes_out;         /* output lanes per wavefront (4 luma columns each): 64 */

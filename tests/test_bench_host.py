@@ -86,3 +86,16 @@ def test_kernel_hash_ignores_comments_only():
     assert bench._code_only(base) == bench._code_only(base.replace("/* block", "/* other"))
     assert bench._code_only(base) == bench._code_only(base.replace("    return", "  return"))
     assert bench._code_only(base) != bench._code_only(base.replace("a + 1", "a + 2"))
+
+
+def test_committed_traffic_summaries_match_the_kernel_code():
+    """Every committed counter summary was taken on the frames kernel's current code, so the
+    benchmark line reports its traffic (a stale summary would make it report null)."""
+    import glob
+    paths = sorted(glob.glob(os.path.join(bench.ROOT, "profiles", "frames_kernel_*_traffic.json")))
+    assert paths
+    for p in paths:
+        with open(p) as f:
+            d = json.load(f)
+        assert d["kernel_sha256"] == bench.kernel_sha(), os.path.basename(p)
+        assert 1.0 <= d["hbm_bytes_per_launch"] / d["algorithmic_bytes_per_launch"] < 1.5, p

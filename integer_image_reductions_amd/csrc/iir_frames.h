@@ -27,8 +27,7 @@
 //     per column, v_dot2_u32_u16 applies two taps per instruction with the rounding constant as
 //     the accumulator, and v_perm_b32 extracts the 16-bit result of a byte-aligned shift. 10-bit
 //     input is pre-scaled by 64 so its vertical shift (10) also becomes a 16-bit byte shift.
-//   * SAD on packed blurred pairs: |a - b| = a + b - 2 min(a, b), with sum(b) kept from the
-//     previous frame, so each pair costs one v_pk_min_u16 and two v_dot2 accumulations.
+//   * SAD on packed blurred pairs: one v_sad_u16 adds both columns' |a - b| to the lane's sum.
 //   * SSE: 8-bit as sum(r^2 + d^2) - 2 sum(r d) with v_dot4_u32_u8 (exact in 32-bit modular
 //     arithmetic, since the true per-lane value is far below 2^32); 10-bit as v_pk_sub_i16 then
 //     v_dot2_i32_i16 of the difference with itself.
@@ -89,10 +88,11 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-__device__ __forceinline__ uint32_t pkmin(uint32_t a, uint32_t b)
+// acc + |a.lo - b.lo| + |a.hi - b.hi| of the unsigned 16-bit halves, in one instruction
+// (v_sad_u16)
+__device__ __forceinline__ uint32_t sad16x2(uint32_t a, uint32_t b, uint32_t acc)
 {
-    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
-                                                                  __builtin_bit_cast(u16x2, b)));
+    return __builtin_amdgcn_sad_u16(a, b, acc);
 }
 
 // lane i receives lane i-1's value (wave_shr:1); lane 0 receives 0 (bound_ctrl, so no register
@@ -487,7 +487,7 @@ struct Tile {
     int rows_valid;              // scalar: output rows of the tile inside the frame
     int lane;
     uint32_t luma_off;           // byte offset of the lane's 4 luma samples in a row
-    uint32_t w0, w1;             // 16-bit weights of the lane's blurred pairs (1 = valid column)
+    uint32_t m0, m1;             // 16-bit masks of the lane's blurred pairs (0xffff = valid)
     bool out_lane;               // lane owns output columns
     uint32_t coff[4];            // byte offsets of the lane's chroma dword in ref U, dist U,
                                  // ref V, dist V (column, plus one row for the upper half-wave
@@ -867,7 +867,7 @@ __device__ __forceinline__ void push_frame_sums(const KernelArgs &a, const Tile 
     const Sq<BPC> zero = 0;
     if constexpr (MOM && BPC == 8) {
         // every 8-bit total fits 32 bits: at most 20 rows x 4 samples x 255^2 per lane, x 64 lanes
-        const uint32_t x[kMaxSums] = {sad,
+        const uint32_t x[kMaxSums] = {T.out_lane ? sad : 0u,
                                       T.out_lane ? ey : 0u,
                                       T.c_on ? eu : 0u,
                                       T.c_on ? ev : 0u,
@@ -880,7 +880,7 @@ __device__ __forceinline__ void push_frame_sums(const KernelArgs &a, const Tile 
         push_sums(a, P, T.lane, sums);
     } else if constexpr (MOM) {
         const unsigned long long sums[kMaxSums] = {
-            wave_sum(sad),
+            wave_sum(T.out_lane ? sad : 0u),
             wave_sum_sq(T.out_lane ? ey : zero),
             wave_sum_sq(T.c_on ? eu : zero),
             wave_sum_sq(T.c_on ? ev : zero),
@@ -890,7 +890,7 @@ __device__ __forceinline__ void push_frame_sums(const KernelArgs &a, const Tile 
             wave_sum_sq(T.out_lane ? S.m2d : zero)};
         push_sums(a, P, T.lane, sums);
     } else {
-        const unsigned long long sums[kSums] = {wave_sum(sad),
+        const unsigned long long sums[kSums] = {wave_sum(T.out_lane ? sad : 0u),
                                                 wave_sum_sq(T.out_lane ? ey : zero),
                                                 wave_sum_sq(T.c_on ? eu : zero),
                                                 wave_sum_sq(T.c_on ? ev : zero)};
@@ -1115,8 +1115,7 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
                                               FrameStats<BPC> &S,
                                               const uint32_t (&prev0)[TH],
                                               const uint32_t (&prev1)[TH], uint32_t (&next0)[TH],
-                                              uint32_t (&next1)[TH], uint32_t &sum_prev,
-                                              bool &have_prev,
+                                              uint32_t (&next1)[TH], bool &have_prev,
                                               Pending<MOM ? kMaxSums : kSums> &P)
 {
     typedef typename Px<BPC>::Luma Luma;
@@ -1138,8 +1137,13 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
             chroma_sse<BPC, TH, GENERIC>(a, T, F, S.su, S.su2, S.sv, S.sv2);
     }
 
-    // blur, SAD against the previous blurred tile, and SSE of the luma rows as they go by
-    uint32_t acc_c = 0, acc_min = 0;
+    // blur, SAD against the previous blurred tile, and SSE of the luma rows as they go by. A lane
+    // whose columns all lie right of the frame drops its sums at the reduction. The generic path
+    // (which also has lanes with only some columns inside, and rows below the frame) clears every
+    // blurred value it keeps outside the frame, so the previous tile's are clear too and those
+    // places add nothing to the SAD; a per-row branch around the SAD instead measured 60 more
+    // VGPRs and spilled at 20 rows.
+    uint32_t sad = 0;
 #pragma unroll
     for (int i = 0; i < TH; ++i) {
         uint32_t pa[4], pb[4], pc[4];
@@ -1165,11 +1169,14 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
         const uint32_t h1 = dot2u(q1, T10, dot2u(q0, T12, dot2u(ql, Tz0, 32768u)));
         const uint32_t h2 = dot2u(qr, T0z, dot2u(q1, T21, dot2u(q0, T01, 32768u)));
         const uint32_t h3 = dot2u(qr, T10, dot2u(q1, T12, dot2u(q0, Tz0, 32768u)));
-        const uint32_t c0 = perm(h1, h0, 0x07060302u);  // Bl of columns c, c+1
-        const uint32_t c1 = perm(h3, h2, 0x07060302u);  // Bl of columns c+2, c+3
+        uint32_t c0 = perm(h1, h0, 0x07060302u);  // Bl of columns c, c+1
+        uint32_t c1 = perm(h3, h2, 0x07060302u);  // Bl of columns c+2, c+3
+        if constexpr (GENERIC) {
+            c0 = i < T.rows_valid ? c0 & T.m0 : 0u;
+            c1 = i < T.rows_valid ? c1 & T.m1 : 0u;
+        }
+        sad = sad16x2(c1, prev1[i], sad16x2(c0, prev0[i], sad));
         if (!GENERIC || i < T.rows_valid) {
-            acc_c = dot2u(c1, T.w1, dot2u(c0, T.w0, acc_c));
-            acc_min = dot2u(pkmin(c1, prev1[i]), T.w1, dot2u(pkmin(c0, prev0[i]), T.w0, acc_min));
             // with moments, staged frames always hold distorted rows (staged_frame's ALL_DIST)
             if ((ROWSTAGE && MOM) || accumulate)
                 luma_row_stats<BPC, TH, GENERIC, MOM>(T, F, i, S);
@@ -1179,8 +1186,7 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
     }
 
     if (accumulate)
-        push_frame_sums<BPC, MOM>(a, T, P, have_prev ? acc_c + sum_prev - 2u * acc_min : 0u, S);
-    sum_prev = acc_c;
+        push_frame_sums<BPC, MOM>(a, T, P, have_prev ? sad : 0u, S);
     have_prev = true;
 }
 
@@ -1284,10 +1290,10 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
                 if constexpr (GENERIC) {
                     // a column outside the frame counts as F = 0
                     if (i < T.rows_valid) {
-                        sad = add_absdiff((T.w0 & 1u) ? f[0] : kV2Zero, kV2Zero, sad);
-                        sad = add_absdiff((T.w0 >> 16) ? f[1] : kV2Zero, kV2Zero, sad);
-                        sad = add_absdiff((T.w1 & 1u) ? f[2] : kV2Zero, kV2Zero, sad);
-                        sad = add_absdiff((T.w1 >> 16) ? f[3] : kV2Zero, kV2Zero, sad);
+                        sad = add_absdiff((T.m0 & 1u) ? f[0] : kV2Zero, kV2Zero, sad);
+                        sad = add_absdiff((T.m0 >> 16) ? f[1] : kV2Zero, kV2Zero, sad);
+                        sad = add_absdiff((T.m1 & 1u) ? f[2] : kV2Zero, kV2Zero, sad);
+                        sad = add_absdiff((T.m1 >> 16) ? f[3] : kV2Zero, kV2Zero, sad);
                     }
                 } else {
 #pragma unroll
@@ -1297,8 +1303,6 @@ __device__ __forceinline__ void compute_frame_v2(const KernelArgs &a, const Tile
                 if (!GENERIC || i < T.rows_valid)
                     luma_row_stats<BPC, TH, GENERIC, MOM>(T, F, i, S);
             }
-            if constexpr (!GENERIC)
-                sad = T.out_lane ? sad : 0u;
         } else {
 #pragma unroll
             for (int i = 0; i < TH; ++i)
@@ -1392,8 +1396,7 @@ __device__ __forceinline__ void staged_start(const KernelArgs &a, const Tile &T,
         load_frame_staged<TH>(a, T, O, min(t0 + 1, f_end - 1), true, lds + Stage<TH>::kRows);
 }
 
-// The previous launch's blurred tile of this wavefront (its rows in the tiled state plane), and
-// its sum over the valid columns and rows (the SAD's "sum of the previous frame").
+// The previous launch's blurred tile of this wavefront (its rows in the tiled state plane).
 template <int TH>
 __device__ __forceinline__ void load_prev_tile(const KernelArgs &a, const Tile &T,
                                                uint32_t (&prev0)[TH], uint32_t (&prev1)[TH])
@@ -1407,18 +1410,6 @@ __device__ __forceinline__ void load_prev_tile(const KernelArgs &a, const Tile &
     }
 }
 
-template <int TH>
-__device__ __forceinline__ uint32_t prev_tile_sum(const Tile &T, const uint32_t (&prev0)[TH],
-                                                  const uint32_t (&prev1)[TH])
-{
-    uint32_t s = 0;
-#pragma unroll
-    for (int i = 0; i < TH; ++i)
-        if (i < T.rows_valid)
-            s = dot2u(prev1[i], T.w1, dot2u(prev0[i], T.w0, s));
-    return s;
-}
-
 // The frames of this workgroup's time chunk. Chunks after the first start by re-blurring the
 // frame before them. STAGED keeps the next frame's loads in flight while the current one is
 // computed: the loads of frame t+1 write the wave's LDS stage (no registers held), issued as soon
@@ -1427,8 +1418,8 @@ __device__ __forceinline__ uint32_t prev_tile_sum(const Tile &T, const uint32_t 
 template <int BPC, int TH, bool GENERIC, bool STAGED, bool MOM, bool ONE = false>
 __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
                                            const StageOffsets<TH> &O, uint32_t (&prev0)[TH],
-                                           uint32_t (&prev1)[TH], uint32_t sum_prev,
-                                           bool have_prev, uint32_t (*lds)[kWave])
+                                           uint32_t (&prev1)[TH], bool have_prev,
+                                           uint32_t (*lds)[kWave])
 {
     const int f_begin = uni(T.chunk * a.chunk_len);
     const int f_end = uni(min(f_begin + a.chunk_len, a.nframes));
@@ -1448,10 +1439,8 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
             if (load_prev)
                 load_prev_tile<TH>(a, T, prev0, prev1);
         });
-        if (load_prev) {
-            sum_prev = prev_tile_sum<TH>(T, prev0, prev1);
+        if (load_prev)
             have_prev = true;
-        }
     } else if constexpr (STAGED) {
         staged_start<TH>(a, T, O, t0, f_begin, f_end, lds, C);
     }
@@ -1475,7 +1464,7 @@ __device__ __forceinline__ void frame_loop(const KernelArgs &a, const Tile &T,
                 set_prio(0u);
         }
         compute_frame<BPC, TH, GENERIC, STAGED, MOM>(a, T, t, t >= f_begin, F, S, i0, i1, o0,
-                                                     o1, sum_prev, have_prev, P);
+                                                     o1, have_prev, P);
     };
     uint32_t alt0[TH], alt1[TH];
     for (int t = t0; t < f_end; t += 2) {
@@ -1748,8 +1737,8 @@ frames_kernel(const KernelArgs a)
         T.hl_addr = lane == 0 ? 4 * 2 : 4 * lane;
         T.hr_addr = lane == kWave - 1 ? 4 * (kWave / 2 + 2) : 4 * lane;
     }
-    T.w0 = (c < W ? 1u : 0u) | (c + 1 < W ? 0x10000u : 0u);
-    T.w1 = (c + 2 < W ? 1u : 0u) | (c + 3 < W ? 0x10000u : 0u);
+    T.m0 = (c < W ? 0xffffu : 0u) | (c + 1 < W ? 0xffff0000u : 0u);
+    T.m1 = (c + 2 < W ? 0xffffu : 0u) | (c + 3 < W ? 0xffff0000u : 0u);
     T.edge_tile = T.strip == a.strips - 1 && W % kStripCols != 0;
     T.mirror_right = c == W;
     // byte permutation building columns W, W+1 from W-2, W-3: staged, from the left neighbour's
@@ -1901,19 +1890,9 @@ frames_kernel(const KernelArgs a)
         // previous blurred tile: from the launch before, else none (chunk 0), or re-blurred by
         // the chunk's prologue (later chunks)
         uint32_t prev0[TH], prev1[TH];
-        uint32_t sum_prev = 0;
         bool have_prev = false;
         if (!ONE && T.chunk == 0 && a.has_prev) {
-            // (loads and sums interleaved; the one-frame kernel's helpers schedule differently)
-            const uint2 *rin = reinterpret_cast<const uint2 *>(a.ring_in);
-#pragma unroll
-            for (int i = 0; i < TH; ++i) {
-                const uint2 v = rin[(T.tile * TH + i) * kWave + lane];
-                prev0[i] = v.x;
-                prev1[i] = v.y;
-                if (i < T.rows_valid)
-                    sum_prev = dot2u(v.y, T.w1, dot2u(v.x, T.w0, sum_prev));
-            }
+            load_prev_tile<TH>(a, T, prev0, prev1);
             have_prev = true;
         } else {
 #pragma unroll
@@ -1921,8 +1900,7 @@ frames_kernel(const KernelArgs a)
                 prev0[i] = prev1[i] = 0;
         }
 
-        frame_loop<BPC, TH, GENERIC, STAGED, MOM, ONE>(a, T, O, prev0, prev1, sum_prev,
-                                                       have_prev, stage);
+        frame_loop<BPC, TH, GENERIC, STAGED, MOM, ONE>(a, T, O, prev0, prev1, have_prev, stage);
 
         // the state stores (TH instructions) drain while the group count is in flight; they are
         // non-temporal, so the launch's end does not find 16 MB (at 4K) of them dirty in L2

@@ -122,6 +122,20 @@ __device__ __forceinline__ uint32_t from_right_or(uint32_t v, uint32_t edge)
     return (uint32_t)__builtin_amdgcn_update_dpp((int)edge, (int)v, 0x130, 0xf, 0xf, false);
 }
 
+// lane i receives lane (i + 1) mod 64's value (wave_rol:1; every lane has a source, so
+// bound_ctrl only spares the copy of an unused old value)
+__device__ __forceinline__ uint32_t rotate_down(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x134, 0xf, 0xf, true);
+}
+
+// lane i receives lane (i + 32) mod 64's value: the halves of the wave swapped
+__device__ __forceinline__ uint32_t swap_halves(uint32_t v, int lane)
+{
+    const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return lane < kWave / 2 ? h[1] : h[0];
+}
+
 // whole-sample mirror into [0, n), exact for -2 <= i <= n + 1, clamped beyond (never used there)
 __device__ __forceinline__ int mirror_clamp(int i, int n)
 {
@@ -511,6 +525,7 @@ struct Tile {
     // right frame edge inside the last strip (W % 256 != 0), fast path: the lane whose first
     // column is W loads the group before it and permutes it into the mirror image
     bool edge_tile;              // scalar: the last strip, with W inside it
+    bool cmask;                  // scalar, staged: the chroma needs its per-byte masks (cmk)
     bool mirror_right;           // lane whose first column is W: columns W, W+1 from W-2, W-3
     uint32_t msel;               // 8-bit: the byte permutation doing the above (identity else)
     // edges (generic path only)
@@ -820,7 +835,7 @@ struct FrameStats {
 };
 
 // Squared error of the staged path's chroma (16 bytes per lane per load, masked to the tile).
-template <int TH>
+template <int TH, bool MASK>
 __device__ __forceinline__ void chroma_sse_x4(const Tile &T, const ChromaX4<TH> &C,
                                               FrameStats<8> &S)
 {
@@ -828,7 +843,7 @@ __device__ __forceinline__ void chroma_sse_x4(const Tile &T, const ChromaX4<TH> 
     for (int q = 0; q < Stage<TH>::kChromaLoads; ++q)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t m = T.cmk[q][j];
+            const uint32_t m = MASK ? T.cmk[q][j] : 0xffffffffu;
             sse_chroma<8>(C.p[0][q][j] & m, C.p[1][q][j] & m, S.su, S.su2);
             sse_chroma<8>(C.p[2][q][j] & m, C.p[3][q][j] & m, S.sv, S.sv2);
         }
@@ -888,6 +903,13 @@ __device__ __forceinline__ void push_frame_sums(const KernelArgs &a, const Tile 
             wave_sum(T.out_lane ? S.m1d : 0u),
             wave_sum_sq(T.out_lane ? S.m2r : zero),
             wave_sum_sq(T.out_lane ? S.m2d : zero)};
+        push_sums(a, P, T.lane, sums);
+    } else if constexpr (BPC == 8) {
+        // the four 8-bit totals fit 32 bits too (20 rows x 4 samples x 65535 per lane for the SAD)
+        const uint32_t x[kSums] = {T.out_lane ? sad : 0u, T.out_lane ? ey : 0u,
+                                   T.c_on ? eu : 0u, T.c_on ? ev : 0u};
+        unsigned long long sums[kSums];
+        wave_sums_u32<kSums>(x, T.lane, sums);
         push_sums(a, P, T.lane, sums);
     } else {
         const unsigned long long sums[kSums] = {wave_sum(T.out_lane ? sad : 0u),
@@ -1129,6 +1151,11 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
     }
     const uint32_t shift = (uint32_t)a.shift;
     const uint32_t hv = halo_vertical<BPC>(F.HL, T.hsel, shift);
+    // Row i's halo pairs are hv of lane i + 2 (left) and lane i + 34 (right). Two copies of hv
+    // rotated one lane per row bring them to the edge lanes: lane 0 of xl holds the left pair of
+    // the current row, lane 63 of xr its right pair; each then serves as the DPP edge operand.
+    uint32_t xl = rotate_down(rotate_down(hv));
+    uint32_t xr = rotate_down(swap_halves(xl, T.lane));
 
     // SSE of the chroma tiles first, which frees their registers before the blur (the staged
     // path has already summed its chroma into S)
@@ -1158,11 +1185,12 @@ __device__ __forceinline__ void compute_frame(const KernelArgs &a, const Tile &T
             v[b] = dot2u(pc[b], T0z, dot2u(pb[b], T21, dot2u(pa[b], T01, kVRound)));
         uint32_t q0 = perm(v[1], v[0], kVSel);  // V of columns c, c+1
         uint32_t q1 = perm(v[3], v[2], kVSel);  // V of columns c+2, c+3
-        // halo V of this row: columns s-2, s-1 (lane i + 2) and e, e+1 (lane i + 34)
-        // (readlane + a broadcast move measured faster here than the ds_bpermute gather of
-        // motion v2: the staged frame's LDS is busy with its own reads)
-        const uint32_t hl = (uint32_t)__builtin_amdgcn_readlane((int)hv, i + 2);
-        const uint32_t hr = (uint32_t)__builtin_amdgcn_readlane((int)hv, i + kWave / 2 + 2);
+        // halo V of this row: columns s-2, s-1 in lane 0 of xl and e, e+1 in lane 63 of xr (a
+        // ds_bpermute gather, as in motion v2, measured slower here: the staged frame's LDS is
+        // busy with its own reads)
+        const uint32_t hl = xl, hr = xr;
+        xl = rotate_down(xl);
+        xr = rotate_down(xr);
         uint32_t ql, qr;
         neighbours<GENERIC, ROWSTAGE>(T, hl, hr, q0, q1, ql, qr);
         const uint32_t h0 = dot2u(q1, T0z, dot2u(q0, T21, dot2u(ql, T01, 32768u)));
@@ -1361,8 +1389,12 @@ __device__ __forceinline__ void staged_frame(const KernelArgs &a, const Tile &T,
         __builtin_amdgcn_s_waitcnt(0x0F70 | Stage<TH>::kDmaLoads);  // vmcnt(one luma group)
     read_stage<TH>(ALL_DIST || t >= f_begin, lds, T.lane, T.hlds, F);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before it is overwritten
-    if (t >= f_begin)
-        chroma_sse_x4<TH>(T, C, S);
+    if (t >= f_begin) {
+        if (T.cmask)
+            chroma_sse_x4<TH, true>(T, C, S);
+        else
+            chroma_sse_x4<TH, false>(T, C, S);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (t + 1 < f_end) {
         load_chroma_x4<TH>(a, T, O, t + 1, C);
@@ -1819,7 +1851,10 @@ frames_kernel(const KernelArgs a)
     if constexpr (STAGED) {
         // staged chroma: lane l reads the 16 bytes at column cs + 16 (l mod 8) of tile chroma row
         // 8q + l / 8; rows past the tile's TH / 2 or past the plane, and columns past Wc, are
-        // masked out
+        // masked out. On the fast path only the last strip's tiles (W inside them) reach past
+        // the plane, since H is a multiple of TH; with one load per plane the rows past TH / 2
+        // are whole lanes, left out of the chroma sums through c_on. So the byte masks are
+        // applied only on the generic path, on edge tiles and with two loads per plane (20 rows).
         const int c16 = cs + 16 * (lane & 7);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -1834,7 +1869,8 @@ frames_kernel(const KernelArgs a)
                 T.cmk[q][j] = row_ok ? m : 0u;
             }
         }
-        T.c_on = true;
+        T.cmask = GENERIC || T.edge_tile || Stage<TH>::kChromaLoads > 1;
+        T.c_on = T.cmask || (lane >> 3) < TH / 2;
     }
     {
         const uint32_t col = T.c_on ? (uint32_t)(ccol * B) : 0u;

@@ -20,9 +20,9 @@
 //     horizontal taps through two DPP lane shifts per row (no LDS round trip, no barrier).
 //   * The two columns left and right of the tile (horizontal halo) arrive transposed: one load
 //     per frame gives lane k the halo samples of tile row k-2 (lanes 0-31 the left side, lanes
-//     32-63 the right side), their vertical pass runs once per frame across lanes, and each row
-//     hands the result to lane 0 and lane 63 with two readlanes (motion v2, with twice the halo
-//     values, gathers them with ds_bpermute instead).
+//     32-63 the right side), their vertical pass runs once per frame across lanes, and two copies
+//     of the result rotated one lane per row bring each row's pairs to lane 0 and lane 63 (motion
+//     v2, with twice the halo values, gathers them with ds_bpermute instead).
 //   * The separable filter runs on packed 16-bit pairs: v_perm_b32 builds (row r, row r+1) pairs
 //     per column, v_dot2_u32_u16 applies two taps per instruction with the rounding constant as
 //     the accumulator, and v_perm_b32 extracts the 16-bit result of a byte-aligned shift. 10-bit

@@ -1884,17 +1884,23 @@ frames_kernel(const KernelArgs a)
     // staged: per-lane offsets of the 16-byte loads (16 lanes per luma row, 8 per chroma row)
     StageOffsets<TH> O;
     if constexpr (STAGED) {
+        // a 16-byte group wholly right of the frame (the last strip of a width that is not a
+        // multiple of 256) loads the strip's first group instead: the same bytes as another lane
+        // of the row, so the request coalesces and no row padding is fetched from HBM. Those
+        // columns feed no output (the right-edge mirror takes the lane to the left's group).
+        const int g = s + 16 * (lane & 15), gc = s / 2 + 16 * (lane & 7);
+        const uint32_t col = (uint32_t)(g < W ? g : s);
+        const uint32_t ccol16 = (uint32_t)(gc < a.Wc ? gc : s / 2);
 #pragma unroll
         for (int q = 0; q < Stage<TH>::kRefLoads; ++q) {
             const int row = mirror_clamp(T.r0 - 2 + 4 * q + (lane >> 4), H);
-            O.ref[q] = (uint32_t)(s + 16 * (lane & 15)) + (uint32_t)row * (uint32_t)a.pitch[0];
+            O.ref[q] = col + (uint32_t)row * (uint32_t)a.pitch[0];
         }
-        O.dist = (uint32_t)(s + 16 * (lane & 15)) + (uint32_t)(lane >> 4) * (uint32_t)a.pitch[3];
+        O.dist = col + (uint32_t)(lane >> 4) * (uint32_t)a.pitch[3];
         const int pk[4] = {1, 4, 2, 5};
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            O.chroma[p] = (uint32_t)(s / 2 + 16 * (lane & 7)) +
-                          (uint32_t)(lane >> 3) * (uint32_t)a.pitch[pk[p]];
+            O.chroma[p] = ccol16 + (uint32_t)(lane >> 3) * (uint32_t)a.pitch[pk[p]];
     }
 
     if constexpr (V2) {

@@ -276,6 +276,30 @@ def test_errors_on_device():
         assert e.value.code == -1
 
 
+def test_empty_submissions():
+    """Zero frames is an argument error and launches nothing; a collect with nothing pending
+    returns no rows; the context then works as usual."""
+    w, h = 64, 32
+    clip = synth.random_clip(w, h, 8, 2, seed=3)
+    ref, dist = _dev(clip)
+    empty = tuple(p[:0] for p in ref), tuple(p[:0] for p in dist)
+    _say("empty submissions")
+    with iir.Context(w, h, 8, max_batch=4) as ctx:
+        sums, hm = ctx.collect()
+        assert len(sums) == 0 and len(hm) == 0
+        for call in (ctx.submit_clip, ctx.run_clip):
+            with pytest.raises(iir.IIRError) as e:
+                call(*empty)
+            assert e.value.code == iir.binding.IIR_EINVAL
+        sums, hm = ctx.collect()
+        assert len(sums) == 0
+        sums, hm = ctx.run_clip(ref, dist)
+    with pytest.raises(iir.IIRError) as e:
+        iir.run_clip_static(w, h, 8, *empty)
+    assert e.value.code == iir.binding.IIR_EINVAL
+    want, want_hm = _oracle(clip)
+    _check(clip, sums, hm, want, want_hm, "after empty submissions")
+
 def _score_check(clip, sums, hm):
     for t in range(len(sums)):
         a = iir.scores(clip.width, clip.height, clip.bpc, sums[t], hm[t])

@@ -386,7 +386,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by frames with no collective; see the design notes)",
+              "(the path would shard by frames: each GPU a run of frames plus the one before "
+              "it, with no collective)",
               file=sys.stderr)
         sys.exit(2)
 
